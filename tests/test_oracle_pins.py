@@ -1,0 +1,292 @@
+"""Pins for the CPU oracle: checks against facts fixed by the pages and by
+mathematics, never against the oracle's own formulas retyped.
+
+Every pin names the mistake it is meant to catch.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from had_workloads import make_inputs
+
+
+# ---------------------------------------------------------------- sigma ----
+def test_sigma_textbook_example():
+    # Population std of 2,4,4,4,5,5,7,9 is exactly 2 (sample std would be
+    # 2.138...): catches ddof=1 and a missing square root.
+    assert oracle.sigma(np.array([2, 4, 4, 4, 5, 5, 7, 9], dtype=np.float32)) == 2.0
+
+
+def test_sigma_two_points_and_constant():
+    # sigma{a, b} = |a - b| / 2; a constant tensor has sigma 0.
+    assert oracle.sigma(np.array([[-3.0], [5.0]])) == pytest.approx(4.0, rel=1e-15)
+    assert oracle.sigma(np.full((3, 7), 2.5)) == 0.0
+
+
+def test_sigma_invariances():
+    # sigma(aX) = |a| sigma(X); sigma(X + c) = sigma(X) catches a missing
+    # mean subtraction (root mean square instead of std).
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((4, 9, 13))
+    s = oracle.sigma(x)
+    assert oracle.sigma(-3.0 * x) == pytest.approx(3.0 * s, rel=1e-12)
+    assert oracle.sigma(x + 17.0) == pytest.approx(s, rel=1e-10)
+
+
+def test_sigma_rejects_nan():
+    with pytest.raises(ValueError):
+        oracle.sigma(np.array([1.0, np.nan]))
+
+
+# ------------------------------------------------------------- binarize ----
+def test_binarize_special_values():
+    # x >= 0 -> +1: both zeros give +1 (value compare, not the sign bit),
+    # infinities keep their sign.
+    x = np.array([-2.0, -0.0, 0.0, 3.0, np.inf, -np.inf, -1e-30, 1e-30], dtype=np.float32)
+    assert oracle.binarize(x).tolist() == [-1, 1, 1, 1, 1, -1, -1, 1]
+
+
+def test_binarize_rejects_nan():
+    with pytest.raises(ValueError):
+        oracle.binarize(np.array([0.0, np.nan]))
+
+
+def test_binarize_is_sigma_invariant():
+    # The standardization divides by sigma > 0 and cannot change a sign.
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 40)).astype(np.float32)
+    s = oracle.sigma(x)
+    assert np.array_equal(oracle.binarize(x / s), oracle.binarize(x))
+    assert np.array_equal(oracle.binarize(x * 1e-20), oracle.binarize(x))
+
+
+# ----------------------------------------------------------------- pack ----
+def _pack_bruteforce(row):
+    """Python-int packing, one bit at a time (independent of numpy shifts)."""
+    d = len(row)
+    words = []
+    for w in range((d + 31) // 32):
+        value = 0
+        for c in range(32 * w, min(d, 32 * w + 32)):
+            if row[c] == -1:
+                value += 2 ** (c - 32 * w)
+        words.append(value)
+    return words
+
+
+@pytest.mark.parametrize("d", [1, 5, 31, 32, 33, 40, 64, 100, 128, 256])
+def test_pack_matches_bruteforce(d):
+    rng = np.random.default_rng(d)
+    b = np.where(rng.random((7, d)) < 0.5, -1, 1).astype(np.int8)
+    packed = oracle.pack_bits(b)
+    assert packed.shape == (7, (d + 31) // 32)
+    for r in range(7):
+        assert [int(x) for x in packed[r]] == _pack_bruteforce(b[r].tolist())
+    assert np.array_equal(oracle.unpack_bits(packed, d), b)
+
+
+def test_pack_hand_examples():
+    # d=5: signs [-,+,-,-,+] -> bits 0,2,3 -> 13.  d=33: element 32 is bit 0
+    # of word 1.  Catches reversed bit order and flipped polarity.
+    assert oracle.pack_bits(np.array([-1, 1, -1, -1, 1])).tolist() == [13]
+    b = np.ones(33, dtype=np.int8)
+    b[32] = -1
+    b[0] = -1
+    assert oracle.pack_bits(b).tolist() == [1, 1]
+
+
+def test_pack_pad_bits_zero_and_negation():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 40)).astype(np.float32)
+    p = oracle.pack_bits(oracle.binarize(x))
+    assert np.all(p[:, 1] < (1 << 8))  # 8 data bits in the last word
+    pn = oracle.pack_bits(oracle.binarize(-x))
+    data_mask = np.array([0xFFFFFFFF, 0xFF], dtype=np.uint32)
+    assert np.array_equal(pn, (~p) & data_mask)  # no zeros in x
+    assert np.array_equal(oracle.pack_bits(oracle.binarize(7.5 * x)), p)
+
+
+# --------------------------------------------------------------- logits ----
+@pytest.mark.parametrize("d", [1, 3, 32, 33, 64, 128])
+def test_logits_equal_xnor_popcount_identity(d):
+    # The pages' statement: the +-1 product is computed by XNOR + popcount,
+    # i.e. s = d - 2 * popcount(q XOR k).  Python-int popcount of the packed
+    # words is an independent route to the same integers.
+    rng = np.random.default_rng(100 + d)
+    bq = np.where(rng.random((9, d)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((11, d)) < 0.5, -1, 1).astype(np.int8)
+    S = oracle.logits(bq, bk)
+    pq, pk = oracle.pack_bits(bq), oracle.pack_bits(bk)
+    for i in range(9):
+        for j in range(11):
+            ham = sum(bin(int(a) ^ int(b)).count("1") for a, b in zip(pq[i], pk[j]))
+            assert S[i, j] == d - 2 * ham
+    # brute-force sum of products on a few entries
+    for i, j in [(0, 0), (3, 7), (8, 10)]:
+        assert S[i, j] == sum(int(a) * int(b) for a, b in zip(bq[i], bk[j]))
+
+
+def test_logits_range_parity_symmetry():
+    rng = np.random.default_rng(8)
+    d = 37
+    b = np.where(rng.random((12, d)) < 0.5, -1, 1).astype(np.int8)
+    S = oracle.logits(b, b)
+    assert S.dtype == np.int64
+    assert np.all(np.abs(S) <= d) and np.all((S - d) % 2 == 0)
+    assert np.array_equal(S, S.T)
+    assert np.all(np.diag(S) == d)
+    assert np.all(np.diag(oracle.logits(b, -b)) == -d)
+
+
+# --------------------------------------------------------------- select ----
+def _brute_select(s_row, topn, nv):
+    """First (lexicographically smallest) index set of size min(N, nv)
+    maximizing the sum of logits: the top-N set with lower-index tie wins."""
+    best = None
+    for comb in itertools.combinations(range(nv), min(topn, nv)):
+        tot = sum(s_row[j] for j in comb)
+        if best is None or tot > best[0]:
+            best = (tot, comb)
+    return list(best[1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,n,topn", [(3, 8, 3), (2, 9, 4), (5, 7, 2), (1, 6, 3), (4, 8, 8), (3, 5, 9)])
+def test_select_matches_subset_bruteforce(d, n, topn, causal):
+    # Small d gives many equal logits, so the tie rule is exercised.
+    rng = np.random.default_rng(d * 100 + n * 10 + topn)
+    bq = np.where(rng.random((n, d)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((n, d)) < 0.5, -1, 1).astype(np.int8)
+    S = oracle.logits(bq, bk)
+    idx = oracle.select_topn(S, topn, causal)
+    for i in range(n):
+        nv = i + 1 if causal else n
+        want = _brute_select(S[i].tolist(), topn, nv)
+        got = [int(j) for j in idx[i] if j >= 0]
+        assert got == want, (i, S[i].tolist())
+        assert len(got) == min(topn, nv)
+        assert all(j == -1 for j in idx[i][len(got):])
+
+
+def test_select_threshold_separation_and_ties():
+    rng = np.random.default_rng(21)
+    bq = np.where(rng.random((64, 16)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((200, 16)) < 0.5, -1, 1).astype(np.int8)
+    S = oracle.logits(bq, bk)
+    idx = oracle.select_topn(S, 37)
+    for i in range(64):
+        kept = idx[i]
+        assert np.all(np.diff(kept) > 0)
+        dropped = np.setdiff1d(np.arange(200), kept)
+        kmin, dmax = S[i, kept].min(), S[i, dropped].max()
+        assert kmin >= dmax
+        if kmin == dmax:  # every kept tie has a lower index than every dropped tie
+            kt = kept[S[i, kept] == kmin]
+            dt = dropped[S[i, dropped] == kmin]
+            assert kt.max() < dt.min()
+
+
+def test_select_rejects_nonpositive_topn():
+    with pytest.raises(ValueError):
+        oracle.select_topn(np.zeros((2, 3), dtype=np.int64), 0)
+
+
+# ------------------------------------------------------- softmax and AV ----
+def test_full_topn_reduces_to_dense_softmax_attention():
+    # N >= n (non-causal) keeps every key: the result must equal dense
+    # softmax(scale * S) V, with scipy's softmax as the library routine.
+    rng = np.random.default_rng(4)
+    n, d = 24, 16
+    bq = np.where(rng.random((n, d)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((n, d)) < 0.5, -1, 1).astype(np.int8)
+    v = rng.standard_normal((n, 5))
+    S = oracle.logits(bq, bk)
+    for topn in (n, n + 5):
+        idx = oracle.select_topn(S, topn)
+        out, _ = oracle.sparse_softmax_av(S, idx, v, 0.3)
+        dense = scipy.special.softmax(0.3 * S.astype(np.float64), axis=1) @ v
+        np.testing.assert_allclose(out, dense, rtol=1e-12, atol=1e-14)
+
+
+def test_rows_sum_to_one_and_convexity():
+    # V = ones gives 1 exactly when the softmax is renormalized over the kept
+    # set (a global softmax followed by a mask would give less than 1).
+    rng = np.random.default_rng(9)
+    bq = np.where(rng.random((30, 8)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((50, 8)) < 0.5, -1, 1).astype(np.int8)
+    S = oracle.logits(bq, bk)
+    idx = oracle.select_topn(S, 7)
+    out, mag = oracle.sparse_softmax_av(S, idx, np.ones((50, 3)), 0.9)
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-12)
+    vpos = rng.random((50, 4))
+    out, mag = oracle.sparse_softmax_av(S, idx, vpos, 0.9)
+    np.testing.assert_allclose(out, mag, rtol=1e-14)
+    for i in range(30):  # convex combination of the kept rows only
+        kept = idx[i]
+        assert np.all(out[i] <= vpos[kept].max(0) + 1e-12)
+        assert np.all(out[i] >= vpos[kept].min(0) - 1e-12)
+
+
+def test_two_kept_keys_follow_the_logistic_closed_form():
+    # With V = identity rows the output is the probability row itself; with
+    # two kept keys the softmax is the logistic function of the logit gap.
+    bq = np.array([[1, 1, 1, 1]], dtype=np.int8)
+    bk = np.array([[1, 1, 1, -1], [1, -1, -1, -1], [1, 1, 1, 1], [-1, -1, -1, -1]], dtype=np.int8)
+    S = oracle.logits(bq, bk)
+    assert S.tolist() == [[2, -2, 4, -4]]
+    idx = oracle.select_topn(S, 2)
+    assert idx.tolist() == [[0, 2]]
+    out, _ = oracle.sparse_softmax_av(S, idx, np.eye(4), 0.7)
+    p2 = 1.0 / (1.0 + math.exp(-0.7 * (4 - 2)))
+    np.testing.assert_allclose(out[0], [1 - p2, 0.0, p2, 0.0], rtol=1e-14, atol=1e-15)
+
+
+def test_equal_logits_or_tiny_scale_give_the_mean_of_kept_rows():
+    rng = np.random.default_rng(13)
+    bq = np.where(rng.random((10, 6)) < 0.5, -1, 1).astype(np.int8)
+    bk = np.where(rng.random((40, 6)) < 0.5, -1, 1).astype(np.int8)
+    v = rng.standard_normal((40, 3))
+    S = oracle.logits(bq, bk)
+    idx = oracle.select_topn(S, 9)
+    out, _ = oracle.sparse_softmax_av(S, idx, v, 1e-13)
+    for i in range(10):
+        np.testing.assert_allclose(out[i], v[idx[i]].mean(0), rtol=1e-9, atol=1e-11)
+    Seq = np.full((3, 40), 5, dtype=np.int64)
+    idx = oracle.select_topn(Seq, 4)
+    assert idx.tolist() == [[0, 1, 2, 3]] * 3  # all tied: the lowest indices
+    out, _ = oracle.sparse_softmax_av(Seq, idx, v, 2.0)
+    np.testing.assert_allclose(out, np.tile(v[:4].mean(0), (3, 1)), rtol=1e-13)
+
+
+# ------------------------------------------------------- golden fixture ----
+def test_hand_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "hand_example_d4_n4.json")))
+    q = np.array(g["q"], dtype=np.float32)
+    k = np.array(g["k"], dtype=np.float32)
+    v = np.array(g["v"], dtype=np.float64)
+    r = oracle.forward(q, k, v, g["topn"], g["scale"])
+    assert r["qbits"][:, 0].tolist() == g["qbits"]
+    assert r["kbits"][:, 0].tolist() == g["kbits"]
+    assert r["S"].tolist() == g["S"]
+    assert r["idx"].tolist() == g["idx"]
+    np.testing.assert_allclose(r["out"], g["out"], rtol=1e-14, atol=1e-15)
+    rc = oracle.forward(q, k, v, g["topn"], g["scale"], causal=True)
+    assert rc["idx"].tolist() == g["causal_idx"]
+    np.testing.assert_allclose(rc["out"], g["causal_out"], rtol=1e-14, atol=1e-15)
+
+
+def test_forward_row_subset_matches_full():
+    w = make_inputs(1, 1, 70, 40, v_dtype="bf16", rank=3, noise="t3", seed=77)
+    q, k, v = w["q"][0, 0], w["k"][0, 0], w["v"][0, 0]
+    full = oracle.forward(q, k, v, 9, 0.2, causal=True)
+    rows = np.array([0, 5, 33, 69])
+    part = oracle.forward(q, k, v, 9, 0.2, causal=True, rows=rows)
+    assert np.array_equal(part["idx"], full["idx"][rows])
+    np.testing.assert_allclose(part["out"], full["out"][rows], rtol=0, atol=0)
