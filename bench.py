@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the HAD inference-attention hot path on one MI355X.
+
+One step = had_pack(Q) + had_pack(K) + had_attention over one batch of
+seeded synthetic input already resident in HBM (all three kernels launched on
+torch's current stream).  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Default workload: the T5-base-shaped long-document encoder attention
+(B=8, H=12, n=1024, d=64, N=256, bf16 V), on which the metric is quoted.
+
+Roofline of the dominant kernel (had_attention), algorithmic work only:
+    int ops = visible_pairs * (2W + 2) + kept * 2   (XOR+popcount per word,
+              histogram + compaction per pair, weight per kept entry)
+    flops   = 2 * kept * d                           (weighted sum of V)
+    lane-op equivalents = int ops + flops / 4        (a packed fp32 FMA lane
+              does 4 flops per lane-op issue)
+    peak    = 256 CU * 4 SIMD * 16 lanes * 2.4 GHz = 39.32 T lane-ops/s
+The kernel puts the logits and the V product on the matrix cores, so it can
+run faster than this vector-unit bound (frac > 1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query rows/sec of HAD attention at n=1024,N=256; % of HBM/VALU roofline"
+VALU_PEAK = 256 * 4 * 16 * 2.4e9  # int32 lane-ops/s
+HBM_PEAK = 8.0e12  # B/s
+
+
+def work_model(w):
+    """Algorithmic work of one had_attention launch on workload w."""
+    W = (w.dim + 31) // 32
+    bh = w.batch * w.heads
+    n, N = w.seq, w.topn
+    if w.causal:
+        vis = n * (n + 1) // 2
+        kept = sum(min(N, i + 1) for i in range(n))
+    else:
+        vis = n * n
+        kept = n * min(N, n)
+    vis *= bh
+    kept *= bh
+    int_ops = vis * (2 * W + 2) + kept * 2
+    flops = 2 * kept * w.dim
+    lane_ops = int_ops + flops / 4.0
+    vbytes = 2 if w.v_dtype == "bf16" else 4
+    hbm = bh * n * (2 * W * 4 + w.dim * vbytes + w.dim * 4)
+    return {"visible_pairs": vis, "kept": kept, "int_ops": int_ops, "flops": flops,
+            "lane_ops": lane_ops, "hbm_bytes": hbm}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_had_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_had_attention_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The plain oracle on a bounded sample of the same workload, one thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    rows = 0
+    heads = 0
+    t0 = time.perf_counter()
+    try:
+        for bh in range(w.batch * w.heads):
+            b, h = divmod(bh, w.heads)
+            oracle.sigma(inp["q"][b, h])
+            oracle.forward(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                           causal=w.causal)
+            rows += w.seq
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} of {w.batch * w.heads} (batch, head) slices, all {w.seq} rows each "
+                      f"(sign, pack, sigma of the slice, logits, stable-sort top-N, softmax, AV), "
+                      f"{dt:.1f} s wall, numpy float64, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time only had_attention launches (for profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the path shards by (batch, head) slice with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_had_amd as had
+    from had_workloads import HEADLINE, WORKLOADS, workload_inputs
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"])
+    v = (v.to(torch.bfloat16) if w.v_dtype == "bf16" else v).to(dev)
+    W = had.words_per_row(w.dim)
+    qb = torch.empty((w.batch, w.heads, w.seq, W), dtype=torch.int32, device=dev)
+    kb = torch.empty_like(qb)
+    sq = torch.empty(1, dtype=torch.float32, device=dev)
+    sk = torch.empty(1, dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.heads, w.seq, w.dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ws_q = torch.zeros(had.pack_workspace_bytes(q.shape), dtype=torch.uint8, device=dev)
+    ws_k = torch.zeros_like(ws_q)
+
+    def step(ev_pair=None):
+        if not args.attention_only:
+            had.pack(q, out=qb, sigma=sq, workspace=ws_q)
+            had.pack(k, out=kb, sigma=sk, workspace=ws_k)
+        if ev_pair is not None:
+            ev_pair[0].record(stream)
+        had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
+        if ev_pair is not None:
+            ev_pair[1].record(stream)
+
+    if args.attention_only:
+        had.pack(q, out=qb, sigma=sq, workspace=ws_q)
+        had.pack(k, out=kb, sigma=sk, workspace=ws_k)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+
+    rows = w.rows
+    model = work_model(w)
+    achieved = model["lane_ops"] / attn_avg_s
+    traffic = traffic_for(name)
+    rec = {
+        "metric": METRIC,
+        "value": rows / (ms_step / 1e3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "batch": w.batch, "heads": w.heads, "seq": w.seq, "dim": w.dim,
+            "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype, "scale": w.scale,
+            "step": "attention only" if args.attention_only else "pack(Q) + pack(K) + attention",
+            "arithmetic": "int8 matrix-core logits (exact), int32 selection, fp32 softmax weights "
+                          "as bf16 hi+lo, bf16 matrix-core V product with fp32 accumulation",
+        },
+        "attention_us": attn_avg_s * 1e6,
+        "attention_rows_per_s": rows / attn_avg_s,
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved / 1e12,
+            "peak": VALU_PEAK / 1e12,
+            "unit": "Tops/s",
+            "frac": achieved / VALU_PEAK,
+            "traffic": traffic,
+            "kernel": "had_attn_kernel",
+            "work_per_launch": {k2: float(v2) for k2, v2 in model.items()},
+            "hbm_frac": (model["hbm_bytes"] / attn_avg_s) / HBM_PEAK,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * had.h - C ABI of the HAD (Hamming Attention Distillation) inference
+ * attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Pith review of "Hamming Attention Distillation: Binarizing Keys
+ * and Queries for Efficient Long-Context Transformers", section "What carries
+ * the argument"): queries and keys are standardized by sigma_Q / sigma_K and
+ * sign-binarized to {-1,+1}; the logits QK^T become +-1 dot products computed
+ * as d - 2*popcount(q XOR k); a top-N mask keeps the largest logits of every
+ * query row; softmax and the value accumulation run over that sparse set with
+ * full-precision V.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, contiguous [B, H, n, d] ("had_shape").
+ *  - Every data pointer is a *device* pointer owned by the caller; the library
+ *    never frees, keeps or allocates caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns without synchronizing.
+ *  - Host-side argument checks run first and synchronously; a failed check
+ *    returns a status and enqueues nothing.  Launch failures return
+ *    HAD_ERR_HIP.  No C++ exception crosses this interface.
+ *  - had_last_error() returns a thread-local text for the last failure.
+ *  - Results are deterministic: identical inputs give bit-identical outputs
+ *    (no floating-point atomics anywhere).
+ */
+#ifndef HAD_H
+#define HAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HAD_OK = 0,
+  HAD_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad value */
+  HAD_ERR_UNSUPPORTED = 2, /* valid request outside the library's limits */
+  HAD_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} had_status;
+
+typedef enum { HAD_F32 = 0, HAD_BF16 = 1 } had_dtype;
+
+/* Device status word bits written by had_pack (see below). */
+#define HAD_DEV_NAN_INPUT 1u
+
+/* Limits: 1 <= d <= HAD_MAX_DIM, 1 <= n <= HAD_MAX_SEQ. */
+#define HAD_MAX_DIM 256
+#define HAD_MAX_SEQ 65536
+
+typedef struct {
+  int64_t batch; /* B */
+  int64_t heads; /* H */
+  int64_t seq;   /* n: tokens per (batch, head) */
+  int64_t dim;   /* d: features per token */
+} had_shape;
+
+/* Number of uint32 words holding the d sign bits of one row: ceil(d / 32). */
+int64_t had_words_per_row(int64_t dim);
+
+/* Workspace bytes that had_pack needs when it computes sigma. */
+size_t had_pack_workspace_bytes(had_shape s);
+
+/*
+ * had_pack - standardize, sign-binarize and bit-pack Q or K.
+ *
+ * Defined by: Pith review, "What carries the argument" (standardization with
+ * data-estimated sigma_Q, sigma_K, then sign quantization to {-1,+1}) and
+ * referee minor comment 6 on Eq. 12 (sigma is the standard deviation over all
+ * elements of the matrix).
+ *
+ *  x          [B,H,n,d] float32, device.  Read once.
+ *  xbits      [B,H,n,W] uint32, device, W = had_words_per_row(d).  Bit
+ *             (c mod 32) of word floor(c/32) of a row is 1 exactly when
+ *             x[c] < 0 (so +0.0 and -0.0 give 0, i.e. +1); unused high bits
+ *             of the last word are 0.  Since sigma > 0 the bits of x/sigma
+ *             equal the bits of x, so they never depend on a reduction.
+ *  sigma      device float*, or NULL.  When non-NULL it receives the
+ *             population standard deviation of all B*H*n*d elements
+ *             (float64 accumulation, deterministic order, rounded to float).
+ *  workspace  device memory of had_pack_workspace_bytes(s) bytes, 8-byte
+ *             aligned, required when sigma != NULL (ignored otherwise).  It
+ *             must be zero-filled before its first use; every call leaves it
+ *             zero-filled again in the parts that must start at zero.  Two
+ *             calls that may run at the same time need distinct workspaces.
+ *  dev_status device uint32*, or NULL.  When non-NULL, HAD_DEV_NAN_INPUT is
+ *             OR-ed into it if x holds a NaN (the bit value of a NaN element
+ *             is then unspecified).  The library never clears it.
+ *  Errors: HAD_ERR_INVALID_ARG for a null x/xbits, a non-positive shape
+ *  field, or a missing/small workspace; HAD_ERR_UNSUPPORTED above the limits.
+ */
+had_status had_pack(const float* x, had_shape s, uint32_t* xbits, float* sigma,
+                    void* workspace, size_t workspace_bytes,
+                    uint32_t* dev_status, void* stream);
+
+/*
+ * had_attention - Hamming logits, top-N selection, softmax over the kept set
+ * and value accumulation, fused; the n x n matrix is never written.
+ *
+ * Defined by: Pith review, "What carries the argument" (XNOR-plus-popcount
+ * logits, top-N mask of the largest logits per row, softmax and value
+ * accumulation on the sparse matrix) and referee major comment 3 (values in
+ * full precision); Pith verdict record, "one_line_summary".
+ *
+ *  qbits, kbits  [B,H,n,W] uint32 sign words as written by had_pack.
+ *  v             [B,H,n,d] values, device, float32 (v_dtype HAD_F32) or
+ *                bfloat16 (HAD_BF16).  16-byte aligned.
+ *  topn          N >= 1.  Row i keeps N_i = min(N, visible_i) keys.
+ *  scale         finite and > 0.  The float logit is scale * s where s is
+ *                the integer +-1 dot product; fold sigma_Q*sigma_K or
+ *                1/sqrt(d) into it as wanted.
+ *  causal        0: row i sees every key.  1: row i sees keys j <= i; the mask
+ *                is applied before selection.
+ *  out           [B,H,n,d] float32, device, 16-byte aligned.
+ *
+ *  Row i keeps S_i = {j visible : s_ij > t_i} plus the lowest-index keys with
+ *  s_ij == t_i, where t_i is the N_i-th largest visible logit, so that
+ *  |S_i| = N_i exactly; out_i = sum_{j in S_i} softmax_{S_i}(scale*s_ij) V_j.
+ *  Precision: logits and selection are exact integers; the softmax weights
+ *  are computed in float32 and applied with float32 accumulation (bf16 V:
+ *  weights split into two bf16 terms, relative weight error below 2^-15).
+ *  Errors: HAD_ERR_INVALID_ARG for null or misaligned pointers, non-positive
+ *  sizes, topn < 1, non-finite or non-positive scale, unknown v_dtype;
+ *  HAD_ERR_UNSUPPORTED above the limits.
+ */
+had_status had_attention(const uint32_t* qbits, const uint32_t* kbits,
+                         const void* v, had_dtype v_dtype, had_shape s,
+                         int64_t topn, float scale, int causal, float* out,
+                         void* stream);
+
+/*
+ * had_logits - inspection export of the integer logits s = d - 2*Hamming
+ * computed by the same logit stage as had_attention (no mask, every key).
+ *
+ * Defined by: Pith review, "What carries the argument" (QK^T by XNOR plus
+ * popcount) and referee major comment 1 (the logits are integers).
+ *
+ *  Slices bh in [bh_begin, bh_begin + bh_count) of the B*H (batch, head)
+ *  slices, query rows [row_begin, row_begin + row_count).
+ *  s_out  [bh_count, row_count, n] int16, device.
+ */
+had_status had_logits(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                      int64_t bh_begin, int64_t bh_count, int64_t row_begin,
+                      int64_t row_count, int16_t* s_out, void* stream);
+
+/*
+ * had_select - inspection export of the top-N sets chosen by had_attention's
+ * selection stage (same kernel code, same tie rule).
+ *
+ * Defined by: Pith review, "What carries the argument" (top-N mask keeps only
+ * the largest logits per row); lower key index wins among equal logits.
+ *
+ *  Slices bh in [bh_begin, bh_begin + bh_count), all n query rows.
+ *  idx  [bh_count, n, topn] int32, device: row i holds its N_i kept key
+ *       indices in ascending order, then -1 in the remaining topn - N_i slots.
+ */
+had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                      int64_t topn, int causal, int64_t bh_begin,
+                      int64_t bh_count, int32_t* idx, void* stream);
+
+/* Static text for a status code. */
+const char* had_status_string(had_status st);
+
+/* Thread-local description of the last failure on the calling thread. */
+const char* had_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HAD_H */

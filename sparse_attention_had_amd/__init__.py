@@ -1,0 +1,261 @@
+"""HAD (Hamming Attention Distillation) inference attention for AMD MI355X.
+
+Thin ctypes binding of libhad.so.  Every step of the path runs in the HIP
+kernels of that library; this module only checks tensor metadata, passes
+device pointers and the current HIP stream, and turns status codes into
+exceptions.  PyTorch provides device memory and streams.
+
+    bits, sigma = pack(x)                       # sign bits + sigma of x
+    out = attention(qbits, kbits, v, topn, scale, causal)
+    s   = logits(qbits, kbits, dim, ...)        # inspection export
+    idx = select(qbits, kbits, dim, topn, ...)  # inspection export
+
+There is no CPU fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "HadError",
+    "library_path",
+    "load_library",
+    "words_per_row",
+    "pack_workspace_bytes",
+    "pack",
+    "attention",
+    "logits",
+    "select",
+    "DEV_NAN_INPUT",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+DEV_NAN_INPUT = 1
+
+HAD_F32 = 0
+HAD_BF16 = 1
+
+
+class HadError(RuntimeError):
+    """A libhad call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, name: str, detail: str):
+        super().__init__(f"{fn} failed with {name} ({status}): {detail}")
+        self.status = status
+        self.status_name = name
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("seq", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.environ.get("HAD_LIBRARY", os.path.join(_PKG, "libhad.so"))
+
+
+def load_library():
+    """Load libhad.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"libhad.so not found at {path}; build it first "
+                "(python -m sparse_attention_had_amd.build)")
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.had_words_per_row.argtypes = [I64]
+        lib.had_words_per_row.restype = I64
+        lib.had_pack_workspace_bytes.argtypes = [Shape]
+        lib.had_pack_workspace_bytes.restype = ctypes.c_size_t
+        lib.had_pack.argtypes = [P, Shape, P, P, P, ctypes.c_size_t, P, P]
+        lib.had_pack.restype = I
+        lib.had_attention.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P]
+        lib.had_attention.restype = I
+        lib.had_logits.argtypes = [P, P, Shape, I64, I64, I64, I64, P, P]
+        lib.had_logits.restype = I
+        lib.had_select.argtypes = [P, P, Shape, I64, I, I64, I64, P, P]
+        lib.had_select.restype = I
+        lib.had_status_string.argtypes = [I]
+        lib.had_status_string.restype = ctypes.c_char_p
+        lib.had_last_error.argtypes = []
+        lib.had_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        name = lib.had_status_string(status).decode()
+        detail = lib.had_last_error().decode()
+        raise HadError(fn, status, name, detail)
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _need_cuda(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+
+
+def _shape4(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have shape [B, H, n, d]")
+    return t.shape
+
+
+def words_per_row(dim: int) -> int:
+    return int(load_library().had_words_per_row(int(dim)))
+
+
+def pack_workspace_bytes(shape) -> int:
+    return int(load_library().had_pack_workspace_bytes(Shape(*[int(x) for x in shape])))
+
+
+_ws_cache = {}
+
+
+def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream_handle)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def pack(x: torch.Tensor, *, with_sigma: bool = True, out: torch.Tensor | None = None,
+         sigma: torch.Tensor | None = None, dev_status: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None, stream=None):
+    """Sign bits ([B,H,n,W] int32 view of uint32 words) and sigma of x.
+
+    Returns (bits, sigma) where sigma is a 1-element float32 device tensor,
+    or None when with_sigma is False.
+    """
+    lib = load_library()
+    _need_cuda(x, "x", torch.float32)
+    B, H, n, d = _shape4(x, "x")
+    W = words_per_row(d)
+    if out is None:
+        out = torch.empty((B, H, n, W), dtype=torch.int32, device=x.device)
+    _need_cuda(out, "out", torch.int32)
+    if tuple(out.shape) != (B, H, n, W):
+        raise ValueError("out must have shape [B, H, n, W]")
+    shape = Shape(B, H, n, d)
+    sh = _stream_handle(x.device, stream)
+    sig_ptr = None
+    ws_ptr = None
+    ws_bytes = 0
+    if with_sigma:
+        if sigma is None:
+            sigma = torch.empty(1, dtype=torch.float32, device=x.device)
+        _need_cuda(sigma, "sigma", torch.float32)
+        need = int(lib.had_pack_workspace_bytes(shape))
+        if workspace is None:
+            workspace = _workspace(x.device, sh, need)
+        _need_cuda(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        sig_ptr = sigma.data_ptr()
+        ws_ptr = workspace.data_ptr()
+    st_ptr = None
+    if dev_status is not None:
+        _need_cuda(dev_status, "dev_status", torch.int32)
+        st_ptr = dev_status.data_ptr()
+    _check("had_pack", lib.had_pack(x.data_ptr(), shape, out.data_ptr(), sig_ptr, ws_ptr,
+                                    ws_bytes, st_ptr, sh))
+    return out, (sigma if with_sigma else None)
+
+
+def attention(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int,
+              scale: float, causal: bool = False, *, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Fused HAD attention; returns out [B,H,n,d] float32."""
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    _need_cuda(v, "v")
+    B, H, n, d = _shape4(v, "v")
+    W = words_per_row(d)
+    if tuple(qbits.shape) != (B, H, n, W) or tuple(kbits.shape) != (B, H, n, W):
+        raise ValueError("qbits/kbits must have shape [B, H, n, ceil(d/32)]")
+    if v.dtype == torch.float32:
+        vdt = HAD_F32
+    elif v.dtype == torch.bfloat16:
+        vdt = HAD_BF16
+    else:
+        raise ValueError("v must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    _need_cuda(out, "out", torch.float32)
+    if tuple(out.shape) != (B, H, n, d):
+        raise ValueError("out must have the shape of v")
+    _check("had_attention", lib.had_attention(
+        qbits.data_ptr(), kbits.data_ptr(), v.data_ptr(), vdt, Shape(B, H, n, d), int(topn),
+        float(scale), int(bool(causal)), out.data_ptr(), _stream_handle(v.device, stream)))
+    return out
+
+
+def logits(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, *, bh_begin: int = 0,
+           bh_count: int | None = None, row_begin: int = 0, row_count: int | None = None,
+           stream=None) -> torch.Tensor:
+    """Integer logits [bh_count, row_count, n] int16 from the kernel's logit stage."""
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    B, H, n, W = _shape4(qbits, "qbits")
+    if tuple(kbits.shape) != tuple(qbits.shape):
+        raise ValueError("kbits must have the shape of qbits")
+    bh_count = B * H - bh_begin if bh_count is None else bh_count
+    row_count = n - row_begin if row_count is None else row_count
+    out = torch.empty((bh_count, row_count, n), dtype=torch.int16, device=qbits.device)
+    _check("had_logits", lib.had_logits(
+        qbits.data_ptr(), kbits.data_ptr(), Shape(B, H, n, int(dim)), int(bh_begin), int(bh_count),
+        int(row_begin), int(row_count), out.data_ptr(), _stream_handle(qbits.device, stream)))
+    return out
+
+
+def select(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, topn: int, causal: bool = False,
+           *, bh_begin: int = 0, bh_count: int | None = None, stream=None) -> torch.Tensor:
+    """Kept key indices [bh_count, n, topn] int32 (ascending, -1 padded)."""
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    B, H, n, W = _shape4(qbits, "qbits")
+    if tuple(kbits.shape) != tuple(qbits.shape):
+        raise ValueError("kbits must have the shape of qbits")
+    bh_count = B * H - bh_begin if bh_count is None else bh_count
+    out = torch.empty((bh_count, n, int(topn)), dtype=torch.int32, device=qbits.device)
+    _check("had_select", lib.had_select(
+        qbits.data_ptr(), kbits.data_ptr(), Shape(B, H, n, int(dim)), int(topn),
+        int(bool(causal)), int(bh_begin), int(bh_count), out.data_ptr(),
+        _stream_handle(qbits.device, stream)))
+    return out

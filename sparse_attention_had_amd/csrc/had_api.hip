@@ -1,0 +1,152 @@
+// Host side of the C ABI: argument checks, error text, dispatch.
+#include <cmath>
+#include <cstdarg>
+#include <cstring>
+
+#include "had_internal.h"
+
+namespace had {
+
+static thread_local char g_last_error[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+had_status check_shape(const had_shape& s) {
+  if (s.batch <= 0 || s.heads <= 0 || s.seq <= 0 || s.dim <= 0)
+    return fail(HAD_ERR_INVALID_ARG, "shape fields must all be positive");
+  if (s.dim > HAD_MAX_DIM) return fail(HAD_ERR_UNSUPPORTED, "dim above HAD_MAX_DIM (256)");
+  if (s.seq > HAD_MAX_SEQ) return fail(HAD_ERR_UNSUPPORTED, "seq above HAD_MAX_SEQ (65536)");
+  const double total = static_cast<double>(s.batch) * s.heads * s.seq * s.dim;
+  if (total > 9.0e15) return fail(HAD_ERR_UNSUPPORTED, "tensor too large");
+  if (static_cast<double>(s.batch) * s.heads > 2.0e9)
+    return fail(HAD_ERR_UNSUPPORTED, "batch*heads too large");
+  return HAD_OK;
+}
+
+static had_status check_bits(const uint32_t* qbits, const uint32_t* kbits, const char* fn) {
+  if (qbits == nullptr || kbits == nullptr) {
+    set_error("%s: null qbits or kbits", fn);
+    return HAD_ERR_INVALID_ARG;
+  }
+  if (!aligned(qbits, 4) || !aligned(kbits, 4)) {
+    set_error("%s: qbits and kbits must be 4-byte aligned", fn);
+    return HAD_ERR_INVALID_ARG;
+  }
+  return HAD_OK;
+}
+
+}  // namespace had
+
+using namespace had;
+
+extern "C" int64_t had_words_per_row(int64_t dim) { return dim > 0 ? words_per_row(dim) : 0; }
+
+extern "C" const char* had_status_string(had_status st) {
+  switch (st) {
+    case HAD_OK: return "HAD_OK";
+    case HAD_ERR_INVALID_ARG: return "HAD_ERR_INVALID_ARG";
+    case HAD_ERR_UNSUPPORTED: return "HAD_ERR_UNSUPPORTED";
+    case HAD_ERR_HIP: return "HAD_ERR_HIP";
+  }
+  return "HAD_ERR_UNKNOWN";
+}
+
+extern "C" const char* had_last_error(void) { return g_last_error; }
+
+extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v,
+                                    had_dtype v_dtype, had_shape s, int64_t topn, float scale,
+                                    int causal, float* out, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if ((st = check_bits(qbits, kbits, "had_attention")) != HAD_OK) return st;
+  if (v == nullptr || out == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_attention: null v or out");
+  if (!aligned(v, 16) || !aligned(out, 16))
+    return fail(HAD_ERR_INVALID_ARG, "had_attention: v and out must be 16-byte aligned");
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16)
+    return fail(HAD_ERR_INVALID_ARG, "had_attention: unknown v_dtype");
+  if (topn < 1) return fail(HAD_ERR_INVALID_ARG, "had_attention: topn must be >= 1");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(HAD_ERR_INVALID_ARG, "had_attention: scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(HAD_ERR_INVALID_ARG, "had_attention: causal must be 0 or 1");
+  AttnArgs a{};
+  a.qbits = qbits;
+  a.kbits = kbits;
+  a.v = v;
+  a.v_dtype = v_dtype;
+  a.bh_total = s.batch * s.heads;
+  a.bh_begin = 0;
+  a.bh_count = a.bh_total;
+  a.n = static_cast<int>(s.seq);
+  a.d = static_cast<int>(s.dim);
+  a.topn = static_cast<int>(topn > s.seq ? s.seq : topn);
+  a.scale = scale;
+  a.causal = causal;
+  a.out = out;
+  return launch_attention_family(AttnMode::Attend, a, static_cast<hipStream_t>(stream));
+}
+
+extern "C" had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                                 int64_t topn, int causal, int64_t bh_begin, int64_t bh_count,
+                                 int32_t* idx, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if ((st = check_bits(qbits, kbits, "had_select")) != HAD_OK) return st;
+  if (idx == nullptr || !aligned(idx, 4)) return fail(HAD_ERR_INVALID_ARG, "had_select: null or unaligned idx");
+  if (topn < 1) return fail(HAD_ERR_INVALID_ARG, "had_select: topn must be >= 1");
+  if (topn > HAD_MAX_SEQ) return fail(HAD_ERR_UNSUPPORTED, "had_select: topn above HAD_MAX_SEQ");
+  if (causal != 0 && causal != 1) return fail(HAD_ERR_INVALID_ARG, "had_select: causal must be 0 or 1");
+  const int64_t bh_total = s.batch * s.heads;
+  if (bh_begin < 0 || bh_count < 1 || bh_begin + bh_count > bh_total)
+    return fail(HAD_ERR_INVALID_ARG, "had_select: bh range outside [0, B*H)");
+  AttnArgs a{};
+  a.qbits = qbits;
+  a.kbits = kbits;
+  a.v_dtype = HAD_BF16;
+  a.bh_total = bh_total;
+  a.bh_begin = bh_begin;
+  a.bh_count = bh_count;
+  a.n = static_cast<int>(s.seq);
+  a.d = static_cast<int>(s.dim);
+  a.topn = static_cast<int>(topn);
+  a.causal = causal;
+  a.idx = idx;
+  return launch_attention_family(AttnMode::Select, a, static_cast<hipStream_t>(stream));
+}
+
+extern "C" had_status had_logits(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                                 int64_t bh_begin, int64_t bh_count, int64_t row_begin,
+                                 int64_t row_count, int16_t* s_out, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if ((st = check_bits(qbits, kbits, "had_logits")) != HAD_OK) return st;
+  if (s_out == nullptr || !aligned(s_out, 2))
+    return fail(HAD_ERR_INVALID_ARG, "had_logits: null or unaligned s_out");
+  const int64_t bh_total = s.batch * s.heads;
+  if (bh_begin < 0 || bh_count < 1 || bh_begin + bh_count > bh_total)
+    return fail(HAD_ERR_INVALID_ARG, "had_logits: bh range outside [0, B*H)");
+  if (row_begin < 0 || row_count < 1 || row_begin + row_count > s.seq)
+    return fail(HAD_ERR_INVALID_ARG, "had_logits: row range outside [0, n)");
+  AttnArgs a{};
+  a.qbits = qbits;
+  a.kbits = kbits;
+  a.v_dtype = HAD_BF16;
+  a.bh_total = bh_total;
+  a.bh_begin = bh_begin;
+  a.bh_count = bh_count;
+  a.n = static_cast<int>(s.seq);
+  a.d = static_cast<int>(s.dim);
+  a.row_begin = static_cast<int>(row_begin);
+  a.row_count = static_cast<int>(row_count);
+  a.logits = s_out;
+  return launch_attention_family(AttnMode::Logits, a, static_cast<hipStream_t>(stream));
+}

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/had.h, and rejects bad arguments with the documented
+status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_had_amd as had
+from sparse_attention_had_amd import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return had.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "had.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(had_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for fn in ["had_pack", "had_attention", "had_logits", "had_select", "had_words_per_row",
+               "had_pack_workspace_bytes", "had_status_string", "had_last_error"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_words_per_row_and_status_strings(lib):
+    assert [lib.had_words_per_row(d) for d in (1, 31, 32, 33, 64, 128, 256)] == [1, 1, 1, 2, 2, 4, 8]
+    assert lib.had_status_string(0) == b"HAD_OK"
+    assert lib.had_status_string(1) == b"HAD_ERR_INVALID_ARG"
+    assert lib.had_status_string(2) == b"HAD_ERR_UNSUPPORTED"
+    assert lib.had_status_string(4) == b"HAD_ERR_HIP"
+
+
+def test_pack_workspace_bytes(lib):
+    assert lib.had_pack_workspace_bytes(Shape(1, 1, 128, 64)) >= 256 + 16
+    assert lib.had_pack_workspace_bytes(Shape(0, 1, 128, 64)) == 0
+
+
+# Fake, never-dereferenced device addresses: every call below must fail its
+# host-side checks before anything is enqueued.
+A16 = 0x10000
+A16B = 0x20000
+A16C = 0x30000
+
+
+def _attn(lib, q=A16, k=A16B, v=A16C, dt=1, shape=(1, 1, 128, 64), topn=32, scale=0.125,
+          causal=0, out=0x40000):
+    return lib.had_attention(q, k, v, dt, Shape(*shape), topn, scale, causal, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(q=A16 + 2), INVALID),          # qbits not 4-byte aligned
+    (dict(v=A16C + 4), INVALID),         # v not 16-byte aligned
+    (dict(out=0x40000 + 8), INVALID),    # out not 16-byte aligned
+    (dict(dt=7), INVALID),
+    (dict(topn=0), INVALID),
+    (dict(topn=-3), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(shape=(0, 1, 128, 64)), INVALID),
+    (dict(shape=(1, 1, 128, 0)), INVALID),
+    (dict(shape=(1, -1, 128, 64)), INVALID),
+    (dict(shape=(1, 1, 128, 257)), UNSUPPORTED),
+    (dict(shape=(1, 1, 65537, 64)), UNSUPPORTED),
+])
+def test_attention_rejects_bad_arguments(lib, kw, status):
+    assert _attn(lib, **kw) == status
+    assert lib.had_last_error() != b""
+
+
+def test_pack_rejects_bad_arguments(lib):
+    s = Shape(1, 1, 128, 64)
+    assert lib.had_pack(None, s, A16, None, None, 0, None, None) == INVALID
+    assert lib.had_pack(A16, s, None, None, None, 0, None, None) == INVALID
+    assert lib.had_pack(A16 + 1, s, A16B, None, None, 0, None, None) == INVALID
+    # sigma requested without (or with a too small) workspace
+    assert lib.had_pack(A16, s, A16B, A16C, None, 0, None, None) == INVALID
+    assert lib.had_pack(A16, s, A16B, A16C, 0x50000, 8, None, None) == INVALID
+    assert lib.had_pack(A16, Shape(1, 1, 0, 64), A16B, None, None, 0, None, None) == INVALID
+    assert lib.had_pack(A16, Shape(1, 1, 8, 300), A16B, None, None, 0, None, None) == UNSUPPORTED
+
+
+def test_select_and_logits_reject_bad_ranges(lib):
+    s = Shape(2, 3, 100, 64)
+    assert lib.had_select(A16, A16B, s, 0, 0, 0, 6, A16C, None) == INVALID
+    assert lib.had_select(A16, A16B, s, 8, 0, 0, 7, A16C, None) == INVALID
+    assert lib.had_select(A16, A16B, s, 8, 0, -1, 2, A16C, None) == INVALID
+    assert lib.had_select(A16, A16B, s, 8, 3, 0, 6, A16C, None) == INVALID
+    assert lib.had_select(None, A16B, s, 8, 0, 0, 6, A16C, None) == INVALID
+    assert lib.had_logits(A16, A16B, s, 0, 6, 0, 101, A16C, None) == INVALID
+    assert lib.had_logits(A16, A16B, s, 5, 2, 0, 10, A16C, None) == INVALID
+    assert lib.had_logits(A16, A16B, s, 0, 6, 99, 2, A16C, None) == INVALID
+    assert lib.had_logits(A16, A16B, s, 0, 6, 0, 10, None, None) == INVALID
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("HAD_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(had, "_lib", None)
+    with pytest.raises(RuntimeError, match="libhad.so not found"):
+        had.load_library()
