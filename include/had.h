@@ -81,9 +81,8 @@ size_t had_pack_workspace_bytes(had_shape s);
  *             (float64 accumulation, deterministic order, rounded to float).
  *  workspace  device memory of had_pack_workspace_bytes(s) bytes, 8-byte
  *             aligned, required when sigma != NULL (ignored otherwise).  It
- *             must be zero-filled before its first use; every call leaves it
- *             zero-filled again in the parts that must start at zero.  Two
- *             calls that may run at the same time need distinct workspaces.
+ *             holds per-block partial sums; no initial contents are needed.
+ *             Calls that may run at the same time need distinct workspaces.
  *  dev_status device uint32*, or NULL.  When non-NULL, HAD_DEV_NAN_INPUT is
  *             OR-ed into it if x holds a NaN (the bit value of a NaN element
  *             is then unspecified).  The library never clears it.

@@ -30,6 +30,8 @@ COMMON_FLAGS = [
     "-Wall",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core operands and accumulators in arch VGPRs (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

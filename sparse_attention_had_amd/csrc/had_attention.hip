@@ -13,10 +13,11 @@
 //
 //  * Logits on the int8 matrix cores.  Sign bits are expanded to +-1 bytes
 //    (K: once per block per key chunk into LDS; Q: once per wave into
-//    registers) and v_mfma_i32_32x32x32_i8 computes S^T = K Q^T, exactly,
-//    32 keys x 32 queries per instruction and 32 features of d.
+//    registers, negated) and v_mfma_i32_32x32x32_i8 computes u = -s for a
+//    tile of 32 keys x 32 queries, 32 features per instruction, exactly.
+//    Carrying u = -s makes every address below a single shift-add.
 //  * Key order.  The block's visible key range [0, kend) is split at Hh into
-//    two halves.  In the S^T tile the output registers i = 0..15 of lane L hold
+//    two halves.  In the output tile the registers i = 0..15 of lane L hold
 //    query L%32 and keys half*Hh + 16*chunk + i with half = L/32, so every lane
 //    walks its half of the keys in ascending order.  "Lower index wins" among
 //    the tied keys then reduces to a per-lane running quota.
@@ -35,6 +36,9 @@
 //    Dense-masked products on the matrix cores beat a per-row gather of the
 //    N kept V rows: a gather reads 2*d bytes of on-chip bandwidth per kept
 //    pair, the tile product reuses every staged V row for 32 query rows.
+//  * Pipelining.  K words (and V rows in pass 2) of the next key group are
+//    loaded into registers while the current group is computed from LDS, then
+//    written to the other LDS buffer: one barrier per key group.
 #include "had_internal.h"
 
 namespace had {
@@ -46,37 +50,44 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCH = 2;          // 16-key chunks per half staged per iteration
 constexpr int kLutEntries = 264;  // weight table: d+1 weights + zero slot
 constexpr int kZeroSlot = 263;
+constexpr int kInvisible = 1 << 12;  // stands in for the logit of a masked key
+constexpr int kByteLutOff = 0;     // 256 x 8 B: byte -> 8 int8 of +-1
+constexpr int kWLutOff = 2048;     // kLutEntries x 4 B
+constexpr int kKxOff = kWLutOff + 4 * kLutEntries;
 
-template <int W>
+__host__ __device__ constexpr int waves_for(int W) { return (W <= 2) ? 4 : (W <= 4 ? 2 : 1); }
+__host__ __device__ constexpr int threads_for(int W) { return 64 * waves_for(W); }
+
+template <int W, bool VF32>
 struct Cfg {
-  static constexpr int kWaves = (W <= 2) ? 4 : (W <= 4 ? 2 : 1);
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kQB = 32 * kWaves;    // query rows per block
-  static constexpr int kDP = 32 * W;         // padded feature count
-  static constexpr int kKxStride = kDP + 16;  // bytes per expanded key row
+  // 16-key chunks per half in one key group (fp32 V tiles are twice as large)
+  static constexpr int kCH = (VF32 && W > 4) ? 1 : 2;
+  static constexpr int kWaves = waves_for(W);
+  static constexpr int kThreads = threads_for(W);
+  static constexpr int kQB = 32 * kWaves;      // query rows per block
+  static constexpr int kDP = 32 * W;           // padded feature count
+  static constexpr int kKxStride = kDP + 16;   // bytes per expanded key row
+  static constexpr int kKxBuf = kCH * 32 * kKxStride;
+  static constexpr int kRegionOff = kKxOff + 2 * kKxBuf;
+  static constexpr int kKItems = kCH * 32 * W;  // K words per key group
+  static constexpr int kKPT = (kKItems + kThreads - 1) / kThreads;
 };
 
-__host__ __device__ constexpr int vt_stride_bytes(bool vf32) { return vf32 ? 144 : 80; }
+template <bool VF32>
+struct VCfg {
+  static constexpr int kStride = VF32 ? 144 : 80;  // bytes per staged feature row
+};
 
+// Static LDS per instance, sized for the largest d of the instance (32W).
 template <int W, bool VF32>
-__host__ __device__ constexpr size_t lds_layout_kx() {
-  return 2048 + 4 * kLutEntries;  // after byte table and weight table
-}
-
-template <int W, bool VF32>
-__host__ __device__ constexpr size_t lds_layout_region() {
-  return lds_layout_kx<W, VF32>() + static_cast<size_t>(kCH) * 32 * Cfg<W>::kKxStride;
-}
-
-template <int W, bool VF32>
-size_t lds_bytes(int d) {
-  const size_t hist = static_cast<size_t>(Cfg<W>::kWaves) * (d + 1) * 32 * 4;
-  const size_t vt = static_cast<size_t>(kCH) * Cfg<W>::kDP * vt_stride_bytes(VF32);
-  return lds_layout_region<W, VF32>() + (hist > vt ? hist : vt);
-}
+struct Lds {
+  using C = Cfg<W, VF32>;
+  static constexpr int kHist = C::kWaves * (C::kDP + 1) * 32 * 4;
+  static constexpr int kVt = 2 * C::kCH * C::kDP * VCfg<VF32>::kStride;
+  static constexpr int kBytes = C::kRegionOff + (kHist > kVt ? kHist : kVt);
+};
 
 __device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -94,7 +105,7 @@ __device__ inline uint32_t expand_nibble(uint32_t nib) {
   return (y * 0xFEu) | 0x01010101u;
 }
 
-// Byte mask keeping the d-elements [base, base+4) that are < d.
+// Byte mask keeping the features [base, base+4) that are < d.
 __device__ inline uint32_t pad_mask4(int base, int d) {
   const int valid = d - base;
   if (valid >= 4) return 0xFFFFFFFFu;
@@ -102,14 +113,35 @@ __device__ inline uint32_t pad_mask4(int base, int d) {
   return (1u << (8 * valid)) - 1u;
 }
 
+__device__ inline uint32_t lds_u32(const unsigned char* lds, int byte_off) {
+  return *reinterpret_cast<const uint32_t*>(lds + byte_off);
+}
+
+// LDS byte address (address space 3) of a location in the kernel's LDS array.
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+__device__ inline uint32_t lds_addr(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_byte*)p));
+}
+__device__ inline uint32_t lds_load_u32(uint32_t addr) {
+  return *(lds_cu32*)(static_cast<uintptr_t>(addr));
+}
+// Keeps a per-lane value in a VGPR as computed (stops re-association that
+// would split an LDS base back out of it).
+__device__ inline uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <int W, bool VF32, int MODE>
-__global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) {
-  using C = Cfg<W>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  uint2* byte_lut = reinterpret_cast<uint2*>(lds);                 // 256 x 8 B
-  uint32_t* wlut = reinterpret_cast<uint32_t*>(lds + 2048);         // kLutEntries
-  unsigned char* kx = lds + lds_layout_kx<W, VF32>();               // kCH x 32 x stride
-  unsigned char* region = lds + lds_layout_region<W, VF32>();      // hist | vt
+__global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
+  using C = Cfg<W, VF32>;
+  constexpr int kCH = C::kCH;
+  constexpr int VS = VCfg<VF32>::kStride;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Lds<W, VF32>::kBytes];
+  const uint2* byte_lut = reinterpret_cast<const uint2*>(lds + kByteLutOff);
+  uint32_t* wlut = reinterpret_cast<uint32_t*>(lds + kWLutOff);
+  unsigned char* region = lds + C::kRegionOff;  // histograms (pass 1) | V tiles (pass 2)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,7 +176,8 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
 
   // ---- constant tables
   for (int t = tid; t < 256; t += C::kThreads)
-    byte_lut[t] = make_uint2(expand_nibble(t & 15u), expand_nibble(t >> 4));
+    reinterpret_cast<uint2*>(lds + kByteLutOff)[t] =
+        make_uint2(expand_nibble(t & 15u), expand_nibble(t >> 4));
   if (MODE == 0) {
     for (int t = tid; t < kLutEntries; t += C::kThreads) {
       uint32_t e = 0;
@@ -161,14 +194,15 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
       wlut[t] = e;
     }
   }
+  __syncthreads();  // tables are read by every wave below
 
-  // ---- Q operand: +-1 bytes of this lane's query, features 32w + 16*half + [0,16)
+  // ---- Q operand: -q as +-1 bytes, features 32w + 16*half + [0,16)
   v4i qx[W];
   {
     const uint32_t* qrow = a.qbits + (bh * n + (qvalid ? i_row : 0)) * W;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const uint32_t word = qvalid ? qrow[w] : 0u;
+      const uint32_t word = qvalid ? ~qrow[w] : ~0u;  // complement: the product is -s
       const uint32_t b16 = (word >> (16 * half)) & 0xFFFFu;
       const int fbase = 32 * w + 16 * half;
 #pragma unroll
@@ -177,19 +211,30 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
     }
   }
 
+  // ---- key-group staging: registers <- global (load), LDS <- registers (store)
   const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(n) * W;
-
-  // Stage the expanded keys of chunks [it*kCH, it*kCH + kCH) into kx.
-  auto stage_k = [&](int it) {
-    for (int item = tid; item < kCH * 32 * W; item += C::kThreads) {
+  uint32_t kreg[C::kKPT];
+  auto k_load = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < C::kKPT; ++j) {
+      const int item = tid + j * C::kThreads;
       const int w = item % W;
       const int m = (item / W) & 31;
       const int c = item / (W * 32);
       const int gc = it * kCH + c;
-      const int hf = (m >> 2) & 1;
-      const int r = 4 * (m >> 3) + (m & 3);
-      const int key = hf * Hh + 16 * gc + r;
-      const uint32_t word = (gc < nchunk && key < kend) ? kb[static_cast<int64_t>(key) * W + w] : 0u;
+      const int key = ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3);
+      kreg[j] = (item < C::kKItems && gc < nchunk && key < kend) ? kb[static_cast<int64_t>(key) * W + w] : 0u;
+    }
+  };
+  auto k_store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < C::kKPT; ++j) {
+      const int item = tid + j * C::kThreads;
+      if (item >= C::kKItems) break;
+      const int w = item % W;
+      const int m = (item / W) & 31;
+      const int c = item / (W * 32);
+      const uint32_t word = kreg[j];
       uint32_t o[8];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -197,16 +242,16 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
         o[2 * b] = e.x & pad_mask4(32 * w + 8 * b, d);
         o[2 * b + 1] = e.y & pad_mask4(32 * w + 8 * b + 4, d);
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(kx + (c * 32 + m) * C::kKxStride + 32 * w);
+      u32x4* dst = reinterpret_cast<u32x4*>(lds + kKxOff + buf * C::kKxBuf + (c * 32 + m) * C::kKxStride + 32 * w);
       dst[0] = u32x4{o[0], o[1], o[2], o[3]};
       dst[1] = u32x4{o[4], o[5], o[6], o[7]};
     }
   };
 
-  // S^T tile of chunk c: acc[i] = logit(query ql, key half*Hh + 16*gc + i).
-  auto logits_tile = [&](int c) {
+  // u = -logit for (query ql, key half*Hh + 16*gc + i), i = 0..15
+  auto logits_tile = [&](int buf, int c) {
     v16i acc = {};
-    const unsigned char* krow = kx + (c * 32 + ql) * C::kKxStride + 16 * half;
+    const unsigned char* krow = lds + kKxOff + buf * C::kKxBuf + (c * 32 + ql) * C::kKxStride + 16 * half;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const v4i kv = *reinterpret_cast<const v4i*>(krow + 32 * w);
@@ -217,62 +262,73 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
 
   // =========================================================== logits export
   if (MODE == 2) {
+    k_load(0);
+    k_store(0);
+    __syncthreads();
     for (int it = 0; it < niter; ++it) {
-      __syncthreads();
-      stage_k(it);
-      __syncthreads();
+      const int buf = it & 1;
+      if (it + 1 < niter) k_load(it + 1);
       for (int c = 0; c < kCH; ++c) {
         const int gc = it * kCH + c;
         if (gc >= nchunk) break;
-        const v16i s = logits_tile(c);
+        const v16i u = logits_tile(buf, c);
         if (!qvalid) continue;
         const int kbase = half * Hh + 16 * gc;
         int16_t* dst = a.logits + (bh_local * a.row_count + (i_row - a.row_begin)) * static_cast<int64_t>(n);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kbase + i < lim) dst[kbase + i] = static_cast<int16_t>(s[i]);
+          if (kbase + i < lim) dst[kbase + i] = static_cast<int16_t>(-u[i]);
       }
+      if (it + 1 < niter) k_store(buf ^ 1);
+      __syncthreads();
     }
     return;
   }
 
   // =========================================================== pass 1: histogram
-  uint32_t* hist = reinterpret_cast<uint32_t*>(region) + wid * (d + 1) * 32;
-  for (int t = lane; t < (d + 1) * 32; t += 64) hist[t] = 0u;
+  {
+    uint32_t* hist = reinterpret_cast<uint32_t*>(region) + wid * (d + 1) * 32;
+    for (int t = lane; t < (d + 1) * 32; t += 64) hist[t] = 0u;
+  }
   const uint32_t addend = half ? 0x10000u : 1u;
+  // byte offset of bin (d + u)/2 for this lane's query: hb + 64*u
+  unsigned char* hb = lds + C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4 + 64 * d;
 
+  k_load(0);
+  k_store(0);
+  __syncthreads();
   for (int it = 0; it < niter; ++it) {
-    __syncthreads();
-    stage_k(it);
-    __syncthreads();
+    const int buf = it & 1;
+    if (it + 1 < niter) k_load(it + 1);
     for (int c = 0; c < kCH; ++c) {
       const int gc = it * kCH + c;
       if (gc >= nchunk) break;
       if (16 * gc >= wlim) break;  // nothing visible to this wave any more
-      const v16i s = logits_tile(c);
+      const v16i u = logits_tile(buf, c);
       const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
-      uint32_t* hq = hist + ql;
       if (__all(L >= 16)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) atomicAdd(hq + ((d - s[i]) >> 1) * 32, addend);
+        for (int i = 0; i < 16; ++i)
+          atomicAdd(reinterpret_cast<uint32_t*>(hb + u[i] * 64), addend);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (i < L) atomicAdd(hq + ((d - s[i]) >> 1) * 32, addend);
+          if (i < L) atomicAdd(reinterpret_cast<uint32_t*>(hb + u[i] * 64), addend);
       }
     }
+    if (it + 1 < niter) k_store(buf ^ 1);
+    __syncthreads();
   }
-  __syncthreads();
 
   // =========================================================== per-row statistics
   const int Ni = qvalid ? min(a.topn, lim) : 0;
   int T = 0, hmin = 0, below0 = 0, ties0 = 0, below = 0;
   {
-    const uint32_t* hq = hist + ql;
+    const int h0 = C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4;
     int cum = 0, cum0 = 0;
     bool have_min = false;
     for (int b = 0; b <= d; ++b) {
-      const uint32_t x = hq[b * 32];
+      const uint32_t x = lds_u32(lds, h0 + b * 128);
       const int c0 = static_cast<int>(x & 0xFFFFu);
       const int cnt = c0 + static_cast<int>(x >> 16);
       if (!have_min && cnt > 0) {
@@ -293,32 +349,36 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
   const int r_tie = Ni - below;
   const int quota0 = min(r_tie, ties0);
   int quota = half ? (r_tie - quota0) : quota0;
-  const int sT = (Ni > 0) ? d - 2 * T : d + 2;  // rows with nothing to keep never match
+  const int uT = (Ni > 0) ? 2 * T - d : -(d + 2);  // rows with nothing to keep never match
 
   if (MODE == 1) {
     // ======================================================= selection export
     int pos = half ? (below0 + quota0) : 0;
     int32_t* dst = a.idx + (bh_local * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(a.topn);
+    k_load(0);
+    k_store(0);
+    __syncthreads();
     for (int it = 0; it < niter; ++it) {
-      __syncthreads();
-      stage_k(it);
-      __syncthreads();
+      const int buf = it & 1;
+      if (it + 1 < niter) k_load(it + 1);
       for (int c = 0; c < kCH; ++c) {
         const int gc = it * kCH + c;
         if (gc >= nchunk) break;
         if (16 * gc >= wlim) break;
-        const v16i s = logits_tile(c);
+        const v16i u = logits_tile(buf, c);
         const int kbase = half * Hh + 16 * gc;
         const int L = lim - kbase;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const bool valid = i < L;
-          const bool eq = valid && (s[i] == sT);
-          const bool keep = (valid && s[i] > sT) || (eq && quota > 0);
+          const bool eq = valid && (u[i] == uT);
+          const bool keep = (valid && u[i] < uT) || (eq && quota > 0);
           quota -= eq ? 1 : 0;
           if (keep && pos < a.topn) dst[pos++] = kbase + i;
         }
       }
+      if (it + 1 < niter) k_store(buf ^ 1);
+      __syncthreads();
     }
     if (qvalid && half == 0)
       for (int p = Ni; p < a.topn; ++p) dst[p] = -1;
@@ -328,9 +388,9 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
   // =========================================================== pass 2: attend
   float Z = 0.0f;
   if (Ni > 0) {
-    const uint32_t* hq = hist + ql;
+    const int h0 = C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4;
     for (int b = hmin; b < T; ++b) {
-      const uint32_t x = hq[b * 32];
+      const uint32_t x = lds_u32(lds, h0 + b * 128);
       const int cnt = static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16);
       const uint32_t e = wlut[b - hmin];
       const float w = VF32 ? u2f(e) : bf16_to_f(e & 0xFFFFu) + bf16_to_f(e >> 16);
@@ -341,104 +401,146 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
     Z += static_cast<float>(r_tie) * w;
   }
   const float invZ = (Z > 0.0f) ? 1.0f / Z : 0.0f;
-  // weight-table index of logit s: (d - s)/2 - hmin
-  const int lut_off = d - 2 * hmin;
+  // weight-table byte address of u: wlut + 4*((d + u)/2 - hmin) = lutc + 2u
+  const uint32_t lutc = opaque(lds_addr(lds + kWLutOff + 2 * d - 4 * hmin));
+  const uint32_t zaddr = opaque(lds_addr(lds + kWLutOff + 4 * kZeroSlot));
+  // Element i of this lane (ascending keys) is kept iff
+  //   u_i < uT, or u_i == uT and fewer than `quota` ties precede it here,
+  // i.e. iff u_i * 2^15 + ties_seen < uT * 2^15 + quota (ties_seen and quota
+  // stay below 2^15 because a half holds at most 32768 + 15 keys).
+  const int tie_key = uT * 32768 + quota;
+  int ties_seen = 0;
 
   v16f acc[W];
 #pragma unroll
   for (int t = 0; t < W; ++t) acc[t] = v16f{};
 
+  // V rows of the slice; staged transposed: vt[buf][c][feature][slot], slot =
+  // 16*half + (key - half*Hh - 16*gc).
   const unsigned char* vsrc = static_cast<const unsigned char*>(a.v) +
                               bh * static_cast<int64_t>(n) * d * (VF32 ? 4 : 2);
-  constexpr int VS = vt_stride_bytes(VF32);
-
-  auto stage_v = [&](int it) {
-    if (VF32) {
-      // items: (c, slot, 4-feature group)
-      const int groups = C::kDP / 4;
-      for (int item = tid; item < kCH * 32 * groups; item += C::kThreads) {
-        const int g = item % groups;
-        const int slot = (item / groups) & 31;
-        const int c = item / (groups * 32);
+  // bf16 items: (slot pair sp, 4-feature group g, chunk c), sp fastest: the
+  // two g parities of a half-wave land 16 banks apart -> conflict-free writes.
+  // fp32 items: (slot, 4-feature group, chunk), slot fastest.
+  constexpr int kVItems = VF32 ? kCH * 32 * (C::kDP / 4) : kCH * 16 * (C::kDP / 4);
+  constexpr int kVPT = (kVItems + C::kThreads - 1) / C::kThreads;
+  uint32_t vreg[kVPT][4];
+  auto v_load = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const int item = tid + j * C::kThreads;
+      if (VF32) {
+        const int slot = item & 31;
+        const int g = (item >> 5) % (C::kDP / 4);
+        const int c = item / (32 * (C::kDP / 4));
         const int gc = it * kCH + c;
         const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
-        const bool kv = (gc < nchunk) && key < kend;
-        const float* src = reinterpret_cast<const float*>(vsrc) + static_cast<int64_t>(key) * d;
-        float f[4];
+        const bool kv = item < kVItems && gc < nchunk && key < kend;
+        const float* row = reinterpret_cast<const float*>(vsrc) + static_cast<int64_t>(kv ? key : 0) * d;
         if (kv && (d & 3) == 0 && 4 * g + 4 <= d) {
-          const float4 t4 = *reinterpret_cast<const float4*>(src + 4 * g);
-          f[0] = t4.x; f[1] = t4.y; f[2] = t4.z; f[3] = t4.w;
+          const u32x4 t = *reinterpret_cast<const u32x4*>(row + 4 * g);
+          vreg[j][0] = t[0]; vreg[j][1] = t[1]; vreg[j][2] = t[2]; vreg[j][3] = t[3];
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) f[k] = (kv && 4 * g + k < d) ? src[4 * g + k] : 0.0f;
+          for (int k = 0; k < 4; ++k) vreg[j][k] = (kv && 4 * g + k < d) ? f2u(row[4 * g + k]) : 0u;
         }
-        unsigned char* dst = region + c * C::kDP * VS + slot * 4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) *reinterpret_cast<float*>(dst + (4 * g + k) * VS) = f[k];
-      }
-    } else {
-      // items: (c, slot pair, 8-feature group)
-      const int groups = C::kDP / 8;
-      for (int item = tid; item < kCH * 16 * groups; item += C::kThreads) {
-        const int g = item % groups;
-        const int sp = (item / groups) & 15;
-        const int c = item / (groups * 16);
+      } else {
+        const int sp = item & 15;
+        const int g = (item >> 4) % (C::kDP / 4);
+        const int c = item / (16 * (C::kDP / 4));
         const int gc = it * kCH + c;
         const int slot = 2 * sp;
         const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
-        uint32_t h0[4], h1[4];
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(vsrc);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          uint32_t* h = kk ? h1 : h0;
-          const bool kv = (gc < nchunk) && (key + kk) < kend;
-          const uint16_t* row = src + static_cast<int64_t>(key + kk) * d;
-          if (kv && (d & 7) == 0 && 8 * g + 8 <= d) {
-            const u32x4 t = *reinterpret_cast<const u32x4*>(row + 8 * g);
-            h[0] = t[0]; h[1] = t[1]; h[2] = t[2]; h[3] = t[3];
+          const bool kv = item < kVItems && gc < nchunk && key + kk < kend;
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(kv ? key + kk : 0) * d;
+          if (kv && (d & 3) == 0 && 4 * g + 4 <= d) {
+            const uint2 t = *reinterpret_cast<const uint2*>(row + 4 * g);
+            vreg[j][2 * kk] = t.x;
+            vreg[j][2 * kk + 1] = t.y;
           } else {
+            uint32_t f[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t lo = (kv && 8 * g + 2 * k < d) ? row[8 * g + 2 * k] : 0u;
-              const uint32_t hi = (kv && 8 * g + 2 * k + 1 < d) ? row[8 * g + 2 * k + 1] : 0u;
-              h[k] = lo | (hi << 16);
-            }
+            for (int k = 0; k < 4; ++k) f[k] = (kv && 4 * g + k < d) ? row[4 * g + k] : 0u;
+            vreg[j][2 * kk] = f[0] | (f[1] << 16);
+            vreg[j][2 * kk + 1] = f[2] | (f[3] << 16);
           }
-        }
-        unsigned char* dst = region + c * C::kDP * VS + slot * 2;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // feature 8g+2k: (key, key+1) low halves; feature 8g+2k+1: high halves
-          *reinterpret_cast<uint32_t*>(dst + (8 * g + 2 * k) * VS) = (h0[k] & 0xFFFFu) | (h1[k] << 16);
-          *reinterpret_cast<uint32_t*>(dst + (8 * g + 2 * k + 1) * VS) = (h0[k] >> 16) | (h1[k] & 0xFFFF0000u);
         }
       }
     }
   };
+  auto v_store = [&](int buf) {
+    unsigned char* vt = region + buf * (kCH * C::kDP * VS);
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const int item = tid + j * C::kThreads;
+      if (item >= kVItems) break;
+      if (VF32) {
+        const int slot = item & 31;
+        const int g = (item >> 5) % (C::kDP / 4);
+        const int c = item / (32 * (C::kDP / 4));
+        unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * slot;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<uint32_t*>(dst + k * VS) = vreg[j][k];
+      } else {
+        const int sp = item & 15;
+        const int g = (item >> 4) % (C::kDP / 4);
+        const int c = item / (16 * (C::kDP / 4));
+        unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * sp;
+        const uint32_t a0 = vreg[j][0], a1 = vreg[j][1], b0 = vreg[j][2], b1 = vreg[j][3];
+        // feature 4g+k: (key, key+1) packed as one dword
+        *reinterpret_cast<uint32_t*>(dst + 0 * VS) = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dst + 1 * VS) = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+        *reinterpret_cast<uint32_t*>(dst + 2 * VS) = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dst + 3 * VS) = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+      }
+    }
+  };
 
+  k_load(0);
+  v_load(0);
+  __syncthreads();  // every wave is done with its histogram (V tiles alias it)
+  k_store(0);
+  v_store(0);
+  __syncthreads();
   for (int it = 0; it < niter; ++it) {
-    __syncthreads();
-    stage_k(it);
-    stage_v(it);
-    __syncthreads();
+    const int buf = it & 1;
+    if (it + 1 < niter) {
+      k_load(it + 1);
+      v_load(it + 1);
+    }
+    const unsigned char* vt = region + buf * (kCH * C::kDP * VS);
+    // all logit tiles of the group first: their matrix-core latency overlaps
+    // the vector work of the previous chunk
+    v16i ug[kCH];
+#pragma unroll
+    for (int c = 0; c < kCH; ++c)
+      if (it * kCH + c < nchunk && 16 * (it * kCH + c) < wlim) ug[c] = logits_tile(buf, c);
+#pragma unroll
     for (int c = 0; c < kCH; ++c) {
       const int gc = it * kCH + c;
       if (gc >= nchunk) break;
       if (16 * gc >= wlim) break;
-      const v16i s = logits_tile(c);
+      const v16i u = ug[c];
       const int L = lim - (half * Hh + 16 * gc);
-      const bool full = __all(L >= 16);
       uint32_t e[16];
+      if (__all(L >= 16)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool valid = full || i < L;
-        const bool eq = valid && (s[i] == sT);
-        const bool keep = (valid && s[i] > sT) || (eq && quota > 0);
-        quota -= eq ? 1 : 0;
-        const int li = keep ? (((lut_off - s[i]) >> 1)) : kZeroSlot;
-        e[i] = wlut[li];
+        for (int i = 0; i < 16; ++i) {
+          const int ui = u[i];
+          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+          ties_seen += (ui == uT) ? 1 : 0;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ui = (i < L) ? u[i] : kInvisible;
+          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+          ties_seen += (ui == uT) ? 1 : 0;
+        }
       }
-      const unsigned char* vbase = region + c * C::kDP * VS;
+      const unsigned char* vbase = vt + c * C::kDP * VS;
       if (VF32) {
 #pragma unroll
         for (int t = 0; t < W; ++t) {
@@ -456,8 +558,8 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
-            ph[k] = (e0 & 0xFFFFu) | (e1 << 16);
-            pl[k] = (e0 >> 16) | (e1 & 0xFFFF0000u);
+            ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
+            pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
           }
           const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
           const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
@@ -471,6 +573,11 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
         }
       }
     }
+    if (it + 1 < niter) {
+      k_store(buf ^ 1);
+      v_store(buf ^ 1);
+    }
+    __syncthreads();
   }
 
   // =========================================================== epilogue
@@ -497,23 +604,13 @@ __global__ __launch_bounds__(Cfg<W>::kThreads) void had_attn_kernel(AttnArgs a) 
 
 template <int W, bool VF32, int MODE>
 had_status launch_one(const AttnArgs& a, hipStream_t st) {
-  using C = Cfg<W>;
+  using C = Cfg<W, VF32>;
   const int qrows = (MODE == 2) ? a.row_count : a.n;
   const int64_t ntq = (qrows + C::kQB - 1) / C::kQB;
   const int64_t blocks = ntq * a.bh_count;
   if (blocks <= 0) return HAD_OK;
   if (blocks > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "grid too large");
-  const size_t lds = lds_bytes<W, VF32>(a.d);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&had_attn_kernel<W, VF32, MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) {
-      set_error("hipFuncSetAttribute(%zu B LDS) failed: %s", lds, hipGetErrorString(e));
-      return HAD_ERR_HIP;
-    }
-  }
-  had_attn_kernel<W, VF32, MODE><<<static_cast<unsigned>(blocks), C::kThreads, lds, st>>>(a);
+  had_attn_kernel<W, VF32, MODE><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
   return check_launch(MODE == 0 ? "had_attention" : (MODE == 1 ? "had_select" : "had_logits"));
 }
 

@@ -15,10 +15,12 @@
 //    such loads in flight.
 //  * other d: one thread per output word (pad bits stay 0).
 //  * sigma: every thread sums x and x*x in float64; blocks reduce in a fixed
-//    order and write one partial pair to the workspace; the last block to
-//    finish (agent-scope acq_rel counter) sums the partials in index order and
-//    writes sigma, then re-zeroes the counter.  No floating-point atomics, so
-//    the result is bit-identical from run to run.
+//    order and store one partial pair each to the workspace; a one-block
+//    finalize kernel on the same stream sums the partials in index order and
+//    writes sigma.  (A "last block finalizes" scheme needs an agent-scope
+//    release per block, which writes back L2 and costs more than the whole
+//    pack.)  No floating-point atomics, so sigma is bit-identical from run to
+//    run.
 #include "had_internal.h"
 
 namespace had {
@@ -27,7 +29,6 @@ namespace {
 constexpr int kPackThreads = 256;
 constexpr int kPackMaxBlocks = 2048;
 constexpr int kUnroll = 8;
-constexpr size_t kWsHeader = 256;  // counter lives here; partials follow
 
 __device__ inline double wave_sum(double v) {
 #pragma unroll
@@ -56,24 +57,24 @@ __device__ inline void block_sum2(double& a, double& b) {
   }
 }
 
-// Last-block finalize: writes sigma from all block partials.
-__device__ void finalize_sigma(double s1, double s2, double* partials, unsigned* counter,
-                               float* sigma, double count) {
-  __shared__ bool is_last;
+// Per-block partial sums (plain stores; the finalize kernel that follows on
+// the same stream sees them through kernel-boundary ordering).
+__device__ void write_partials(double s1, double s2, double* partials) {
   block_sum2(s1, s2);
   if (threadIdx.x == 0) {
     partials[2 * blockIdx.x + 0] = s1;
     partials[2 * blockIdx.x + 1] = s2;
-    unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == gridDim.x - 1);
   }
-  __syncthreads();
-  if (!is_last) return;
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+}
+
+// One block: sum the partials in index order and write sigma.
+__global__ __launch_bounds__(kPackThreads) void sigma_finalize_kernel(const double* partials,
+                                                                       int nblocks, double count,
+                                                                       float* sigma) {
   double a = 0.0, b = 0.0;
-  for (unsigned i = threadIdx.x; i < gridDim.x; i += kPackThreads) {
-    a += __hip_atomic_load(&partials[2 * i + 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    b += __hip_atomic_load(&partials[2 * i + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < nblocks; i += kPackThreads) {
+    a += partials[2 * i + 0];
+    b += partials[2 * i + 1];
   }
   block_sum2(a, b);
   if (threadIdx.x == 0) {
@@ -81,7 +82,6 @@ __device__ void finalize_sigma(double s1, double s2, double* partials, unsigned*
     double var = b / count - mean * mean;
     if (!(var > 0.0)) var = 0.0;
     *sigma = static_cast<float>(sqrt(var));
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -89,7 +89,7 @@ __device__ void finalize_sigma(double s1, double s2, double* partials, unsigned*
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
     const float* __restrict__ x, uint32_t* __restrict__ bits, int64_t elems, double* partials,
-    unsigned* counter, float* sigma, uint32_t* dev_status) {
+    uint32_t* dev_status) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x) >> 6;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPackThreads / 64);
@@ -119,14 +119,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
   }
   if (dev_status != nullptr && __ballot(nan_seen) != 0 && lane == 0)
     atomicOr(dev_status, HAD_DEV_NAN_INPUT);
-  if (kSigma) finalize_sigma(s1, s2, partials, counter, sigma, static_cast<double>(elems));
+  if (kSigma) write_partials(s1, s2, partials);
 }
 
 // Any d: one thread per output word.
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(
     const float* __restrict__ x, uint32_t* __restrict__ bits, int64_t rows, int d, int W,
-    double* partials, unsigned* counter, float* sigma, uint32_t* dev_status) {
+    double* partials, uint32_t* dev_status) {
   const int64_t nwords = rows * W;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kPackThreads;
   double s1 = 0.0, s2 = 0.0;
@@ -152,8 +152,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(
   }
   if (dev_status != nullptr && __ballot(nan_seen) != 0 && (threadIdx.x & 63) == 0)
     atomicOr(dev_status, HAD_DEV_NAN_INPUT);
-  if (kSigma)
-    finalize_sigma(s1, s2, partials, counter, sigma, static_cast<double>(rows) * d);
+  if (kSigma) write_partials(s1, s2, partials);
 }
 
 }  // namespace
@@ -180,7 +179,7 @@ using namespace had;
 
 extern "C" size_t had_pack_workspace_bytes(had_shape s) {
   if (check_shape(s) != HAD_OK) return 0;
-  return kWsHeader + sizeof(double) * 2 * static_cast<size_t>(pack_grid_blocks(s));
+  return sizeof(double) * 2 * static_cast<size_t>(pack_grid_blocks(s));
 }
 
 extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, float* sigma,
@@ -196,15 +195,13 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
     return fail(HAD_ERR_INVALID_ARG, "had_pack: dev_status must be 4-byte aligned");
   const int blocks = pack_grid_blocks(s);
   double* partials = nullptr;
-  unsigned* counter = nullptr;
   if (sigma != nullptr) {
     if (!aligned(sigma, 4)) return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma must be 4-byte aligned");
     if (workspace == nullptr || !aligned(workspace, 8))
       return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma requested but workspace is null or unaligned");
     if (workspace_bytes < had_pack_workspace_bytes(s))
       return fail(HAD_ERR_INVALID_ARG, "had_pack: workspace smaller than had_pack_workspace_bytes()");
-    counter = static_cast<unsigned*>(workspace);
-    partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kWsHeader);
+    partials = static_cast<double*>(workspace);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int64_t rows = s.batch * s.heads * s.seq;
@@ -212,19 +209,18 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   if (d % 32 == 0) {
     const int64_t elems = rows * d;
     if (sigma)
-      pack_stream_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, partials, counter,
-                                                                sigma, dev_status);
+      pack_stream_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, partials, dev_status);
     else
-      pack_stream_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, nullptr, nullptr,
-                                                                 nullptr, dev_status);
+      pack_stream_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, nullptr, dev_status);
   } else {
     const int W = static_cast<int>(words_per_row(d));
     if (sigma)
-      pack_rows_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, partials,
-                                                              counter, sigma, dev_status);
+      pack_rows_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, partials, dev_status);
     else
-      pack_rows_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, nullptr,
-                                                               nullptr, nullptr, dev_status);
+      pack_rows_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, nullptr, dev_status);
   }
+  had_status ls = check_launch("had_pack");
+  if (ls != HAD_OK || sigma == nullptr) return ls;
+  sigma_finalize_kernel<<<1, kPackThreads, 0, hs>>>(partials, blocks, static_cast<double>(rows) * d, sigma);
   return check_launch("had_pack");
 }
