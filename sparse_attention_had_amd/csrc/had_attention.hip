@@ -11,16 +11,17 @@
 // GPU design (gfx950 / CDNA4), one work-group = WAVES waves x 32 query rows of
 // one (batch, head) slice; the n x n matrix never leaves the registers.
 //
-//  * Logits on the int8 matrix cores.  Sign bits are expanded to +-1 bytes
-//    (K: once per block per key chunk into LDS; Q: once per wave into
-//    registers, negated) and v_mfma_i32_32x32x32_i8 computes u = -s for a
-//    tile of 32 keys x 32 queries, 32 features per instruction, exactly.
-//    Carrying u = -s makes every address below a single shift-add.
+//  * Logits on the int8 matrix cores.  v_mfma_i32_32x32x32_i8 computes
+//    u = -s exactly for a tile of 32 keys x 32 queries and 32 features: the Q
+//    operand holds -q as +-1 bytes (expanded once per wave, zero in the pad
+//    features), the K operand is expanded per wave from the packed key words
+//    in LDS through a 256-entry byte table.  Carrying u = -s makes every
+//    address below a single shift-add.
 //  * Key order.  The block's visible key range [0, kend) is split at Hh into
 //    two halves.  In the output tile the registers i = 0..15 of lane L hold
 //    query L%32 and keys half*Hh + 16*chunk + i with half = L/32, so every lane
 //    walks its half of the keys in ascending order.  "Lower index wins" among
-//    the tied keys then reduces to a per-lane running quota.
+//    the tied keys then reduces to a per-lane running count.
 //  * Selection, pass 1.  Per-wave LDS histogram over the d+1 possible logits:
 //    dword [bin][query] holds the half-0 count in its low and the half-1
 //    count in its high 16 bits (ds_add_u32 of 1 or 1<<16; the two lane halves
@@ -28,17 +29,20 @@
 //    A scan per row gives the threshold bin T, the tie quota r split over the
 //    halves, h_min and the softmax denominator Z (from counts, without V).
 //  * Pass 2.  The logits are recomputed on the matrix cores (cheaper than
-//    storing them), each element is kept or dropped, its weight
-//    exp(-2*scale*(h - h_min)) is read from an LDS table as a pair of bf16
-//    terms (hi + lo, relative error < 2^-15), and out^T = V^T P^T runs on
-//    v_mfma_f32_32x32x16_bf16 (two products, hi and lo) with V staged
-//    transposed in LDS.  fp32 V uses v_mfma_f32_32x32x2_f32 with fp32 weights.
-//    Dense-masked products on the matrix cores beat a per-row gather of the
-//    N kept V rows: a gather reads 2*d bytes of on-chip bandwidth per kept
-//    pair, the tile product reuses every staged V row for 32 query rows.
-//  * Pipelining.  K words (and V rows in pass 2) of the next key group are
+//    storing them), each element is kept or dropped with one compare of a
+//    composite key, its weight exp(-2*scale*(h - h_min)) is read from an LDS
+//    table as a pair of bf16 terms (hi + lo, relative error < 2^-15), and
+//    out^T = V^T P^T runs on v_mfma_f32_32x32x16_bf16 (two products, hi and
+//    lo) with V staged transposed in LDS.  fp32 V uses v_mfma_f32_32x32x2_f32
+//    with fp32 weights.  Dense-masked products on the matrix cores beat a
+//    per-row gather of the N kept V rows: a gather reads 2*d bytes of on-chip
+//    bandwidth per kept pair, the tile product reuses every staged V row for
+//    32 query rows.
+//  * Staging.  Key words (and, in pass 2, V rows) of the next key group are
 //    loaded into registers while the current group is computed from LDS, then
-//    written to the other LDS buffer: one barrier per key group.
+//    written to the other LDS buffer: one barrier per key group.  Groups are
+//    large (pass 1: 4 KB of key words; pass 2: about 16 KB of V) so that the
+//    compute of one group hides the load latency of the next.
 #include "had_internal.h"
 
 namespace had {
@@ -50,43 +54,35 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLutEntries = 264;  // weight table: d+1 weights + zero slot
+constexpr int kLutEntries = 264;        // weight table: d+1 weights + zero slot
 constexpr int kZeroSlot = 263;
-constexpr int kInvisible = 1 << 12;  // stands in for the logit of a masked key
-constexpr int kByteLutOff = 0;     // 256 x 8 B: byte -> 8 int8 of +-1
-constexpr int kWLutOff = 2048;     // kLutEntries x 4 B
-constexpr int kKxOff = kWLutOff + 4 * kLutEntries;
+constexpr int kInvisible = 1 << 12;     // stands in for the logit of a masked key
+constexpr int kByteLutOff = 0;          // 256 x 8 B: byte -> 8 int8 of +-1
+constexpr int kWLutOff = 2048;          // kLutEntries x 4 B
+constexpr int kKbOff = kWLutOff + 4 * kLutEntries;
 
-__host__ __device__ constexpr int waves_for(int W) { return (W <= 2) ? 4 : (W <= 4 ? 2 : 1); }
+__host__ __device__ constexpr int waves_for(int W) { return W <= 4 ? 4 : 2; }
 __host__ __device__ constexpr int threads_for(int W) { return 64 * waves_for(W); }
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int W, bool VF32>
 struct Cfg {
-  // 16-key chunks per half in one key group (fp32 V tiles are twice as large)
-  static constexpr int kCH = (VF32 && W > 4) ? 1 : 2;
   static constexpr int kWaves = waves_for(W);
   static constexpr int kThreads = threads_for(W);
-  static constexpr int kQB = 32 * kWaves;      // query rows per block
-  static constexpr int kDP = 32 * W;           // padded feature count
-  static constexpr int kKxStride = kDP + 16;   // bytes per expanded key row
-  static constexpr int kKxBuf = kCH * 32 * kKxStride;
-  static constexpr int kRegionOff = kKxOff + 2 * kKxBuf;
-  static constexpr int kKItems = kCH * 32 * W;  // K words per key group
-  static constexpr int kKPT = (kKItems + kThreads - 1) / kThreads;
-};
-
-template <bool VF32>
-struct VCfg {
-  static constexpr int kStride = VF32 ? 144 : 80;  // bytes per staged feature row
-};
-
-// Static LDS per instance, sized for the largest d of the instance (32W).
-template <int W, bool VF32>
-struct Lds {
-  using C = Cfg<W, VF32>;
-  static constexpr int kHist = C::kWaves * (C::kDP + 1) * 32 * 4;
-  static constexpr int kVt = 2 * C::kCH * C::kDP * VCfg<VF32>::kStride;
-  static constexpr int kBytes = C::kRegionOff + (kHist > kVt ? kHist : kVt);
+  static constexpr int kQB = 32 * kWaves;  // query rows per block
+  static constexpr int kDP = 32 * W;       // padded feature count
+  // 16-key chunks per half in one key group: K-only loops (4 KB of key
+  // words) and the attend loop (V tile of about 16 KB)
+  static constexpr int kCH1 = 32 / W;
+  static constexpr int kCH2 = VF32 ? (W <= 2 ? 2 : 1) : (W <= 2 ? 4 : (W <= 4 ? 2 : 1));
+  static constexpr int kKb1 = kCH1 * 32 * W * 4;  // bytes of key words per group
+  static constexpr int kKb2 = kCH2 * 32 * W * 4;
+  static constexpr int kKbBuf = cmax(kKb1, kKb2);
+  static constexpr int kVS = VF32 ? 144 : 80;     // bytes per staged feature row
+  static constexpr int kVBuf = kCH2 * kDP * kVS;
+  static constexpr int kHist = kWaves * (kDP + 1) * 32 * 4;
+  static constexpr int kRegionOff = kKbOff + 2 * kKbBuf;
+  static constexpr int kLdsBytes = kRegionOff + cmax(kHist, 2 * kVBuf);
 };
 
 __device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -113,13 +109,10 @@ __device__ inline uint32_t pad_mask4(int base, int d) {
   return (1u << (8 * valid)) - 1u;
 }
 
-__device__ inline uint32_t lds_u32(const unsigned char* lds, int byte_off) {
-  return *reinterpret_cast<const uint32_t*>(lds + byte_off);
-}
-
 // LDS byte address (address space 3) of a location in the kernel's LDS array.
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 __device__ inline uint32_t lds_addr(const unsigned char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_byte*)p));
 }
@@ -136,9 +129,8 @@ __device__ inline uint32_t opaque(uint32_t v) {
 template <int W, bool VF32, int MODE>
 __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   using C = Cfg<W, VF32>;
-  constexpr int kCH = C::kCH;
-  constexpr int VS = VCfg<VF32>::kStride;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Lds<W, VF32>::kBytes];
+  constexpr int VS = C::kVS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::kLdsBytes];
   const uint2* byte_lut = reinterpret_cast<const uint2*>(lds + kByteLutOff);
   uint32_t* wlut = reinterpret_cast<uint32_t*>(lds + kWLutOff);
   unsigned char* region = lds + C::kRegionOff;  // histograms (pass 1) | V tiles (pass 2)
@@ -168,11 +160,11 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   const int kend = causal ? min(n, q0 + C::kQB) : n;
   const int Hh = ((kend + 1) / 2 + 15) & ~15;  // half split, multiple of 16
   const int nchunk = Hh / 16;
-  const int niter = (nchunk + kCH - 1) / kCH;
   // keys j < lim are visible to this lane's query row
   const int lim = !qvalid ? 0 : (causal ? min(i_row + 1, n) : n);
   const int wave_q0 = q0 + wid * 32;
   const int wlim = (wave_q0 >= qend) ? 0 : (causal ? min(n, wave_q0 + 32) : n);
+  const int wchunks = min(nchunk, (wlim + 15) / 16);  // chunks with keys this wave sees
 
   // ---- constant tables
   for (int t = tid; t < 256; t += C::kThreads)
@@ -194,9 +186,8 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
       wlut[t] = e;
     }
   }
-  __syncthreads();  // tables are read by every wave below
 
-  // ---- Q operand: -q as +-1 bytes, features 32w + 16*half + [0,16)
+  // ---- Q operand: -q as +-1 bytes, features 32w + 16*half + [0,16); pad = 0
   v4i qx[W];
   {
     const uint32_t* qrow = a.qbits + (bh * n + (qvalid ? i_row : 0)) * W;
@@ -211,77 +202,92 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- key-group staging: registers <- global (load), LDS <- registers (store)
-  const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(n) * W;
-  uint32_t kreg[C::kKPT];
-  auto k_load = [&](int it) {
+  // ---- key words: kb[c][m][w], m = MFMA row of the logit tile.  Row m holds
+  // key (m>>2 & 1)*Hh + 16*gc + 4*(m>>3) + (m&3), i.e. register i of lane L
+  // gets key half*Hh + 16*gc + i.  Pad features need no masking: the Q
+  // operand is zero there.
+  const uint32_t* kbg = a.kbits + bh * static_cast<int64_t>(n) * W;
+  auto key_of = [&](int gc, int m) { return ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3); };
+  constexpr int kKPT1 = (C::kCH1 * 32 * W + C::kThreads - 1) / C::kThreads;
+  constexpr int kKPT2 = (C::kCH2 * 32 * W + C::kThreads - 1) / C::kThreads;
+  constexpr int kKPT = cmax(kKPT1, kKPT2);
+  uint32_t kreg[kKPT];
+  auto k_load = [&](int g0, int ch) {  // chunks [g0, g0 + ch)
 #pragma unroll
-    for (int j = 0; j < C::kKPT; ++j) {
+    for (int j = 0; j < kKPT; ++j) {
       const int item = tid + j * C::kThreads;
       const int w = item % W;
       const int m = (item / W) & 31;
       const int c = item / (W * 32);
-      const int gc = it * kCH + c;
-      const int key = ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3);
-      kreg[j] = (item < C::kKItems && gc < nchunk && key < kend) ? kb[static_cast<int64_t>(key) * W + w] : 0u;
+      const int gc = g0 + c;
+      const int key = key_of(gc, m);
+      kreg[j] = (c < ch && gc < nchunk && key < kend) ? kbg[static_cast<int64_t>(key) * W + w] : 0u;
     }
   };
-  auto k_store = [&](int buf) {
+  auto k_store = [&](int buf, int ch) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lds + kKbOff + buf * C::kKbBuf);
 #pragma unroll
-    for (int j = 0; j < C::kKPT; ++j) {
+    for (int j = 0; j < kKPT; ++j) {
       const int item = tid + j * C::kThreads;
-      if (item >= C::kKItems) break;
-      const int w = item % W;
-      const int m = (item / W) & 31;
-      const int c = item / (W * 32);
-      const uint32_t word = kreg[j];
-      uint32_t o[8];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint2 e = byte_lut[(word >> (8 * b)) & 0xFFu];
-        o[2 * b] = e.x & pad_mask4(32 * w + 8 * b, d);
-        o[2 * b + 1] = e.y & pad_mask4(32 * w + 8 * b + 4, d);
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(lds + kKxOff + buf * C::kKxBuf + (c * 32 + m) * C::kKxStride + 32 * w);
-      dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-      dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+      if (item < ch * 32 * W) dst[item] = kreg[j];
     }
   };
 
-  // u = -logit for (query ql, key half*Hh + 16*gc + i), i = 0..15
+  // u = -logit for (query ql, key half*Hh + 16*gc + i), i = 0..15, chunk c of
+  // the key-word buffer buf.
   auto logits_tile = [&](int buf, int c) {
+    const uint32_t* krow = reinterpret_cast<const uint32_t*>(lds + kKbOff + buf * C::kKbBuf) + (c * 32 + ql) * W;
+    uint32_t words[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) words[w] = krow[w];
     v16i acc = {};
-    const unsigned char* krow = lds + kKxOff + buf * C::kKxBuf + (c * 32 + ql) * C::kKxStride + 16 * half;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const v4i kv = *reinterpret_cast<const v4i*>(krow + 32 * w);
+      const uint32_t b16 = words[w] >> (16 * half);
+      const uint2 lo = byte_lut[b16 & 0xFFu];
+      const uint2 hi = byte_lut[(b16 >> 8) & 0xFFu];
+      const v4i kv = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y)};
       acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qx[w], acc, 0, 0, 0);
     }
     return acc;
   };
 
-  // =========================================================== logits export
-  if (MODE == 2) {
-    k_load(0);
-    k_store(0);
+  // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
+  // body(u, gc) runs per chunk with a one-chunk logit lookahead.
+  auto k_sweep = [&](auto&& body) {
+    const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
+    k_load(0, C::kCH1);
+    __syncthreads();  // previous users of the key buffers are done
+    k_store(0, C::kCH1);
     __syncthreads();
-    for (int it = 0; it < niter; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < niter) k_load(it + 1);
-      for (int c = 0; c < kCH; ++c) {
-        const int gc = it * kCH + c;
-        if (gc >= nchunk) break;
-        const v16i u = logits_tile(buf, c);
-        if (!qvalid) continue;
-        const int kbase = half * Hh + 16 * gc;
-        int16_t* dst = a.logits + (bh_local * a.row_count + (i_row - a.row_begin)) * static_cast<int64_t>(n);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kbase + i < lim) dst[kbase + i] = static_cast<int16_t>(-u[i]);
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int buf = gi & 1;
+      if (gi + 1 < ngroups) k_load((gi + 1) * C::kCH1, C::kCH1);
+      const int g0 = gi * C::kCH1;
+      const int cend = min(C::kCH1, wchunks - g0);
+      if (cend > 0) {
+        v16i u_next = logits_tile(buf, 0);
+        for (int c = 0; c < cend; ++c) {
+          const v16i u = u_next;
+          if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
+          body(u, g0 + c);
+        }
       }
-      if (it + 1 < niter) k_store(buf ^ 1);
+      if (gi + 1 < ngroups) k_store(buf ^ 1, C::kCH1);
       __syncthreads();
     }
+  };
+
+  // =========================================================== logits export
+  if (MODE == 2) {
+    int16_t* dst = a.logits + (bh_local * a.row_count + (qvalid ? i_row - a.row_begin : 0)) * static_cast<int64_t>(n);
+    k_sweep([&](const v16i& u, int gc) {
+      if (!qvalid) return;
+      const int kbase = half * Hh + 16 * gc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kbase + i < lim) dst[kbase + i] = static_cast<int16_t>(-u[i]);
+    });
     return;
   }
 
@@ -291,44 +297,29 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     for (int t = lane; t < (d + 1) * 32; t += 64) hist[t] = 0u;
   }
   const uint32_t addend = half ? 0x10000u : 1u;
-  // byte offset of bin (d + u)/2 for this lane's query: hb + 64*u
-  unsigned char* hb = lds + C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4 + 64 * d;
-
-  k_load(0);
-  k_store(0);
-  __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < niter) k_load(it + 1);
-    for (int c = 0; c < kCH; ++c) {
-      const int gc = it * kCH + c;
-      if (gc >= nchunk) break;
-      if (16 * gc >= wlim) break;  // nothing visible to this wave any more
-      const v16i u = logits_tile(buf, c);
-      const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
-      if (__all(L >= 16)) {
+  // LDS address of bin (d + u)/2 for this lane's query: hb + 64*u
+  const uint32_t hb = opaque(lds_addr(region + (wid * (d + 1) * 32 + ql) * 4 + 64 * d));
+  k_sweep([&](const v16i& u, int gc) {
+    const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
+    if (__all(L >= 16)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          atomicAdd(reinterpret_cast<uint32_t*>(hb + u[i] * 64), addend);
-      } else {
+      for (int i = 0; i < 16; ++i) __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(hb + u[i] * 64)), addend, __ATOMIC_RELAXED);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < L) atomicAdd(reinterpret_cast<uint32_t*>(hb + u[i] * 64), addend);
-      }
+      for (int i = 0; i < 16; ++i)
+        if (i < L) __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(hb + u[i] * 64)), addend, __ATOMIC_RELAXED);
     }
-    if (it + 1 < niter) k_store(buf ^ 1);
-    __syncthreads();
-  }
+  });
 
   // =========================================================== per-row statistics
   const int Ni = qvalid ? min(a.topn, lim) : 0;
   int T = 0, hmin = 0, below0 = 0, ties0 = 0, below = 0;
+  const uint32_t* hq = reinterpret_cast<const uint32_t*>(region) + wid * (d + 1) * 32 + ql;
   {
-    const int h0 = C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4;
     int cum = 0, cum0 = 0;
     bool have_min = false;
     for (int b = 0; b <= d; ++b) {
-      const uint32_t x = lds_u32(lds, h0 + b * 128);
+      const uint32_t x = hq[b * 32];
       const int c0 = static_cast<int>(x & 0xFFFFu);
       const int cnt = c0 + static_cast<int>(x >> 16);
       if (!have_min && cnt > 0) {
@@ -348,38 +339,30 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   }
   const int r_tie = Ni - below;
   const int quota0 = min(r_tie, ties0);
-  int quota = half ? (r_tie - quota0) : quota0;
+  const int quota = half ? (r_tie - quota0) : quota0;
   const int uT = (Ni > 0) ? 2 * T - d : -(d + 2);  // rows with nothing to keep never match
+  // Element i of this lane (ascending keys) is kept iff
+  //   u_i < uT, or u_i == uT and fewer than `quota` ties precede it here,
+  // i.e. iff u_i * 2^15 + ties_seen < uT * 2^15 + quota (ties_seen and quota
+  // stay below 2^15 because a half holds at most 32768 + 15 keys).
+  const int tie_key = uT * 32768 + quota;
+  int ties_seen = 0;
 
   if (MODE == 1) {
     // ======================================================= selection export
     int pos = half ? (below0 + quota0) : 0;
     int32_t* dst = a.idx + (bh_local * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(a.topn);
-    k_load(0);
-    k_store(0);
-    __syncthreads();
-    for (int it = 0; it < niter; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < niter) k_load(it + 1);
-      for (int c = 0; c < kCH; ++c) {
-        const int gc = it * kCH + c;
-        if (gc >= nchunk) break;
-        if (16 * gc >= wlim) break;
-        const v16i u = logits_tile(buf, c);
-        const int kbase = half * Hh + 16 * gc;
-        const int L = lim - kbase;
+    k_sweep([&](const v16i& u, int gc) {
+      const int kbase = half * Hh + 16 * gc;
+      const int L = lim - kbase;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool valid = i < L;
-          const bool eq = valid && (u[i] == uT);
-          const bool keep = (valid && u[i] < uT) || (eq && quota > 0);
-          quota -= eq ? 1 : 0;
-          if (keep && pos < a.topn) dst[pos++] = kbase + i;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int ui = (i < L) ? u[i] : kInvisible;
+        const bool keep = ui * 32768 + ties_seen < tie_key;
+        ties_seen += (ui == uT) ? 1 : 0;
+        if (keep && pos < a.topn) dst[pos++] = kbase + i;
       }
-      if (it + 1 < niter) k_store(buf ^ 1);
-      __syncthreads();
-    }
+    });
     if (qvalid && half == 0)
       for (int p = Ni; p < a.topn; ++p) dst[p] = -1;
     return;
@@ -388,9 +371,8 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // =========================================================== pass 2: attend
   float Z = 0.0f;
   if (Ni > 0) {
-    const int h0 = C::kRegionOff + (wid * (d + 1) * 32 + ql) * 4;
     for (int b = hmin; b < T; ++b) {
-      const uint32_t x = lds_u32(lds, h0 + b * 128);
+      const uint32_t x = hq[b * 32];
       const int cnt = static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16);
       const uint32_t e = wlut[b - hmin];
       const float w = VF32 ? u2f(e) : bf16_to_f(e & 0xFFFFu) + bf16_to_f(e >> 16);
@@ -401,39 +383,34 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     Z += static_cast<float>(r_tie) * w;
   }
   const float invZ = (Z > 0.0f) ? 1.0f / Z : 0.0f;
-  // weight-table byte address of u: wlut + 4*((d + u)/2 - hmin) = lutc + 2u
+  // weight-table LDS address of u: wlut + 4*((d + u)/2 - hmin) = lutc + 2u
   const uint32_t lutc = opaque(lds_addr(lds + kWLutOff + 2 * d - 4 * hmin));
   const uint32_t zaddr = opaque(lds_addr(lds + kWLutOff + 4 * kZeroSlot));
-  // Element i of this lane (ascending keys) is kept iff
-  //   u_i < uT, or u_i == uT and fewer than `quota` ties precede it here,
-  // i.e. iff u_i * 2^15 + ties_seen < uT * 2^15 + quota (ties_seen and quota
-  // stay below 2^15 because a half holds at most 32768 + 15 keys).
-  const int tie_key = uT * 32768 + quota;
-  int ties_seen = 0;
 
   v16f acc[W];
 #pragma unroll
   for (int t = 0; t < W; ++t) acc[t] = v16f{};
 
-  // V rows of the slice; staged transposed: vt[buf][c][feature][slot], slot =
-  // 16*half + (key - half*Hh - 16*gc).
+  // V rows of the slice, staged transposed: vt[buf][c][feature][slot] with
+  // slot = 16*half + (key - half*Hh - 16*gc).
   const unsigned char* vsrc = static_cast<const unsigned char*>(a.v) +
                               bh * static_cast<int64_t>(n) * d * (VF32 ? 4 : 2);
   // bf16 items: (slot pair sp, 4-feature group g, chunk c), sp fastest: the
   // two g parities of a half-wave land 16 banks apart -> conflict-free writes.
   // fp32 items: (slot, 4-feature group, chunk), slot fastest.
-  constexpr int kVItems = VF32 ? kCH * 32 * (C::kDP / 4) : kCH * 16 * (C::kDP / 4);
+  constexpr int kG = C::kDP / 4;
+  constexpr int kVItems = VF32 ? C::kCH2 * 32 * kG : C::kCH2 * 16 * kG;
   constexpr int kVPT = (kVItems + C::kThreads - 1) / C::kThreads;
   uint32_t vreg[kVPT][4];
-  auto v_load = [&](int it) {
+  auto v_load = [&](int g0) {
 #pragma unroll
     for (int j = 0; j < kVPT; ++j) {
       const int item = tid + j * C::kThreads;
       if (VF32) {
         const int slot = item & 31;
-        const int g = (item >> 5) % (C::kDP / 4);
-        const int c = item / (32 * (C::kDP / 4));
-        const int gc = it * kCH + c;
+        const int g = (item >> 5) % kG;
+        const int c = item / (32 * kG);
+        const int gc = g0 + c;
         const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
         const bool kv = item < kVItems && gc < nchunk && key < kend;
         const float* row = reinterpret_cast<const float*>(vsrc) + static_cast<int64_t>(kv ? key : 0) * d;
@@ -446,11 +423,10 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
         }
       } else {
         const int sp = item & 15;
-        const int g = (item >> 4) % (C::kDP / 4);
-        const int c = item / (16 * (C::kDP / 4));
-        const int gc = it * kCH + c;
-        const int slot = 2 * sp;
-        const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
+        const int g = (item >> 4) % kG;
+        const int c = item / (16 * kG);
+        const int gc = g0 + c;
+        const int key = ((2 * sp) >> 4) * Hh + 16 * gc + ((2 * sp) & 15);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const bool kv = item < kVItems && gc < nchunk && key + kk < kend;
@@ -471,22 +447,22 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     }
   };
   auto v_store = [&](int buf) {
-    unsigned char* vt = region + buf * (kCH * C::kDP * VS);
+    unsigned char* vt = region + buf * C::kVBuf;
 #pragma unroll
     for (int j = 0; j < kVPT; ++j) {
       const int item = tid + j * C::kThreads;
       if (item >= kVItems) break;
       if (VF32) {
         const int slot = item & 31;
-        const int g = (item >> 5) % (C::kDP / 4);
-        const int c = item / (32 * (C::kDP / 4));
+        const int g = (item >> 5) % kG;
+        const int c = item / (32 * kG);
         unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * slot;
 #pragma unroll
         for (int k = 0; k < 4; ++k) *reinterpret_cast<uint32_t*>(dst + k * VS) = vreg[j][k];
       } else {
         const int sp = item & 15;
-        const int g = (item >> 4) % (C::kDP / 4);
-        const int c = item / (16 * (C::kDP / 4));
+        const int g = (item >> 4) % kG;
+        const int c = item / (16 * kG);
         unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * sp;
         const uint32_t a0 = vreg[j][0], a1 = vreg[j][1], b0 = vreg[j][2], b1 = vreg[j][3];
         // feature 4g+k: (key, key+1) packed as one dword
@@ -498,83 +474,81 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     }
   };
 
-  k_load(0);
+  const int ngroups2 = (nchunk + C::kCH2 - 1) / C::kCH2;
+  k_load(0, C::kCH2);
   v_load(0);
   __syncthreads();  // every wave is done with its histogram (V tiles alias it)
-  k_store(0);
+  k_store(0, C::kCH2);
   v_store(0);
   __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < niter) {
-      k_load(it + 1);
-      v_load(it + 1);
+  for (int gi = 0; gi < ngroups2; ++gi) {
+    const int buf = gi & 1;
+    if (gi + 1 < ngroups2) {
+      k_load((gi + 1) * C::kCH2, C::kCH2);
+      v_load((gi + 1) * C::kCH2);
     }
-    const unsigned char* vt = region + buf * (kCH * C::kDP * VS);
-    // all logit tiles of the group first: their matrix-core latency overlaps
-    // the vector work of the previous chunk
-    v16i ug[kCH];
-#pragma unroll
-    for (int c = 0; c < kCH; ++c)
-      if (it * kCH + c < nchunk && 16 * (it * kCH + c) < wlim) ug[c] = logits_tile(buf, c);
-#pragma unroll
-    for (int c = 0; c < kCH; ++c) {
-      const int gc = it * kCH + c;
-      if (gc >= nchunk) break;
-      if (16 * gc >= wlim) break;
-      const v16i u = ug[c];
-      const int L = lim - (half * Hh + 16 * gc);
-      uint32_t e[16];
-      if (__all(L >= 16)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ui = u[i];
-          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-          ties_seen += (ui == uT) ? 1 : 0;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ui = (i < L) ? u[i] : kInvisible;
-          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-          ties_seen += (ui == uT) ? 1 : 0;
-        }
-      }
-      const unsigned char* vbase = vt + c * C::kDP * VS;
-      if (VF32) {
-#pragma unroll
-        for (int t = 0; t < W; ++t) {
-          const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
+    const unsigned char* vt = region + buf * C::kVBuf;
+    const int g0 = gi * C::kCH2;
+    const int cend = min(C::kCH2, wchunks - g0);
+    if (cend > 0) {
+      v16i u_next = logits_tile(buf, 0);
+      for (int c = 0; c < cend; ++c) {
+        const v16i u = u_next;
+        if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
+        const int gc = g0 + c;
+        const int L = lim - (half * Hh + 16 * gc);
+        uint32_t e[16];
+        if (__all(L >= 16)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
+            const int ui = u[i];
+            e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+            ties_seen += (ui == uT) ? 1 : 0;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ui = (i < L) ? u[i] : kInvisible;
+            e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+            ties_seen += (ui == uT) ? 1 : 0;
           }
         }
-      } else {
-#pragma unroll
-        for (int ab = 0; ab < 2; ++ab) {
-          u32x4 ph, pl;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
-            ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
-            pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
-          }
-          const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
-          const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
+        const unsigned char* vbase = vt + c * C::kDP * VS;
+        if (VF32) {
 #pragma unroll
           for (int t = 0; t < W; ++t) {
-            const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (32 * t + ql) * VS + 32 * half + 16 * ab);
-            const v8bf av = __builtin_bit_cast(v8bf, vv);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
+            const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab) {
+            u32x4 ph, pl;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
+              ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
+              pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
+            }
+            const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
+            const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
+#pragma unroll
+            for (int t = 0; t < W; ++t) {
+              const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (32 * t + ql) * VS + 32 * half + 16 * ab);
+              const v8bf av = __builtin_bit_cast(v8bf, vv);
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
+            }
           }
         }
       }
     }
-    if (it + 1 < niter) {
-      k_store(buf ^ 1);
+    if (gi + 1 < ngroups2) {
+      k_store(buf ^ 1, C::kCH2);
       v_store(buf ^ 1);
     }
     __syncthreads();
