@@ -65,24 +65,30 @@ __host__ __device__ constexpr int waves_for(int W) { return W <= 4 ? 4 : 2; }
 __host__ __device__ constexpr int threads_for(int W) { return 64 * waves_for(W); }
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int W, bool VF32>
+template <int W, bool VF32, bool VDIRECT>
 struct Cfg {
   static constexpr int kWaves = waves_for(W);
   static constexpr int kThreads = threads_for(W);
   static constexpr int kQB = 32 * kWaves;  // query rows per block
   static constexpr int kDP = 32 * W;       // padded feature count
-  // 16-key chunks per half in one key group: K-only loops (4 KB of key
+  // 16-key chunks per half in one key group: K-only loops (2 KB of key
   // words) and the attend loop (V tile of about 16 KB)
-  static constexpr int kCH1 = 32 / W;
+  static constexpr int kCH1 = W <= 2 ? 16 / W : 32 / W;
   static constexpr int kCH2 = VF32 ? (W <= 2 ? 2 : 1) : (W <= 2 ? 4 : (W <= 4 ? 2 : 1));
   static constexpr int kKb1 = kCH1 * 32 * W * 4;  // bytes of key words per group
   static constexpr int kKb2 = kCH2 * 32 * W * 4;
   static constexpr int kKbBuf = cmax(kKb1, kKb2);
   static constexpr int kVS = VF32 ? 144 : 80;     // bytes per staged feature row
-  static constexpr int kVBuf = kCH2 * kDP * kVS;
+  // V tile: transposed [feature][slot] rows of kVS bytes, or (VDIRECT) the
+  // row-major [slot][feature] rows copied straight from global memory
+  static constexpr int kVBuf = VDIRECT ? kCH2 * 32 * 2 * kDP : kCH2 * kDP * kVS;
   static constexpr int kHist = kWaves * (kDP + 1) * 32 * 4;
   static constexpr int kRegionOff = kKbOff + 2 * kKbBuf;
   static constexpr int kLdsBytes = kRegionOff + cmax(kHist, 2 * kVBuf);
+  // 16-byte pieces of a row-major V row, and the piece swizzle that makes the
+  // transposed operand reads bank-conflict free (power-of-two rows only)
+  static constexpr int kPieces = kDP / 8;
+  static constexpr int kSwzMask = ((kPieces & (kPieces - 1)) == 0) ? (kPieces - 1) & 6 : 0;
 };
 
 __device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -113,6 +119,9 @@ __device__ inline uint32_t pad_mask4(int base, int d) {
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 __device__ inline uint32_t lds_addr(const unsigned char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_byte*)p));
 }
@@ -126,9 +135,9 @@ __device__ inline uint32_t opaque(uint32_t v) {
   return v;
 }
 
-template <int W, bool VF32, int MODE>
+template <int W, bool VF32, int MODE, bool VDIRECT>
 __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
-  using C = Cfg<W, VF32>;
+  using C = Cfg<W, VF32, VDIRECT>;
   constexpr int VS = C::kVS;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::kLdsBytes];
   const uint2* byte_lut = reinterpret_cast<const uint2*>(lds + kByteLutOff);
@@ -208,29 +217,29 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // operand is zero there.
   const uint32_t* kbg = a.kbits + bh * static_cast<int64_t>(n) * W;
   auto key_of = [&](int gc, int m) { return ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3); };
-  constexpr int kKPT1 = (C::kCH1 * 32 * W + C::kThreads - 1) / C::kThreads;
-  constexpr int kKPT2 = (C::kCH2 * 32 * W + C::kThreads - 1) / C::kThreads;
-  constexpr int kKPT = cmax(kKPT1, kKPT2);
-  uint32_t kreg[kKPT];
-  auto k_load = [&](int g0, int ch) {  // chunks [g0, g0 + ch)
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) {
-      const int item = tid + j * C::kThreads;
-      const int w = item % W;
-      const int m = (item / W) & 31;
-      const int c = item / (W * 32);
-      const int gc = g0 + c;
-      const int key = key_of(gc, m);
-      kreg[j] = (c < ch && gc < nchunk && key < kend) ? kbg[static_cast<int64_t>(key) * W + w] : 0u;
+  // Copies the key words of chunks [g0, g0 + ch) straight into buffer buf
+  // (global_load_lds, 4 bytes per lane, lane-ordered); keys outside the
+  // visible range load key 0 (their logits are masked).
+  auto k_issue = [&](int g0, int ch, int buf) {
+    const int items = ch * 32 * W;
+    for (int j = wid; j * 64 < items; j += C::kWaves) {
+      const int item = j * 64 + lane;
+      if (item < items) {
+        const int w = item % W;
+        const int m = (item / W) & 31;
+        const int c = item / (W * 32);
+        const int gc = g0 + c;
+        int key = key_of(gc, m);
+        if (gc >= nchunk || key >= kend) key = 0;
+        __builtin_amdgcn_global_load_lds(kbg + static_cast<int64_t>(key) * W + w,
+                                         (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
+      }
     }
   };
-  auto k_store = [&](int buf, int ch) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(lds + kKbOff + buf * C::kKbBuf);
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) {
-      const int item = tid + j * C::kThreads;
-      if (item < ch * 32 * W) dst[item] = kreg[j];
-    }
+  // all of this thread's copies have landed; then the block barrier
+  auto copies_done = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   // u = -logit for (query ql, key half*Hh + 16*gc + i), i = 0..15, chunk c of
@@ -256,13 +265,12 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // body(u, gc) runs per chunk with a one-chunk logit lookahead.
   auto k_sweep = [&](auto&& body) {
     const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
-    k_load(0, C::kCH1);
     __syncthreads();  // previous users of the key buffers are done
-    k_store(0, C::kCH1);
-    __syncthreads();
+    k_issue(0, C::kCH1, 0);
+    copies_done();
     for (int gi = 0; gi < ngroups; ++gi) {
       const int buf = gi & 1;
-      if (gi + 1 < ngroups) k_load((gi + 1) * C::kCH1, C::kCH1);
+      if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, C::kCH1, buf ^ 1);
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
       if (cend > 0) {
@@ -273,8 +281,7 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
           body(u, g0 + c);
         }
       }
-      if (gi + 1 < ngroups) k_store(buf ^ 1, C::kCH1);
-      __syncthreads();
+      copies_done();
     }
   };
 
@@ -391,167 +398,223 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < W; ++t) acc[t] = v16f{};
 
-  // V rows of the slice, staged transposed: vt[buf][c][feature][slot] with
-  // slot = 16*half + (key - half*Hh - 16*gc).
   const unsigned char* vsrc = static_cast<const unsigned char*>(a.v) +
                               bh * static_cast<int64_t>(n) * d * (VF32 ? 4 : 2);
+
+  // ---- V staging, VDIRECT: row-major [slot][feature] bf16 tiles copied by
+  // global_load_lds (16 bytes per lane).  Piece pp of row r holds features
+  // 8*(pp ^ swz(r)) .. +7, swz(r) = 2*(r & 3) (masked to the row), so that
+  // the transposed operand reads below hit 32 distinct banks per 16 lanes.
+  // Keys outside the visible range copy key 0 (their weights are zero).
+  auto v_issue = [&](int g0, int buf) {
+    if constexpr (VDIRECT) {
+      constexpr int kInst = C::kCH2 * 32 * C::kPieces / 64;
+      for (int j = wid; j < kInst; j += C::kWaves) {
+        const int item = j * 64 + lane;
+        const int pp = item % C::kPieces;
+        const int r = (item / C::kPieces) & 31;
+        const int c = item / (C::kPieces * 32);
+        const int gc = g0 + c;
+        int key = (r >> 4) * Hh + 16 * gc + (r & 15);
+        if (gc >= nchunk || key >= kend) key = 0;
+        const int pc = pp ^ ((2 * (r & 3)) & C::kSwzMask);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(key) * d + 8 * pc,
+            (lds_void*)(region + buf * C::kVBuf + j * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- V staging, register path (fp32 V, or d not a multiple of 32):
+  // transposed vt[buf][c][feature][slot] with slot = 16*half + key offset.
   // bf16 items: (slot pair sp, 4-feature group g, chunk c), sp fastest: the
   // two g parities of a half-wave land 16 banks apart -> conflict-free writes.
   // fp32 items: (slot, 4-feature group, chunk), slot fastest.
   constexpr int kG = C::kDP / 4;
-  constexpr int kVItems = VF32 ? C::kCH2 * 32 * kG : C::kCH2 * 16 * kG;
-  constexpr int kVPT = (kVItems + C::kThreads - 1) / C::kThreads;
+  constexpr int kVItems = VDIRECT ? 0 : (VF32 ? C::kCH2 * 32 * kG : C::kCH2 * 16 * kG);
+  constexpr int kVPT = VDIRECT ? 1 : (kVItems + C::kThreads - 1) / C::kThreads;
   uint32_t vreg[kVPT][4];
   auto v_load = [&](int g0) {
+    if constexpr (!VDIRECT) {
 #pragma unroll
-    for (int j = 0; j < kVPT; ++j) {
-      const int item = tid + j * C::kThreads;
-      if (VF32) {
-        const int slot = item & 31;
-        const int g = (item >> 5) % kG;
-        const int c = item / (32 * kG);
-        const int gc = g0 + c;
-        const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
-        const bool kv = item < kVItems && gc < nchunk && key < kend;
-        const float* row = reinterpret_cast<const float*>(vsrc) + static_cast<int64_t>(kv ? key : 0) * d;
-        if (kv && (d & 3) == 0 && 4 * g + 4 <= d) {
-          const u32x4 t = *reinterpret_cast<const u32x4*>(row + 4 * g);
-          vreg[j][0] = t[0]; vreg[j][1] = t[1]; vreg[j][2] = t[2]; vreg[j][3] = t[3];
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vreg[j][k] = (kv && 4 * g + k < d) ? f2u(row[4 * g + k]) : 0u;
-        }
-      } else {
-        const int sp = item & 15;
-        const int g = (item >> 4) % kG;
-        const int c = item / (16 * kG);
-        const int gc = g0 + c;
-        const int key = ((2 * sp) >> 4) * Hh + 16 * gc + ((2 * sp) & 15);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bool kv = item < kVItems && gc < nchunk && key + kk < kend;
-          const uint16_t* row = reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(kv ? key + kk : 0) * d;
+      for (int j = 0; j < kVPT; ++j) {
+        const int item = tid + j * C::kThreads;
+        if (VF32) {
+          const int slot = item & 31;
+          const int g = (item >> 5) % kG;
+          const int c = item / (32 * kG);
+          const int gc = g0 + c;
+          const int key = (slot >> 4) * Hh + 16 * gc + (slot & 15);
+          const bool kv = item < kVItems && gc < nchunk && key < kend;
+          const float* row = reinterpret_cast<const float*>(vsrc) + static_cast<int64_t>(kv ? key : 0) * d;
           if (kv && (d & 3) == 0 && 4 * g + 4 <= d) {
-            const uint2 t = *reinterpret_cast<const uint2*>(row + 4 * g);
-            vreg[j][2 * kk] = t.x;
-            vreg[j][2 * kk + 1] = t.y;
+            const u32x4 t = *reinterpret_cast<const u32x4*>(row + 4 * g);
+            vreg[j][0] = t[0]; vreg[j][1] = t[1]; vreg[j][2] = t[2]; vreg[j][3] = t[3];
           } else {
-            uint32_t f[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) f[k] = (kv && 4 * g + k < d) ? row[4 * g + k] : 0u;
-            vreg[j][2 * kk] = f[0] | (f[1] << 16);
-            vreg[j][2 * kk + 1] = f[2] | (f[3] << 16);
+            for (int k = 0; k < 4; ++k) vreg[j][k] = (kv && 4 * g + k < d) ? f2u(row[4 * g + k]) : 0u;
+          }
+        } else {
+          const int sp = item & 15;
+          const int g = (item >> 4) % kG;
+          const int c = item / (16 * kG);
+          const int gc = g0 + c;
+          const int key = ((2 * sp) >> 4) * Hh + 16 * gc + ((2 * sp) & 15);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bool kv = item < kVItems && gc < nchunk && key + kk < kend;
+            const uint16_t* row = reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(kv ? key + kk : 0) * d;
+            if (kv && (d & 3) == 0 && 4 * g + 4 <= d) {
+              const uint2 t = *reinterpret_cast<const uint2*>(row + 4 * g);
+              vreg[j][2 * kk] = t.x;
+              vreg[j][2 * kk + 1] = t.y;
+            } else {
+              uint32_t f[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) f[k] = (kv && 4 * g + k < d) ? row[4 * g + k] : 0u;
+              vreg[j][2 * kk] = f[0] | (f[1] << 16);
+              vreg[j][2 * kk + 1] = f[2] | (f[3] << 16);
+            }
           }
         }
       }
     }
   };
   auto v_store = [&](int buf) {
-    unsigned char* vt = region + buf * C::kVBuf;
+    if constexpr (!VDIRECT) {
+      unsigned char* vt = region + buf * C::kVBuf;
 #pragma unroll
-    for (int j = 0; j < kVPT; ++j) {
-      const int item = tid + j * C::kThreads;
-      if (item >= kVItems) break;
-      if (VF32) {
-        const int slot = item & 31;
-        const int g = (item >> 5) % kG;
-        const int c = item / (32 * kG);
-        unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * slot;
+      for (int j = 0; j < kVPT; ++j) {
+        const int item = tid + j * C::kThreads;
+        if (item >= kVItems) break;
+        if (VF32) {
+          const int slot = item & 31;
+          const int g = (item >> 5) % kG;
+          const int c = item / (32 * kG);
+          unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * slot;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *reinterpret_cast<uint32_t*>(dst + k * VS) = vreg[j][k];
+          for (int k = 0; k < 4; ++k) *reinterpret_cast<uint32_t*>(dst + k * VS) = vreg[j][k];
+        } else {
+          const int sp = item & 15;
+          const int g = (item >> 4) % kG;
+          const int c = item / (16 * kG);
+          unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * sp;
+          const uint32_t a0 = vreg[j][0], a1 = vreg[j][1], b0 = vreg[j][2], b1 = vreg[j][3];
+          // feature 4g+k: (key, key+1) packed as one dword
+          *reinterpret_cast<uint32_t*>(dst + 0 * VS) = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+          *reinterpret_cast<uint32_t*>(dst + 1 * VS) = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+          *reinterpret_cast<uint32_t*>(dst + 2 * VS) = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+          *reinterpret_cast<uint32_t*>(dst + 3 * VS) = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+        }
+      }
+    }
+  };
+
+  // Transposed-read addressing (VDIRECT): within each 16-lane group G, lane
+  // 4k+q supplies the 8-byte row piece (slot S + k, features f0 + 4q) and
+  // ds_read_b64_tr_b16 returns to lane j the four values (slot S + k,
+  // feature f0 + j), k = 0..3.  S = 16*(G>>1) + 8*ab + 4*second_read,
+  // f0 = 32*t + 16*(G&1).
+  const int trG = lane >> 4, trk = (lane >> 2) & 3, trq = lane & 3;
+  const int tr_row = 16 * (trG >> 1) + trk;                 // + 8*ab + 4*second
+  const int tr_swz = (2 * trk) & C::kSwzMask;               // slot & 3 == trk
+  const int tr_f = 16 * (trG & 1) + 4 * trq;                // + 32*t
+  auto v_operand = [&](const unsigned char* vchunk, int t, int ab) {
+    const int f = 32 * t + tr_f;
+    const int off = (tr_row + 8 * ab) * 2 * C::kDP + (((f >> 3) ^ tr_swz) << 4) + 2 * (f & 7);
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vchunk + off));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vchunk + off + 4 * 2 * C::kDP));
+    const u32x4 u = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(r0, r0, 0, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(r0, r0, 2, 3)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(r1, r1, 0, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(r1, r1, 2, 3))};
+    return __builtin_bit_cast(v8bf, u);
+  };
+
+  auto attend_group = [&](int buf, int gi) {
+    const unsigned char* vt = region + buf * C::kVBuf;
+    const int g0 = gi * C::kCH2;
+    const int cend = min(C::kCH2, wchunks - g0);
+    if (cend <= 0) return;
+    v16i u_next = logits_tile(buf, 0);
+    for (int c = 0; c < cend; ++c) {
+      const v16i u = u_next;
+      if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
+      const int gc = g0 + c;
+      const int L = lim - (half * Hh + 16 * gc);
+      uint32_t e[16];
+      if (__all(L >= 16)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ui = u[i];
+          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+          ties_seen += (ui == uT) ? 1 : 0;
+        }
       } else {
-        const int sp = item & 15;
-        const int g = (item >> 4) % kG;
-        const int c = item / (16 * kG);
-        unsigned char* dst = vt + (c * C::kDP + 4 * g) * VS + 4 * sp;
-        const uint32_t a0 = vreg[j][0], a1 = vreg[j][1], b0 = vreg[j][2], b1 = vreg[j][3];
-        // feature 4g+k: (key, key+1) packed as one dword
-        *reinterpret_cast<uint32_t*>(dst + 0 * VS) = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(dst + 1 * VS) = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-        *reinterpret_cast<uint32_t*>(dst + 2 * VS) = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(dst + 3 * VS) = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ui = (i < L) ? u[i] : kInvisible;
+          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
+          ties_seen += (ui == uT) ? 1 : 0;
+        }
+      }
+      if constexpr (VF32) {
+        const unsigned char* vbase = vt + c * C::kDP * VS;
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab) {
+          u32x4 ph, pl;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
+            ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
+            pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
+          }
+          const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
+          const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
+#pragma unroll
+          for (int t = 0; t < W; ++t) {
+            v8bf av;
+            if constexpr (VDIRECT) {
+              av = v_operand(vt + c * 32 * 2 * C::kDP, t, ab);
+            } else {
+              const u32x4 vv = *reinterpret_cast<const u32x4*>(vt + c * C::kDP * VS + (32 * t + ql) * VS + 32 * half + 16 * ab);
+              av = __builtin_bit_cast(v8bf, vv);
+            }
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
+          }
+        }
       }
     }
   };
 
   const int ngroups2 = (nchunk + C::kCH2 - 1) / C::kCH2;
-  k_load(0, C::kCH2);
   v_load(0);
   __syncthreads();  // every wave is done with its histogram (V tiles alias it)
-  k_store(0, C::kCH2);
+  k_issue(0, C::kCH2, 0);
+  v_issue(0, 0);
   v_store(0);
-  __syncthreads();
+  copies_done();
   for (int gi = 0; gi < ngroups2; ++gi) {
     const int buf = gi & 1;
     if (gi + 1 < ngroups2) {
-      k_load((gi + 1) * C::kCH2, C::kCH2);
+      k_issue((gi + 1) * C::kCH2, C::kCH2, buf ^ 1);
+      v_issue((gi + 1) * C::kCH2, buf ^ 1);
       v_load((gi + 1) * C::kCH2);
     }
-    const unsigned char* vt = region + buf * C::kVBuf;
-    const int g0 = gi * C::kCH2;
-    const int cend = min(C::kCH2, wchunks - g0);
-    if (cend > 0) {
-      v16i u_next = logits_tile(buf, 0);
-      for (int c = 0; c < cend; ++c) {
-        const v16i u = u_next;
-        if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
-        const int gc = g0 + c;
-        const int L = lim - (half * Hh + 16 * gc);
-        uint32_t e[16];
-        if (__all(L >= 16)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ui = u[i];
-            e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-            ties_seen += (ui == uT) ? 1 : 0;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ui = (i < L) ? u[i] : kInvisible;
-            e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-            ties_seen += (ui == uT) ? 1 : 0;
-          }
-        }
-        const unsigned char* vbase = vt + c * C::kDP * VS;
-        if (VF32) {
-#pragma unroll
-          for (int t = 0; t < W; ++t) {
-            const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            u32x4 ph, pl;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
-              ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
-              pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
-            }
-            const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
-            const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
-#pragma unroll
-            for (int t = 0; t < W; ++t) {
-              const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (32 * t + ql) * VS + 32 * half + 16 * ab);
-              const v8bf av = __builtin_bit_cast(v8bf, vv);
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-    if (gi + 1 < ngroups2) {
-      k_store(buf ^ 1, C::kCH2);
-      v_store(buf ^ 1);
-    }
-    __syncthreads();
+    attend_group(buf, gi);
+    if (gi + 1 < ngroups2) v_store(buf ^ 1);
+    copies_done();
   }
 
   // =========================================================== epilogue
@@ -576,15 +639,15 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   }
 }
 
-template <int W, bool VF32, int MODE>
+template <int W, bool VF32, int MODE, bool VDIRECT = false>
 had_status launch_one(const AttnArgs& a, hipStream_t st) {
-  using C = Cfg<W, VF32>;
+  using C = Cfg<W, VF32, VDIRECT>;
   const int qrows = (MODE == 2) ? a.row_count : a.n;
   const int64_t ntq = (qrows + C::kQB - 1) / C::kQB;
   const int64_t blocks = ntq * a.bh_count;
   if (blocks <= 0) return HAD_OK;
   if (blocks > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "grid too large");
-  had_attn_kernel<W, VF32, MODE><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
+  had_attn_kernel<W, VF32, MODE, VDIRECT><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
   return check_launch(MODE == 0 ? "had_attention" : (MODE == 1 ? "had_select" : "had_logits"));
 }
 
@@ -592,7 +655,10 @@ template <int W>
 had_status launch_w(AttnMode mode, const AttnArgs& a, hipStream_t st) {
   switch (mode) {
     case AttnMode::Attend:
-      return a.v_dtype == HAD_F32 ? launch_one<W, true, 0>(a, st) : launch_one<W, false, 0>(a, st);
+      if (a.v_dtype == HAD_F32) return launch_one<W, true, 0>(a, st);
+      // bf16 V with d a multiple of 32: rows copied straight into LDS
+      if (a.d == 32 * W) return launch_one<W, false, 0, true>(a, st);
+      return launch_one<W, false, 0>(a, st);
     case AttnMode::Select:
       return launch_one<W, false, 1>(a, st);
     case AttnMode::Logits:

@@ -165,6 +165,9 @@ ATTN_CASES = [
     (1, 1, 130, 64, 1, False, "f32", 0.125),
     (1, 1, 1, 64, 4, True, "bf16", 0.125),
     (1, 1, 100, 64, 16, False, "bf16", 3.0),   # sharp softmax
+    (2, 2, 177, 32, 20, True, "bf16", 0.2),    # d = 32: one word per row
+    (1, 2, 160, 96, 30, False, "bf16", 0.1),   # d = 96: three words per row
+    (1, 1, 90, 256, 40, True, "f32", 1 / 16),  # fp32 V at d = 256
 ]
 
 
