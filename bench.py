@@ -24,7 +24,6 @@ run faster than this vector-unit bound (frac > 1).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -62,17 +61,11 @@ def work_model(w):
             "lane_ops": lane_ops, "hbm_bytes": hbm}
 
 
-def source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_attention_had_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_for(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
+    from sparse_attention_had_amd.profiling import source_hash
+
     path = os.path.join(ROOT, "profiles", f"traffic_had_attention_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -124,6 +117,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only had_attention launches (for profiling runs)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for HBM counter runs: 3 attention launches, then one plain "
+                         "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -152,6 +148,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ws_q = torch.zeros(had.pack_workspace_bytes(q.shape), dtype=torch.uint8, device=dev)
     ws_k = torch.zeros_like(ws_q)
+
+    if args.traffic_probe:
+        from sparse_attention_had_amd.profiling import COPY_BYTES
+
+        had.pack(q, out=qb, sigma=sq, workspace=ws_q)
+        had.pack(k, out=kb, sigma=sk, workspace=ws_k)
+        for _ in range(3):
+            had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": name, "copy_bytes": COPY_BYTES}), flush=True)
+        return
 
     def step():
         if not args.attention_only:
