@@ -70,7 +70,8 @@ size_t had_pack_workspace_bytes(had_shape s);
  * referee minor comment 6 on Eq. 12 (sigma is the standard deviation over all
  * elements of the matrix).
  *
- *  x          [B,H,n,d] float32, device.  Read once.
+ *  x          [B,H,n,d] float32, device, 4-byte aligned (16-byte alignment
+ *             takes the faster vector path).  Read once.
  *  xbits      [B,H,n,W] uint32, device, W = had_words_per_row(d).  Bit
  *             (c mod 32) of word floor(c/32) of a row is 1 exactly when
  *             x[c] < 0 (so +0.0 and -0.0 give 0, i.e. +1); unused high bits
@@ -79,7 +80,7 @@ size_t had_pack_workspace_bytes(had_shape s);
  *  sigma      device float*, or NULL.  When non-NULL it receives the
  *             population standard deviation of all B*H*n*d elements
  *             (float64 accumulation, deterministic order, rounded to float).
- *  workspace  device memory of had_pack_workspace_bytes(s) bytes, 8-byte
+ *  workspace  device memory of had_pack_workspace_bytes(s) bytes, 16-byte
  *             aligned, required when sigma != NULL (ignored otherwise).  It
  *             holds per-block partial sums; no initial contents are needed.
  *             Calls that may run at the same time need distinct workspaces.

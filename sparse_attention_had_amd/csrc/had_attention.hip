@@ -12,11 +12,13 @@
 // one (batch, head) slice; the n x n matrix never leaves the registers.
 //
 //  * Logits on the int8 matrix cores.  v_mfma_i32_32x32x32_i8 computes
-//    u = -s exactly for a tile of 32 keys x 32 queries and 32 features: the Q
-//    operand holds -q as +-1 bytes (expanded once per wave, zero in the pad
-//    features), the K operand is expanded per wave from the packed key words
-//    in LDS through a 256-entry byte table.  Carrying u = -s makes every
-//    address below a single shift-add.
+//    c + k*u, u = -s, exactly for a tile of 32 keys x 32 queries and 32
+//    features: the Q operand holds -k*q as bytes (k = 64 in pass 1, 2 in
+//    pass 2; zero in the pad features), the K operand is expanded per wave
+//    from the packed key words in LDS through a 256-entry byte table, and the
+//    accumulator starts at a per-lane LDS base c.  The result is then directly
+//    the LDS address of the element's histogram bin (pass 1) or weight-table
+//    entry (pass 2): no address arithmetic per element.
 //  * Key order.  The block's visible key range [0, kend) is split at Hh into
 //    two halves.  In the output tile the registers i = 0..15 of lane L hold
 //    query L%32 and keys half*Hh + 16*chunk + i with half = L/32, so every lane
@@ -30,7 +32,8 @@
 //    halves, h_min and the softmax denominator Z (from counts, without V).
 //  * Pass 2.  The logits are recomputed on the matrix cores (cheaper than
 //    storing them), each element is kept or dropped with one compare of a
-//    composite key, its weight exp(-2*scale*(h - h_min)) is read from an LDS
+//    composite key (its table address shifted left by 15 plus the running
+//    tie count), its weight exp(-2*scale*(h - h_min)) is read from an LDS
 //    table as a pair of bf16 terms (hi + lo, relative error < 2^-15), and
 //    out^T = V^T P^T runs on v_mfma_f32_32x32x16_bf16 (two products, hi and
 //    lo) with V staged transposed in LDS.  fp32 V uses v_mfma_f32_32x32x2_f32
@@ -39,10 +42,12 @@
 //    bandwidth per kept pair, the tile product reuses every staged V row for
 //    32 query rows.
 //  * Staging.  Key words (and, in pass 2, V rows) of the next key group are
-//    loaded into registers while the current group is computed from LDS, then
-//    written to the other LDS buffer: one barrier per key group.  Groups are
-//    large (pass 1: 4 KB of key words; pass 2: about 16 KB of V) so that the
-//    compute of one group hides the load latency of the next.
+//    copied into the other LDS buffer with asynchronous global-to-LDS loads
+//    while the current group is computed: one barrier per key group.  fp32 V
+//    and feature counts that are not a multiple of 32 go through registers
+//    and are stored transposed.  Groups are large (pass 1: 4 KB of key words;
+//    pass 2: about 16 KB of V) so that the compute of one group hides the load
+//    latency of the next.
 #include "had_internal.h"
 
 namespace had {
@@ -56,7 +61,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLutEntries = 264;        // weight table: d+1 weights + zero slot
 constexpr int kZeroSlot = 263;
-constexpr int kInvisible = 1 << 12;     // stands in for the logit of a masked key
 constexpr int kByteLutOff = 0;          // 256 x 8 B: byte -> 8 int8 of +-1
 constexpr int kWLutOff = 2048;          // kLutEntries x 4 B
 constexpr int kKbOff = kWLutOff + 4 * kLutEntries;
@@ -101,11 +105,13 @@ __device__ inline uint32_t bf16_rne(float f) {
 }
 __device__ inline float bf16_to_f(uint32_t b) { return u2f(b << 16); }
 
-// 4 sign bits -> 4 int8 lanes of +1 (bit 0) / -1 (bit 1).
-__device__ inline uint32_t expand_nibble(uint32_t nib) {
+// 4 sign bits -> 4 int8 lanes of +k (bit 0) / -k (bit 1); pos is the byte
+// of +k and flip = byte(+k) ^ byte(-k).
+__device__ inline uint32_t expand_nibble_k(uint32_t nib, uint32_t pos, uint32_t flip) {
   const uint32_t y = (nib * 0x00204081u) & 0x01010101u;  // bit k -> byte k
-  return (y * 0xFEu) | 0x01010101u;
+  return (y * flip) ^ (pos * 0x01010101u);
 }
+__device__ inline uint32_t expand_nibble(uint32_t nib) { return expand_nibble_k(nib, 0x01u, 0xFEu); }
 
 // Byte mask keeping the features [base, base+4) that are < d.
 __device__ inline uint32_t pad_mask4(int base, int d) {
@@ -196,20 +202,25 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- Q operand: -q as +-1 bytes, features 32w + 16*half + [0,16); pad = 0
+  // ---- Q operand: -k*q as bytes, features 32w + 16*half + [0,16); pad = 0
   v4i qx[W];
+  uint32_t qwords[W];
   {
     const uint32_t* qrow = a.qbits + (bh * n + (qvalid ? i_row : 0)) * W;
 #pragma unroll
+    for (int w = 0; w < W; ++w) qwords[w] = qvalid ? ~qrow[w] : ~0u;  // complement: the product is -s
+  }
+  auto make_q = [&](uint32_t pos, uint32_t flip) {
+#pragma unroll
     for (int w = 0; w < W; ++w) {
-      const uint32_t word = qvalid ? ~qrow[w] : ~0u;  // complement: the product is -s
-      const uint32_t b16 = (word >> (16 * half)) & 0xFFFFu;
+      const uint32_t b16 = (qwords[w] >> (16 * half)) & 0xFFFFu;
       const int fbase = 32 * w + 16 * half;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        qx[w][k] = static_cast<int>(expand_nibble((b16 >> (4 * k)) & 15u) & pad_mask4(fbase + 4 * k, d));
+        qx[w][k] = static_cast<int>(expand_nibble_k((b16 >> (4 * k)) & 15u, pos, flip) &
+                                    pad_mask4(fbase + 4 * k, d));
     }
-  }
+  };
 
   // ---- key words: kb[c][m][w], m = MFMA row of the logit tile.  Row m holds
   // key (m>>2 & 1)*Hh + 16*gc + 4*(m>>3) + (m&3), i.e. register i of lane L
@@ -229,8 +240,8 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
         const int m = (item / W) & 31;
         const int c = item / (W * 32);
         const int gc = g0 + c;
-        int key = key_of(gc, m);
-        if (gc >= nchunk || key >= kend) key = 0;
+        // keys past the visible range (never used) load a valid row
+        const int key = min(key_of(gc, m), kend - 1);
         __builtin_amdgcn_global_load_lds(kbg + static_cast<int64_t>(key) * W + w,
                                          (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
       }
@@ -242,14 +253,16 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  // u = -logit for (query ql, key half*Hh + 16*gc + i), i = 0..15, chunk c of
-  // the key-word buffer buf.
-  auto logits_tile = [&](int buf, int c) {
+  // cin + k*u, u = -logit, for (query ql, key half*Hh + 16*gc + i),
+  // i = 0..15, chunk c of the key-word buffer buf (k set by make_q).
+  auto logits_tile = [&](int buf, int c, uint32_t cin) {
     const uint32_t* krow = reinterpret_cast<const uint32_t*>(lds + kKbOff + buf * C::kKbBuf) + (c * 32 + ql) * W;
     uint32_t words[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) words[w] = krow[w];
-    v16i acc = {};
+    v16i acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = static_cast<int>(cin);
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const uint32_t b16 = words[w] >> (16 * half);
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
 
   // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
   // body(u, gc) runs per chunk with a one-chunk logit lookahead.
-  auto k_sweep = [&](auto&& body) {
+  auto k_sweep = [&](uint32_t cin, auto&& body) {
     const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
     __syncthreads();  // previous users of the key buffers are done
     k_issue(0, C::kCH1, 0);
@@ -274,10 +287,10 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
       if (cend > 0) {
-        v16i u_next = logits_tile(buf, 0);
+        v16i u_next = logits_tile(buf, 0, cin);
         for (int c = 0; c < cend; ++c) {
           const v16i u = u_next;
-          if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
+          if (c + 1 < cend) u_next = logits_tile(buf, c + 1, cin);
           body(u, g0 + c);
         }
       }
@@ -288,7 +301,8 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // =========================================================== logits export
   if (MODE == 2) {
     int16_t* dst = a.logits + (bh_local * a.row_count + (qvalid ? i_row - a.row_begin : 0)) * static_cast<int64_t>(n);
-    k_sweep([&](const v16i& u, int gc) {
+    make_q(0x01u, 0xFEu);  // +-1: the tile holds u itself
+    k_sweep(0u, [&](const v16i& u, int gc) {
       if (!qvalid) return;
       const int kbase = half * Hh + 16 * gc;
 #pragma unroll
@@ -304,17 +318,21 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     for (int t = lane; t < (d + 1) * 32; t += 64) hist[t] = 0u;
   }
   const uint32_t addend = half ? 0x10000u : 1u;
-  // LDS address of bin (d + u)/2 for this lane's query: hb + 64*u
-  const uint32_t hb = opaque(lds_addr(region + (wid * (d + 1) * 32 + ql) * 4 + 64 * d));
-  k_sweep([&](const v16i& u, int gc) {
+  // LDS address of bin (d + u)/2 for this lane's query: hb + 64*u, which is
+  // what the tile holds with k = 64 and cin = hb
+  const uint32_t hb = lds_addr(region + (wid * (d + 1) * 32 + ql) * 4 + 64 * d);
+  make_q(0x40u, 0x80u);  // +-64
+  k_sweep(hb, [&](const v16i& t, int gc) {
     const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
     if (__all(L >= 16)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(hb + u[i] * 64)), addend, __ATOMIC_RELAXED);
+      for (int i = 0; i < 16; ++i)
+        __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (i < L) __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(hb + u[i] * 64)), addend, __ATOMIC_RELAXED);
+        if (i < L)
+          __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
     }
   });
 
@@ -323,50 +341,62 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   int T = 0, hmin = 0, below0 = 0, ties0 = 0, below = 0;
   const uint32_t* hq = reinterpret_cast<const uint32_t*>(region) + wid * (d + 1) * 32 + ql;
   {
+    // scan bins upward, 8 independent LDS reads at a time; every lane stops
+    // at its threshold (the visible count is >= Ni, so each lane finds one)
     int cum = 0, cum0 = 0;
-    bool have_min = false;
-    for (int b = 0; b <= d; ++b) {
-      const uint32_t x = hq[b * 32];
-      const int c0 = static_cast<int>(x & 0xFFFFu);
-      const int cnt = c0 + static_cast<int>(x >> 16);
-      if (!have_min && cnt > 0) {
-        hmin = b;
-        have_min = true;
+    bool have_min = false, found = false;
+    for (int b0 = 0; !found; b0 += 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (b0 + k <= d) ? hq[(b0 + k) * 32] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c0 = static_cast<int>(x[k] & 0xFFFFu);
+        const int cnt = c0 + static_cast<int>(x[k] >> 16);
+        if (!have_min && cnt > 0) hmin = b0 + k;
+        have_min |= cnt > 0;
+        const bool hit = !found && b0 + k <= d && cum + cnt >= Ni;
+        if (hit) {
+          T = b0 + k;
+          below = cum;
+          below0 = cum0;
+          ties0 = c0;
+        }
+        found |= hit;
+        cum += cnt;
+        cum0 += c0;
       }
-      if (cum + cnt >= Ni) {
-        T = b;
-        below = cum;
-        below0 = cum0;
-        ties0 = c0;
-        break;
-      }
-      cum += cnt;
-      cum0 += c0;
     }
   }
   const int r_tie = Ni - below;
   const int quota0 = min(r_tie, ties0);
   const int quota = half ? (r_tie - quota0) : quota0;
   const int uT = (Ni > 0) ? 2 * T - d : -(d + 2);  // rows with nothing to keep never match
-  // Element i of this lane (ascending keys) is kept iff
-  //   u_i < uT, or u_i == uT and fewer than `quota` ties precede it here,
-  // i.e. iff u_i * 2^15 + ties_seen < uT * 2^15 + quota (ties_seen and quota
-  // stay below 2^15 because a half holds at most 32768 + 15 keys).
-  const int tie_key = uT * 32768 + quota;
-  int ties_seen = 0;
+  // Selection works on au = lutc + 2u, the weight-table address of the
+  // element (a pass-2 tile with k = 2 and cin = lutc; lutc is set below).
+  // Element i of this lane (ascending keys) is kept iff u_i < uT, or
+  // u_i == uT and fewer than `quota` ties precede it here, i.e. iff
+  //   (au_i - auT) * 2^15 + ties_seen - quota < 0,
+  // evaluated as D = (au_i << 15) + sp with sp = ties_seen - quota - (auT << 15)
+  // in 32-bit wrap-around arithmetic (au < 2^12, and ties_seen and quota stay
+  // below 2^15 + 16 because a half holds at most 32768 + 15 keys).
+  const uint32_t lutc = opaque(lds_addr(lds + kWLutOff + 2 * d - 4 * hmin));
+  const uint32_t auT = lutc + 2u * static_cast<uint32_t>(uT);
+  uint32_t sp = 0u - static_cast<uint32_t>(quota) - (auT << 15);
 
   if (MODE == 1) {
     // ======================================================= selection export
     int pos = half ? (below0 + quota0) : 0;
     int32_t* dst = a.idx + (bh_local * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(a.topn);
-    k_sweep([&](const v16i& u, int gc) {
+    make_q(0x02u, 0xFCu);  // +-2
+    k_sweep(lutc, [&](const v16i& t, int gc) {
       const int kbase = half * Hh + 16 * gc;
       const int L = lim - kbase;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int ui = (i < L) ? u[i] : kInvisible;
-        const bool keep = ui * 32768 + ties_seen < tie_key;
-        ties_seen += (ui == uT) ? 1 : 0;
+        const uint32_t au = static_cast<uint32_t>(t[i]);
+        const bool keep = i < L && static_cast<int32_t>((au << 15) + sp) < 0;
+        sp += (au == auT) ? 1u : 0u;
         if (keep && pos < a.topn) dst[pos++] = kbase + i;
       }
     });
@@ -378,12 +408,20 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // =========================================================== pass 2: attend
   float Z = 0.0f;
   if (Ni > 0) {
-    for (int b = hmin; b < T; ++b) {
-      const uint32_t x = hq[b * 32];
-      const int cnt = static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16);
-      const uint32_t e = wlut[b - hmin];
-      const float w = VF32 ? u2f(e) : bf16_to_f(e & 0xFFFFu) + bf16_to_f(e >> 16);
-      Z += static_cast<float>(cnt) * w;
+    for (int b0 = hmin; b0 < T; b0 += 8) {
+      uint32_t x[8], e[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool in = b0 + k < T;
+        x[k] = in ? hq[(b0 + k) * 32] : 0u;
+        e[k] = in ? wlut[b0 + k - hmin] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cnt = static_cast<int>(x[k] & 0xFFFFu) + static_cast<int>(x[k] >> 16);
+        const float w = VF32 ? u2f(e[k]) : bf16_to_f(e[k] & 0xFFFFu) + bf16_to_f(e[k] >> 16);
+        Z += static_cast<float>(cnt) * w;
+      }
     }
     const uint32_t e = wlut[T - hmin];
     const float w = VF32 ? u2f(e) : bf16_to_f(e & 0xFFFFu) + bf16_to_f(e >> 16);
@@ -391,7 +429,6 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   }
   const float invZ = (Z > 0.0f) ? 1.0f / Z : 0.0f;
   // weight-table LDS address of u: wlut + 4*((d + u)/2 - hmin) = lutc + 2u
-  const uint32_t lutc = opaque(lds_addr(lds + kWLutOff + 2 * d - 4 * hmin));
   const uint32_t zaddr = opaque(lds_addr(lds + kWLutOff + 4 * kZeroSlot));
 
   v16f acc[W];
@@ -415,8 +452,8 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
         const int r = (item / C::kPieces) & 31;
         const int c = item / (C::kPieces * 32);
         const int gc = g0 + c;
-        int key = (r >> 4) * Hh + 16 * gc + (r & 15);
-        if (gc >= nchunk || key >= kend) key = 0;
+        // keys past the visible range (weight 0 or never used) copy a valid row
+        const int key = min((r >> 4) * Hh + 16 * gc + (r & 15), kend - 1);
         const int pc = pp ^ ((2 * (r & 3)) & C::kSwzMask);
         __builtin_amdgcn_global_load_lds(
             reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(key) * d + 8 * pc,
@@ -536,26 +573,28 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     const int g0 = gi * C::kCH2;
     const int cend = min(C::kCH2, wchunks - g0);
     if (cend <= 0) return;
-    v16i u_next = logits_tile(buf, 0);
+    v16i t_next = logits_tile(buf, 0, lutc);
     for (int c = 0; c < cend; ++c) {
-      const v16i u = u_next;
-      if (c + 1 < cend) u_next = logits_tile(buf, c + 1);
+      const v16i t = t_next;
+      if (c + 1 < cend) t_next = logits_tile(buf, c + 1, lutc);
       const int gc = g0 + c;
       const int L = lim - (half * Hh + 16 * gc);
       uint32_t e[16];
       if (__all(L >= 16)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int ui = u[i];
-          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-          ties_seen += (ui == uT) ? 1 : 0;
+          const uint32_t au = static_cast<uint32_t>(t[i]);
+          // all-ones when kept: a bit select, no lane mask
+          const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
+          e[i] = lds_load_u32((au & m) | (zaddr & ~m));
+          sp += (au == auT) ? 1u : 0u;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int ui = (i < L) ? u[i] : kInvisible;
-          e[i] = lds_load_u32(ui * 32768 + ties_seen < tie_key ? lutc + ui * 2 : zaddr);
-          ties_seen += (ui == uT) ? 1 : 0;
+          const uint32_t au = static_cast<uint32_t>(t[i]);
+          e[i] = lds_load_u32(i < L && static_cast<int32_t>((au << 15) + sp) < 0 ? au : zaddr);
+          sp += (au == auT) ? 1u : 0u;
         }
       }
       if constexpr (VF32) {
@@ -599,6 +638,7 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   };
 
   const int ngroups2 = (nchunk + C::kCH2 - 1) / C::kCH2;
+  make_q(0x02u, 0xFCu);  // +-2: the tile holds au = lutc + 2u
   v_load(0);
   __syncthreads();  // every wave is done with its histogram (V tiles alias it)
   k_issue(0, C::kCH2, 0);

@@ -9,10 +9,12 @@
 //
 // Data path (HBM-bound, one read of x):
 //  * d % 32 == 0: the rows are contiguous, so the flat element stream maps
-//    onto the flat word stream (word = element / 32).  A wave loads 64
-//    consecutive floats per instruction (256 B, coalesced), one ballot turns
-//    them into two sign words, lanes 0/1 store them.  Each wave keeps UNROLL
-//    such loads in flight.
+//    onto the flat word stream (word = element / 32).  With x 16-byte
+//    aligned, lane L of a wave loads floats 4L..4L+3 of a 256-float segment;
+//    the 8 lanes that cover one word OR their sign nibbles together and one
+//    of them stores the word.  Each wave owns a contiguous run of segments
+//    (runs differ by at most one segment) and keeps up to kUnroll 1 KiB loads
+//    in flight.  Unaligned x falls back to one 64-float ballot per load.
 //  * other d: one thread per output word (pad bits stay 0).
 //  * sigma: every thread sums x and x*x in float64; blocks reduce in a fixed
 //    order and store one partial pair each to the workspace; a one-block
@@ -27,8 +29,11 @@ namespace had {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr int kPackMaxBlocks = 2048;
+constexpr int kPackMaxBlocks = 1024;
 constexpr int kUnroll = 8;
+constexpr int kSegsPerWave = 4;  // grid sizing target for small inputs
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline double wave_sum(double v) {
 #pragma unroll
@@ -67,14 +72,23 @@ __device__ void write_partials(double s1, double s2, double* partials) {
   }
 }
 
-// One block: sum the partials in index order and write sigma.
-__global__ __launch_bounds__(kPackThreads) void sigma_finalize_kernel(const double* partials,
+// One block: sum the partials in a fixed order and write sigma.  Thread t
+// owns partials t, t + 256, ...; all of its loads are issued before the sum.
+__global__ __launch_bounds__(kPackThreads) void sigma_finalize_kernel(const double2* partials,
                                                                        int nblocks, double count,
                                                                        float* sigma) {
+  constexpr int kPer = kPackMaxBlocks / kPackThreads;
+  double2 p[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = threadIdx.x + k * kPackThreads;
+    p[k] = i < nblocks ? partials[i] : double2{0.0, 0.0};
+  }
   double a = 0.0, b = 0.0;
-  for (int i = threadIdx.x; i < nblocks; i += kPackThreads) {
-    a += partials[2 * i + 0];
-    b += partials[2 * i + 1];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    a += p[k].x;
+    b += p[k].y;
   }
   block_sum2(a, b);
   if (threadIdx.x == 0) {
@@ -85,7 +99,55 @@ __global__ __launch_bounds__(kPackThreads) void sigma_finalize_kernel(const doub
   }
 }
 
-// d % 32 == 0: flat stream, 64 elements -> 2 words per ballot.
+// d % 32 == 0 and x 16-byte aligned: 256-float segments, 8 words each.
+template <bool kSigma>
+__global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(
+    const f32x4* __restrict__ x, uint32_t* __restrict__ bits, int64_t elems, double* partials,
+    uint32_t* dev_status) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPackThreads / 64);
+  const int64_t nseg = (elems + 255) >> 8;
+  const int64_t seg_end = (wave + 1) * nseg / nwaves;
+  const int64_t nvec = elems >> 2;
+  const int64_t nwords = elems >> 5;
+  const int shift = 4 * (lane & 7);
+  double s1 = 0.0, s2 = 0.0;
+  bool nan_seen = false;
+  for (int64_t s0 = wave * nseg / nwaves; s0 < seg_end; s0 += kUnroll) {
+    f32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = (s0 + u) * 64 + lane;
+      v[u] = (s0 + u < seg_end && i < nvec) ? __builtin_nontemporal_load(x + i)
+                                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const f32x4 e = v[u];
+      uint32_t w = (static_cast<uint32_t>(e.x < 0.0f) | (static_cast<uint32_t>(e.y < 0.0f) << 1) |
+                    (static_cast<uint32_t>(e.z < 0.0f) << 2) |
+                    (static_cast<uint32_t>(e.w < 0.0f) << 3))
+                   << shift;
+      w |= __shfl_xor(w, 1, 64);
+      w |= __shfl_xor(w, 2, 64);
+      w |= __shfl_xor(w, 4, 64);
+      const int64_t wi = (s0 + u) * 8 + (lane >> 3);
+      if ((lane & 7) == 0 && s0 + u < seg_end && wi < nwords) bits[wi] = w;
+      nan_seen |= (e.x != e.x) | (e.y != e.y) | (e.z != e.z) | (e.w != e.w);
+      if (kSigma) {
+        const double a = e.x, b = e.y, c = e.z, d = e.w;
+        s1 += (a + b) + (c + d);
+        s2 += fma(a, a, b * b) + fma(c, c, d * d);
+      }
+    }
+  }
+  if (dev_status != nullptr && __ballot(nan_seen) != 0 && lane == 0)
+    atomicOr(dev_status, HAD_DEV_NAN_INPUT);
+  if (kSigma) write_partials(s1, s2, partials);
+}
+
+// d % 32 == 0, x not 16-byte aligned: 64 elements -> 2 words per ballot.
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
     const float* __restrict__ x, uint32_t* __restrict__ bits, int64_t elems, double* partials,
@@ -161,8 +223,8 @@ int pack_grid_blocks(const had_shape& s) {
   const int64_t elems = s.batch * s.heads * s.seq * s.dim;
   int64_t blocks;
   if (s.dim % 32 == 0) {
-    const int64_t chunks = (elems + 63) / 64;
-    const int64_t waves = (chunks + kUnroll - 1) / kUnroll;
+    const int64_t segs = (elems + 255) / 256;
+    const int64_t waves = (segs + kSegsPerWave - 1) / kSegsPerWave;
     blocks = (waves + kPackThreads / 64 - 1) / (kPackThreads / 64);
   } else {
     const int64_t words = s.batch * s.heads * s.seq * words_per_row(s.dim);
@@ -197,7 +259,7 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   double* partials = nullptr;
   if (sigma != nullptr) {
     if (!aligned(sigma, 4)) return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma must be 4-byte aligned");
-    if (workspace == nullptr || !aligned(workspace, 8))
+    if (workspace == nullptr || !aligned(workspace, 16))
       return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma requested but workspace is null or unaligned");
     if (workspace_bytes < had_pack_workspace_bytes(s))
       return fail(HAD_ERR_INVALID_ARG, "had_pack: workspace smaller than had_pack_workspace_bytes()");
@@ -208,7 +270,12 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   const int d = static_cast<int>(s.dim);
   if (d % 32 == 0) {
     const int64_t elems = rows * d;
-    if (sigma)
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    if (aligned(x, 16) && sigma)
+      pack_vec_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x4, xbits, elems, partials, dev_status);
+    else if (aligned(x, 16))
+      pack_vec_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x4, xbits, elems, nullptr, dev_status);
+    else if (sigma)
       pack_stream_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, partials, dev_status);
     else
       pack_stream_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, nullptr, dev_status);
@@ -221,6 +288,6 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   }
   had_status ls = check_launch("had_pack");
   if (ls != HAD_OK || sigma == nullptr) return ls;
-  sigma_finalize_kernel<<<1, kPackThreads, 0, hs>>>(partials, blocks, static_cast<double>(rows) * d, sigma);
+  sigma_finalize_kernel<<<1, kPackThreads, 0, hs>>>(reinterpret_cast<const double2*>(partials), blocks, static_cast<double>(rows) * d, sigma);
   return check_launch("had_pack");
 }

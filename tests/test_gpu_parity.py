@@ -26,7 +26,8 @@ def _gpu():
 
 # --------------------------------------------------------------------- pack
 @pytest.mark.parametrize("shape", [(1, 1, 128, 64), (2, 3, 77, 128), (1, 2, 50, 40), (3, 1, 9, 33),
-                                   (1, 1, 5, 5), (1, 2, 31, 256), (1, 1, 1, 1), (4, 4, 300, 32)])
+                                   (1, 1, 5, 5), (1, 2, 31, 256), (1, 1, 1, 1), (4, 4, 300, 32),
+                                   (1, 1, 999, 32), (2, 3, 1001, 64), (1, 4, 8192, 128)])
 def test_pack_bits_and_sigma(shape):
     log(f"pack {shape}")
     rng = np.random.default_rng(sum(shape))
@@ -51,6 +52,23 @@ def test_pack_bits_and_sigma(shape):
     _, sig2 = had.pack(xs)
     ref = oracle.sigma(x_sig)
     assert abs(float(sig2.item()) - ref) <= 1e-6 * ref + 1e-30
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 77, 64), (1, 1, 999, 32)])
+def test_pack_unaligned_input(shape):
+    """x at a 4-byte but not 16-byte aligned address takes the scalar path."""
+    log(f"pack unaligned {shape}")
+    rng = np.random.default_rng(7 + shape[2])
+    x = rng.standard_normal(shape).astype(np.float32)
+    buf = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = torch.from_numpy(x.reshape(-1)).cuda()
+    xt = buf[1:].view(shape)
+    assert xt.data_ptr() % 16 != 0
+    bits, sig = had.pack(xt)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_np(bits), oracle.pack_bits(oracle.binarize(x)))
+    ref = oracle.sigma(x)
+    assert abs(float(sig.item()) - ref) <= 1e-6 * ref
 
 
 def test_pack_flags_nan_and_is_deterministic():
