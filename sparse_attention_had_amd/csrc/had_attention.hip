@@ -568,71 +568,90 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     return __builtin_bit_cast(v8bf, u);
   };
 
+  // Weights of the 16 elements of chunk gc from its tile t (au values).
+  auto select_chunk = [&](const v16i& t, int gc, uint32_t* e) {
+    const int L = lim - (half * Hh + 16 * gc);
+    if (__all(L >= 16)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t au = static_cast<uint32_t>(t[i]);
+        // all-ones when kept: a bit select, no lane mask
+        const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
+        e[i] = lds_load_u32((au & m) | (zaddr & ~m));
+        sp = opaque(sp + ((au == auT) ? 1u : 0u));  // one compare + add-with-carry
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t au = static_cast<uint32_t>(t[i]);
+        e[i] = lds_load_u32(i < L && static_cast<int32_t>((au << 15) + sp) < 0 ? au : zaddr);
+        sp += (au == auT) ? 1u : 0u;
+      }
+    }
+  };
+
+  // out^T += V^T P^T for chunk c of the V tile vt, weights e.
+  auto pv_chunk = [&](const unsigned char* vt, int c, const uint32_t* e) {
+    if constexpr (VF32) {
+      const unsigned char* vbase = vt + c * C::kDP * VS;
+#pragma unroll
+      for (int t = 0; t < W; ++t) {
+        const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ab = 0; ab < 2; ++ab) {
+        u32x4 ph, pl;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
+          ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
+          pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
+        }
+        const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
+        const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          v8bf av;
+          if constexpr (VDIRECT) {
+            av = v_operand(vt + c * 32 * 2 * C::kDP, t, ab);
+          } else {
+            const u32x4 vv = *reinterpret_cast<const u32x4*>(vt + c * C::kDP * VS + (32 * t + ql) * VS + 32 * half + 16 * ab);
+            av = __builtin_bit_cast(v8bf, vv);
+          }
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One key group, software-pipelined: the selection of chunk c + 1 (vector
+  // ALU and LDS table reads) is issued before the products of chunk c, so
+  // the table-read latency hides behind the matrix-core work.  Unrolled over
+  // the group so that the weights of consecutive chunks live in distinct
+  // registers.
   auto attend_group = [&](int buf, int gi) {
     const unsigned char* vt = region + buf * C::kVBuf;
     const int g0 = gi * C::kCH2;
     const int cend = min(C::kCH2, wchunks - g0);
     if (cend <= 0) return;
-    v16i t_next = logits_tile(buf, 0, lutc);
-    for (int c = 0; c < cend; ++c) {
-      const v16i t = t_next;
-      if (c + 1 < cend) t_next = logits_tile(buf, c + 1, lutc);
-      const int gc = g0 + c;
-      const int L = lim - (half * Hh + 16 * gc);
-      uint32_t e[16];
-      if (__all(L >= 16)) {
+    uint32_t e[C::kCH2][16];
+    select_chunk(logits_tile(buf, 0, lutc), g0, e[0]);
+    v16i t_next = logits_tile(buf, cend > 1 ? 1 : 0, lutc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t au = static_cast<uint32_t>(t[i]);
-          // all-ones when kept: a bit select, no lane mask
-          const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
-          e[i] = lds_load_u32((au & m) | (zaddr & ~m));
-          sp += (au == auT) ? 1u : 0u;
+    for (int c = 0; c < C::kCH2; ++c) {
+      if (c < cend) {
+        if (c + 1 < cend) {
+          select_chunk(t_next, g0 + c + 1, e[(c + 1) % C::kCH2]);
+          if (c + 2 < cend) t_next = logits_tile(buf, c + 2, lutc);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t au = static_cast<uint32_t>(t[i]);
-          e[i] = lds_load_u32(i < L && static_cast<int32_t>((au << 15) + sp) < 0 ? au : zaddr);
-          sp += (au == auT) ? 1u : 0u;
-        }
-      }
-      if constexpr (VF32) {
-        const unsigned char* vbase = vt + c * C::kDP * VS;
-#pragma unroll
-        for (int t = 0; t < W; ++t) {
-          const unsigned char* vrow = vbase + (32 * t + ql) * VS + 64 * half;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float av = *reinterpret_cast<const float*>(vrow + 4 * i);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, u2f(e[i]), acc[t], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int ab = 0; ab < 2; ++ab) {
-          u32x4 ph, pl;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t e0 = e[8 * ab + 2 * k], e1 = e[8 * ab + 2 * k + 1];
-            ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
-            pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
-          }
-          const v8bf bh8 = __builtin_bit_cast(v8bf, ph);
-          const v8bf bl8 = __builtin_bit_cast(v8bf, pl);
-#pragma unroll
-          for (int t = 0; t < W; ++t) {
-            v8bf av;
-            if constexpr (VDIRECT) {
-              av = v_operand(vt + c * 32 * 2 * C::kDP, t, ab);
-            } else {
-              const u32x4 vv = *reinterpret_cast<const u32x4*>(vt + c * C::kDP * VS + (32 * t + ql) * VS + 32 * half + 16 * ab);
-              av = __builtin_bit_cast(v8bf, vv);
-            }
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, acc[t], 0, 0, 0);
-          }
-        }
+        pv_chunk(vt, c, e[c]);
       }
     }
   };
