@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the HAD inference-attention hot path on one MI355X.
 
-One step = had_pack(Q) + had_pack(K) + had_attention over one batch of
-seeded synthetic input already resident in HBM (all three kernels launched on
-torch's current stream).  Prints ONE JSON line.
+One step = the whole path over one batch of seeded synthetic input already
+resident in HBM: had_forward, i.e. the pack of Q and K (sign bits and sigma
+partials) in one launch, then the attention launch, which also finalizes both
+sigmas (--separate-calls times had_pack(Q), had_pack(K), had_attention
+instead).  Everything runs on torch's current stream.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
@@ -117,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only had_attention launches (for profiling runs)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="step = had_pack(Q), had_pack(K), had_attention (5 launches) "
+                         "instead of had_forward (2 launches)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for HBM counter runs: 3 attention launches, then one plain "
                          "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")
@@ -148,6 +153,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ws_q = torch.zeros(had.pack_workspace_bytes(q.shape), dtype=torch.uint8, device=dev)
     ws_k = torch.zeros_like(ws_q)
+    ws_f = torch.zeros(2 * ws_q.numel(), dtype=torch.uint8, device=dev)
 
     if args.traffic_probe:
         from sparse_attention_had_amd.profiling import COPY_BYTES
@@ -165,10 +171,15 @@ def main():
         return
 
     def step():
-        if not args.attention_only:
+        if args.attention_only:
+            had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
+        elif args.separate_calls:
             had.pack(q, out=qb, sigma=sq, workspace=ws_q)
             had.pack(k, out=kb, sigma=sk, workspace=ws_k)
-        had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
+            had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
+        else:
+            had.forward(q, k, v, w.topn, w.scale, w.causal, out=out, qbits=qb, kbits=kb,
+                        sigma_q=sq, sigma_k=sk, workspace=ws_f)
 
     had.pack(q, out=qb, sigma=sq, workspace=ws_q)
     had.pack(k, out=kb, sigma=sk, workspace=ws_k)
@@ -220,7 +231,9 @@ def main():
         "config": {
             "workload": name, "batch": w.batch, "heads": w.heads, "seq": w.seq, "dim": w.dim,
             "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype, "scale": w.scale,
-            "step": "attention only" if args.attention_only else "pack(Q) + pack(K) + attention",
+            "step": ("attention only" if args.attention_only else
+                     "had_pack(Q), had_pack(K), had_attention" if args.separate_calls else
+                     "had_forward: pack(Q)+pack(K) in one launch, attention with sigma finalize"),
             "arithmetic": "int8 matrix-core logits (exact), int32 selection, fp32 softmax weights "
                           "as bf16 hi+lo, bf16 matrix-core V product with fp32 accumulation",
         },

@@ -129,6 +129,39 @@ had_status had_attention(const uint32_t* qbits, const uint32_t* kbits,
                          int64_t topn, float scale, int causal, float* out,
                          void* stream);
 
+/* Workspace bytes that had_forward needs when it computes sigma. */
+size_t had_forward_workspace_bytes(had_shape s);
+
+/*
+ * had_forward - the whole inference path in two kernel launches: the pack of
+ * Q and of K in one launch, then the attention launch, which also finalizes
+ * sigma_Q and sigma_K.  Every output equals that of had_pack(q),
+ * had_pack(k) and had_attention(qbits, kbits, ...) called one after the other
+ * with the same arguments (bits, sigma and out bit for bit).
+ *
+ * Defined by: the passages cited for had_pack and had_attention (Pith review,
+ * "What carries the argument"; referee minor comment 6 on Eq. 12 and major
+ * comment 3).
+ *
+ *  q, k        [B,H,n,d] float32, device, 4-byte aligned.  Read once each.
+ *  qbits,kbits [B,H,n,W] uint32, device: receive the sign words (as had_pack)
+ *              and are read by the attention launch.
+ *  v, v_dtype, topn, scale, causal, out: as had_attention.
+ *  sigma_q, sigma_k  device float*, or NULL each (as had_pack's sigma).
+ *  workspace   device memory of had_forward_workspace_bytes(s) bytes, 16-byte
+ *              aligned, required when a sigma is requested.  No initial
+ *              contents needed; calls that may overlap need distinct ones.
+ *  dev_status  as had_pack, for a NaN in q or k.
+ *  Errors: those of had_pack and had_attention; nothing is enqueued then.
+ */
+had_status had_forward(const float* q, const float* k, const void* v,
+                       had_dtype v_dtype, had_shape s, int64_t topn,
+                       float scale, int causal, uint32_t* qbits,
+                       uint32_t* kbits, float* out, float* sigma_q,
+                       float* sigma_k, void* workspace,
+                       size_t workspace_bytes, uint32_t* dev_status,
+                       void* stream);
+
 /*
  * had_logits - inspection export of the integer logits s = d - 2*Hamming
  * computed by the same logit stage as had_attention (no mask, every key).

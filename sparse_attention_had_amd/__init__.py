@@ -96,6 +96,11 @@ def load_library():
         lib.had_logits.restype = I
         lib.had_select.argtypes = [P, P, Shape, I64, I, I64, I64, P, P]
         lib.had_select.restype = I
+        lib.had_forward_workspace_bytes.argtypes = [Shape]
+        lib.had_forward_workspace_bytes.restype = ctypes.c_size_t
+        lib.had_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P,
+                                    ctypes.c_size_t, P, P]
+        lib.had_forward.restype = I
         lib.had_status_string.argtypes = [I]
         lib.had_status_string.restype = ctypes.c_char_p
         lib.had_last_error.argtypes = []
@@ -222,6 +227,77 @@ def attention(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: i
         qbits.data_ptr(), kbits.data_ptr(), v.data_ptr(), vdt, Shape(B, H, n, d), int(topn),
         float(scale), int(bool(causal)), out.data_ptr(), _stream_handle(v.device, stream)))
     return out
+
+
+def _v_dtype(v: torch.Tensor) -> int:
+    if v.dtype == torch.float32:
+        return HAD_F32
+    if v.dtype == torch.bfloat16:
+        return HAD_BF16
+    raise ValueError("v must be float32 or bfloat16")
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale: float,
+            causal: bool = False, *, with_sigma: bool = True, out: torch.Tensor | None = None,
+            qbits: torch.Tensor | None = None, kbits: torch.Tensor | None = None,
+            sigma_q: torch.Tensor | None = None, sigma_k: torch.Tensor | None = None,
+            dev_status: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            stream=None):
+    """Pack Q and K and run the attention in two launches (had_forward).
+
+    Returns (out, qbits, kbits, sigma_q, sigma_k); the sigmas are None when
+    with_sigma is False.
+    """
+    lib = load_library()
+    _need_cuda(q, "q", torch.float32)
+    _need_cuda(k, "k", torch.float32)
+    _need_cuda(v, "v")
+    B, H, n, d = _shape4(q, "q")
+    if tuple(k.shape) != (B, H, n, d) or tuple(v.shape) != (B, H, n, d):
+        raise ValueError("q, k and v must have the same shape [B, H, n, d]")
+    W = words_per_row(d)
+    dev = q.device
+    if qbits is None:
+        qbits = torch.empty((B, H, n, W), dtype=torch.int32, device=dev)
+    if kbits is None:
+        kbits = torch.empty((B, H, n, W), dtype=torch.int32, device=dev)
+    for t, name in ((qbits, "qbits"), (kbits, "kbits")):
+        _need_cuda(t, name, torch.int32)
+        if tuple(t.shape) != (B, H, n, W):
+            raise ValueError(f"{name} must have shape [B, H, n, ceil(d/32)]")
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+    _need_cuda(out, "out", torch.float32)
+    if tuple(out.shape) != (B, H, n, d):
+        raise ValueError("out must have the shape of v")
+    shape = Shape(B, H, n, d)
+    sh = _stream_handle(dev, stream)
+    sq_ptr = sk_ptr = ws_ptr = None
+    ws_bytes = 0
+    if with_sigma:
+        if sigma_q is None:
+            sigma_q = torch.empty(1, dtype=torch.float32, device=dev)
+        if sigma_k is None:
+            sigma_k = torch.empty(1, dtype=torch.float32, device=dev)
+        _need_cuda(sigma_q, "sigma_q", torch.float32)
+        _need_cuda(sigma_k, "sigma_k", torch.float32)
+        need = int(lib.had_forward_workspace_bytes(shape))
+        if workspace is None:
+            workspace = _workspace(dev, sh, need)
+        _need_cuda(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        sq_ptr, sk_ptr, ws_ptr = sigma_q.data_ptr(), sigma_k.data_ptr(), workspace.data_ptr()
+    st_ptr = None
+    if dev_status is not None:
+        _need_cuda(dev_status, "dev_status", torch.int32)
+        st_ptr = dev_status.data_ptr()
+    _check("had_forward", lib.had_forward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(topn), float(scale),
+        int(bool(causal)), qbits.data_ptr(), kbits.data_ptr(), out.data_ptr(), sq_ptr, sk_ptr,
+        ws_ptr, ws_bytes, st_ptr, sh))
+    if not with_sigma:
+        return out, qbits, kbits, None, None
+    return out, qbits, kbits, sigma_q, sigma_k
 
 
 def logits(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, *, bh_begin: int = 0,

@@ -18,6 +18,14 @@ void set_error(const char* fmt, ...) {
 
 void clear_error() { g_last_error[0] = '\0'; }
 
+had_status failf(had_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
 had_status check_shape(const had_shape& s) {
   if (s.batch <= 0 || s.heads <= 0 || s.seq <= 0 || s.dim <= 0)
     return fail(HAD_ERR_INVALID_ARG, "shape fields must all be positive");
@@ -60,23 +68,21 @@ extern "C" const char* had_status_string(had_status st) {
 
 extern "C" const char* had_last_error(void) { return g_last_error; }
 
-extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v,
-                                    had_dtype v_dtype, had_shape s, int64_t topn, float scale,
-                                    int causal, float* out, void* stream) {
-  clear_error();
-  had_status st = check_shape(s);
-  if (st != HAD_OK) return st;
-  if ((st = check_bits(qbits, kbits, "had_attention")) != HAD_OK) return st;
-  if (v == nullptr || out == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_attention: null v or out");
+// Checks of had_attention's arguments; fills the launch arguments.
+static had_status attend_args(const uint32_t* qbits, const uint32_t* kbits, const void* v,
+                              had_dtype v_dtype, const had_shape& s, int64_t topn, float scale,
+                              int causal, float* out, const char* fn, AttnArgs& a) {
+  had_status st;
+  if ((st = check_bits(qbits, kbits, fn)) != HAD_OK) return st;
+  if (v == nullptr || out == nullptr) return failf(HAD_ERR_INVALID_ARG, "%s: null v or out", fn);
   if (!aligned(v, 16) || !aligned(out, 16))
-    return fail(HAD_ERR_INVALID_ARG, "had_attention: v and out must be 16-byte aligned");
-  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16)
-    return fail(HAD_ERR_INVALID_ARG, "had_attention: unknown v_dtype");
-  if (topn < 1) return fail(HAD_ERR_INVALID_ARG, "had_attention: topn must be >= 1");
+    return failf(HAD_ERR_INVALID_ARG, "%s: v and out must be 16-byte aligned", fn);
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", fn);
+  if (topn < 1) return failf(HAD_ERR_INVALID_ARG, "%s: topn must be >= 1", fn);
   if (!std::isfinite(scale) || !(scale > 0.0f))
-    return fail(HAD_ERR_INVALID_ARG, "had_attention: scale must be finite and > 0");
-  if (causal != 0 && causal != 1) return fail(HAD_ERR_INVALID_ARG, "had_attention: causal must be 0 or 1");
-  AttnArgs a{};
+    return failf(HAD_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (causal != 0 && causal != 1) return failf(HAD_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  a = AttnArgs{};
   a.qbits = qbits;
   a.kbits = kbits;
   a.v = v;
@@ -90,7 +96,61 @@ extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits
   a.scale = scale;
   a.causal = causal;
   a.out = out;
+  return HAD_OK;
+}
+
+extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v,
+                                    had_dtype v_dtype, had_shape s, int64_t topn, float scale,
+                                    int causal, float* out, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  AttnArgs a;
+  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_attention", a)) != HAD_OK)
+    return st;
   return launch_attention_family(AttnMode::Attend, a, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t had_forward_workspace_bytes(had_shape s) {
+  if (check_shape(s) != HAD_OK) return 0;
+  return 2 * had_pack_workspace_bytes(s);
+}
+
+extern "C" had_status had_forward(const float* q, const float* k, const void* v, had_dtype v_dtype,
+                                  had_shape s, int64_t topn, float scale, int causal,
+                                  uint32_t* qbits, uint32_t* kbits, float* out, float* sigma_q,
+                                  float* sigma_k, void* workspace, size_t workspace_bytes,
+                                  uint32_t* dev_status, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if ((st = check_pack_args(q, qbits, sigma_q, "had_forward")) != HAD_OK) return st;
+  if ((st = check_pack_args(k, kbits, sigma_k, "had_forward")) != HAD_OK) return st;
+  if (dev_status != nullptr && !aligned(dev_status, 4))
+    return fail(HAD_ERR_INVALID_ARG, "had_forward: dev_status must be 4-byte aligned");
+  AttnArgs a;
+  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_forward", a)) != HAD_OK)
+    return st;
+  double* part[2] = {nullptr, nullptr};
+  if (sigma_q != nullptr || sigma_k != nullptr) {
+    if (workspace == nullptr || !aligned(workspace, 16))
+      return fail(HAD_ERR_INVALID_ARG, "had_forward: sigma requested but workspace is null or unaligned");
+    if (workspace_bytes < had_forward_workspace_bytes(s))
+      return fail(HAD_ERR_INVALID_ARG, "had_forward: workspace smaller than had_forward_workspace_bytes()");
+    double* ws = static_cast<double*>(workspace);
+    if (sigma_q != nullptr) part[0] = ws;
+    if (sigma_k != nullptr) part[1] = ws + 2 * pack_grid_blocks(s);
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const PackJob jobs[2] = {{q, qbits, part[0]}, {k, kbits, part[1]}};
+  if ((st = launch_pack(jobs, 2, s, dev_status, hs)) != HAD_OK) return st;
+  a.sigma_partials[0] = reinterpret_cast<const double2*>(part[0]);
+  a.sigma_partials[1] = reinterpret_cast<const double2*>(part[1]);
+  a.sigma_out[0] = sigma_q;
+  a.sigma_out[1] = sigma_k;
+  a.sigma_nblocks = pack_grid_blocks(s);
+  a.sigma_count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
+  return launch_attention_family(AttnMode::Attend, a, hs);
 }
 
 extern "C" had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,

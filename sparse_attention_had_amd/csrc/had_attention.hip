@@ -181,6 +181,15 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   const int wlim = (wave_q0 >= qend) ? 0 : (causal ? min(n, wave_q0 + 32) : n);
   const int wchunks = min(nchunk, (wlim + 15) / 16);  // chunks with keys this wave sees
 
+  // ---- sigma of the fused forward call: wave 0 of the last block (the
+  // lightest one when causal) reduces the pack partials before its own work
+  if (MODE == 0 && wid == 0 && blockIdx.x == gridDim.x - 1) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (a.sigma_out[t] != nullptr)
+        sigma_from_partials(a.sigma_partials[t], a.sigma_nblocks, a.sigma_count, a.sigma_out[t]);
+  }
+
   // ---- constant tables
   for (int t = tid; t < 256; t += C::kThreads)
     reinterpret_cast<uint2*>(lds + kByteLutOff)[t] =

@@ -19,6 +19,7 @@ inline had_status fail(had_status st, const char* what) {
   set_error("%s", what);
   return st;
 }
+had_status failf(had_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 inline had_status check_launch(const char* kernel) {
   hipError_t e = hipGetLastError();
@@ -38,8 +39,62 @@ inline int64_t words_per_row(int64_t d) { return (d + 31) / 32; }
 // Shape checks common to every entry point.
 had_status check_shape(const had_shape& s);
 
-// ---- pack ----
+// ---- pack (had_pack.hip) ----
+constexpr int kPackThreads = 1024;   // threads per pack block
+constexpr int kPackMaxBlocks = 256;  // sigma partial pairs per tensor, at most
+
 int pack_grid_blocks(const had_shape& s);
+
+// One tensor of a pack launch.
+struct PackJob {
+  const float* x;
+  uint32_t* bits;
+  double* partials;  // 2 doubles per pack block, or null (no sigma)
+};
+
+had_status check_pack_args(const float* x, uint32_t* xbits, float* sigma, const char* who);
+// Packs njobs (1 or 2) tensors of shape s; one launch when the two can share it.
+had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint32_t* dev_status,
+                       hipStream_t st);
+// One-wave kernel: sigma from the partials of a pack launch of shape s.
+had_status launch_sigma_finalize(const double* partials, const had_shape& s, float* sigma,
+                                 hipStream_t st);
+
+// Fixed-order butterfly sum over a wave; lane 0's result is the same on every run.
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave (lanes 0..63 of the calling wave): sigma from per-block partial
+// pairs (sum x, sum x^2).  Lane l sums partials l, l + 64, ... in order, then
+// a fixed butterfly; lane 0 writes the population standard deviation.
+__device__ inline void sigma_from_partials(const double2* partials, int nblocks, double count,
+                                           float* sigma) {
+  constexpr int kPer = kPackMaxBlocks / 64;
+  const int lane = threadIdx.x & 63;
+  double2 p[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = lane + 64 * k;
+    p[k] = i < nblocks ? partials[i] : double2{0.0, 0.0};
+  }
+  double a = 0.0, b = 0.0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    a += p[k].x;
+    b += p[k].y;
+  }
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
+  if (lane == 0) {
+    const double mean = a / count;
+    double var = b / count - mean * mean;
+    if (!(var > 0.0)) var = 0.0;
+    *sigma = static_cast<float>(sqrt(var));
+  }
+}
 
 // ---- attention family (had_attention.hip) ----
 enum class AttnMode : int { Attend = 0, Select = 1, Logits = 2 };
@@ -62,6 +117,12 @@ struct AttnArgs {
   float* out;        // Attend output [bh_total, n, d]
   int32_t* idx;      // Select output [bh_count, n, topn]
   int16_t* logits;   // Logits output [bh_count, row_count, n]
+  // Optional sigma finalize (fused forward call): wave 0 of the last block
+  // turns the partials of a preceding pack launch into sigma_out[t].
+  const double2* sigma_partials[2];
+  float* sigma_out[2];
+  int sigma_nblocks;
+  double sigma_count;
 };
 
 had_status launch_attention_family(AttnMode mode, const AttnArgs& a, hipStream_t st);

@@ -16,36 +16,59 @@
 //    (runs differ by at most one segment) and keeps up to kUnroll 1 KiB loads
 //    in flight.  Unaligned x falls back to one 64-float ballot per load.
 //  * other d: one thread per output word (pad bits stay 0).
+//  * One launch packs one tensor, or two tensors of the same shape (Q and K
+//    of the fused forward call): blocks [0, nb0) work on the first, the rest
+//    on the second, each exactly as a launch of its own would.
 //  * sigma: every thread sums x and x*x in float64; blocks reduce in a fixed
-//    order and store one partial pair each to the workspace; a one-block
-//    finalize kernel on the same stream sums the partials in index order and
-//    writes sigma.  (A "last block finalizes" scheme needs an agent-scope
-//    release per block, which writes back L2 and costs more than the whole
-//    pack.)  No floating-point atomics, so sigma is bit-identical from run to
-//    run.
+//    order and store one partial pair each to the workspace; one wave (a
+//    finalize kernel on the same stream, or a wave of the attention launch in
+//    the fused call) sums the partials in a fixed order and writes sigma.  (A
+//    "last block finalizes" scheme needs an agent-scope release per block,
+//    which writes back L2 and costs more than the whole pack.)  No
+//    floating-point atomics, so sigma is bit-identical from run to run.
 #include "had_internal.h"
 
 namespace had {
 namespace {
 
-constexpr int kPackThreads = 256;
-constexpr int kPackMaxBlocks = 1024;
 constexpr int kUnroll = 8;
 constexpr int kSegsPerWave = 4;  // grid sizing target for small inputs
+constexpr int kWavesPerBlock = kPackThreads / 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// The tensors of one launch.
+struct PackJobs {
+  PackJob job[2];
+  int nb0;              // blocks of job 0; the rest of the grid is job 1
+  int64_t elems;        // B*H*n*d per tensor
+  int64_t rows;         // B*H*n per tensor
+  int d;
+  int W;
+  uint32_t* dev_status;
+};
+
+// This block's tensor, block index and block count within that tensor.
+struct BlockJob {
+  PackJob job;
+  int64_t blk;
+  int64_t nblk;
+};
+
+__device__ inline BlockJob block_job(const PackJobs& p) {
+  const bool second = static_cast<int>(blockIdx.x) >= p.nb0;
+  BlockJob b;
+  b.job = second ? p.job[1] : p.job[0];
+  b.blk = second ? blockIdx.x - p.nb0 : blockIdx.x;
+  b.nblk = second ? gridDim.x - p.nb0 : p.nb0;
+  return b;
 }
 
 // Block-level fixed-order sum of two doubles; result valid in thread 0.
 __device__ inline void block_sum2(double& a, double& b) {
-  __shared__ double red[2][kPackThreads / 64];
-  a = wave_sum(a);
-  b = wave_sum(b);
+  __shared__ double red[2][kWavesPerBlock];
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     red[0][wid] = a;
@@ -55,62 +78,47 @@ __device__ inline void block_sum2(double& a, double& b) {
   if (threadIdx.x == 0) {
     a = 0.0;
     b = 0.0;
-    for (int w = 0; w < kPackThreads / 64; ++w) {
+    for (int w = 0; w < kWavesPerBlock; ++w) {
       a += red[0][w];
       b += red[1][w];
     }
   }
 }
 
-// Per-block partial sums (plain stores; the finalize kernel that follows on
-// the same stream sees them through kernel-boundary ordering).
-__device__ void write_partials(double s1, double s2, double* partials) {
+// Per-block partial sums (plain stores; the reader runs in a later kernel on
+// the same stream and sees them through kernel-boundary ordering).
+__device__ void write_partials(double s1, double s2, const BlockJob& bj) {
   block_sum2(s1, s2);
   if (threadIdx.x == 0) {
-    partials[2 * blockIdx.x + 0] = s1;
-    partials[2 * blockIdx.x + 1] = s2;
+    bj.job.partials[2 * bj.blk + 0] = s1;
+    bj.job.partials[2 * bj.blk + 1] = s2;
   }
 }
 
-// One block: sum the partials in a fixed order and write sigma.  Thread t
-// owns partials t, t + 256, ...; all of its loads are issued before the sum.
-__global__ __launch_bounds__(kPackThreads) void sigma_finalize_kernel(const double2* partials,
-                                                                       int nblocks, double count,
-                                                                       float* sigma) {
-  constexpr int kPer = kPackMaxBlocks / kPackThreads;
-  double2 p[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = threadIdx.x + k * kPackThreads;
-    p[k] = i < nblocks ? partials[i] : double2{0.0, 0.0};
-  }
-  double a = 0.0, b = 0.0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    a += p[k].x;
-    b += p[k].y;
-  }
-  block_sum2(a, b);
-  if (threadIdx.x == 0) {
-    const double mean = a / count;
-    double var = b / count - mean * mean;
-    if (!(var > 0.0)) var = 0.0;
-    *sigma = static_cast<float>(sqrt(var));
-  }
+__device__ inline void flag_nan(bool nan_seen, uint32_t* dev_status) {
+  if (dev_status != nullptr && __ballot(nan_seen) != 0 && (threadIdx.x & 63) == 0)
+    atomicOr(dev_status, HAD_DEV_NAN_INPUT);
+}
+
+// One wave: sigma from the partial pairs.
+__global__ __launch_bounds__(64) void sigma_finalize_kernel(const double2* partials, int nblocks,
+                                                            double count, float* sigma) {
+  sigma_from_partials(partials, nblocks, count, sigma);
 }
 
 // d % 32 == 0 and x 16-byte aligned: 256-float segments, 8 words each.
 template <bool kSigma>
-__global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(
-    const f32x4* __restrict__ x, uint32_t* __restrict__ bits, int64_t elems, double* partials,
-    uint32_t* dev_status) {
+__global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
+  const BlockJob bj = block_job(p);
+  const f32x4* __restrict__ x = reinterpret_cast<const f32x4*>(bj.job.x);
+  uint32_t* __restrict__ bits = bj.job.bits;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPackThreads / 64);
-  const int64_t nseg = (elems + 255) >> 8;
+  const int64_t wave = (bj.blk * kPackThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = bj.nblk * kWavesPerBlock;
+  const int64_t nseg = (p.elems + 255) >> 8;
   const int64_t seg_end = (wave + 1) * nseg / nwaves;
-  const int64_t nvec = elems >> 2;
-  const int64_t nwords = elems >> 5;
+  const int64_t nvec = p.elems >> 2;
+  const int64_t nwords = p.elems >> 5;
   const int shift = 4 * (lane & 7);
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
@@ -142,21 +150,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(
       }
     }
   }
-  if (dev_status != nullptr && __ballot(nan_seen) != 0 && lane == 0)
-    atomicOr(dev_status, HAD_DEV_NAN_INPUT);
-  if (kSigma) write_partials(s1, s2, partials);
+  flag_nan(nan_seen, p.dev_status);
+  if (kSigma) write_partials(s1, s2, bj);
 }
 
 // d % 32 == 0, x not 16-byte aligned: 64 elements -> 2 words per ballot.
 template <bool kSigma>
-__global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
-    const float* __restrict__ x, uint32_t* __restrict__ bits, int64_t elems, double* partials,
-    uint32_t* dev_status) {
+__global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(PackJobs p) {
+  const BlockJob bj = block_job(p);
+  const float* __restrict__ x = bj.job.x;
+  uint32_t* __restrict__ bits = bj.job.bits;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPackThreads / 64);
-  const int64_t nchunks = (elems + 63) >> 6;
-  const int64_t nwords = elems >> 5;
+  const int64_t wave = (bj.blk * kPackThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = bj.nblk * kWavesPerBlock;
+  const int64_t nchunks = (p.elems + 63) >> 6;
+  const int64_t nwords = p.elems >> 5;
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
   for (int64_t c0 = wave * kUnroll; c0 < nchunks; c0 += nwaves * kUnroll) {
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t e = (c0 + u) * 64 + lane;
-      v[u] = (e < elems) ? __builtin_nontemporal_load(x + e) : 0.0f;
+      v[u] = (e < p.elems) ? __builtin_nontemporal_load(x + e) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -179,22 +187,22 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(
       if (lane < 2 && w < nwords) bits[w] = static_cast<uint32_t>(m >> (32 * lane));
     }
   }
-  if (dev_status != nullptr && __ballot(nan_seen) != 0 && lane == 0)
-    atomicOr(dev_status, HAD_DEV_NAN_INPUT);
-  if (kSigma) write_partials(s1, s2, partials);
+  flag_nan(nan_seen, p.dev_status);
+  if (kSigma) write_partials(s1, s2, bj);
 }
 
 // Any d: one thread per output word.
 template <bool kSigma>
-__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(
-    const float* __restrict__ x, uint32_t* __restrict__ bits, int64_t rows, int d, int W,
-    double* partials, uint32_t* dev_status) {
-  const int64_t nwords = rows * W;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kPackThreads;
+__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(PackJobs p) {
+  const BlockJob bj = block_job(p);
+  const float* __restrict__ x = bj.job.x;
+  uint32_t* __restrict__ bits = bj.job.bits;
+  const int d = p.d, W = p.W;
+  const int64_t nwords = p.rows * W;
+  const int64_t stride = bj.nblk * kPackThreads;
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
-  for (int64_t wi = static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x; wi < nwords;
-       wi += stride) {
+  for (int64_t wi = bj.blk * kPackThreads + threadIdx.x; wi < nwords; wi += stride) {
     const int64_t r = wi / W;
     const int w = static_cast<int>(wi - r * W);
     const float* row = x + r * d;
@@ -212,9 +220,24 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(
     }
     bits[wi] = word;
   }
-  if (dev_status != nullptr && __ballot(nan_seen) != 0 && (threadIdx.x & 63) == 0)
-    atomicOr(dev_status, HAD_DEV_NAN_INPUT);
-  if (kSigma) write_partials(s1, s2, partials);
+  flag_nan(nan_seen, p.dev_status);
+  if (kSigma) write_partials(s1, s2, bj);
+}
+
+enum class PackPath { Vec, Stream, Rows };
+
+PackPath path_for(const float* x, int64_t d) {
+  if (d % 32 != 0) return PackPath::Rows;
+  return aligned(x, 16) ? PackPath::Vec : PackPath::Stream;
+}
+
+template <bool kSigma>
+void launch_path(PackPath path, const PackJobs& p, int blocks, hipStream_t st) {
+  switch (path) {
+    case PackPath::Vec: pack_vec_kernel<kSigma><<<blocks, kPackThreads, 0, st>>>(p); break;
+    case PackPath::Stream: pack_stream_kernel<kSigma><<<blocks, kPackThreads, 0, st>>>(p); break;
+    case PackPath::Rows: pack_rows_kernel<kSigma><<<blocks, kPackThreads, 0, st>>>(p); break;
+  }
 }
 
 }  // namespace
@@ -225,7 +248,7 @@ int pack_grid_blocks(const had_shape& s) {
   if (s.dim % 32 == 0) {
     const int64_t segs = (elems + 255) / 256;
     const int64_t waves = (segs + kSegsPerWave - 1) / kSegsPerWave;
-    blocks = (waves + kPackThreads / 64 - 1) / (kPackThreads / 64);
+    blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   } else {
     const int64_t words = s.batch * s.heads * s.seq * words_per_row(s.dim);
     blocks = (words + kPackThreads - 1) / kPackThreads;
@@ -233,6 +256,54 @@ int pack_grid_blocks(const had_shape& s) {
   if (blocks < 1) blocks = 1;
   if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
   return static_cast<int>(blocks);
+}
+
+had_status check_pack_args(const float* x, uint32_t* xbits, float* sigma, const char* who) {
+  if (x == nullptr || xbits == nullptr) return failf(HAD_ERR_INVALID_ARG, "%s: null input or bits", who);
+  if (!aligned(x, 4) || !aligned(xbits, 4))
+    return failf(HAD_ERR_INVALID_ARG, "%s: inputs and bits must be 4-byte aligned", who);
+  if (sigma != nullptr && !aligned(sigma, 4))
+    return failf(HAD_ERR_INVALID_ARG, "%s: sigma must be 4-byte aligned", who);
+  return HAD_OK;
+}
+
+had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint32_t* dev_status,
+                       hipStream_t st) {
+  const int blocks = pack_grid_blocks(s);
+  PackJobs p{};
+  p.elems = s.batch * s.heads * s.seq * s.dim;
+  p.rows = s.batch * s.heads * s.seq;
+  p.d = static_cast<int>(s.dim);
+  p.W = static_cast<int>(words_per_row(s.dim));
+  p.dev_status = dev_status;
+  const bool sigma = jobs[0].partials != nullptr;
+  // one launch for both tensors when they take the same path and both or
+  // neither need sigma partials; otherwise one launch each
+  const bool fuse = njobs == 2 && path_for(jobs[0].x, s.dim) == path_for(jobs[1].x, s.dim) &&
+                    (jobs[0].partials != nullptr) == (jobs[1].partials != nullptr);
+  for (int j = 0; j < njobs; ++j) {
+    p.job[0] = jobs[j];
+    p.job[1] = fuse ? jobs[1] : jobs[j];
+    p.nb0 = blocks;
+    const int grid = fuse ? 2 * blocks : blocks;
+    const PackPath path = path_for(jobs[j].x, s.dim);
+    if (jobs[j].partials != nullptr || (fuse && sigma))
+      launch_path<true>(path, p, grid, st);
+    else
+      launch_path<false>(path, p, grid, st);
+    had_status ls = check_launch("had_pack");
+    if (ls != HAD_OK) return ls;
+    if (fuse) break;
+  }
+  return HAD_OK;
+}
+
+had_status launch_sigma_finalize(const double* partials, const had_shape& s, float* sigma,
+                                 hipStream_t st) {
+  const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
+  sigma_finalize_kernel<<<1, 64, 0, st>>>(reinterpret_cast<const double2*>(partials),
+                                          pack_grid_blocks(s), count, sigma);
+  return check_launch("had_pack");
 }
 
 }  // namespace had
@@ -250,15 +321,11 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   clear_error();
   had_status st = check_shape(s);
   if (st != HAD_OK) return st;
-  if (x == nullptr || xbits == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_pack: null x or xbits");
-  if (!aligned(x, 4) || !aligned(xbits, 4))
-    return fail(HAD_ERR_INVALID_ARG, "had_pack: x and xbits must be 4-byte aligned");
+  if ((st = check_pack_args(x, xbits, sigma, "had_pack")) != HAD_OK) return st;
   if (dev_status != nullptr && !aligned(dev_status, 4))
     return fail(HAD_ERR_INVALID_ARG, "had_pack: dev_status must be 4-byte aligned");
-  const int blocks = pack_grid_blocks(s);
   double* partials = nullptr;
   if (sigma != nullptr) {
-    if (!aligned(sigma, 4)) return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma must be 4-byte aligned");
     if (workspace == nullptr || !aligned(workspace, 16))
       return fail(HAD_ERR_INVALID_ARG, "had_pack: sigma requested but workspace is null or unaligned");
     if (workspace_bytes < had_pack_workspace_bytes(s))
@@ -266,28 +333,8 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
     partials = static_cast<double*>(workspace);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const int64_t rows = s.batch * s.heads * s.seq;
-  const int d = static_cast<int>(s.dim);
-  if (d % 32 == 0) {
-    const int64_t elems = rows * d;
-    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-    if (aligned(x, 16) && sigma)
-      pack_vec_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x4, xbits, elems, partials, dev_status);
-    else if (aligned(x, 16))
-      pack_vec_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x4, xbits, elems, nullptr, dev_status);
-    else if (sigma)
-      pack_stream_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, partials, dev_status);
-    else
-      pack_stream_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, elems, nullptr, dev_status);
-  } else {
-    const int W = static_cast<int>(words_per_row(d));
-    if (sigma)
-      pack_rows_kernel<true><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, partials, dev_status);
-    else
-      pack_rows_kernel<false><<<blocks, kPackThreads, 0, hs>>>(x, xbits, rows, d, W, nullptr, dev_status);
-  }
-  had_status ls = check_launch("had_pack");
-  if (ls != HAD_OK || sigma == nullptr) return ls;
-  sigma_finalize_kernel<<<1, kPackThreads, 0, hs>>>(reinterpret_cast<const double2*>(partials), blocks, static_cast<double>(rows) * d, sigma);
-  return check_launch("had_pack");
+  const PackJob job{x, xbits, partials};
+  if ((st = launch_pack(&job, 1, s, dev_status, hs)) != HAD_OK) return st;
+  if (sigma == nullptr) return HAD_OK;
+  return launch_sigma_finalize(partials, s, sigma, hs);
 }

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for fn in ["had_pack", "had_attention", "had_logits", "had_select", "had_words_per_row",
-               "had_pack_workspace_bytes", "had_status_string", "had_last_error"]:
+               "had_pack_workspace_bytes", "had_forward", "had_forward_workspace_bytes",
+               "had_status_string", "had_last_error"]:
         assert fn in names
 
 
@@ -50,6 +51,9 @@ def test_words_per_row_and_status_strings(lib):
 def test_pack_workspace_bytes(lib):
     assert lib.had_pack_workspace_bytes(Shape(1, 1, 128, 64)) >= 16
     assert lib.had_pack_workspace_bytes(Shape(0, 1, 128, 64)) == 0
+    big = Shape(8, 12, 1024, 64)
+    assert lib.had_forward_workspace_bytes(big) == 2 * lib.had_pack_workspace_bytes(big)
+    assert lib.had_forward_workspace_bytes(Shape(1, 0, 1, 1)) == 0
 
 
 # Fake, never-dereferenced device addresses: every call below must fail its
@@ -101,6 +105,33 @@ def test_pack_rejects_bad_arguments(lib):
     assert lib.had_pack(A16, s, A16B, A16C, 0x50000, 8, None, None) == INVALID
     assert lib.had_pack(A16, Shape(1, 1, 0, 64), A16B, None, None, 0, None, None) == INVALID
     assert lib.had_pack(A16, Shape(1, 1, 8, 300), A16B, None, None, 0, None, None) == UNSUPPORTED
+
+
+def _fwd(lib, q=A16, k=0x40000, v=0x60000, vdt=1, shape=None, topn=8, scale=0.125, causal=0,
+         qb=0x70000, kb=0x80000, out=0x90000, sq=None, sk=None, ws=None, wsb=0, st=None):
+    shape = shape or Shape(1, 2, 100, 64)
+    return lib.had_forward(q, k, v, vdt, shape, topn, scale, causal, qb, kb, out, sq, sk, ws, wsb,
+                           st, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, k=A16 + 2) == INVALID
+    assert _fwd(lib, qb=None) == INVALID
+    assert _fwd(lib, v=A16 + 4) == INVALID
+    assert _fwd(lib, out=None) == INVALID
+    assert _fwd(lib, topn=0) == INVALID
+    assert _fwd(lib, scale=-1.0) == INVALID
+    assert _fwd(lib, causal=2) == INVALID
+    assert _fwd(lib, vdt=7) == INVALID
+    assert _fwd(lib, st=A16 + 2) == INVALID
+    # a sigma without (or with a too small / unaligned) workspace
+    assert _fwd(lib, sq=0xA0000) == INVALID
+    assert _fwd(lib, sk=0xA0000, ws=0xB0000, wsb=16) == INVALID
+    assert _fwd(lib, sq=0xA0000, ws=0xB0008, wsb=1 << 20) == INVALID
+    assert _fwd(lib, shape=Shape(1, 1, 8, 257)) == UNSUPPORTED
+    assert _fwd(lib, shape=Shape(1, 1, 65537, 8)) == UNSUPPORTED
+    assert lib.had_last_error() != b""
 
 
 def test_select_and_logits_reject_bad_ranges(lib):
