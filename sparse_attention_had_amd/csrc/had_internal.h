@@ -60,16 +60,32 @@ had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint3
 had_status launch_sigma_finalize(const double* partials, const had_shape& s, float* sigma,
                                  hipStream_t st);
 
-// Fixed-order butterfly sum over a wave; lane 0's result is the same on every run.
+// v + (the value DPP control kCtrl brings to this lane, 0.0 where the row
+// mask leaves a lane out), on the two 32-bit halves of a double.
+template <int kCtrl, int kRowMask>
+__device__ inline double dpp_add_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, kRowMask, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, false);
+  const uint64_t w = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+  return v + __builtin_bit_cast(double, w);
+}
+
+// Wave sum of a double in a fixed order (neighbour pairs, quads, rows of 16,
+// then across rows); lane 63 holds the total, the same on every run.
 __device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  v = dpp_add_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add_f64<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_add_f64<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_add_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
 // One wave (lanes 0..63 of the calling wave): sigma from per-block partial
 // pairs (sum x, sum x^2).  Lane l sums partials l, l + 64, ... in order, then
-// a fixed butterfly; lane 0 writes the population standard deviation.
+// a fixed-order wave sum; lane 63 writes the population standard deviation.
 __device__ inline void sigma_from_partials(const double2* partials, int nblocks, double count,
                                            float* sigma) {
   constexpr int kPer = kPackMaxBlocks / 64;
@@ -88,7 +104,7 @@ __device__ inline void sigma_from_partials(const double2* partials, int nblocks,
   }
   a = wave_sum_f64(a);
   b = wave_sum_f64(b);
-  if (lane == 0) {
+  if (lane == 63) {
     const double mean = a / count;
     double var = b / count - mean * mean;
     if (!(var > 0.0)) var = 0.0;

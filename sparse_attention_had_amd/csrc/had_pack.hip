@@ -43,6 +43,8 @@ struct PackJobs {
   int nb0;              // blocks of job 0; the rest of the grid is job 1
   int64_t elems;        // B*H*n*d per tensor
   int64_t rows;         // B*H*n per tensor
+  int64_t seg_base;     // vector path: every wave of a tensor owns seg_base
+  int64_t seg_rem;      // 256-float segments, the first seg_rem waves one more
   int d;
   int W;
   uint32_t* dev_status;
@@ -70,7 +72,7 @@ __device__ inline void block_sum2(double& a, double& b) {
   a = wave_sum_f64(a);
   b = wave_sum_f64(b);
   const int wid = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  if ((threadIdx.x & 63) == 63) {
     red[0][wid] = a;
     red[1][wid] = b;
   }
@@ -114,15 +116,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
   uint32_t* __restrict__ bits = bj.job.bits;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (bj.blk * kPackThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = bj.nblk * kWavesPerBlock;
-  const int64_t nseg = (p.elems + 255) >> 8;
-  const int64_t seg_end = (wave + 1) * nseg / nwaves;
+  // contiguous run of segments [seg_begin, seg_end), sizes differ by <= 1
+  const int64_t seg_begin = wave * p.seg_base + min(wave, p.seg_rem);
+  const int64_t seg_end = seg_begin + p.seg_base + (wave < p.seg_rem ? 1 : 0);
   const int64_t nvec = p.elems >> 2;
   const int64_t nwords = p.elems >> 5;
   const int shift = 4 * (lane & 7);
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
-  for (int64_t s0 = wave * nseg / nwaves; s0 < seg_end; s0 += kUnroll) {
+  for (int64_t s0 = seg_begin; s0 < seg_end; s0 += kUnroll) {
     f32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -275,6 +277,10 @@ had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint3
   p.rows = s.batch * s.heads * s.seq;
   p.d = static_cast<int>(s.dim);
   p.W = static_cast<int>(words_per_row(s.dim));
+  const int64_t nseg = (p.elems + 255) / 256;
+  const int64_t nwaves = static_cast<int64_t>(blocks) * kWavesPerBlock;
+  p.seg_base = nseg / nwaves;
+  p.seg_rem = nseg % nwaves;
   p.dev_status = dev_status;
   const bool sigma = jobs[0].partials != nullptr;
   // one launch for both tensors when they take the same path and both or
