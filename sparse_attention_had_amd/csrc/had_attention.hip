@@ -59,8 +59,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLutEntries = 264;        // weight table: d+1 weights + zero slot
-constexpr int kZeroSlot = 263;
+// weight table: d+1 weights, then a zero slot in the last bank of its
+// 64-dword row, away from the low entries every row uses
+constexpr int kLutEntries = 320;
+constexpr int kZeroSlot = 319;
 constexpr int kByteLutOff = 0;          // 256 x 8 B: byte -> 8 int8 of +-1
 constexpr int kWLutOff = 2048;          // kLutEntries x 4 B
 constexpr int kKbOff = kWLutOff + 4 * kLutEntries;
@@ -240,19 +242,25 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   // Copies the key words of chunks [g0, g0 + ch) straight into buffer buf
   // (global_load_lds, 4 bytes per lane, lane-ordered); keys outside the
   // visible range load key 0 (their logits are masked).
-  auto k_issue = [&](int g0, int ch, int buf) {
-    const int items = ch * 32 * W;
-    for (int j = wid; j * 64 < items; j += C::kWaves) {
+  // (the per-lane part of each copy address is fixed; only the group base
+  // 16*g0 keys moves, and offsets stay 32-bit within the slice)
+  auto k_issue = [&](int g0, auto ch_c, int buf) {
+    constexpr int kItems = decltype(ch_c)::value * 32 * W;
+    constexpr int kJ = (kItems + 64 * C::kWaves - 1) / (64 * C::kWaves);
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = wid + jj * C::kWaves;
       const int item = j * 64 + lane;
-      if (item < items) {
+      if (item < kItems) {
         const int w = item % W;
         const int m = (item / W) & 31;
         const int c = item / (W * 32);
-        const int gc = g0 + c;
         // keys past the visible range (never used) load a valid row
-        const int key = min(key_of(gc, m), kend - 1);
-        __builtin_amdgcn_global_load_lds(kbg + static_cast<int64_t>(key) * W + w,
-                                         (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
+        const int key = min(key_of(c, m) + 16 * g0, kend - 1);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(kbg) +
+                                              static_cast<uint32_t>(4 * (key * W + w))),
+            (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
       }
     }
   };
@@ -288,11 +296,11 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   auto k_sweep = [&](uint32_t cin, auto&& body) {
     const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
     __syncthreads();  // previous users of the key buffers are done
-    k_issue(0, C::kCH1, 0);
+    k_issue(0, std::integral_constant<int, C::kCH1>{}, 0);
     copies_done();
     for (int gi = 0; gi < ngroups; ++gi) {
       const int buf = gi & 1;
-      if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, C::kCH1, buf ^ 1);
+      if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, std::integral_constant<int, C::kCH1>{}, buf ^ 1);
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
       if (cend > 0) {
@@ -455,18 +463,23 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   auto v_issue = [&](int g0, int buf) {
     if constexpr (VDIRECT) {
       constexpr int kInst = C::kCH2 * 32 * C::kPieces / 64;
-      for (int j = wid; j < kInst; j += C::kWaves) {
-        const int item = j * 64 + lane;
-        const int pp = item % C::kPieces;
-        const int r = (item / C::kPieces) & 31;
-        const int c = item / (C::kPieces * 32);
-        const int gc = g0 + c;
-        // keys past the visible range (weight 0 or never used) copy a valid row
-        const int key = min((r >> 4) * Hh + 16 * gc + (r & 15), kend - 1);
-        const int pc = pp ^ ((2 * (r & 3)) & C::kSwzMask);
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const uint16_t*>(vsrc) + static_cast<int64_t>(key) * d + 8 * pc,
-            (lds_void*)(region + buf * C::kVBuf + j * 1024), 16, 0, 0);
+      constexpr int kJ = (kInst + C::kWaves - 1) / C::kWaves;
+#pragma unroll
+      for (int jj = 0; jj < kJ; ++jj) {
+        const int j = wid + jj * C::kWaves;
+        if (j < kInst) {
+          const int item = j * 64 + lane;
+          const int pp = item % C::kPieces;
+          const int r = (item / C::kPieces) & 31;
+          const int c = item / (C::kPieces * 32);
+          // keys past the visible range (weight 0 or never used) copy a valid row
+          const int key = min((r >> 4) * Hh + 16 * c + (r & 15) + 16 * g0, kend - 1);
+          const int pc = pp ^ ((2 * (r & 3)) & C::kSwzMask);
+          __builtin_amdgcn_global_load_lds(
+              reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(vsrc) +
+                                                static_cast<uint32_t>(2 * (key * d + 8 * pc))),
+              (lds_void*)(region + buf * C::kVBuf + j * 1024), 16, 0, 0);
+        }
       }
     }
   };
@@ -669,14 +682,14 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
   make_q(0x02u, 0xFCu);  // +-2: the tile holds au = lutc + 2u
   v_load(0);
   __syncthreads();  // every wave is done with its histogram (V tiles alias it)
-  k_issue(0, C::kCH2, 0);
+  k_issue(0, std::integral_constant<int, C::kCH2>{}, 0);
   v_issue(0, 0);
   v_store(0);
   copies_done();
   for (int gi = 0; gi < ngroups2; ++gi) {
     const int buf = gi & 1;
     if (gi + 1 < ngroups2) {
-      k_issue((gi + 1) * C::kCH2, C::kCH2, buf ^ 1);
+      k_issue((gi + 1) * C::kCH2, std::integral_constant<int, C::kCH2>{}, buf ^ 1);
       v_issue((gi + 1) * C::kCH2, buf ^ 1);
       v_load((gi + 1) * C::kCH2);
     }
