@@ -69,6 +69,11 @@ constexpr int kKbOff = kWLutOff + 4 * kLutEntries;
 
 __host__ __device__ constexpr int waves_for(int W) { return W <= 4 ? 4 : 2; }
 __host__ __device__ constexpr int threads_for(int W) { return 64 * waves_for(W); }
+// Register budget of the bf16 attention kernel with directly copied V
+// tiles: at d <= 64 keep 3 waves per SIMD (<= 168 VGPRs); otherwise 2.
+__host__ __device__ constexpr int min_waves_for(int W, bool vf32, int mode, bool vdirect) {
+  return (W <= 2 && !vf32 && mode == 0 && vdirect) ? 3 : 2;
+}
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int W, bool VF32, bool VDIRECT>
@@ -144,7 +149,9 @@ __device__ inline uint32_t opaque(uint32_t v) {
 }
 
 template <int W, bool VF32, int MODE, bool VDIRECT>
-__global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(threads_for(W))
+__attribute__((amdgpu_waves_per_eu(min_waves_for(W, VF32, MODE, VDIRECT))))
+void had_attn_kernel(AttnArgs a) {
   using C = Cfg<W, VF32, VDIRECT>;
   constexpr int VS = C::kVS;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::kLdsBytes];
@@ -590,28 +597,6 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     return __builtin_bit_cast(v8bf, u);
   };
 
-  // Weights of the 16 elements of chunk gc from its tile t (au values).
-  auto select_chunk = [&](const v16i& t, int gc, uint32_t* e) {
-    const int L = lim - (half * Hh + 16 * gc);
-    if (__all(L >= 16)) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t au = static_cast<uint32_t>(t[i]);
-        // all-ones when kept: a bit select, no lane mask
-        const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
-        e[i] = lds_load_u32((au & m) | (zaddr & ~m));
-        sp = opaque(sp + ((au == auT) ? 1u : 0u));  // one compare + add-with-carry
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t au = static_cast<uint32_t>(t[i]);
-        e[i] = lds_load_u32(i < L && static_cast<int32_t>((au << 15) + sp) < 0 ? au : zaddr);
-        sp += (au == auT) ? 1u : 0u;
-      }
-    }
-  };
-
   // out^T += V^T P^T for chunk c of the V tile vt, weights e.
   auto pv_chunk = [&](const unsigned char* vt, int c, const uint32_t* e) {
     if constexpr (VF32) {
@@ -653,28 +638,65 @@ __global__ __launch_bounds__(threads_for(W)) void had_attn_kernel(AttnArgs a) {
     }
   };
 
-  // One key group, software-pipelined: the selection of chunk c + 1 (vector
-  // ALU and LDS table reads) is issued before the products of chunk c, so
-  // the table-read latency hides behind the matrix-core work.  Unrolled over
-  // the group so that the weights of consecutive chunks live in distinct
-  // registers.
+  // Tile of chunk gc (au = lutc + 2u per element) with every element that
+  // this lane's row cannot see pushed up by kHidden: such an element then
+  // fails the keep test and never equals auT, so the selection below needs
+  // no visibility test of its own.  The adjustment runs only for the chunks
+  // that some lane of the wave does not fully see.
+  constexpr uint32_t kHidden = 2048;  // > 4*d_max + 4; au stays below 2^13
+  auto attend_tile = [&](int buf, int c, int gc) {
+    v16i t = logits_tile(buf, c, lutc);
+    // chunks from wchunks on hold no key this wave sees (and from nchunk on,
+    // half 0's slots would repeat half 1's keys)
+    const int L = gc < wchunks ? lim - (half * Hh + 16 * gc) : 0;
+    if (!__all(L >= 16)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] += (i < L) ? 0 : static_cast<int>(kHidden);
+    }
+    return t;
+  };
+
+  // Weights of the 16 elements of one chunk.  Element i is kept iff
+  // D = (au << 15) + sp < 0; the sign becomes a mask that selects au or the
+  // zero slot, and the tie counter advances on au == auT: 5 vector ops.
+  auto select_chunk = [&](const v16i& t, uint32_t* e) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t au = static_cast<uint32_t>(t[i]);
+      const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
+      e[i] = lds_load_u32((au & m) | (zaddr & ~m));
+      sp = opaque(sp + ((au == auT) ? 1u : 0u));  // one compare + add-with-carry
+    }
+  };
+
+  // One key group, software-pipelined and branch-free in its body: every
+  // one of the kCH2 chunks is processed (chunks past this wave's keys are
+  // entirely hidden and add zero), and the selection of chunk c + 1 (vector
+  // ALU and table reads) is interleaved with the matrix-core products of
+  // chunk c, one product per ~8 vector ops, so neither unit waits on the
+  // other.  Unrolled over the group so that consecutive chunks' weights live
+  // in distinct registers.
   auto attend_group = [&](int buf, int gi) {
     const unsigned char* vt = region + buf * C::kVBuf;
     const int g0 = gi * C::kCH2;
-    const int cend = min(C::kCH2, wchunks - g0);
-    if (cend <= 0) return;
+    if (wchunks - g0 <= 0) return;
     uint32_t e[C::kCH2][16];
-    select_chunk(logits_tile(buf, 0, lutc), g0, e[0]);
-    v16i t_next = logits_tile(buf, cend > 1 ? 1 : 0, lutc);
+    select_chunk(attend_tile(buf, 0, g0), e[0]);
+    v16i tn = attend_tile(buf, C::kCH2 > 1 ? 1 : 0, g0 + (C::kCH2 > 1 ? 1 : 0));
 #pragma unroll
     for (int c = 0; c < C::kCH2; ++c) {
-      if (c < cend) {
-        if (c + 1 < cend) {
-          select_chunk(t_next, g0 + c + 1, e[(c + 1) % C::kCH2]);
-          if (c + 2 < cend) t_next = logits_tile(buf, c + 2, lutc);
+      if (c + 1 < C::kCH2) select_chunk(tn, e[c + 1]);
+      pv_chunk(vt, c, e[c]);
+      if (c + 2 < C::kCH2) tn = attend_tile(buf, c + 2, g0 + c + 2);
+      if (!VF32 && c + 1 < C::kCH2) {
+#pragma unroll
+        for (int k = 0; k < 4 * W + 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // vector ALU
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
         }
-        pv_chunk(vt, c, e[c]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // nothing moves across chunks
     }
   };
 
