@@ -656,26 +656,27 @@ void had_attn_kernel(AttnArgs a) {
     return t;
   };
 
-  // Weights of the 16 elements of one chunk.  Element i is kept iff
+  // Weight of element i of a chunk from its tile t.  Element i is kept iff
   // D = (au << 15) + sp < 0; the sign becomes a mask that selects au or the
   // zero slot, and the tie counter advances on au == auT: 5 vector ops.
+  auto select_elem = [&](const v16i& t, int i, uint32_t* e) {
+    const uint32_t au = static_cast<uint32_t>(t[i]);
+    const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
+    e[i] = lds_load_u32((au & m) | (zaddr & ~m));
+    sp = opaque(sp + ((au == auT) ? 1u : 0u));  // one compare + add-with-carry
+  };
   auto select_chunk = [&](const v16i& t, uint32_t* e) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t au = static_cast<uint32_t>(t[i]);
-      const uint32_t m = opaque(static_cast<uint32_t>(static_cast<int32_t>((au << 15) + sp) >> 31));
-      e[i] = lds_load_u32((au & m) | (zaddr & ~m));
-      sp = opaque(sp + ((au == auT) ? 1u : 0u));  // one compare + add-with-carry
-    }
+    for (int i = 0; i < 16; ++i) select_elem(t, i, e);
   };
 
-  // One key group, software-pipelined and branch-free in its body: every
-  // one of the kCH2 chunks is processed (chunks past this wave's keys are
-  // entirely hidden and add zero), and the selection of chunk c + 1 (vector
-  // ALU and table reads) is interleaved with the matrix-core products of
-  // chunk c, one product per ~8 vector ops, so neither unit waits on the
-  // other.  Unrolled over the group so that consecutive chunks' weights live
-  // in distinct registers.
+  // One key group, software-pipelined: every one of the kCH2 chunks is
+  // processed (chunks past this wave's keys are entirely hidden and add
+  // zero), and the selection of chunk c + 1 is interleaved in program order
+  // with the 4W matrix-core products of chunk c (bf16 V): a product, then
+  // 16/(4W) elements of vector work, so each product runs while the vector
+  // ALU works and no product waits on its accumulator.  Unrolled over the
+  // group so that consecutive chunks' weights live in distinct registers.
   auto attend_group = [&](int buf, int gi) {
     const unsigned char* vt = region + buf * C::kVBuf;
     const int g0 = gi * C::kCH2;
@@ -685,18 +686,47 @@ void had_attn_kernel(AttnArgs a) {
     v16i tn = attend_tile(buf, C::kCH2 > 1 ? 1 : 0, g0 + (C::kCH2 > 1 ? 1 : 0));
 #pragma unroll
     for (int c = 0; c < C::kCH2; ++c) {
-      if (c + 1 < C::kCH2) select_chunk(tn, e[c + 1]);
-      pv_chunk(vt, c, e[c]);
-      if (c + 2 < C::kCH2) tn = attend_tile(buf, c + 2, g0 + c + 2);
-      if (!VF32 && c + 1 < C::kCH2) {
+      if constexpr (VF32) {
+        if (c + 1 < C::kCH2) select_chunk(tn, e[c + 1]);
+        pv_chunk(vt, c, e[c]);
+      } else {
+        // operands of chunk c's products: weights as bf16 hi / lo pairs, and
+        // the transposed V tile pieces
+        v8bf bh[2], bl[2], av[2][W];
 #pragma unroll
-        for (int k = 0; k < 4 * W + 2; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // vector ALU
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        for (int ab = 0; ab < 2; ++ab) {
+          u32x4 ph, pl;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t e0 = e[c][8 * ab + 2 * k], e1 = e[c][8 * ab + 2 * k + 1];
+            ph[k] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // hi terms
+            pl[k] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // lo terms
+          }
+          bh[ab] = __builtin_bit_cast(v8bf, ph);
+          bl[ab] = __builtin_bit_cast(v8bf, pl);
+#pragma unroll
+          for (int t = 0; t < W; ++t) {
+            if constexpr (VDIRECT) {
+              av[ab][t] = v_operand(vt + c * 32 * 2 * C::kDP, t, ab);
+            } else {
+              const u32x4 vv = *reinterpret_cast<const u32x4*>(
+                  vt + c * C::kDP * VS + (32 * t + ql) * VS + 32 * half + 16 * ab);
+              av[ab][t] = __builtin_bit_cast(v8bf, vv);
+            }
+          }
+        }
+        constexpr int kProducts = 4 * W;
+#pragma unroll
+        for (int p = 0; p < kProducts; ++p) {
+          const int ab = p / (2 * W), hl = (p / W) & 1, t = p % W;
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ab][t], hl ? bl[ab] : bh[ab], acc[t], 0, 0, 0);
+          if (c + 1 < C::kCH2) {
+#pragma unroll
+            for (int i = (p * 16) / kProducts; i < ((p + 1) * 16) / kProducts; ++i) select_elem(tn, i, e[c + 1]);
+          }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);  // nothing moves across chunks
+      if (c + 2 < C::kCH2) tn = attend_tile(buf, c + 2, g0 + c + 2);
     }
   };
 
