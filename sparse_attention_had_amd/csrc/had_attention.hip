@@ -190,6 +190,46 @@ void had_attn_kernel(AttnArgs a) {
   const int wlim = (wave_q0 >= qend) ? 0 : (causal ? min(n, wave_q0 + 32) : n);
   const int wchunks = min(nchunk, (wlim + 15) / 16);  // chunks with keys this wave sees
 
+  // ---- key words: kb[c][m][w], m = MFMA row of the logit tile.  Row m holds
+  // key (m>>2 & 1)*Hh + 16*gc + 4*(m>>3) + (m&3), i.e. register i of lane L
+  // gets key half*Hh + 16*gc + i.  Pad features need no masking: the Q
+  // operand is zero there.
+  const uint32_t* kbg = a.kbits + bh * static_cast<int64_t>(n) * W;
+  auto key_of = [&](int gc, int m) { return ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3); };
+  // Copies the key words of chunks [g0, g0 + ch) straight into buffer buf
+  // (global_load_lds, 4 bytes per lane, lane-ordered); keys outside the
+  // visible range load a valid row (their logits are masked).  The per-lane
+  // part of each copy address is fixed; only the group base 16*g0 moves, and
+  // offsets stay 32-bit within the slice.
+  auto k_issue = [&](int g0, auto ch_c, int buf) {
+    constexpr int kItems = decltype(ch_c)::value * 32 * W;
+    constexpr int kJ = (kItems + 64 * C::kWaves - 1) / (64 * C::kWaves);
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = wid + jj * C::kWaves;
+      const int item = j * 64 + lane;
+      if (item < kItems) {
+        const int w = item % W;
+        const int m = (item / W) & 31;
+        const int c = item / (W * 32);
+        // keys past the visible range (never used) load a valid row
+        const int key = min(key_of(c, m) + 16 * g0, kend - 1);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(kbg) +
+                                              static_cast<uint32_t>(4 * (key * W + w))),
+            (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
+      }
+    }
+  };
+  // all of this thread's copies have landed; then the block barrier
+  auto copies_done = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // the first key group of the first sweep is in flight during the set-up
+  k_issue(0, std::integral_constant<int, C::kCH1>{}, 0);
+
   // ---- sigma of the fused forward call: wave 0 of the last block (the
   // lightest one when causal) reduces the pack partials before its own work
   if (MODE == 0 && wid == 0 && blockIdx.x == gridDim.x - 1) {
@@ -240,43 +280,6 @@ void had_attn_kernel(AttnArgs a) {
     }
   };
 
-  // ---- key words: kb[c][m][w], m = MFMA row of the logit tile.  Row m holds
-  // key (m>>2 & 1)*Hh + 16*gc + 4*(m>>3) + (m&3), i.e. register i of lane L
-  // gets key half*Hh + 16*gc + i.  Pad features need no masking: the Q
-  // operand is zero there.
-  const uint32_t* kbg = a.kbits + bh * static_cast<int64_t>(n) * W;
-  auto key_of = [&](int gc, int m) { return ((m >> 2) & 1) * Hh + 16 * gc + 4 * (m >> 3) + (m & 3); };
-  // Copies the key words of chunks [g0, g0 + ch) straight into buffer buf
-  // (global_load_lds, 4 bytes per lane, lane-ordered); keys outside the
-  // visible range load key 0 (their logits are masked).
-  // (the per-lane part of each copy address is fixed; only the group base
-  // 16*g0 keys moves, and offsets stay 32-bit within the slice)
-  auto k_issue = [&](int g0, auto ch_c, int buf) {
-    constexpr int kItems = decltype(ch_c)::value * 32 * W;
-    constexpr int kJ = (kItems + 64 * C::kWaves - 1) / (64 * C::kWaves);
-#pragma unroll
-    for (int jj = 0; jj < kJ; ++jj) {
-      const int j = wid + jj * C::kWaves;
-      const int item = j * 64 + lane;
-      if (item < kItems) {
-        const int w = item % W;
-        const int m = (item / W) & 31;
-        const int c = item / (W * 32);
-        // keys past the visible range (never used) load a valid row
-        const int key = min(key_of(c, m) + 16 * g0, kend - 1);
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(kbg) +
-                                              static_cast<uint32_t>(4 * (key * W + w))),
-            (lds_void*)(lds + kKbOff + buf * C::kKbBuf + j * 256), 4, 0, 0);
-      }
-    }
-  };
-  // all of this thread's copies have landed; then the block barrier
-  auto copies_done = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-
   // cin + k*u, u = -logit, for (query ql, key half*Hh + 16*gc + i),
   // i = 0..15, chunk c of the key-word buffer buf (k set by make_q).
   auto logits_tile = [&](int buf, int c, uint32_t cin) {
@@ -300,10 +303,13 @@ void had_attn_kernel(AttnArgs a) {
 
   // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
   // body(u, gc) runs per chunk with a one-chunk logit lookahead.
-  auto k_sweep = [&](uint32_t cin, auto&& body) {
+  // first_issued: group 0 was copied at kernel entry.
+  auto k_sweep = [&](uint32_t cin, bool first_issued, auto&& body) {
     const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
-    __syncthreads();  // previous users of the key buffers are done
-    k_issue(0, std::integral_constant<int, C::kCH1>{}, 0);
+    if (!first_issued) {
+      __syncthreads();  // previous users of the key buffers are done
+      k_issue(0, std::integral_constant<int, C::kCH1>{}, 0);
+    }
     copies_done();
     for (int gi = 0; gi < ngroups; ++gi) {
       const int buf = gi & 1;
@@ -326,7 +332,7 @@ void had_attn_kernel(AttnArgs a) {
   if (MODE == 2) {
     int16_t* dst = a.logits + (bh_local * a.row_count + (qvalid ? i_row - a.row_begin : 0)) * static_cast<int64_t>(n);
     make_q(0x01u, 0xFEu);  // +-1: the tile holds u itself
-    k_sweep(0u, [&](const v16i& u, int gc) {
+    k_sweep(0u, true, [&](const v16i& u, int gc) {
       if (!qvalid) return;
       const int kbase = half * Hh + 16 * gc;
 #pragma unroll
@@ -346,7 +352,7 @@ void had_attn_kernel(AttnArgs a) {
   // what the tile holds with k = 64 and cin = hb
   const uint32_t hb = lds_addr(region + (wid * (d + 1) * 32 + ql) * 4 + 64 * d);
   make_q(0x40u, 0x80u);  // +-64
-  k_sweep(hb, [&](const v16i& t, int gc) {
+  k_sweep(hb, true, [&](const v16i& t, int gc) {
     const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
     if (__all(L >= 16)) {
 #pragma unroll
@@ -359,6 +365,10 @@ void had_attn_kernel(AttnArgs a) {
           __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
     }
   });
+
+  // the key buffers are free again (the sweep ended with a barrier): the
+  // first key group of pass 2 is copied while the statistics are computed
+  if (MODE == 0) k_issue(0, std::integral_constant<int, C::kCH2>{}, 0);
 
   // =========================================================== per-row statistics
   const int Ni = qvalid ? min(a.topn, lim) : 0;
@@ -413,7 +423,7 @@ void had_attn_kernel(AttnArgs a) {
     int pos = half ? (below0 + quota0) : 0;
     int32_t* dst = a.idx + (bh_local * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(a.topn);
     make_q(0x02u, 0xFCu);  // +-2
-    k_sweep(lutc, [&](const v16i& t, int gc) {
+    k_sweep(lutc, false, [&](const v16i& t, int gc) {
       const int kbase = half * Hh + 16 * gc;
       const int L = lim - kbase;
 #pragma unroll
@@ -734,7 +744,6 @@ void had_attn_kernel(AttnArgs a) {
   make_q(0x02u, 0xFCu);  // +-2: the tile holds au = lutc + 2u
   v_load(0);
   __syncthreads();  // every wave is done with its histogram (V tiles alias it)
-  k_issue(0, std::integral_constant<int, C::kCH2>{}, 0);
   v_issue(0, 0);
   v_store(0);
   copies_done();
