@@ -45,7 +45,8 @@ typedef enum { HAD_F32 = 0, HAD_BF16 = 1 } had_dtype;
 /* Device status word bits written by had_pack (see below). */
 #define HAD_DEV_NAN_INPUT 1u
 
-/* Limits: 1 <= d <= HAD_MAX_DIM, 1 <= n <= HAD_MAX_SEQ. */
+/* Limits: 1 <= d <= HAD_MAX_DIM; 1 <= n <= HAD_MAX_SEQ for the attention
+   calls (had_pack accepts n up to HAD_MAX_DECODE_KEYS, to pack key caches). */
 #define HAD_MAX_DIM 256
 #define HAD_MAX_SEQ 65536
 
@@ -55,6 +56,19 @@ typedef struct {
   int64_t seq;   /* n: tokens per (batch, head) */
   int64_t dim;   /* d: features per token */
 } had_shape;
+
+/* Decoding against a key/value cache (had_decode). */
+#define HAD_MAX_DECODE_Q 64            /* new query rows per (batch, head) */
+#define HAD_MAX_DECODE_KEYS (1 << 22)  /* rows of the cache (k_stride) */
+
+typedef struct {
+  int64_t batch;    /* B */
+  int64_t heads;    /* H */
+  int64_t n_q;      /* new query rows per (batch, head) */
+  int64_t n_k;      /* valid rows of the key/value cache */
+  int64_t k_stride; /* allocated rows of the cache per (batch, head), >= n_k */
+  int64_t dim;      /* d */
+} had_decode_shape;
 
 /* Number of uint32 words holding the d sign bits of one row: ceil(d / 32). */
 int64_t had_words_per_row(int64_t dim);
@@ -191,6 +205,42 @@ had_status had_logits(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
 had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
                       int64_t topn, int causal, int64_t bh_begin,
                       int64_t bh_count, int32_t* idx, void* stream);
+
+/* Workspace bytes that had_decode needs for shape s. */
+size_t had_decode_workspace_bytes(had_decode_shape s);
+
+/*
+ * had_decode - the attention of n_q new query rows against a cache of n_k
+ * packed keys and their values: the decoding step of long-context inference.
+ *
+ * Defined by: the passages cited for had_attention (Pith review, "What
+ * carries the argument"; referee major comment 3), with the query rows at
+ * positions q_pos0 .. q_pos0 + n_q - 1 of the sequence whose first n_k rows
+ * the cache holds.
+ *
+ *  qbits  [B,H,n_q,W] uint32 sign words of the new rows (had_pack output).
+ *  kbits  [B,H,k_stride,W] uint32 sign words of the cache; rows >= n_k unused.
+ *  v      [B,H,k_stride,d] float32 (HAD_F32) or bfloat16 (HAD_BF16) values;
+ *         rows >= n_k unused.  4-byte aligned.
+ *  q_pos0 position of the first new row (>= 0).  causal = 1: row i sees the
+ *         keys j <= q_pos0 + i (and j < n_k); causal = 0: every key.
+ *  topn, scale: as had_attention; row i keeps N_i = min(N, visible_i) keys,
+ *         lower key index first among equal logits.
+ *  out    [B,H,n_q,d] float32.
+ *  workspace  device memory of had_decode_workspace_bytes(s) bytes, 256-byte
+ *         aligned; no initial contents needed; calls that may overlap need
+ *         distinct ones.
+ *  Precision: exact integer logits and selection; weights exp(-2*scale*(h -
+ *  h_min)) and sums in float32.  Only the kept V rows are read.
+ *  Errors: HAD_ERR_INVALID_ARG for null or misaligned pointers, bad sizes,
+ *  k_stride < n_k, q_pos0 < 0, topn < 1, bad scale, causal or v_dtype, a
+ *  small workspace; HAD_ERR_UNSUPPORTED above the limits.
+ */
+had_status had_decode(const uint32_t* qbits, const uint32_t* kbits,
+                      const void* v, had_dtype v_dtype, had_decode_shape s,
+                      int64_t q_pos0, int64_t topn, float scale, int causal,
+                      float* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Static text for a status code. */
 const char* had_status_string(had_status st);

@@ -38,6 +38,7 @@ __all__ = [
     "select_topn",
     "sparse_softmax_av",
     "forward",
+    "decode",
 ]
 
 
@@ -242,6 +243,35 @@ def forward(q, k, v, topn: int, scale: float, causal: bool = False, rows=None):
     bq = binarize(q)
     bk = binarize(k)
     S = logits(bq[rows], bk)
+    idx = select_topn(S, topn, causal, row_index=rows)
+    out, mag = sparse_softmax_av(S, idx, v, scale)
+    return {
+        "qbits": pack_bits(bq),
+        "kbits": pack_bits(bk),
+        "S": S,
+        "idx": idx,
+        "out": out,
+        "E": mag,
+        "rows": rows,
+    }
+
+
+def decode(q, k, v, topn: int, scale: float, q_pos0: int = 0, causal: bool = True):
+    """Attention of new query rows against a cache of keys and values (one head).
+
+    The same path as forward(): the rows of q sit at positions q_pos0,
+    q_pos0 + 1, ... of the sequence whose first rows the cache k, v holds;
+    under a causal mask row i sees the keys j <= q_pos0 + i.  Returns the
+    dict of forward() (rows = the query positions).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    if q_pos0 < 0:
+        raise ValueError("q_pos0 must be >= 0")
+    rows = q_pos0 + np.arange(q.shape[0], dtype=np.int64)
+    bq = binarize(q)
+    bk = binarize(k)
+    S = logits(bq, bk)
     idx = select_topn(S, topn, causal, row_index=rows)
     out, mag = sparse_softmax_av(S, idx, v, scale)
     return {

@@ -59,6 +59,13 @@ class Shape(ctypes.Structure):
     ]
 
 
+class DecodeShape(ctypes.Structure):
+    """had_decode_shape: B, H, new query rows, valid cache rows, cache rows, d."""
+
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("n_q", ctypes.c_int64),
+                ("n_k", ctypes.c_int64), ("k_stride", ctypes.c_int64), ("dim", ctypes.c_int64)]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -101,6 +108,11 @@ def load_library():
         lib.had_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P,
                                     ctypes.c_size_t, P, P]
         lib.had_forward.restype = I
+        lib.had_decode_workspace_bytes.argtypes = [DecodeShape]
+        lib.had_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.had_decode.argtypes = [P, P, P, I, DecodeShape, I64, I64, ctypes.c_float, I, P, P,
+                                   ctypes.c_size_t, P]
+        lib.had_decode.restype = I
         lib.had_status_string.argtypes = [I]
         lib.had_status_string.restype = ctypes.c_char_p
         lib.had_last_error.argtypes = []
@@ -298,6 +310,52 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale:
     if not with_sigma:
         return out, qbits, kbits, None, None
     return out, qbits, kbits, sigma_q, sigma_k
+
+
+def decode_workspace_bytes(batch: int, heads: int, n_q: int, n_k: int, k_stride: int,
+                           dim: int) -> int:
+    return int(load_library().had_decode_workspace_bytes(
+        DecodeShape(batch, heads, n_q, n_k, k_stride, dim)))
+
+
+def decode(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int, scale: float,
+           q_pos0: int = 0, causal: bool = True, *, n_k: int | None = None,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """New query rows against a key/value cache (had_decode).
+
+    qbits [B,H,n_q,W] int32 (had_pack of the new rows), kbits [B,H,k_stride,W]
+    int32, v [B,H,k_stride,d] float32 or bfloat16; the first n_k cache rows are
+    valid (default: all).  Returns out [B,H,n_q,d] float32.
+    """
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    _need_cuda(v, "v")
+    B, H, ks, d = _shape4(v, "v")
+    W = words_per_row(d)
+    nq = qbits.shape[2]
+    if qbits.dim() != 4 or tuple(qbits.shape) != (B, H, nq, W):
+        raise ValueError("qbits must have shape [B, H, n_q, ceil(d/32)]")
+    if tuple(kbits.shape) != (B, H, ks, W):
+        raise ValueError("kbits must have shape [B, H, k_stride, ceil(d/32)]")
+    nk = ks if n_k is None else int(n_k)
+    shape = DecodeShape(B, H, nq, nk, ks, d)
+    if out is None:
+        out = torch.empty((B, H, nq, d), dtype=torch.float32, device=v.device)
+    _need_cuda(out, "out", torch.float32)
+    if tuple(out.shape) != (B, H, nq, d):
+        raise ValueError("out must have shape [B, H, n_q, d]")
+    sh = _stream_handle(v.device, stream)
+    need = int(lib.had_decode_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(v.device, sh, need)
+    _need_cuda(workspace, "workspace")
+    _check("had_decode", lib.had_decode(
+        qbits.data_ptr(), kbits.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(q_pos0),
+        int(topn), float(scale), int(bool(causal)), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), sh))
+    return out
 
 
 def logits(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, *, bh_begin: int = 0,

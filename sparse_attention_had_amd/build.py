@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhad.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip"]
+SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -26,11 +26,11 @@ had_status failf(had_status st, const char* fmt, ...) {
   return st;
 }
 
-had_status check_shape(const had_shape& s) {
+had_status check_shape(const had_shape& s, int64_t max_seq) {
   if (s.batch <= 0 || s.heads <= 0 || s.seq <= 0 || s.dim <= 0)
     return fail(HAD_ERR_INVALID_ARG, "shape fields must all be positive");
   if (s.dim > HAD_MAX_DIM) return fail(HAD_ERR_UNSUPPORTED, "dim above HAD_MAX_DIM (256)");
-  if (s.seq > HAD_MAX_SEQ) return fail(HAD_ERR_UNSUPPORTED, "seq above HAD_MAX_SEQ (65536)");
+  if (s.seq > max_seq) return failf(HAD_ERR_UNSUPPORTED, "seq above the limit (%lld)", static_cast<long long>(max_seq));
   const double total = static_cast<double>(s.batch) * s.heads * s.seq * s.dim;
   if (total > 9.0e15) return fail(HAD_ERR_UNSUPPORTED, "tensor too large");
   if (static_cast<double>(s.batch) * s.heads > 2.0e9)

@@ -36,8 +36,9 @@ inline bool aligned(const void* p, uintptr_t a) {
 
 inline int64_t words_per_row(int64_t d) { return (d + 31) / 32; }
 
-// Shape checks common to every entry point.
-had_status check_shape(const had_shape& s);
+// Shape checks common to every entry point; seq may not exceed max_seq
+// (HAD_MAX_SEQ for the attention calls, the cache limit for had_pack).
+had_status check_shape(const had_shape& s, int64_t max_seq = HAD_MAX_SEQ);
 
 // ---- pack (had_pack.hip) ----
 constexpr int kPackThreads = 1024;   // threads per pack block

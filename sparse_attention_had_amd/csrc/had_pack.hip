@@ -317,7 +317,7 @@ had_status launch_sigma_finalize(const double* partials, const had_shape& s, flo
 using namespace had;
 
 extern "C" size_t had_pack_workspace_bytes(had_shape s) {
-  if (check_shape(s) != HAD_OK) return 0;
+  if (check_shape(s, HAD_MAX_DECODE_KEYS) != HAD_OK) return 0;
   return sizeof(double) * 2 * static_cast<size_t>(pack_grid_blocks(s));
 }
 
@@ -325,7 +325,7 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
                                void* workspace, size_t workspace_bytes, uint32_t* dev_status,
                                void* stream) {
   clear_error();
-  had_status st = check_shape(s);
+  had_status st = check_shape(s, HAD_MAX_DECODE_KEYS);  // also packs key caches
   if (st != HAD_OK) return st;
   if ((st = check_pack_args(x, xbits, sigma, "had_pack")) != HAD_OK) return st;
   if (dev_status != nullptr && !aligned(dev_status, 4))

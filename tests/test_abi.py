@@ -105,6 +105,9 @@ def test_pack_rejects_bad_arguments(lib):
     assert lib.had_pack(A16, s, A16B, A16C, 0x50000, 8, None, None) == INVALID
     assert lib.had_pack(A16, Shape(1, 1, 0, 64), A16B, None, None, 0, None, None) == INVALID
     assert lib.had_pack(A16, Shape(1, 1, 8, 300), A16B, None, None, 0, None, None) == UNSUPPORTED
+    # key caches longer than the attention limit can be packed, up to the cache limit
+    assert lib.had_pack_workspace_bytes(Shape(1, 1, 70000, 64)) > 0
+    assert lib.had_pack(A16, Shape(1, 1, (1 << 22) + 1, 64), A16B, None, None, 0, None, None) == UNSUPPORTED
 
 
 def _fwd(lib, q=A16, k=0x40000, v=0x60000, vdt=1, shape=None, topn=8, scale=0.125, causal=0,
@@ -131,6 +134,34 @@ def test_forward_rejects_bad_arguments(lib):
     assert _fwd(lib, sq=0xA0000, ws=0xB0008, wsb=1 << 20) == INVALID
     assert _fwd(lib, shape=Shape(1, 1, 8, 257)) == UNSUPPORTED
     assert _fwd(lib, shape=Shape(1, 1, 65537, 8)) == UNSUPPORTED
+    assert lib.had_last_error() != b""
+
+
+def test_decode_rejects_bad_arguments(lib):
+    D = had.DecodeShape
+    ok = D(1, 2, 4, 1000, 1024, 64)
+    ws_bytes = lib.had_decode_workspace_bytes(ok)
+    assert ws_bytes > 0
+    assert lib.had_decode_workspace_bytes(D(1, 2, 4, 1000, 999, 64)) == 0   # k_stride < n_k
+
+    def dec(q=A16, k=A16B, v=A16C, vdt=1, s=ok, p0=996, topn=8, scale=0.125, causal=1,
+            out=0x40000, ws=0x100000, wsb=ws_bytes):
+        return lib.had_decode(q, k, v, vdt, s, p0, topn, scale, causal, out, ws, wsb, None)
+
+    assert dec(q=None) == INVALID
+    assert dec(v=A16C + 2) == INVALID
+    assert dec(vdt=5) == INVALID
+    assert dec(p0=-1) == INVALID
+    assert dec(topn=0) == INVALID
+    assert dec(scale=float("nan")) == INVALID
+    assert dec(causal=3) == INVALID
+    assert dec(ws=None) == INVALID
+    assert dec(ws=0x100010) == INVALID
+    assert dec(wsb=ws_bytes - 1) == INVALID
+    assert dec(s=D(1, 2, 0, 1000, 1024, 64)) == INVALID
+    assert dec(s=D(1, 2, 65, 1000, 1024, 64)) == UNSUPPORTED
+    assert dec(s=D(1, 2, 4, 1000, 1024, 300)) == UNSUPPORTED
+    assert dec(s=D(1, 2, 4, 1000, (1 << 22) + 1, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
 
 

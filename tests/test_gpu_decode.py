@@ -1,0 +1,86 @@
+"""GPU parity of had_decode (new query rows against a key/value cache)
+through the C ABI, against the CPU oracle's decode().
+
+Cache rows past n_k hold large finite garbage so that a read of an unused
+row shows up in the outputs.  Outputs must be within 1e-5 * sum(p|V|) (fp32
+V) or 2e-3 * max|V| (bf16 V, max over the valid cache).  Every case prints
+its name, shape and seed first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_had_amd as had
+from had_workloads import make_inputs
+from parity_util import check_out, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    had.load_library()
+
+
+CASES = [
+    # B, H, n_q, n_k, k_stride, d, topn, q_pos0, causal, v dtype, scale
+    (1, 1, 1, 16384, 16384, 128, 2048, 16383, True, "bf16", 1 / np.sqrt(128)),
+    (2, 3, 4, 300, 320, 64, 37, 296, True, "bf16", 0.125),
+    (1, 2, 16, 1000, 1000, 64, 100, 0, False, "f32", 0.2),
+    (1, 1, 64, 5000, 5000, 5, 50, 4936, True, "bf16", 0.9),   # d = 5: ties everywhere
+    (1, 1, 3, 1, 8, 256, 4, 0, True, "f32", 1 / 16),          # one cached key
+    (2, 2, 5, 4097, 4100, 96, 512, 3000, True, "bf16", 0.1),  # rows see a prefix
+    (1, 2, 2, 70000, 70000, 64, 256, 69998, True, "bf16", 0.125),  # n_k > 65536
+    (1, 1, 2, 50, 50, 64, 80, 48, True, "bf16", 0.125),       # N > visible
+    (1, 1, 2, 100, 100, 64, 10, 500, True, "f32", 0.3),       # every key visible
+    (3, 1, 17, 777, 800, 33, 20, 760, False, "bf16", 0.25),   # two row batches
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_decode_matches_oracle(case):
+    B, H, nq, nk, ks, d, topn, p0, causal, vdt, scale = case
+    seed = nk + 7 * nq + d
+    log(f"decode {case} seed {seed}")
+    total = max(nk, p0 + nq)
+    inp = make_inputs(B, H, total, d, v_dtype=vdt, rank=8, noise="t3", seed=seed)
+    rows = np.arange(p0, p0 + nq) % total
+    qn = np.ascontiguousarray(inp["q"][:, :, rows])
+    kc = np.full((B, H, ks, d), 3.0e5, dtype=np.float32)
+    kc[:, :, :nk] = inp["k"][:, :, :nk]
+    kc[:, :, nk:, ::2] = -3.0e5
+    vc = np.full((B, H, ks, d), 1.0e6, dtype=np.float32)
+    vc[:, :, :nk] = inp["v"][:, :, :nk]
+    q_t = torch.from_numpy(qn).cuda()
+    k_t = torch.from_numpy(kc).cuda()
+    v_t = torch.from_numpy(vc)
+    v_t = (v_t.to(torch.bfloat16) if vdt == "bf16" else v_t).cuda()
+    qb, _ = had.pack(q_t, with_sigma=False)
+    kb, _ = had.pack(k_t, with_sigma=False)
+    out = had.decode(qb, kb, v_t, topn, scale, q_pos0=p0, causal=causal, n_k=nk).cpu().numpy()
+    vvalid = inp["v"][:, :, :nk]
+    for b in range(B):
+        for h in range(H):
+            r = oracle.decode(qn[b, h], inp["k"][b, h, :nk], vvalid[b, h], topn, scale,
+                              q_pos0=p0, causal=causal)
+            check_out(out[b, h], r["out"], r["E"], vvalid, vdt, where=f"slice {(b, h)}")
+
+
+def test_decode_is_deterministic_and_reuses_its_workspace():
+    B, H, nq, nk, d = 2, 4, 8, 3000, 64
+    log(f"decode determinism {(B, H, nq, nk, d)}")
+    inp = make_inputs(B, H, nk, d, v_dtype="bf16", rank=8, noise="t3", seed=5)
+    q_t = torch.from_numpy(np.ascontiguousarray(inp["q"][:, :, -nq:])).cuda()
+    k_t = torch.from_numpy(inp["k"]).cuda()
+    v_t = torch.from_numpy(inp["v"]).to(torch.bfloat16).cuda()
+    qb, _ = had.pack(q_t, with_sigma=False)
+    kb, _ = had.pack(k_t, with_sigma=False)
+    ws = torch.empty(had.decode_workspace_bytes(B, H, nq, nk, nk, d), dtype=torch.uint8, device="cuda")
+    o1 = had.decode(qb, kb, v_t, 300, 0.125, q_pos0=nk - nq, workspace=ws).clone()
+    o2 = had.decode(qb, kb, v_t, 300, 0.125, q_pos0=nk - nq, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

@@ -290,3 +290,48 @@ def test_forward_row_subset_matches_full():
     part = oracle.forward(q, k, v, 9, 0.2, causal=True, rows=rows)
     assert np.array_equal(part["idx"], full["idx"][rows])
     np.testing.assert_allclose(part["out"], full["out"][rows], rtol=0, atol=0)
+
+
+# --------------------------------------------------------------- decode ----
+def test_decode_rows_match_the_same_rows_of_the_full_sequence():
+    # New rows at positions p0..p0+m-1 against the cache of the first n_k
+    # tokens: exactly the rows p0.. of the full-sequence path (catches an
+    # off-by-one in the query positions or the causal limit).
+    inp = make_inputs(1, 1, 80, 40, rank=4, noise="t3", seed=12, v_dtype="f32")
+    q, k, v = inp["q"][0, 0], inp["k"][0, 0], inp["v"][0, 0]
+    for causal in (False, True):
+        for p0, m in ((0, 1), (17, 5), (75, 5)):
+            rows = np.arange(p0, p0 + m)
+            full = oracle.forward(q, k, v, 9, 0.3, causal=causal, rows=rows)
+            dec = oracle.decode(q[rows], k, v, 9, 0.3, q_pos0=p0, causal=causal)
+            assert np.array_equal(dec["idx"], full["idx"])
+            np.testing.assert_array_equal(dec["out"], full["out"])
+
+
+def test_decode_first_position_sees_only_the_first_key():
+    # Causal row at position 0: one visible key, so the output is V[0]
+    # itself whatever N and the logits (closed form).
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 33))
+    k = rng.standard_normal((50, 33))
+    v = rng.standard_normal((50, 7))
+    r = oracle.decode(q, k, v, 5, 0.4, q_pos0=0, causal=True)
+    assert r["idx"][0].tolist() == [0, -1, -1, -1, -1]
+    np.testing.assert_allclose(r["out"][0], v[0], rtol=0, atol=0)
+
+
+def test_decode_with_every_visible_key_is_dense_softmax_over_the_prefix():
+    # N >= visible keys: softmax over the visible prefix (scipy) times V.
+    rng = np.random.default_rng(9)
+    n_k, d = 30, 24
+    q = rng.standard_normal((3, d))
+    k = rng.standard_normal((n_k, d))
+    v = rng.standard_normal((n_k, 4))
+    r = oracle.decode(q, k, v, 64, 0.25, q_pos0=10, causal=True)
+    sq = np.where(q >= 0, 1.0, -1.0)
+    sk = np.where(k >= 0, 1.0, -1.0)
+    for i in range(3):
+        vis = 10 + i + 1
+        s = sk[:vis] @ sq[i]
+        want = scipy.special.softmax(0.25 * s) @ v[:vis]
+        np.testing.assert_allclose(r["out"][i], want, rtol=1e-12, atol=1e-14)
