@@ -12,21 +12,24 @@
 //
 // GPU design.  With n_q << n_k the work is a scan of the key cache, so it is
 // split over (key range, slice) work-groups and runs in four launches:
-//  1. dec_hist: per split, h of every (query, key) pair by XOR + popcount on
-//     the vector ALU (the query words are wave-uniform scalars), written as
-//     16-bit values (0xFFFF for keys the row cannot see), and a per-split
-//     (d+1)-bin histogram per query built with LDS atomics.
+//  1. dec_hist: per split and batch of up to 16 rows, h of every (row, key)
+//     pair by XOR + popcount on the vector ALU (the query words are
+//     wave-uniform scalars) into a per-split (d+1)-bin histogram per row
+//     (LDS atomics).
 //  2. dec_stats: one wave per row sums the split histograms, finds the
 //     threshold bin T and the tie quota r (as in had_attention), hands each
 //     split its share of the r ties in split order (lower keys first), and
 //     computes the softmax denominator Z from the counts.
-//  3. dec_gather: per split and row, a wave walks the split's keys in order,
-//     keeps h < T and the first quota keys with h == T (ballot ranks), and
-//     reads only the kept V rows (2d bytes each for bf16, coalesced across
-//     the wave), accumulating exp(-2*scale*(h - h_min)) * V_j in fp32.
+//  3. dec_gather: one 256-thread work-group per (split, row) recomputes h
+//     from the key words (L2-resident after step 1), keeps h < T and the
+//     first quota keys with h == T in key order (wave ballots plus a
+//     work-group prefix over the waves), compacts the kept keys and their
+//     weights exp(-2*scale*(h - h_min)) into LDS, and then reads only the
+//     kept V rows, 16 bytes of a row per lane, accumulating in fp32; the
+//     row groups are summed in a fixed order.
 //  4. dec_reduce: out = (sum over splits, in split order) / Z.
-// HBM bytes per slice and row: the key words once (d/8 bytes per key, shared
-// by the rows of a slice), 4 bytes per key for h, and 2d bytes per kept key.
+// HBM bytes per slice: the key words (d/8 bytes per key), and per row the
+// 2d bytes (bf16) of each kept key; everything else is small.
 #include <cmath>
 
 #include "had_internal.h"
@@ -35,10 +38,11 @@ namespace had {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecQBatch = 16;        // rows per histogram work-group
-constexpr int kDecMaxSplits = 512;
+constexpr int kDecQBatch = 16;           // rows per histogram work-group
+constexpr int kDecMaxSplits = 1024;
 constexpr int kDecMinKeysPerSplit = 256;
-constexpr uint32_t kDecHidden = 0xFFFFu;
+constexpr int kDecMaxKeysPerSplit = 4096;
+constexpr int kDecList = 512;            // kept keys buffered before a gather
 
 struct DecArgs {
   const uint32_t* qbits;  // [BH, nq, W]
@@ -52,14 +56,12 @@ struct DecArgs {
   float scale;
   int causal;
   float* out;             // [BH, nq, d]
-  uint16_t* hbuf;         // [BH, nq, nk_pad]
   uint32_t* hist;         // [BH, nq, splits, d + 1]
   uint32_t* quota;        // [BH, nq, splits]
   int32_t* stats;         // [BH, nq, 4]: T, h_min, Z bits, N_i
   float* part;            // [BH, nq, splits, d]
   int splits;
   int keys_per_split;
-  int nk_pad;
 };
 
 __device__ inline int visible_keys(const DecArgs& a, int q) {
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   for (int t = threadIdx.x; t < nqh * nb; t += kDecThreads) hl[t] = 0u;
   __syncthreads();
   const uint32_t* qrow = a.qbits + (bh * a.nq + q0) * W;
-  for (int jb = k0; jb < k0 + a.keys_per_split && jb < a.nk_pad; jb += kDecThreads) {
+  for (int jb = k0; jb < k1; jb += kDecThreads) {
     const int j = jb + static_cast<int>(threadIdx.x);
     const bool valid = j < k1;
     uint32_t kw[W];
@@ -97,7 +99,6 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
 #pragma unroll
       for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[w] ^ qrow[q * W + w]);
       const bool vis = valid && (!a.causal || j <= a.qpos0 + q0 + q);
-      if (j < a.nk_pad) a.hbuf[(bh * a.nq + q0 + q) * a.nk_pad + j] = static_cast<uint16_t>(vis ? h : kDecHidden);
       if (vis) atomicAdd(&hl[q * nb + h], 1u);
     }
   }
@@ -133,8 +134,15 @@ __global__ __launch_bounds__(64) void dec_stats_kernel(DecArgs a) {
   for (int r = 0; r < kR; ++r) {
     const int b = 64 * r + lane;
     uint32_t c = 0;
-    if (b < nb)
-      for (int s = 0; s < a.splits; ++s) c += hp[s * nb + b];
+    if (b < nb) {
+      for (int s0 = 0; s0 < a.splits; s0 += 8) {  // 8 loads in flight
+        uint32_t t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = s0 + u < a.splits ? hp[(s0 + u) * nb + b] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += t[u];
+      }
+    }
     cnt[r] = c;
   }
   // threshold bin T: first bin whose inclusive count reaches N_i; h_min: first
@@ -190,81 +198,156 @@ __global__ __launch_bounds__(64) void dec_stats_kernel(DecArgs a) {
   }
 }
 
-// ---- 3. selection and gather of the kept V rows, per split ------------------
-template <int F, bool VF32>
+// ---- 3. selection and gather of the kept V rows, per (split, row) ------------
+// V rows are read 8 features per lane: kVec = 16-byte vector loads (bf16 with
+// d % 8 == 0, or fp32 with d % 4 == 0, and a 16-byte aligned base).
+template <int W, bool VF32, bool kVec>
 __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
+  __shared__ int32_t list_j[kDecList];
+  __shared__ float list_w[kDecList];
+  __shared__ uint32_t wcnt[2][2][kDecThreads / 64];  // [parity][ties | kept][wave]
+  __shared__ float red[kDecThreads * 8];
   const int64_t bid = blockIdx.x;
   const int s = static_cast<int>(bid % a.splits);
-  const int64_t bh = bid / a.splits;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int64_t rest = bid / a.splits;
+  const int q = static_cast<int>(rest % a.nq);
+  const int64_t bh = rest / a.nq;
+  const int64_t bhq = bh * a.nq + q;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = a.d;
   const int k0 = s * a.keys_per_split;
   const int k1 = min(a.nk, k0 + a.keys_per_split);
-  const int d = a.d;
+  const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk);  // keys j <= last
+  const int32_t* st = a.stats + bhq * 4;
+  const uint32_t T = static_cast<uint32_t>(st[0]);
+  const int hmin = st[1];
+  const uint32_t quota = a.quota[bhq * a.splits + s];
+  const uint32_t* qw = a.qbits + bhq * W;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int q = wid; q < a.nq; q += kDecThreads / 64) {
-    const int64_t bhq = bh * a.nq + q;
-    const int32_t* st = a.stats + bhq * 4;
-    const uint32_t T = static_cast<uint32_t>(st[0]);
-    const int hmin = st[1];
-    const uint32_t quota = a.quota[bhq * a.splits + s];
-    const uint16_t* hrow = a.hbuf + bhq * a.nk_pad;
-    float acc[F];
+  // gather geometry: lpr lanes per V row, 8 features each; R rows per step
+  const int lpr = (d + 7) / 8;
+  const int R = kDecThreads / lpr;
+  const int g = tid / lpr, li = tid - (tid / lpr) * lpr;
+  float acc[8];
 #pragma unroll
-    for (int f = 0; f < F; ++f) acc[f] = 0.0f;
-    uint32_t tc = 0;  // ties of this row seen so far in this split
-    for (int j0 = k0; j0 < k1; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t h = j < k1 ? hrow[j] : kDecHidden;
-      const uint64_t tm = __ballot(h == T);
-      const uint32_t rank = tc + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
-      const bool keep = h < T || (h == T && rank < quota);
-      tc += static_cast<uint32_t>(__builtin_popcountll(tm));
-      const float wgt = keep ? expf(-2.0f * a.scale * static_cast<float>(static_cast<int>(h) - hmin)) : 0.0f;
-      uint64_t km = __ballot(keep);
-      // gather the kept rows, four in flight
-      while (km != 0) {
-        int jj[4];
-        float ww[4];
+  for (int f = 0; f < 8; ++f) acc[f] = 0.0f;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
+                               bh * static_cast<int64_t>(a.kstride) * d * (VF32 ? 4 : 2);
+  auto load8 = [&](int jj, float* x) {
+    const int c0 = 8 * li;
+    if constexpr (VF32) {
+      const float* row = reinterpret_cast<const float*>(vbase) + static_cast<int64_t>(jj) * d;
+      if (kVec && c0 + 8 <= d) {
+        const float4 u0 = *reinterpret_cast<const float4*>(row + c0);
+        const float4 u1 = *reinterpret_cast<const float4*>(row + c0 + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+      } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (km != 0) {
-            const int l = __builtin_ctzll(km);
-            km &= km - 1;
-            jj[u] = __builtin_amdgcn_readlane(j, l);
-            ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), l));
-          } else {
-            jj[u] = k0;
-            ww[u] = 0.0f;
-          }
+        for (int f = 0; f < 8; ++f) x[f] = c0 + f < d ? row[c0 + f] : 0.0f;
+      }
+    } else {
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + static_cast<int64_t>(jj) * d;
+      uint32_t w4[4];
+      if (kVec && c0 + 8 <= d) {
+        const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
+        w4[0] = u.x; w4[1] = u.y; w4[2] = u.z; w4[3] = u.w;
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const uint32_t lo = c0 + 2 * f < d ? row[c0 + 2 * f] : 0u;
+          const uint32_t hi = c0 + 2 * f + 1 < d ? row[c0 + 2 * f + 1] : 0u;
+          w4[f] = lo | (hi << 16);
         }
-        float vv[4][F];
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t row = (bh * a.kstride + jj[u]) * static_cast<int64_t>(d);
-#pragma unroll
-          for (int f = 0; f < F; ++f) {
-            const int c = lane * F + f;
-            if (VF32) {
-              vv[u][f] = c < d ? static_cast<const float*>(a.v)[row + c] : 0.0f;
-            } else {
-              const uint16_t b = c < d ? static_cast<const uint16_t*>(a.v)[row + c] : 0;
-              vv[u][f] = __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int f = 0; f < F; ++f) acc[f] = fmaf(ww[u], vv[u][f], acc[f]);
+      for (int f = 0; f < 4; ++f) {
+        x[2 * f] = __builtin_bit_cast(float, w4[f] << 16);
+        x[2 * f + 1] = __builtin_bit_cast(float, w4[f] & 0xFFFF0000u);
       }
     }
-    float* prow = a.part + (bhq * a.splits + s) * static_cast<int64_t>(d);
+  };
+  // accumulate the buffered kept rows [0, nl), two rows per row group in flight
+  auto gather = [&](int nl) {
+    if (g >= R) return;
+    for (int e0 = g; e0 < nl; e0 += 2 * R) {
+      float x0[8], x1[8];
+      const int e1 = e0 + R;
+      const float w0 = list_w[e0];
+      const float w1 = e1 < nl ? list_w[e1] : 0.0f;
+      load8(list_j[e0], x0);
+      load8(e1 < nl ? list_j[e1] : list_j[e0], x1);
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const int c = lane * F + f;
-      if (c < d) prow[c] = acc[f];
+      for (int f = 0; f < 8; ++f) acc[f] = fmaf(w1, x1[f], fmaf(w0, x0[f], acc[f]));
     }
+  };
+  if (k0 <= last) {
+    uint32_t run_ties = 0;
+    int nl = 0;
+    int it = 0;
+    for (int jb = k0; jb < k1; jb += kDecThreads, ++it) {
+      const int j = jb + tid;
+      const bool vis = j < k1 && j <= last;
+      uint32_t h = 0;
+      if (vis) {
+        const uint32_t* krow = a.kbits + (bh * a.kstride + j) * W;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(krow[w] ^ qw[w]);
+      }
+      const bool tie = vis && h == T;
+      const bool strict = vis && h < T;
+      const int par = it & 1;
+      const uint64_t tm = __ballot(tie);
+      if (lane == 0) wcnt[par][0][wid] = static_cast<uint32_t>(__builtin_popcountll(tm));
+      __syncthreads();
+      uint32_t before = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kDecThreads / 64; ++w) {
+        const uint32_t c = wcnt[par][0][w];
+        before += w < wid ? c : 0u;
+        tot += c;
+      }
+      const uint32_t rank = run_ties + before + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
+      const bool keep = strict || (tie && rank < quota);
+      run_ties += tot;
+      const uint64_t km = __ballot(keep);
+      if (lane == 0) wcnt[par][1][wid] = static_cast<uint32_t>(__builtin_popcountll(km));
+      __syncthreads();
+      int kbefore = 0, ktot = 0;
+#pragma unroll
+      for (int w = 0; w < kDecThreads / 64; ++w) {
+        const int c = static_cast<int>(wcnt[par][1][w]);
+        kbefore += w < wid ? c : 0;
+        ktot += c;
+      }
+      if (keep) {
+        const int pos = nl + kbefore + __builtin_popcountll(km & lt_mask);
+        list_j[pos] = j;
+        list_w[pos] = expf(-2.0f * a.scale * static_cast<float>(static_cast<int>(h) - hmin));
+      }
+      nl += ktot;
+      if (nl > kDecList - kDecThreads || jb + kDecThreads >= k1) {
+        __syncthreads();  // the list is complete
+        gather(nl);
+        nl = 0;
+        __syncthreads();  // the list may be refilled
+      }
+    }
+  }
+  // row-group partial sums, then a fixed-order sum over the groups
+  if (g < R) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int c = 8 * li + f;
+      if (c < d) red[g * d + c] = acc[f];
+    }
+  }
+  __syncthreads();
+  float* prow = a.part + (bhq * a.splits + s) * static_cast<int64_t>(d);
+  for (int c = tid; c < d; c += kDecThreads) {
+    float sum = 0.0f;
+    for (int gg = 0; gg < R; ++gg) sum += red[gg * d + c];
+    prow[c] = sum;
   }
 }
 
@@ -276,46 +359,50 @@ __global__ __launch_bounds__(64) void dec_reduce_kernel(DecArgs a) {
   const float* p = a.part + bhq * a.splits * static_cast<int64_t>(a.d);
   for (int c = threadIdx.x; c < a.d; c += 64) {
     float sum = 0.0f;
-    for (int s = 0; s < a.splits; ++s) sum += p[s * static_cast<int64_t>(a.d) + c];
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {  // 8 loads in flight, summed in order
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = s0 + u < a.splits ? p[(s0 + u) * static_cast<int64_t>(a.d) + c] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += t[u];
+    }
     a.out[bhq * a.d + c] = sum * invZ;
   }
 }
 
 // Work split and workspace layout, from the shape alone.
 struct DecPlan {
-  int splits, keys_per_split, nk_pad;
-  size_t off_h, off_hist, off_quota, off_stats, off_part, bytes;
+  int splits, keys_per_split;
+  size_t off_hist, off_quota, off_stats, off_part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 DecPlan plan_for(const had_decode_shape& s) {
   DecPlan p{};
-  const int64_t bh = s.batch * s.heads;
+  const int64_t rows = s.batch * s.heads * s.n_q;
   const int64_t nk = s.n_k;
-  int64_t splits = (2048 + bh - 1) / bh;                 // aim at >= 2048 work-groups
+  int64_t splits = (2048 + rows - 1) / rows;  // aim at >= 2048 gather work-groups
   const int64_t max_by_keys = (nk + kDecMinKeysPerSplit - 1) / kDecMinKeysPerSplit;
+  const int64_t min_by_keys = (nk + kDecMaxKeysPerSplit - 1) / kDecMaxKeysPerSplit;
   if (splits > max_by_keys) splits = max_by_keys;
+  if (splits < min_by_keys) splits = min_by_keys;
   if (splits > kDecMaxSplits) splits = kDecMaxSplits;
   if (splits < 1) splits = 1;
   int64_t per = (nk + splits - 1) / splits;
-  per = (per + 255) / 256 * 256;
+  per = (per + kDecThreads - 1) / kDecThreads * kDecThreads;
   splits = (nk + per - 1) / per;
   p.splits = static_cast<int>(splits);
   p.keys_per_split = static_cast<int>(per);
-  p.nk_pad = static_cast<int>((nk + 3) / 4 * 4);
-  const size_t rows = static_cast<size_t>(bh) * static_cast<size_t>(s.n_q);
   size_t off = 0;
-  p.off_h = off;
-  off = align256(off + rows * p.nk_pad * sizeof(uint16_t));
   p.off_hist = off;
-  off = align256(off + rows * p.splits * (s.dim + 1) * sizeof(uint32_t));
+  off = align256(off + static_cast<size_t>(rows) * p.splits * (s.dim + 1) * sizeof(uint32_t));
   p.off_quota = off;
-  off = align256(off + rows * p.splits * sizeof(uint32_t));
+  off = align256(off + static_cast<size_t>(rows) * p.splits * sizeof(uint32_t));
   p.off_stats = off;
-  off = align256(off + rows * 4 * sizeof(int32_t));
+  off = align256(off + static_cast<size_t>(rows) * 4 * sizeof(int32_t));
   p.off_part = off;
-  off = align256(off + rows * p.splits * s.dim * sizeof(float));
+  off = align256(off + static_cast<size_t>(rows) * p.splits * s.dim * sizeof(float));
   p.bytes = off;
   return p;
 }
@@ -338,12 +425,16 @@ void launch_hist(const DecArgs& a, int64_t blocks, hipStream_t st) {
   dec_hist_kernel<W><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
 }
 
-template <int F>
-void launch_gather(const DecArgs& a, int64_t blocks, hipStream_t st) {
-  if (a.vf32)
-    dec_gather_kernel<F, true><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
-  else
-    dec_gather_kernel<F, false><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+template <int W>
+void launch_gather(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
+  const unsigned nb = static_cast<unsigned>(blocks);
+  if (a.vf32) {
+    if (vec) dec_gather_kernel<W, true, true><<<nb, kDecThreads, 0, st>>>(a);
+    else dec_gather_kernel<W, true, false><<<nb, kDecThreads, 0, st>>>(a);
+  } else {
+    if (vec) dec_gather_kernel<W, false, true><<<nb, kDecThreads, 0, st>>>(a);
+    else dec_gather_kernel<W, false, false><<<nb, kDecThreads, 0, st>>>(a);
+  }
 }
 
 }  // namespace
@@ -396,18 +487,16 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   a.scale = scale;
   a.causal = causal;
   a.out = out;
-  a.hbuf = reinterpret_cast<uint16_t*>(ws + p.off_h);
   a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   a.quota = reinterpret_cast<uint32_t*>(ws + p.off_quota);
   a.stats = reinterpret_cast<int32_t*>(ws + p.off_stats);
   a.part = reinterpret_cast<float*>(ws + p.off_part);
   a.splits = p.splits;
   a.keys_per_split = p.keys_per_split;
-  a.nk_pad = p.nk_pad;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int64_t nqb = (s.n_q + kDecQBatch - 1) / kDecQBatch;
   const int64_t hist_blocks = a.bh_total * nqb * p.splits;
-  const int64_t gather_blocks = a.bh_total * p.splits;
+  const int64_t gather_blocks = a.bh_total * s.n_q * p.splits;
   const int64_t rows = a.bh_total * s.n_q;
   if (hist_blocks > 0x7FFFFFFF || gather_blocks > 0x7FFFFFFF || rows > 0x7FFFFFFF)
     return fail(HAD_ERR_UNSUPPORTED, "had_decode: grid too large");
@@ -424,12 +513,18 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
   dec_stats_kernel<<<static_cast<unsigned>(rows), 64, 0, hs>>>(a);
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
-  if (a.d <= 64)
-    launch_gather<1>(a, gather_blocks, hs);
-  else if (a.d <= 128)
-    launch_gather<2>(a, gather_blocks, hs);
-  else
-    launch_gather<4>(a, gather_blocks, hs);
+  // 16-byte row slices need 16-byte aligned rows
+  const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
+  switch (a.W) {
+    case 1: launch_gather<1>(a, vec, gather_blocks, hs); break;
+    case 2: launch_gather<2>(a, vec, gather_blocks, hs); break;
+    case 3: launch_gather<3>(a, vec, gather_blocks, hs); break;
+    case 4: launch_gather<4>(a, vec, gather_blocks, hs); break;
+    case 5: launch_gather<5>(a, vec, gather_blocks, hs); break;
+    case 6: launch_gather<6>(a, vec, gather_blocks, hs); break;
+    case 7: launch_gather<7>(a, vec, gather_blocks, hs); break;
+    default: launch_gather<8>(a, vec, gather_blocks, hs); break;
+  }
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
   dec_reduce_kernel<<<static_cast<unsigned>(rows), 64, 0, hs>>>(a);
   return check_launch("had_decode");
