@@ -11,23 +11,22 @@
 // causal masking it sees keys j <= q_pos0 + i.
 //
 // GPU design.  With n_q << n_k the work is a scan of the key cache, so it is
-// split over (key range, slice) work-groups and runs in four launches:
+// split over (key range, slice) work-groups and runs in three launches:
 //  1. dec_hist: per split and batch of up to 16 rows, h of every (row, key)
 //     pair by XOR + popcount on the vector ALU (the query words are
 //     wave-uniform scalars) into a per-split (d+1)-bin histogram per row
 //     (LDS atomics).
-//  2. dec_stats: one wave per row sums the split histograms, finds the
-//     threshold bin T and the tie quota r (as in had_attention), hands each
-//     split its share of the r ties in split order (lower keys first), and
-//     computes the softmax denominator Z from the counts.
-//  3. dec_gather: one 256-thread work-group per (split, row) recomputes h
-//     from the key words (L2-resident after step 1), keeps h < T and the
-//     first quota keys with h == T in key order (wave ballots plus a
-//     work-group prefix over the waves), compacts the kept keys and their
-//     weights exp(-2*scale*(h - h_min)) into LDS, and then reads only the
-//     kept V rows, 16 bytes of a row per lane, accumulating in fp32; the
-//     row groups are summed in a fixed order.
-//  4. dec_reduce: out = (sum over splits, in split order) / Z.
+//  2. dec_gather: one 256-thread work-group per (split, row).  Wave 0 sums
+//     the row's split histograms, finds the threshold bin T and the tie
+//     quota r (as in had_attention) and this split's share of the r ties
+//     (lower splits first); the split-0 work-group also writes the softmax
+//     denominator Z.  Then h is recomputed from the key words (L2-resident
+//     after step 1), h < T and the first quota keys with h == T are kept in
+//     key order (wave ballots plus a work-group prefix over the waves), the
+//     kept keys and their weights exp(-2*scale*(h - h_min)) are compacted in
+//     LDS, and only the kept V rows are read, 16 bytes of a row per lane,
+//     accumulating in fp32; the row groups are summed in a fixed order.
+//  3. dec_reduce: out = (sum over splits, in split order) / Z.
 // HBM bytes per slice: the key words (d/8 bytes per key), and per row the
 // 2d bytes (bf16) of each kept key; everything else is small.
 #include <cmath>
@@ -57,7 +56,6 @@ struct DecArgs {
   int causal;
   float* out;             // [BH, nq, d]
   uint32_t* hist;         // [BH, nq, splits, d + 1]
-  uint32_t* quota;        // [BH, nq, splits]
   int32_t* stats;         // [BH, nq, 4]: T, h_min, Z bits, N_i
   float* part;            // [BH, nq, splits, d]
   int splits;
@@ -87,19 +85,26 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   for (int t = threadIdx.x; t < nqh * nb; t += kDecThreads) hl[t] = 0u;
   __syncthreads();
   const uint32_t* qrow = a.qbits + (bh * a.nq + q0) * W;
-  for (int jb = k0; jb < k1; jb += kDecThreads) {
-    const int j = jb + static_cast<int>(threadIdx.x);
-    const bool valid = j < k1;
-    uint32_t kw[W];
-    const uint32_t* krow = a.kbits + (bh * a.kstride + (valid ? j : 0)) * W;
+  constexpr int kU = 4;  // keys per thread in flight
+  for (int jb = k0; jb < k1; jb += kU * kDecThreads) {
+    uint32_t kw[kU][W];
+    int j[kU];
 #pragma unroll
-    for (int w = 0; w < W; ++w) kw[w] = valid ? krow[w] : 0u;
+    for (int u = 0; u < kU; ++u) {
+      j[u] = jb + u * kDecThreads + static_cast<int>(threadIdx.x);
+      const uint32_t* krow = a.kbits + (bh * a.kstride + (j[u] < k1 ? j[u] : 0)) * W;
+#pragma unroll
+      for (int w = 0; w < W; ++w) kw[u][w] = j[u] < k1 ? krow[w] : 0u;
+    }
     for (int q = 0; q < nqh; ++q) {
-      uint32_t h = 0;
 #pragma unroll
-      for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[w] ^ qrow[q * W + w]);
-      const bool vis = valid && (!a.causal || j <= a.qpos0 + q0 + q);
-      if (vis) atomicAdd(&hl[q * nb + h], 1u);
+      for (int u = 0; u < kU; ++u) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[u][w] ^ qrow[q * W + w]);
+        const bool vis = j[u] < k1 && (!a.causal || j[u] <= a.qpos0 + q0 + q);
+        if (vis) atomicAdd(&hl[q * nb + h], 1u);
+      }
     }
   }
   __syncthreads();
@@ -120,10 +125,19 @@ __device__ inline uint32_t wave_scan_incl(uint32_t x) {
   return x;
 }
 
-// ---- 2. per-row threshold, tie quotas and normalizer ------------------------
-__global__ __launch_bounds__(64) void dec_stats_kernel(DecArgs a) {
-  const int64_t bhq = blockIdx.x;
-  const int q = static_cast<int>(bhq % a.nq);
+// ---- 2. per-row threshold, this split's tie quota and the normalizer ---------
+// Run by one wave (lanes 0..63).  Sums the row's split histograms, finds the
+// threshold bin T (the first bin whose count from h = 0 up reaches N_i) and
+// h_min (the first non-empty bin), and gives split s_self its share of the
+// r = N_i - (keys below T) ties: the ties of lower splits come first.  With
+// write_stats, also writes T, h_min, Z and N_i for the final reduce.
+struct RowStats {
+  uint32_t T;
+  int hmin;
+  uint32_t quota;
+};
+
+__device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, bool write_stats) {
   const int lane = threadIdx.x & 63;
   const int nb = a.d + 1;
   const uint32_t* hp = a.hist + bhq * a.splits * nb;
@@ -145,8 +159,6 @@ __global__ __launch_bounds__(64) void dec_stats_kernel(DecArgs a) {
     }
     cnt[r] = c;
   }
-  // threshold bin T: first bin whose inclusive count reaches N_i; h_min: first
-  // non-empty bin
   int T = -1, hmin = -1;
   uint32_t below = 0, run = 0;
 #pragma unroll
@@ -167,35 +179,38 @@ __global__ __launch_bounds__(64) void dec_stats_kernel(DecArgs a) {
   if (T < 0) T = a.d;  // unreachable: the visible count is >= N_i
   if (hmin < 0) hmin = 0;
   const uint32_t rtie = static_cast<uint32_t>(Ni) - below;
-  // Z = sum_{b < T} cnt_b w(b - h_min) + r w(T - h_min), w(t) = exp(-2 scale t)
-  double z = 0.0;
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int b = 64 * r + lane;
-    const uint32_t c = b < T ? cnt[r] : (b == T ? rtie : 0u);
-    if (c != 0) z += static_cast<double>(c) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
-  }
-  z = wave_sum_f64(z);  // total in lane 63, fixed order
-  // the r ties go to the splits in key order
-  uint32_t before = 0;
+  // ties at T in the splits before s_self
+  uint32_t before = 0, mine = 0;
   for (int s0 = 0; s0 < a.splits; s0 += 64) {
     const int s = s0 + lane;
     const uint32_t tie = s < a.splits ? hp[s * nb + T] : 0u;
-    const uint32_t incl = wave_scan_incl(tie) + before;
-    const uint32_t excl = incl - tie;
-    if (s < a.splits) {
-      const uint32_t left = rtie > excl ? rtie - excl : 0u;
-      a.quota[bhq * a.splits + s] = left < tie ? left : tie;
+    uint32_t x = s < s_self ? tie : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    before += x;
+    if (s_self >= s0 && s_self < s0 + 64) mine = __shfl(tie, s_self - s0, 64);
+  }
+  const uint32_t left = rtie > before ? rtie - before : 0u;
+  RowStats rs{static_cast<uint32_t>(T), hmin, left < mine ? left : mine};
+  if (write_stats) {
+    // Z = sum_{b < T} cnt_b w(b - h_min) + r w(T - h_min), w(t) = exp(-2 scale t)
+    double z = 0.0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int b = 64 * r + lane;
+      const uint32_t c = b < T ? cnt[r] : (b == T ? rtie : 0u);
+      if (c != 0) z += static_cast<double>(c) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
     }
-    before = __shfl(incl, 63, 64);
+    z = wave_sum_f64(z);  // total in lane 63, fixed order
+    if (lane == 63) {
+      int32_t* st = a.stats + bhq * 4;
+      st[0] = T;
+      st[1] = hmin;
+      st[2] = __builtin_bit_cast(int32_t, static_cast<float>(z));
+      st[3] = Ni;
+    }
   }
-  if (lane == 63) {
-    int32_t* st = a.stats + bhq * 4;
-    st[0] = T;
-    st[1] = hmin;
-    st[2] = __builtin_bit_cast(int32_t, static_cast<float>(z));
-    st[3] = Ni;
-  }
+  return rs;
 }
 
 // ---- 3. selection and gather of the kept V rows, per (split, row) ------------
@@ -218,10 +233,16 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   const int k0 = s * a.keys_per_split;
   const int k1 = min(a.nk, k0 + a.keys_per_split);
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk);  // keys j <= last
-  const int32_t* st = a.stats + bhq * 4;
-  const uint32_t T = static_cast<uint32_t>(st[0]);
-  const int hmin = st[1];
-  const uint32_t quota = a.quota[bhq * a.splits + s];
+  // the row's threshold and this split's tie quota (wave 0), shared through LDS
+  __shared__ RowStats rs_sh;
+  if (wid == 0) {
+    const RowStats r0 = row_stats(a, bhq, q, s, s == 0);
+    if (lane == 0) rs_sh = r0;
+  }
+  __syncthreads();
+  const uint32_t T = rs_sh.T;
+  const int hmin = rs_sh.hmin;
+  const uint32_t quota = rs_sh.quota;
   const uint32_t* qw = a.qbits + bhq * W;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // gather geometry: lpr lanes per V row, 8 features each; R rows per step
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(64) void dec_reduce_kernel(DecArgs a) {
 // Work split and workspace layout, from the shape alone.
 struct DecPlan {
   int splits, keys_per_split;
-  size_t off_hist, off_quota, off_stats, off_part, bytes;
+  size_t off_hist, off_stats, off_part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -397,8 +418,6 @@ DecPlan plan_for(const had_decode_shape& s) {
   size_t off = 0;
   p.off_hist = off;
   off = align256(off + static_cast<size_t>(rows) * p.splits * (s.dim + 1) * sizeof(uint32_t));
-  p.off_quota = off;
-  off = align256(off + static_cast<size_t>(rows) * p.splits * sizeof(uint32_t));
   p.off_stats = off;
   off = align256(off + static_cast<size_t>(rows) * 4 * sizeof(int32_t));
   p.off_part = off;
@@ -488,7 +507,6 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   a.causal = causal;
   a.out = out;
   a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
-  a.quota = reinterpret_cast<uint32_t*>(ws + p.off_quota);
   a.stats = reinterpret_cast<int32_t*>(ws + p.off_stats);
   a.part = reinterpret_cast<float*>(ws + p.off_part);
   a.splits = p.splits;
@@ -510,8 +528,6 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
     case 7: launch_hist<7>(a, hist_blocks, hs); break;
     default: launch_hist<8>(a, hist_blocks, hs); break;
   }
-  if ((st = check_launch("had_decode")) != HAD_OK) return st;
-  dec_stats_kernel<<<static_cast<unsigned>(rows), 64, 0, hs>>>(a);
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
   // 16-byte row slices need 16-byte aligned rows
   const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
