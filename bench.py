@@ -109,6 +109,127 @@ def cpu_baseline(w, inp, budget_s):
                       f"{dt:.1f} s wall, numpy float64, 1 thread"}
 
 
+def decode_model(w):
+    """Algorithmic HBM bytes of one had_decode call on decode workload w: the
+    cached key words once, the kept V rows of every new row, the new rows'
+    query words and outputs."""
+    W = (w.dim + 31) // 32
+    bh = w.batch * w.heads
+    vbytes = 2 if w.v_dtype == "bf16" else 4
+    kept = 0
+    for i in range(w.n_q):
+        vis = min(w.n_k, w.q_pos0 + i + 1) if w.causal else w.n_k
+        kept += min(w.topn, vis)
+    per_slice = w.n_k * W * 4 + kept * w.dim * vbytes + w.n_q * (W * 4 + w.dim * 4)
+    return {"kept": bh * kept, "hbm_bytes": bh * per_slice}
+
+
+def decode_cpu_baseline(w, inp, budget_s):
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    rows = heads = 0
+    t0 = time.perf_counter()
+    try:
+        for bh in range(w.batch * w.heads):
+            b, h = divmod(bh, w.heads)
+            oracle.decode(inp["q_new"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                          q_pos0=w.q_pos0, causal=w.causal)
+            rows += w.n_q
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} of {w.batch * w.heads} (batch, head) slices, {w.n_q} new rows "
+                      f"each against {w.n_k} cached keys (sign, pack, logits, stable-sort "
+                      f"top-N, softmax, AV), {dt:.1f} s wall, numpy float64, 1 thread"}
+
+
+def bench_decode(args, w):
+    """One step = had_pack of the new rows' queries + had_decode against the
+    packed cache (packed once, outside the timed region)."""
+    import torch
+    import sparse_attention_had_amd as had
+    from had_workloads import decode_inputs
+
+    inp = decode_inputs(w)
+    dev = torch.device("cuda:0")
+    qn = torch.from_numpy(inp["q_new"]).to(dev)
+    kc = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"])
+    v = (v.to(torch.bfloat16) if w.v_dtype == "bf16" else v).to(dev)
+    kb, _ = had.pack(kc, with_sigma=False)
+    del kc
+    W = had.words_per_row(w.dim)
+    qb = torch.empty((w.batch, w.heads, w.n_q, W), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.heads, w.n_q, w.dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(had.decode_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.n_k, w.dim),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        had.pack(qn, out=qb, with_sigma=False)
+        had.decode(qb, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal, out=out,
+                   workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
+        had.decode(qb, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal, out=out,
+                   workspace=ws)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_s = d0.elapsed_time(d1) / args.steps / 1e3
+    model = decode_model(w)
+    achieved = model["hbm_bytes"] / dec_s
+    rec = {
+        "metric": f"query rows/sec of HAD decode against a {w.n_k}-key cache; % of HBM roofline",
+        "value": w.rows / (ms_step / 1e3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.v_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_k": w.n_k,
+                   "n_q": w.n_q, "dim": w.dim, "topn": w.topn, "causal": w.causal,
+                   "v_dtype": w.v_dtype, "scale": w.scale,
+                   "step": "had_pack(new rows' Q) + had_decode (4 launches)"},
+        "decode_us": dec_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
+                     "kernel": "had_decode (dec_hist, dec_stats, dec_gather, dec_reduce)",
+                     "work_per_launch": {k2: float(v2) for k2, v2 in model.items()}},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = decode_cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,9 +255,11 @@ def main():
 
     import torch
     import sparse_attention_had_amd as had
-    from had_workloads import HEADLINE, WORKLOADS, workload_inputs
+    from had_workloads import DECODE_WORKLOADS, HEADLINE, WORKLOADS, workload_inputs
 
     name = args.workload or HEADLINE
+    if name in DECODE_WORKLOADS:
+        return bench_decode(args, DECODE_WORKLOADS[name])
     w = WORKLOADS[name]
     inp = workload_inputs(w)
     dev = torch.device("cuda:0")

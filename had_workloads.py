@@ -72,6 +72,51 @@ WORKLOADS = {
 HEADLINE = "t5-base-n1024"
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """New query rows at the end of a sequence against its key/value cache."""
+
+    name: str
+    batch: int
+    heads: int
+    n_k: int  # cached tokens (the new rows are the last n_q of them)
+    n_q: int
+    dim: int
+    topn: int
+    causal: bool
+    v_dtype: str
+    rank: int
+    noise: str
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.heads * self.n_q
+
+    @property
+    def q_pos0(self) -> int:
+        return self.n_k - self.n_q
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.dim))
+
+
+# Decoding shapes next to the long-context causal workload: the same head
+# size and N = n/8, one new token (or a block of 16 being verified) per
+# sequence.
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode-n16384", 4, 32, 16384, 1, 128, 2048, True, "bf16", 8, "t3", 6,
+                       "one new token per sequence against a 16384-token cache"),
+        DecodeWorkload("decode-n16384-q16", 4, 32, 16384, 16, 128, 2048, True, "bf16", 8, "t3", 7,
+                       "16 new tokens per sequence against a 16384-token cache"),
+    ]
+}
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), as float32."""
     a = np.ascontiguousarray(x, dtype=np.float32)
@@ -130,3 +175,11 @@ def make_inputs(batch, heads, seq, dim, *, v_dtype="bf16", rank=8, noise="normal
 def workload_inputs(w: Workload):
     return make_inputs(w.batch, w.heads, w.seq, w.dim, v_dtype=w.v_dtype,
                        rank=w.rank, noise=w.noise, seed=w.seed)
+
+
+def decode_inputs(w: DecodeWorkload):
+    """The whole sequence (recipe above); the new rows' queries are its last n_q rows."""
+    inp = make_inputs(w.batch, w.heads, w.n_k, w.dim, v_dtype=w.v_dtype, rank=w.rank,
+                      noise=w.noise, seed=w.seed)
+    inp["q_new"] = np.ascontiguousarray(inp["q"][:, :, w.n_k - w.n_q:])
+    return inp
