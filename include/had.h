@@ -206,6 +206,27 @@ had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
                       int64_t topn, int causal, int64_t bh_begin,
                       int64_t bh_count, int32_t* idx, void* stream);
 
+/*
+ * had_topn_mass - measurement: for every query row, the smallest N whose N
+ * largest softmax weights (of scale * s over the visible keys) sum to at least
+ * mass, from the same histogram stage as had_attention.
+ *
+ * Defined by: Pith verdict record, "concrete_test" (the fraction of softmax
+ * mass captured by the top-N logits as n grows) and the Pith review's
+ * Figure 4 (attention mass versus N); the top-N rule of "What carries the
+ * argument".
+ *
+ *  Slices bh in [bh_begin, bh_begin + bh_count), all n rows; causal as
+ *  had_attention.  mass in (0, 1]; mass >= 1 gives the visible count.
+ *  n_out  [bh_count, n] int32, device.
+ *  Precision: the weights exp(-2*scale*(h - h_min)) and their sums in float64;
+ *  keys of one logit value share one weight, so N is exact up to that
+ *  rounding.
+ */
+had_status had_topn_mass(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                         float scale, int causal, double mass, int64_t bh_begin,
+                         int64_t bh_count, int32_t* n_out, void* stream);
+
 /* Workspace bytes that had_decode needs for shape s. */
 size_t had_decode_workspace_bytes(had_decode_shape s);
 

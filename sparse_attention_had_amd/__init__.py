@@ -108,6 +108,8 @@ def load_library():
         lib.had_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P,
                                     ctypes.c_size_t, P, P]
         lib.had_forward.restype = I
+        lib.had_topn_mass.argtypes = [P, P, Shape, ctypes.c_float, I, ctypes.c_double, I64, I64, P, P]
+        lib.had_topn_mass.restype = I
         lib.had_decode_workspace_bytes.argtypes = [DecodeShape]
         lib.had_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.had_decode.argtypes = [P, P, P, I, DecodeShape, I64, I64, ctypes.c_float, I, P, P,
@@ -356,6 +358,26 @@ def decode(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int,
         int(topn), float(scale), int(bool(causal)), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), sh))
     return out
+
+
+def topn_mass(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, scale: float, mass: float,
+              causal: bool = False, *, bh_begin: int = 0, bh_count: int | None = None,
+              stream=None) -> torch.Tensor:
+    """Smallest N per row whose top-N softmax weights reach mass: [bh_count, n] int32."""
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    B, H, n, W = _shape4(qbits, "qbits")
+    if W != words_per_row(dim) or tuple(kbits.shape) != (B, H, n, W):
+        raise ValueError("qbits/kbits must have shape [B, H, n, ceil(dim/32)]")
+    if bh_count is None:
+        bh_count = B * H - bh_begin
+    nout = torch.empty((bh_count, n), dtype=torch.int32, device=qbits.device)
+    _check("had_topn_mass", lib.had_topn_mass(
+        qbits.data_ptr(), kbits.data_ptr(), Shape(B, H, n, dim), float(scale), int(bool(causal)),
+        float(mass), int(bh_begin), int(bh_count), nout.data_ptr(),
+        _stream_handle(qbits.device, stream)))
+    return nout
 
 
 def logits(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, *, bh_begin: int = 0,

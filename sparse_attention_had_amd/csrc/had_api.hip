@@ -182,6 +182,38 @@ extern "C" had_status had_select(const uint32_t* qbits, const uint32_t* kbits, h
   return launch_attention_family(AttnMode::Select, a, static_cast<hipStream_t>(stream));
 }
 
+extern "C" had_status had_topn_mass(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
+                                    float scale, int causal, double mass, int64_t bh_begin,
+                                    int64_t bh_count, int32_t* n_out, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if ((st = check_bits(qbits, kbits, "had_topn_mass")) != HAD_OK) return st;
+  if (n_out == nullptr || !aligned(n_out, 4)) return fail(HAD_ERR_INVALID_ARG, "had_topn_mass: null or unaligned n_out");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(HAD_ERR_INVALID_ARG, "had_topn_mass: scale must be finite and > 0");
+  if (!(mass > 0.0) || !std::isfinite(mass)) return fail(HAD_ERR_INVALID_ARG, "had_topn_mass: mass must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(HAD_ERR_INVALID_ARG, "had_topn_mass: causal must be 0 or 1");
+  const int64_t bh_total = s.batch * s.heads;
+  if (bh_begin < 0 || bh_count < 1 || bh_begin + bh_count > bh_total)
+    return fail(HAD_ERR_INVALID_ARG, "had_topn_mass: bh range outside [0, B*H)");
+  AttnArgs a{};
+  a.qbits = qbits;
+  a.kbits = kbits;
+  a.v_dtype = HAD_BF16;
+  a.bh_total = bh_total;
+  a.bh_begin = bh_begin;
+  a.bh_count = bh_count;
+  a.n = static_cast<int>(s.seq);
+  a.d = static_cast<int>(s.dim);
+  a.topn = 1;
+  a.scale = scale;
+  a.causal = causal;
+  a.mass = mass;
+  a.nmass = n_out;
+  return launch_attention_family(AttnMode::Mass, a, static_cast<hipStream_t>(stream));
+}
+
 extern "C" had_status had_logits(const uint32_t* qbits, const uint32_t* kbits, had_shape s,
                                  int64_t bh_begin, int64_t bh_count, int64_t row_begin,
                                  int64_t row_count, int16_t* s_out, void* stream) {

@@ -370,6 +370,47 @@ void had_attn_kernel(AttnArgs a) {
   // first key group of pass 2 is copied while the statistics are computed
   if (MODE == 0) k_issue(0, std::integral_constant<int, C::kCH2>{}, 0);
 
+  if (MODE == 3) {
+    // ===================================================== top-N mass export
+    // Smallest N whose N largest softmax weights reach mass * Z: the keys of
+    // a histogram bin share one weight w_h = exp(-2*scale*(h - h_min)), so
+    // the largest weights are whole bins from h_min up, then ceil(rest / w_T)
+    // keys of the bin T where the running sum crosses (float64 throughout).
+    if (qvalid && half == 0) {
+      const uint32_t* hq3 = reinterpret_cast<const uint32_t*>(region) + wid * (d + 1) * 32 + ql;
+      int hmin3 = -1;
+      double Z = 0.0;
+      for (int b = 0; b <= d; ++b) {
+        const uint32_t x = hq3[b * 32];
+        const int cnt = static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16);
+        if (cnt > 0 && hmin3 < 0) hmin3 = b;
+        if (cnt > 0) Z += cnt * exp(-2.0 * static_cast<double>(a.scale) * (b - hmin3));
+      }
+      int N = lim;  // mass >= 1, or a rounding shortfall: every visible key
+      if (a.mass < 1.0) {
+        const double target = a.mass * Z;
+        double M = 0.0;
+        int before = 0;
+        for (int b = hmin3; b <= d; ++b) {
+          const uint32_t x = hq3[b * 32];
+          const int cnt = static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16);
+          if (cnt == 0) continue;
+          const double w = exp(-2.0 * static_cast<double>(a.scale) * (b - hmin3));
+          if (M + cnt * w >= target) {
+            int k = static_cast<int>(ceil((target - M) / w));
+            k = k < 1 ? 1 : (k > cnt ? cnt : k);
+            N = before + k;
+            break;
+          }
+          M += cnt * w;
+          before += cnt;
+        }
+      }
+      a.nmass[bh_local * n + i_row] = N;
+    }
+    return;
+  }
+
   // =========================================================== per-row statistics
   const int Ni = qvalid ? min(a.topn, lim) : 0;
   int T = 0, hmin = 0, below0 = 0, ties0 = 0, below = 0;
@@ -790,7 +831,8 @@ had_status launch_one(const AttnArgs& a, hipStream_t st) {
   if (blocks <= 0) return HAD_OK;
   if (blocks > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "grid too large");
   had_attn_kernel<W, VF32, MODE, VDIRECT><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
-  return check_launch(MODE == 0 ? "had_attention" : (MODE == 1 ? "had_select" : "had_logits"));
+  return check_launch(MODE == 0 ? "had_attention"
+                      : (MODE == 1 ? "had_select" : (MODE == 2 ? "had_logits" : "had_topn_mass")));
 }
 
 template <int W>
@@ -805,6 +847,8 @@ had_status launch_w(AttnMode mode, const AttnArgs& a, hipStream_t st) {
       return launch_one<W, false, 1>(a, st);
     case AttnMode::Logits:
       return launch_one<W, false, 2>(a, st);
+    case AttnMode::Mass:
+      return launch_one<W, false, 3>(a, st);
   }
   return fail(HAD_ERR_INVALID_ARG, "unknown mode");
 }

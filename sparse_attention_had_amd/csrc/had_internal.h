@@ -114,7 +114,7 @@ __device__ inline void sigma_from_partials(const double2* partials, int nblocks,
 }
 
 // ---- attention family (had_attention.hip) ----
-enum class AttnMode : int { Attend = 0, Select = 1, Logits = 2 };
+enum class AttnMode : int { Attend = 0, Select = 1, Logits = 2, Mass = 3 };
 
 struct AttnArgs {
   const uint32_t* qbits;
@@ -134,6 +134,8 @@ struct AttnArgs {
   float* out;        // Attend output [bh_total, n, d]
   int32_t* idx;      // Select output [bh_count, n, topn]
   int16_t* logits;   // Logits output [bh_count, row_count, n]
+  double mass;       // Mass: softmax mass to reach
+  int32_t* nmass;    // Mass output [bh_count, n]
   // Optional sigma finalize (fused forward call): wave 0 of the last block
   // turns the partials of a preceding pack launch into sigma_out[t].
   const double2* sigma_partials[2];

@@ -165,6 +165,19 @@ def test_decode_rejects_bad_arguments(lib):
     assert lib.had_last_error() != b""
 
 
+def test_topn_mass_rejects_bad_arguments(lib):
+    s = Shape(2, 3, 100, 64)
+    f = lib.had_topn_mass
+    assert f(A16, A16B, s, 0.125, 0, 0.9, 0, 6, None, None) == INVALID
+    assert f(A16, A16B, s, 0.0, 0, 0.9, 0, 6, A16C, None) == INVALID
+    assert f(A16, A16B, s, 0.125, 0, 0.0, 0, 6, A16C, None) == INVALID
+    assert f(A16, A16B, s, 0.125, 0, float("inf"), 0, 6, A16C, None) == INVALID
+    assert f(A16, A16B, s, 0.125, 2, 0.9, 0, 6, A16C, None) == INVALID
+    assert f(A16, A16B, s, 0.125, 0, 0.9, 4, 3, A16C, None) == INVALID
+    assert f(None, A16B, s, 0.125, 0, 0.9, 0, 6, A16C, None) == INVALID
+    assert f(A16, A16B, Shape(2, 3, 100, 300), 0.125, 0, 0.9, 0, 6, A16C, None) == UNSUPPORTED
+
+
 def test_select_and_logits_reject_bad_ranges(lib):
     s = Shape(2, 3, 100, 64)
     assert lib.had_select(A16, A16B, s, 0, 0, 0, 6, A16C, None) == INVALID

@@ -293,3 +293,43 @@ def test_workload_causal_n16384_sampled():
                     sample_rows=lambda bh: np.unique(np.r_[0, 1, 2047, 2048, 16383,
                                                            rng.integers(0, 16384, 4)]),
                     select_heads={7})
+
+
+# ------------------------------------------------------------ top-N mass
+MASS_CASES = [
+    # B, H, n, d, causal, scale
+    (1, 2, 300, 64, False, 0.125),
+    (2, 1, 257, 64, True, 0.125),
+    (1, 1, 97, 5, False, 0.9),     # few distinct logits: large tie bins
+    (1, 2, 200, 128, True, 1 / np.sqrt(128)),
+    (1, 1, 64, 40, False, 2.0),    # sharp softmax
+]
+
+
+@pytest.mark.parametrize("case", MASS_CASES)
+def test_topn_mass_matches_oracle(case):
+    B, H, n, d, causal, scale = case
+    log(f"topn mass {case}")
+    inp = make_inputs(B, H, n, d, rank=8, noise="t3", seed=n + d)
+    q, k, _ = to_dev(inp)
+    qb, _ = had.pack(q, with_sigma=False)
+    kb, _ = had.pack(k, with_sigma=False)
+    sc = float(np.float32(scale))
+    for mass in (0.5, 0.9, 0.99, 1.0):
+        got = had.topn_mass(qb, kb, d, scale, mass, causal).cpu().numpy().astype(np.int64)
+        for b in range(B):
+            for h in range(H):
+                S = oracle.logits(oracle.binarize(inp["q"][b, h]), oracle.binarize(inp["k"][b, h]))
+                want = oracle.topn_mass(S, sc, mass, causal)
+                g = got[b * H + h]
+                bad = np.nonzero(g != want)[0]
+                for r in bad:
+                    # only a decision within rounding of the float64 sums may differ
+                    nv = oracle.visible_count(int(r), n, causal)
+                    z = sc * S[r, :nv].astype(np.float64)
+                    p = np.sort(np.exp(z - z.max()) / np.exp(z - z.max()).sum())[::-1]
+                    c = np.cumsum(p)
+                    margin = min(abs(c[want[r] - 1] - mass),
+                                 abs(c[want[r] - 2] - mass) if want[r] >= 2 else 1.0)
+                    assert abs(int(g[r]) - int(want[r])) == 1 and margin < 1e-12, \
+                        f"mass {mass} slice {(b, h)} row {r}: got {g[r]} want {want[r]}"

@@ -335,3 +335,40 @@ def test_decode_with_every_visible_key_is_dense_softmax_over_the_prefix():
         s = sk[:vis] @ sq[i]
         want = scipy.special.softmax(0.25 * s) @ v[:vis]
         np.testing.assert_allclose(r["out"][i], want, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------ top-N mass ----
+def test_topn_mass_equal_logits_closed_form():
+    # Equal logits: every weight is 1/n, so N = ceil(mass * n).
+    S = np.zeros((1, 40))
+    for mass in (0.01, 0.3, 0.5, 0.97):
+        assert oracle.topn_mass(S, 0.7, mass)[0] == math.ceil(mass * 40 - 1e-12)
+
+
+def test_topn_mass_two_levels_closed_form():
+    # a keys at logit 1, b keys at logit 0: each top key weighs e/(a e + b).
+    a, b, scale = 3, 9, 2.0
+    S = np.array([[1.0] * a + [0.0] * b])
+    wt = math.exp(scale) / (a * math.exp(scale) + b)
+    wl = 1.0 / (a * math.exp(scale) + b)
+    for mass in (0.1, 0.4, 0.6, 0.9, 0.99):
+        k = math.ceil(mass / wt - 1e-12)
+        want = k if k <= a else a + math.ceil((mass - a * wt) / wl - 1e-12)
+        assert oracle.topn_mass(S, scale, mass)[0] == want
+
+
+def test_topn_mass_brute_force_and_limits():
+    # Brute force over subsets: the smallest subset whose softmax mass reaches
+    # the target (any subset, not only prefixes); mass >= 1 keeps everything;
+    # a causal row sees its prefix only.
+    rng = np.random.default_rng(21)
+    S = rng.integers(-4, 5, size=(6, 7)).astype(np.float64)
+    for mass in (0.25, 0.5, 0.8):
+        got = oracle.topn_mass(S, 0.6, mass)
+        for r in range(6):
+            p = np.exp(0.6 * S[r]) / np.exp(0.6 * S[r]).sum()
+            best = min(len(c) for k in range(1, 8) for c in itertools.combinations(range(7), k)
+                       if p[list(c)].sum() >= mass - 1e-15)
+            assert got[r] == best
+    assert oracle.topn_mass(S, 0.6, 1.0).tolist() == [7] * 6
+    assert oracle.topn_mass(S, 0.6, 1.0, causal=True).tolist() == [1, 2, 3, 4, 5, 6]
