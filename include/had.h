@@ -109,6 +109,36 @@ had_status had_pack(const float* x, had_shape s, uint32_t* xbits, float* sigma,
                     uint32_t* dev_status, void* stream);
 
 /*
+ * Running sigma calibration (the per-layer estimate over many calibration
+ * minibatches described for Eq. 12: Pith review, referee minor comment 6 and
+ * "Assumptions & free parameters").  A had_sigma_state lives in device
+ * memory; set it to zero (e.g. hipMemsetAsync) to start a calibration.
+ */
+typedef struct {
+  double count;  /* elements seen */
+  double sum;    /* sum of x */
+  double sum_sq; /* sum of x*x */
+  double reserved;
+} had_sigma_state;
+
+/*
+ * had_pack_calibrate - had_pack without a per-call sigma: packs x into xbits
+ * and adds the element count, sum and sum of squares of x to *state (device,
+ * 8-byte aligned).  Calls on one stream add in stream order, so the state is
+ * the same on every run.  workspace: had_pack_workspace_bytes(s) bytes,
+ * 16-byte aligned.  Calls that may overlap need distinct workspaces and must
+ * not share a state.
+ */
+had_status had_pack_calibrate(const float* x, had_shape s, uint32_t* xbits,
+                              had_sigma_state* state, void* workspace,
+                              size_t workspace_bytes, uint32_t* dev_status,
+                              void* stream);
+
+/* had_sigma_from_state - *sigma = population standard deviation of every
+ * element added to *state so far (0 for an empty state), one device float. */
+had_status had_sigma_from_state(const had_sigma_state* state, float* sigma, void* stream);
+
+/*
  * had_attention - Hamming logits, top-N selection, softmax over the kept set
  * and value accumulation, fused; the n x n matrix is never written.
  *

@@ -108,6 +108,10 @@ def load_library():
         lib.had_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P,
                                     ctypes.c_size_t, P, P]
         lib.had_forward.restype = I
+        lib.had_pack_calibrate.argtypes = [P, Shape, P, P, P, ctypes.c_size_t, P, P]
+        lib.had_pack_calibrate.restype = I
+        lib.had_sigma_from_state.argtypes = [P, P, P]
+        lib.had_sigma_from_state.restype = I
         lib.had_topn_mass.argtypes = [P, P, Shape, ctypes.c_float, I, ctypes.c_double, I64, I64, P, P]
         lib.had_topn_mass.restype = I
         lib.had_decode_workspace_bytes.argtypes = [DecodeShape]
@@ -378,6 +382,50 @@ def topn_mass(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, scale: float, 
         float(mass), int(bh_begin), int(bh_count), nout.data_ptr(),
         _stream_handle(qbits.device, stream)))
     return nout
+
+
+def sigma_state(device="cuda") -> torch.Tensor:
+    """A zeroed had_sigma_state (4 float64 on the device) for pack_calibrate."""
+    return torch.zeros(4, dtype=torch.float64, device=device)
+
+
+def pack_calibrate(x: torch.Tensor, state: torch.Tensor, *, out: torch.Tensor | None = None,
+                   dev_status: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Sign bits of x (as pack) and x's count / sum / sum of squares added to state."""
+    lib = load_library()
+    _need_cuda(x, "x", torch.float32)
+    _need_cuda(state, "state", torch.float64)
+    if state.numel() != 4:
+        raise ValueError("state must hold 4 float64 (had_sigma_state)")
+    B, H, n, d = _shape4(x, "x")
+    W = words_per_row(d)
+    if out is None:
+        out = torch.empty((B, H, n, W), dtype=torch.int32, device=x.device)
+    _need_cuda(out, "out", torch.int32)
+    shape = Shape(B, H, n, d)
+    sh = _stream_handle(x.device, stream)
+    need = int(lib.had_pack_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(x.device, sh, need)
+    st_ptr = None
+    if dev_status is not None:
+        _need_cuda(dev_status, "dev_status", torch.int32)
+        st_ptr = dev_status.data_ptr()
+    _check("had_pack_calibrate", lib.had_pack_calibrate(
+        x.data_ptr(), shape, out.data_ptr(), state.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), st_ptr, sh))
+    return out
+
+
+def sigma_from_state(state: torch.Tensor, stream=None) -> torch.Tensor:
+    """Population standard deviation of everything added to state (1-element float32)."""
+    lib = load_library()
+    _need_cuda(state, "state", torch.float64)
+    sigma = torch.empty(1, dtype=torch.float32, device=state.device)
+    _check("had_sigma_from_state", lib.had_sigma_from_state(
+        state.data_ptr(), sigma.data_ptr(), _stream_handle(state.device, stream)))
+    return sigma
 
 
 def logits(qbits: torch.Tensor, kbits: torch.Tensor, dim: int, *, bh_begin: int = 0,

@@ -108,6 +108,42 @@ __global__ __launch_bounds__(64) void sigma_finalize_kernel(const double2* parti
   sigma_from_partials(partials, nblocks, count, sigma);
 }
 
+// One wave: adds this call's element count, sum and sum of squares to a
+// running calibration state (calls on one stream add in stream order).
+__global__ __launch_bounds__(64) void sigma_accumulate_kernel(const double2* partials, int nblocks,
+                                                              double count, had_sigma_state* state) {
+  constexpr int kPer = kPackMaxBlocks / 64;
+  const int lane = threadIdx.x & 63;
+  double a = 0.0, b = 0.0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = lane + 64 * k;
+    const double2 p = i < nblocks ? partials[i] : double2{0.0, 0.0};
+    a += p.x;
+    b += p.y;
+  }
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
+  if (lane == 63) {
+    state->count += count;
+    state->sum += a;
+    state->sum_sq += b;
+  }
+}
+
+__global__ __launch_bounds__(64) void sigma_from_state_kernel(const had_sigma_state* state, float* sigma) {
+  if (threadIdx.x == 0) {
+    const double n = state->count;
+    double var = 0.0;
+    if (n > 0.0) {
+      const double mean = state->sum / n;
+      var = state->sum_sq / n - mean * mean;
+      if (!(var > 0.0)) var = 0.0;
+    }
+    *sigma = static_cast<float>(sqrt(var));
+  }
+}
+
 // d % 32 == 0 and x 16-byte aligned: 256-float segments, 8 words each.
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
@@ -343,4 +379,37 @@ extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, flo
   if ((st = launch_pack(&job, 1, s, dev_status, hs)) != HAD_OK) return st;
   if (sigma == nullptr) return HAD_OK;
   return launch_sigma_finalize(partials, s, sigma, hs);
+}
+
+extern "C" had_status had_pack_calibrate(const float* x, had_shape s, uint32_t* xbits,
+                                         had_sigma_state* state, void* workspace,
+                                         size_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  clear_error();
+  had_status st = check_shape(s, HAD_MAX_DECODE_KEYS);
+  if (st != HAD_OK) return st;
+  if ((st = check_pack_args(x, xbits, nullptr, "had_pack_calibrate")) != HAD_OK) return st;
+  if (state == nullptr || !aligned(state, 8))
+    return fail(HAD_ERR_INVALID_ARG, "had_pack_calibrate: state must be non-null and 8-byte aligned");
+  if (dev_status != nullptr && !aligned(dev_status, 4))
+    return fail(HAD_ERR_INVALID_ARG, "had_pack_calibrate: dev_status must be 4-byte aligned");
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(HAD_ERR_INVALID_ARG, "had_pack_calibrate: workspace is null or unaligned");
+  if (workspace_bytes < had_pack_workspace_bytes(s))
+    return fail(HAD_ERR_INVALID_ARG, "had_pack_calibrate: workspace smaller than had_pack_workspace_bytes()");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  double* partials = static_cast<double*>(workspace);
+  const PackJob job{x, xbits, partials};
+  if ((st = launch_pack(&job, 1, s, dev_status, hs)) != HAD_OK) return st;
+  const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
+  sigma_accumulate_kernel<<<1, 64, 0, hs>>>(reinterpret_cast<const double2*>(partials),
+                                            pack_grid_blocks(s), count, state);
+  return check_launch("had_pack_calibrate");
+}
+
+extern "C" had_status had_sigma_from_state(const had_sigma_state* state, float* sigma, void* stream) {
+  clear_error();
+  if (state == nullptr || sigma == nullptr || !aligned(state, 8) || !aligned(sigma, 4))
+    return fail(HAD_ERR_INVALID_ARG, "had_sigma_from_state: null or unaligned state or sigma");
+  sigma_from_state_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(state, sigma);
+  return check_launch("had_sigma_from_state");
 }

@@ -178,6 +178,20 @@ def test_topn_mass_rejects_bad_arguments(lib):
     assert f(A16, A16B, Shape(2, 3, 100, 300), 0.125, 0, 0.9, 0, 6, A16C, None) == UNSUPPORTED
 
 
+def test_calibration_rejects_bad_arguments(lib):
+    s = Shape(1, 2, 100, 64)
+    wsb = lib.had_pack_workspace_bytes(s)
+    c = lib.had_pack_calibrate
+    assert c(A16, s, A16B, None, 0x50000, wsb, None, None) == INVALID
+    assert c(A16, s, A16B, A16C + 4, 0x50000, wsb, None, None) == INVALID
+    assert c(A16, s, A16B, A16C, None, wsb, None, None) == INVALID
+    assert c(A16, s, A16B, A16C, 0x50000, wsb - 1, None, None) == INVALID
+    assert c(None, s, A16B, A16C, 0x50000, wsb, None, None) == INVALID
+    assert c(A16, Shape(1, 2, 100, 257), A16B, A16C, 0x50000, wsb, None, None) == UNSUPPORTED
+    assert lib.had_sigma_from_state(None, A16, None) == INVALID
+    assert lib.had_sigma_from_state(A16, None, None) == INVALID
+
+
 def test_select_and_logits_reject_bad_ranges(lib):
     s = Shape(2, 3, 100, 64)
     assert lib.had_select(A16, A16B, s, 0, 0, 0, 6, A16C, None) == INVALID

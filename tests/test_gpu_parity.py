@@ -333,3 +333,27 @@ def test_topn_mass_matches_oracle(case):
                                  abs(c[want[r] - 2] - mass) if want[r] >= 2 else 1.0)
                     assert abs(int(g[r]) - int(want[r])) == 1 and margin < 1e-12, \
                         f"mass {mass} slice {(b, h)} row {r}: got {g[r]} want {want[r]}"
+
+
+# ------------------------------------------------------- sigma calibration
+def test_sigma_calibration_over_batches():
+    """Running calibration over several minibatches equals the population
+    std of all their elements together; bits are had_pack's."""
+    log("sigma calibration")
+    rng = np.random.default_rng(77)
+    shapes = [(2, 3, 77, 64), (1, 2, 300, 64), (4, 1, 5, 33), (1, 1, 1, 1), (3, 2, 64, 128)]
+    xs = [(rng.standard_normal(sh) * 1.7 + 0.4).astype(np.float32) for sh in shapes]
+    state = had.sigma_state()
+    assert float(had.sigma_from_state(state).item()) == 0.0
+    for x in xs:
+        bits = had.pack_calibrate(torch.from_numpy(x).cuda(), state)
+        assert np.array_equal(bits_np(bits), oracle.pack_bits(oracle.binarize(x)))
+    sig = float(had.sigma_from_state(state).item())
+    ref = oracle.sigma(np.concatenate([x.reshape(-1) for x in xs]))
+    assert abs(sig - ref) <= 1e-6 * ref
+    again = had.sigma_state()
+    for x in xs:
+        had.pack_calibrate(torch.from_numpy(x).cuda(), again)
+    torch.cuda.synchronize()
+    assert torch.equal(state, again)
+    assert float(state[0].item()) == sum(x.size for x in xs)
