@@ -153,6 +153,27 @@ def decode_cpu_baseline(w, inp, budget_s):
                       f"top-N, softmax, AV), {dt:.1f} s wall, numpy float64, 1 thread"}
 
 
+def settle(step, seconds):
+    """Untimed steps until `seconds` of wall time have passed (at most 20000):
+    the GPU ramps its clocks up over the first tens of milliseconds of load,
+    and the timed steps should see the steady state.  Returns the count."""
+    import torch
+
+    if seconds <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < 20000:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
 def bench_decode(args, w):
     """One step = had_pack of the new rows' queries + had_decode against the
     packed cache (packed once, outside the timed region)."""
@@ -183,6 +204,7 @@ def bench_decode(args, w):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settled = settle(step, args.settle_s)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -209,6 +231,7 @@ def bench_decode(args, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -218,11 +241,11 @@ def bench_decode(args, w):
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_k": w.n_k,
                    "n_q": w.n_q, "dim": w.dim, "topn": w.topn, "causal": w.causal,
                    "v_dtype": w.v_dtype, "scale": w.scale,
-                   "step": "had_pack(new rows' Q) + had_decode (4 launches)"},
+                   "step": "had_pack(new rows' Q) + had_decode (3 launches)"},
         "decode_us": dec_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "had_decode (dec_hist, dec_stats, dec_gather, dec_reduce)",
+                     "kernel": "had_decode (dec_hist, dec_gather, dec_reduce)",
                      "work_per_launch": {k2: float(v2) for k2, v2 in model.items()}},
     }
     if not args.no_cpu_baseline:
@@ -238,6 +261,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.2,
+                    help="untimed steps for this many seconds after the warmup steps, so "
+                         "that the timed steps run at steady-state clocks (0: none)")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only had_attention launches (for profiling runs)")
     ap.add_argument("--separate-calls", action="store_true",
@@ -309,6 +335,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settled = settle(step, args.settle_s)
 
     # timed region 1: whole steps
     t_start = torch.cuda.Event(enable_timing=True)
@@ -345,6 +372,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",

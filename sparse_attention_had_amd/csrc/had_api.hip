@@ -139,7 +139,7 @@ extern "C" had_status had_forward(const float* q, const float* k, const void* v,
       return fail(HAD_ERR_INVALID_ARG, "had_forward: workspace smaller than had_forward_workspace_bytes()");
     double* ws = static_cast<double*>(workspace);
     if (sigma_q != nullptr) part[0] = ws;
-    if (sigma_k != nullptr) part[1] = ws + 2 * pack_grid_blocks(s);
+    if (sigma_k != nullptr) part[1] = ws + 2 * pack_partials(s);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const PackJob jobs[2] = {{q, qbits, part[0]}, {k, kbits, part[1]}};
@@ -148,7 +148,7 @@ extern "C" had_status had_forward(const float* q, const float* k, const void* v,
   a.sigma_partials[1] = reinterpret_cast<const double2*>(part[1]);
   a.sigma_out[0] = sigma_q;
   a.sigma_out[1] = sigma_k;
-  a.sigma_nblocks = pack_grid_blocks(s);
+  a.sigma_nparts = pack_partials(s);
   a.sigma_count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
   return launch_attention_family(AttnMode::Attend, a, hs);
 }

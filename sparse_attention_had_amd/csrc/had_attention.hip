@@ -236,7 +236,7 @@ void had_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       if (a.sigma_out[t] != nullptr)
-        sigma_from_partials(a.sigma_partials[t], a.sigma_nblocks, a.sigma_count, a.sigma_out[t]);
+        sigma_from_partials(a.sigma_partials[t], a.sigma_nparts, a.sigma_count, a.sigma_out[t]);
   }
 
   // ---- constant tables

@@ -41,10 +41,14 @@ inline int64_t words_per_row(int64_t d) { return (d + 31) / 32; }
 had_status check_shape(const had_shape& s, int64_t max_seq = HAD_MAX_SEQ);
 
 // ---- pack (had_pack.hip) ----
-constexpr int kPackThreads = 1024;   // threads per pack block
-constexpr int kPackMaxBlocks = 256;  // sigma partial pairs per tensor, at most
+constexpr int kPackThreads = 256;    // threads per pack block
+constexpr int kPackMaxBlocks = 512;  // pack blocks per tensor, at most
+constexpr int kPackWavesPerBlock = kPackThreads / 64;
 
 int pack_grid_blocks(const had_shape& s);
+// Sigma partial pairs (sum x, sum x^2) a pack launch writes per tensor: one
+// per block, at most kPackMaxBlocks.
+int pack_partials(const had_shape& s);
 
 // One tensor of a pack launch.
 struct PackJob {
@@ -84,28 +88,39 @@ __device__ inline double wave_sum_f64(double v) {
   return v;
 }
 
-// One wave (lanes 0..63 of the calling wave): sigma from per-block partial
-// pairs (sum x, sum x^2).  Lane l sums partials l, l + 64, ... in order, then
-// a fixed-order wave sum; lane 63 writes the population standard deviation.
-__device__ inline void sigma_from_partials(const double2* partials, int nblocks, double count,
-                                           float* sigma) {
-  constexpr int kPer = kPackMaxBlocks / 64;
+// One wave (lanes 0..63 of the calling wave): totals of the nparts partial
+// pairs (sum x, sum x^2) in a fixed order.  Lane l sums partials l, l + 64,
+// ... in order (eight loads in flight), then a fixed-order wave sum; the
+// totals are valid in lane 63.
+__device__ inline void partials_total(const double2* partials, int nparts, double& a, double& b) {
+  constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63;
-  double2 p[kPer];
+  a = 0.0;
+  b = 0.0;
+  for (int base = 0; base < nparts; base += 64 * kBatch) {
+    double2 p[kBatch];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = lane + 64 * k;
-    p[k] = i < nblocks ? partials[i] : double2{0.0, 0.0};
-  }
-  double a = 0.0, b = 0.0;
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + lane + 64 * k;
+      p[k] = i < nparts ? partials[i] : double2{0.0, 0.0};
+    }
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    a += p[k].x;
-    b += p[k].y;
+    for (int k = 0; k < kBatch; ++k) {
+      a += p[k].x;
+      b += p[k].y;
+    }
   }
   a = wave_sum_f64(a);
   b = wave_sum_f64(b);
-  if (lane == 63) {
+}
+
+// One wave: lane 63 writes the population standard deviation of count
+// elements from the partial pairs of their pack launch.
+__device__ inline void sigma_from_partials(const double2* partials, int nparts, double count,
+                                           float* sigma) {
+  double a, b;
+  partials_total(partials, nparts, a, b);
+  if ((threadIdx.x & 63) == 63) {
     const double mean = a / count;
     double var = b / count - mean * mean;
     if (!(var > 0.0)) var = 0.0;
@@ -140,7 +155,7 @@ struct AttnArgs {
   // turns the partials of a preceding pack launch into sigma_out[t].
   const double2* sigma_partials[2];
   float* sigma_out[2];
-  int sigma_nblocks;
+  int sigma_nparts;
   double sigma_count;
 };
 

@@ -12,28 +12,37 @@
 //    onto the flat word stream (word = element / 32).  With x 16-byte
 //    aligned, lane L of a wave loads floats 4L..4L+3 of a 256-float segment;
 //    the 8 lanes that cover one word OR their sign nibbles together and one
-//    of them stores the word.  Each wave owns a contiguous run of segments
-//    (runs differ by at most one segment) and keeps up to kUnroll 1 KiB loads
-//    in flight.  Unaligned x falls back to one 64-float ballot per load.
+//    of them stores the word.  The waves of a tensor sweep it together (wave
+//    w of nw takes segments w, w + nw, ...), kUnroll 1 KiB loads in flight
+//    each: at any moment all waves read neighbouring addresses, which streams
+//    from HBM faster than giving each wave a far-apart contiguous run.  Unaligned x falls back to one 64-float ballot per load.
+//    The 8-lane OR runs on DPP lane moves (no LDS round trip).
 //  * other d: one thread per output word (pad bits stay 0).
 //  * One launch packs one tensor, or two tensors of the same shape (Q and K
 //    of the fused forward call): blocks [0, nb0) work on the first, the rest
 //    on the second, each exactly as a launch of its own would.
-//  * sigma: every thread sums x and x*x in float64; blocks reduce in a fixed
-//    order and store one partial pair each to the workspace; one wave (a
-//    finalize kernel on the same stream, or a wave of the attention launch in
-//    the fused call) sums the partials in a fixed order and writes sigma.  (A
+//  * sigma: every thread sums x and x*x in float64; each wave reduces its
+//    lanes in a fixed order into an LDS slot and bumps an LDS counter; the
+//    wave that arrives last adds the slots in index order and stores the
+//    block's partial pair (no end-of-block barrier, so a wave that is done
+//    leaves at once).  One wave (a finalize kernel on the same stream, or a
+//    wave of the attention launch in the fused call) sums the partials in a
+//    fixed order and writes sigma.  (A
 //    "last block finalizes" scheme needs an agent-scope release per block,
 //    which writes back L2 and costs more than the whole pack.)  No
 //    floating-point atomics, so sigma is bit-identical from run to run.
+//  * NaN: with sigma, a NaN anywhere in a lane's elements makes its float64
+//    sum of squares NaN (squares of +-inf stay +inf), so the status flag is
+//    read off that sum; without sigma each element is compared.
 #include "had_internal.h"
 
 namespace had {
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 4;
+constexpr int kNonTemporal = 2;  // buffer-op cache policy: streaming (nt)
 constexpr int kSegsPerWave = 4;  // grid sizing target for small inputs
-constexpr int kWavesPerBlock = kPackThreads / 64;
+constexpr int kWavesPerBlock = kPackWavesPerBlock;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -43,8 +52,6 @@ struct PackJobs {
   int nb0;              // blocks of job 0; the rest of the grid is job 1
   int64_t elems;        // B*H*n*d per tensor
   int64_t rows;         // B*H*n per tensor
-  int64_t seg_base;     // vector path: every wave of a tensor owns seg_base
-  int64_t seg_rem;      // 256-float segments, the first seg_rem waves one more
   int d;
   int W;
   uint32_t* dev_status;
@@ -66,35 +73,47 @@ __device__ inline BlockJob block_job(const PackJobs& p) {
   return b;
 }
 
-// Block-level fixed-order sum of two doubles; result valid in thread 0.
-__device__ inline void block_sum2(double& a, double& b) {
-  __shared__ double red[2][kWavesPerBlock];
-  a = wave_sum_f64(a);
-  b = wave_sum_f64(b);
-  const int wid = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 63) {
-    red[0][wid] = a;
-    red[1][wid] = b;
-  }
+// Per-block sigma reduction state in LDS.
+__shared__ double2 s_wave_part[kWavesPerBlock];
+__shared__ uint32_t s_waves_done;
+
+// Called by every thread at kernel entry when sigma is requested.
+__device__ inline void partials_begin() {
+  if (threadIdx.x == 0) s_waves_done = 0;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    a = 0.0;
-    b = 0.0;
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      a += red[0][w];
-      b += red[1][w];
+}
+
+// Wave sums into the block's LDS slots; the last wave to arrive adds the
+// slots in index order and stores the block's pair (plain stores; the reader
+// runs in a later kernel on the same stream and sees them through
+// kernel-boundary ordering).  The result does not depend on arrival order.
+__device__ void write_partials(double s1, double s2, const BlockJob& bj) {
+  s1 = wave_sum_f64(s1);
+  s2 = wave_sum_f64(s2);
+  if ((threadIdx.x & 63) == 63) {
+    s_wave_part[threadIdx.x >> 6] = double2{s1, s2};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (atomicAdd(&s_waves_done, 1u) == kWavesPerBlock - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      double a = 0.0, b = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const double2 p = s_wave_part[w];
+        a += p.x;
+        b += p.y;
+      }
+      bj.job.partials[2 * bj.blk + 0] = a;
+      bj.job.partials[2 * bj.blk + 1] = b;
     }
   }
 }
 
-// Per-block partial sums (plain stores; the reader runs in a later kernel on
-// the same stream and sees them through kernel-boundary ordering).
-__device__ void write_partials(double s1, double s2, const BlockJob& bj) {
-  block_sum2(s1, s2);
-  if (threadIdx.x == 0) {
-    bj.job.partials[2 * bj.blk + 0] = s1;
-    bj.job.partials[2 * bj.blk + 1] = s2;
-  }
+// OR of w over the 8 lanes 8j..8j+7 of a wave; every lane of the group gets it.
+__device__ inline uint32_t or8_lanes(uint32_t w) {
+  w |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  w |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  w |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0x141, 0xF, 0xF, false)); // row_half_mirror
+  return w;
 }
 
 __device__ inline void flag_nan(bool nan_seen, uint32_t* dev_status) {
@@ -103,28 +122,18 @@ __device__ inline void flag_nan(bool nan_seen, uint32_t* dev_status) {
 }
 
 // One wave: sigma from the partial pairs.
-__global__ __launch_bounds__(64) void sigma_finalize_kernel(const double2* partials, int nblocks,
+__global__ __launch_bounds__(64) void sigma_finalize_kernel(const double2* partials, int nparts,
                                                             double count, float* sigma) {
-  sigma_from_partials(partials, nblocks, count, sigma);
+  sigma_from_partials(partials, nparts, count, sigma);
 }
 
 // One wave: adds this call's element count, sum and sum of squares to a
 // running calibration state (calls on one stream add in stream order).
-__global__ __launch_bounds__(64) void sigma_accumulate_kernel(const double2* partials, int nblocks,
+__global__ __launch_bounds__(64) void sigma_accumulate_kernel(const double2* partials, int nparts,
                                                               double count, had_sigma_state* state) {
-  constexpr int kPer = kPackMaxBlocks / 64;
-  const int lane = threadIdx.x & 63;
-  double a = 0.0, b = 0.0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = lane + 64 * k;
-    const double2 p = i < nblocks ? partials[i] : double2{0.0, 0.0};
-    a += p.x;
-    b += p.y;
-  }
-  a = wave_sum_f64(a);
-  b = wave_sum_f64(b);
-  if (lane == 63) {
+  double a, b;
+  partials_total(partials, nparts, a, b);
+  if ((threadIdx.x & 63) == 63) {
     state->count += count;
     state->sum += a;
     state->sum_sq += b;
@@ -144,30 +153,45 @@ __global__ __launch_bounds__(64) void sigma_from_state_kernel(const had_sigma_st
   }
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zeros and stores past the end are dropped by the hardware range check.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(static_cast<uint32_t>(n)), 0x00020000);
+}
+
 // d % 32 == 0 and x 16-byte aligned: 256-float segments, 8 words each.
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
   const BlockJob bj = block_job(p);
-  const f32x4* __restrict__ x = reinterpret_cast<const f32x4*>(bj.job.x);
-  uint32_t* __restrict__ bits = bj.job.bits;
+  if (kSigma) partials_begin();
+  const float* x = bj.job.x;
+  uint32_t* bits = bj.job.bits;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (bj.blk * kPackThreads + threadIdx.x) >> 6;
-  // contiguous run of segments [seg_begin, seg_end), sizes differ by <= 1
-  const int64_t seg_begin = wave * p.seg_base + min(wave, p.seg_rem);
-  const int64_t seg_end = seg_begin + p.seg_base + (wave < p.seg_rem ? 1 : 0);
-  const int64_t nvec = p.elems >> 2;
+  // the tensor's nw waves sweep it together: wave w takes segments w, w + nw, ...
+  const int64_t nw = bj.nblk * kWavesPerBlock;
+  const int64_t wave = bj.blk * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nseg = (p.elems + 255) >> 8;
   const int64_t nwords = p.elems >> 5;
   const int shift = 4 * (lane & 7);
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
-  for (int64_t s0 = seg_begin; s0 < seg_end; s0 += kUnroll) {
-    f32x4 v[kUnroll];
+  // A batch is segments s0 + u * nw (u < kUnroll), addressed through buffer
+  // resources based at segment s0, so past-the-end segments read as zeros
+  // (adding nothing to the sums) and their words are not stored.  Two batch
+  // buffers alternate: the next batch's loads are issued before the current
+  // one is processed, so every wave keeps loads in flight.
+  auto load_batch = [&](int64_t s0, f32x4 (&v)[kUnroll]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(x + s0 * 256, (p.elems - s0 * 256) * 4);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = (s0 + u) * 64 + lane;
-      v[u] = (s0 + u < seg_end && i < nvec) ? __builtin_nontemporal_load(x + i)
-                                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     r, static_cast<int>(u * nw * 1024 + lane * 16), 0, kNonTemporal));
+  };
+  auto process = [&](int64_t s0, const f32x4 (&v)[kUnroll]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(bits + s0 * 8, (nwords - s0 * 8) * 4);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const f32x4 e = v[u];
@@ -175,19 +199,27 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
                     (static_cast<uint32_t>(e.z < 0.0f) << 2) |
                     (static_cast<uint32_t>(e.w < 0.0f) << 3))
                    << shift;
-      w |= __shfl_xor(w, 1, 64);
-      w |= __shfl_xor(w, 2, 64);
-      w |= __shfl_xor(w, 4, 64);
-      const int64_t wi = (s0 + u) * 8 + (lane >> 3);
-      if ((lane & 7) == 0 && s0 + u < seg_end && wi < nwords) bits[wi] = w;
-      nan_seen |= (e.x != e.x) | (e.y != e.y) | (e.z != e.z) | (e.w != e.w);
+      w = or8_lanes(w);
+      if ((lane & 7) == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(w, r, static_cast<int>((u * nw * 8 + (lane >> 3)) * 4), 0, 0);
+      if (!kSigma) nan_seen |= (e.x != e.x) | (e.y != e.y) | (e.z != e.z) | (e.w != e.w);
       if (kSigma) {
         const double a = e.x, b = e.y, c = e.z, d = e.w;
         s1 += (a + b) + (c + d);
         s2 += fma(a, a, b * b) + fma(c, c, d * d);
       }
     }
+  };
+  const int64_t step = kUnroll * nw;
+  f32x4 va[kUnroll], vb[kUnroll];
+  load_batch(wave, va);
+  for (int64_t s0 = wave; s0 < nseg; s0 += 2 * step) {
+    load_batch(s0 + step, vb);
+    process(s0, va);
+    load_batch(s0 + 2 * step, va);
+    process(s0 + step, vb);
   }
+  if (kSigma) nan_seen = s2 != s2;
   flag_nan(nan_seen, p.dev_status);
   if (kSigma) write_partials(s1, s2, bj);
 }
@@ -196,6 +228,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(PackJobs p) {
   const BlockJob bj = block_job(p);
+  if (kSigma) partials_begin();
   const float* __restrict__ x = bj.job.x;
   uint32_t* __restrict__ bits = bj.job.bits;
   const int lane = threadIdx.x & 63;
@@ -233,6 +266,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(PackJobs p) {
 template <bool kSigma>
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(PackJobs p) {
   const BlockJob bj = block_job(p);
+  if (kSigma) partials_begin();
   const float* __restrict__ x = bj.job.x;
   uint32_t* __restrict__ bits = bj.job.bits;
   const int d = p.d, W = p.W;
@@ -296,6 +330,8 @@ int pack_grid_blocks(const had_shape& s) {
   return static_cast<int>(blocks);
 }
 
+int pack_partials(const had_shape& s) { return pack_grid_blocks(s); }
+
 had_status check_pack_args(const float* x, uint32_t* xbits, float* sigma, const char* who) {
   if (x == nullptr || xbits == nullptr) return failf(HAD_ERR_INVALID_ARG, "%s: null input or bits", who);
   if (!aligned(x, 4) || !aligned(xbits, 4))
@@ -313,10 +349,6 @@ had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint3
   p.rows = s.batch * s.heads * s.seq;
   p.d = static_cast<int>(s.dim);
   p.W = static_cast<int>(words_per_row(s.dim));
-  const int64_t nseg = (p.elems + 255) / 256;
-  const int64_t nwaves = static_cast<int64_t>(blocks) * kWavesPerBlock;
-  p.seg_base = nseg / nwaves;
-  p.seg_rem = nseg % nwaves;
   p.dev_status = dev_status;
   const bool sigma = jobs[0].partials != nullptr;
   // one launch for both tensors when they take the same path and both or
@@ -344,7 +376,7 @@ had_status launch_sigma_finalize(const double* partials, const had_shape& s, flo
                                  hipStream_t st) {
   const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
   sigma_finalize_kernel<<<1, 64, 0, st>>>(reinterpret_cast<const double2*>(partials),
-                                          pack_grid_blocks(s), count, sigma);
+                                          pack_partials(s), count, sigma);
   return check_launch("had_pack");
 }
 
@@ -354,7 +386,7 @@ using namespace had;
 
 extern "C" size_t had_pack_workspace_bytes(had_shape s) {
   if (check_shape(s, HAD_MAX_DECODE_KEYS) != HAD_OK) return 0;
-  return sizeof(double) * 2 * static_cast<size_t>(pack_grid_blocks(s));
+  return sizeof(double) * 2 * static_cast<size_t>(pack_partials(s));
 }
 
 extern "C" had_status had_pack(const float* x, had_shape s, uint32_t* xbits, float* sigma,
@@ -402,7 +434,7 @@ extern "C" had_status had_pack_calibrate(const float* x, had_shape s, uint32_t* 
   if ((st = launch_pack(&job, 1, s, dev_status, hs)) != HAD_OK) return st;
   const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
   sigma_accumulate_kernel<<<1, 64, 0, hs>>>(reinterpret_cast<const double2*>(partials),
-                                            pack_grid_blocks(s), count, state);
+                                            pack_partials(s), count, state);
   return check_launch("had_pack_calibrate");
 }
 

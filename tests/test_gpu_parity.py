@@ -27,7 +27,8 @@ def _gpu():
 # --------------------------------------------------------------------- pack
 @pytest.mark.parametrize("shape", [(1, 1, 128, 64), (2, 3, 77, 128), (1, 2, 50, 40), (3, 1, 9, 33),
                                    (1, 1, 5, 5), (1, 2, 31, 256), (1, 1, 1, 1), (4, 4, 300, 32),
-                                   (1, 1, 999, 32), (2, 3, 1001, 64), (1, 4, 8192, 128)])
+                                   (1, 1, 999, 32), (2, 3, 1001, 64), (1, 4, 8192, 128),
+                                   (2, 8, 8192, 128)])
 def test_pack_bits_and_sigma(shape):
     log(f"pack {shape}")
     rng = np.random.default_rng(sum(shape))
