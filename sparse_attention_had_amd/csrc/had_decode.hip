@@ -38,10 +38,9 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecQBatch = 16;           // rows per histogram work-group
-constexpr int kDecMaxSplits = 1024;
+constexpr int kDecMaxSplits = 2048;
 constexpr int kDecMinKeysPerSplit = 256;
-constexpr int kDecMaxKeysPerSplit = 4096;
-constexpr int kDecList = 512;            // kept keys buffered before a gather
+constexpr int kDecMaxKeysPerSplit = 2048;
 
 struct DecArgs {
   const uint32_t* qbits;  // [BH, nq, W]
@@ -55,6 +54,8 @@ struct DecArgs {
   float scale;
   int causal;
   float* out;             // [BH, nq, d]
+  uint8_t* bins;          // [BH, nq, nkp] Hamming distance of every (row, key), or null
+  int64_t nkp;            // bins row length (splits * keys_per_split)
   uint32_t* hist;         // [BH, nq, splits, d + 1]
   int32_t* stats;         // [BH, nq, 4]: T, h_min, Z bits, N_i
   float* part;            // [BH, nq, splits, d]
@@ -68,8 +69,31 @@ __device__ inline int visible_keys(const DecArgs& a, int q) {
   return static_cast<int>(last + 1 < a.nk ? last + 1 : a.nk);
 }
 
+// Key words of one key: W dwords, as vector loads where the row alignment
+// allows (kKVec: the cache base is 16-byte aligned for W % 4 == 0, 8-byte
+// aligned for W % 2 == 0).
+template <int W, bool kKVec>
+__device__ inline void load_key_words(const uint32_t* krow, uint32_t* kw) {
+  if constexpr (kKVec && W % 4 == 0) {
+#pragma unroll
+    for (int w = 0; w < W; w += 4) {
+      const uint4 t = *reinterpret_cast<const uint4*>(krow + w);
+      kw[w] = t.x; kw[w + 1] = t.y; kw[w + 2] = t.z; kw[w + 3] = t.w;
+    }
+  } else if constexpr (kKVec && W % 2 == 0) {
+#pragma unroll
+    for (int w = 0; w < W; w += 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(krow + w);
+      kw[w] = t.x; kw[w + 1] = t.y;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < W; ++w) kw[w] = krow[w];
+  }
+}
+
 // ---- 1. logits and per-split histograms -------------------------------------
-template <int W>
+template <int W, bool kKVec>
 __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   __shared__ uint32_t hl[kDecQBatch * (HAD_MAX_DIM + 1)];
   const int nqb = (a.nq + kDecQBatch - 1) / kDecQBatch;
@@ -92,9 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       j[u] = jb + u * kDecThreads + static_cast<int>(threadIdx.x);
-      const uint32_t* krow = a.kbits + (bh * a.kstride + (j[u] < k1 ? j[u] : 0)) * W;
-#pragma unroll
-      for (int w = 0; w < W; ++w) kw[u][w] = j[u] < k1 ? krow[w] : 0u;
+      load_key_words<W, kKVec>(a.kbits + (bh * a.kstride + (j[u] < k1 ? j[u] : 0)) * W, kw[u]);
     }
     for (int q = 0; q < nqh; ++q) {
 #pragma unroll
@@ -104,6 +126,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
         for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[u][w] ^ qrow[q * W + w]);
         const bool vis = j[u] < k1 && (!a.causal || j[u] <= a.qpos0 + q0 + q);
         if (vis) atomicAdd(&hl[q * nb + h], 1u);
+        if (a.bins != nullptr && j[u] < k1) a.bins[(bh * a.nq + q0 + q) * a.nkp + j[u]] = static_cast<uint8_t>(h);
       }
     }
   }
@@ -114,14 +137,23 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (integers: any order is exact).
+// x + (the value DPP control kCtrl brings to this lane; 0 where there is no
+// source lane or the row mask leaves this lane out).
+template <int kCtrl, int kRowMask>
+__device__ inline uint32_t dpp_add_u32(uint32_t x) {
+  return x + static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, kRowMask, 0xF, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave on DPP lane moves: shifts
+// by 1, 2, 4, 8 within rows of 16, then each row adds the last lane of the
+// rows before it (integers: any order is exact).
 __device__ inline uint32_t wave_scan_incl(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = dpp_add_u32<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add_u32<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add_u32<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add_u32<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add_u32<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add_u32<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -170,11 +202,11 @@ __device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, 
     if (T < 0 && hm != 0) {
       const int l = __builtin_ctzll(hm);
       T = 64 * r + l;
-      below = __shfl(excl, l, 64);
+      below = __builtin_amdgcn_readlane(excl, l);
     }
     const uint64_t nz = __ballot(64 * r + lane < nb && cnt[r] > 0);
     if (hmin < 0 && nz != 0) hmin = 64 * r + __builtin_ctzll(nz);
-    run = __shfl(incl, 63, 64);
+    run = __builtin_amdgcn_readlane(incl, 63);
   }
   if (T < 0) T = a.d;  // unreachable: the visible count is >= N_i
   if (hmin < 0) hmin = 0;
@@ -182,9 +214,9 @@ __device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, 
   // ties at T in the splits before s_self
   uint32_t before = 0, mine = 0;
   for (int s0 = 0; s0 < a.splits; s0 += 64) {
-    const int s = s0 + lane;
-    const uint32_t tie = s < a.splits ? hp[s * nb + T] : 0u;
-    uint32_t x = s < s_self ? tie : 0u;
+    const int sp = s0 + lane;
+    const uint32_t tie = sp < a.splits ? hp[sp * nb + T] : 0u;
+    uint32_t x = sp < s_self ? tie : 0u;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     before += x;
@@ -214,14 +246,35 @@ __device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, 
 }
 
 // ---- 3. selection and gather of the kept V rows, per (split, row) ------------
-// V rows are read 8 features per lane: kVec = 16-byte vector loads (bf16 with
-// d % 8 == 0, or fp32 with d % 4 == 0, and a 16-byte aligned base).
-template <int W, bool VF32, bool kVec>
+// Thread t owns the keys k0 + t + 256*u (u < kKPT = keys_per_split / 256, a
+// power of two <= 8), so key order is (u, wave, lane) and every load below
+// is coalesced across the wave.  The Hamming distances come from the bins
+// the histogram launch wrote (kBins: one byte per key) or are recomputed
+// from the key words (kGrp keys per batch); either way the first loads are
+// in flight while wave 0 computes the row statistics.  A kept key's slot in
+// the list is (strict keys before it) + min(ties before it, quota), from
+// per-(u, wave) ballot counts.  The list (key offset << 16 | h per entry)
+// lives in dynamic LDS of keys_per_split dwords; the row-group partial sums
+// reuse that space after the gather.  V rows are read 8 features per lane:
+// kVec = 16-byte vector loads (bf16 with d % 8 == 0, or fp32 with d % 4 == 0,
+// and a 16-byte aligned base), several rows per lane group in flight.
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+
+size_t gather_lds_bytes(int keys_per_split) {
+  const size_t list = static_cast<size_t>(keys_per_split) * 4;
+  const size_t red = static_cast<size_t>(kDecThreads) * 8 * 4;
+  return list > red ? list : red;
+}
+
+template <int W, bool VF32, bool kVec, bool kKVec, bool kBins, int kKPT>
 __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
-  __shared__ int32_t list_j[kDecList];
-  __shared__ float list_w[kDecList];
-  __shared__ uint32_t wcnt[2][2][kDecThreads / 64];  // [parity][ties | kept][wave]
-  __shared__ float red[kDecThreads * 8];
+  extern __shared__ uint32_t dyn[];  // list, then red
+  __shared__ float wtab[HAD_MAX_DIM + 1];
+  __shared__ uint32_t cnt[kKPT][kDecWaves];  // strict | ties << 16, per (u, wave)
+  __shared__ RowStats rs_sh;
+  uint32_t* list = dyn;
+  float* red = reinterpret_cast<float*>(dyn);
   const int64_t bid = blockIdx.x;
   const int s = static_cast<int>(bid % a.splits);
   const int64_t rest = bid / a.splits;
@@ -233,19 +286,110 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   const int k0 = s * a.keys_per_split;
   const int k1 = min(a.nk, k0 + a.keys_per_split);
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk);  // keys j <= last
+  const int kend = static_cast<int>(min(static_cast<int64_t>(k1), last + 1));  // visible: [k0, kend)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // ---- Hamming distances of this thread's keys (meaningless where a key is
+  // not visible; never used there)
+  uint32_t hh[kKPT];
+  // keys per batch: a power of two (so it divides kKPT), about 16 key words in flight
+  constexpr int kGrp = cmin(kKPT, W <= 2 ? 8 : (W <= 4 ? 4 : 2));
+  uint32_t kw[kBins ? 1 : kGrp][W];
+  const uint32_t* qw = a.qbits + bhq * W;
+  const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
+  auto load_batch = [&](int u0) {
+    if constexpr (!kBins) {
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g) {
+        const int j = k0 + (u0 + g) * kDecThreads + tid;
+        if (j < kend) {
+          load_key_words<W, kKVec>(kb + static_cast<int64_t>(j) * W, kw[g]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < W; ++w) kw[g][w] = 0u;
+        }
+      }
+    }
+  };
+  auto finish_batch = [&](int u0) {
+    if constexpr (!kBins) {
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[g][w] ^ qw[w]);
+        hh[u0 + g] = h;
+      }
+    }
+  };
+  if constexpr (kBins) {
+    // one byte per key, 64 consecutive bytes per wave; the bins row holds
+    // splits * keys_per_split entries, so every load stays inside it
+    const uint8_t* brow = a.bins + bhq * a.nkp + k0 + tid;
+#pragma unroll
+    for (int u = 0; u < kKPT; ++u) hh[u] = brow[u * kDecThreads];
+  } else {
+    load_batch(0);
+  }
+  for (int t = tid; t <= d; t += kDecThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
   // the row's threshold and this split's tie quota (wave 0), shared through LDS
-  __shared__ RowStats rs_sh;
   if (wid == 0) {
     const RowStats r0 = row_stats(a, bhq, q, s, s == 0);
     if (lane == 0) rs_sh = r0;
+  }
+  if constexpr (!kBins) {
+    finish_batch(0);
+#pragma unroll
+    for (int u0 = kGrp; u0 < kKPT; u0 += kGrp) {
+      load_batch(u0);
+      finish_batch(u0);
+    }
   }
   __syncthreads();
   const uint32_t T = rs_sh.T;
   const int hmin = rs_sh.hmin;
   const uint32_t quota = rs_sh.quota;
-  const uint32_t* qw = a.qbits + bhq * W;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // gather geometry: lpr lanes per V row, 8 features each; R rows per step
+
+  // ---- per-(u, wave) counts of strict keys (h < T) and ties (h == T),
+  // packed as strict | ties << 16 (a split holds at most 2048 keys)
+#pragma unroll
+  for (int u = 0; u < kKPT; ++u) {
+    const bool vis = k0 + u * kDecThreads + tid < kend;
+    const uint64_t sm = __ballot(vis && hh[u] < T);
+    const uint64_t tm = __ballot(vis && hh[u] == T);
+    if (lane == 0)
+      cnt[u][wid] = static_cast<uint32_t>(__builtin_popcountll(sm)) |
+                    (static_cast<uint32_t>(__builtin_popcountll(tm)) << 16);
+  }
+  __syncthreads();
+  // ---- ranks and the compacted list, in key order
+  uint32_t run = 0;  // strict | ties << 16 in earlier u
+#pragma unroll
+  for (int u = 0; u < kKPT; ++u) {
+    const int j = k0 + u * kDecThreads + tid;
+    const bool vis = j < kend;
+    const bool strict = vis && hh[u] < T;
+    const bool tie = vis && hh[u] == T;
+    const uint64_t sm = __ballot(strict);
+    const uint64_t tm = __ballot(tie);
+    uint32_t wb = 0, ut = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const uint32_t c = cnt[u][w];
+      wb += w < wid ? c : 0u;
+      ut += c;
+    }
+    const uint32_t b = run + wb;
+    const uint32_t sbefore = (b & 0xFFFFu) + static_cast<uint32_t>(__builtin_popcountll(sm & lt_mask));
+    const uint32_t tbefore = (b >> 16) + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
+    if (strict || (tie && tbefore < quota))
+      list[sbefore + min(tbefore, quota)] = (static_cast<uint32_t>(j - k0) << 16) | hh[u];
+    run += ut;
+  }
+  const int nl = static_cast<int>((run & 0xFFFFu) + min(run >> 16, quota));
+  __syncthreads();  // the list is complete
+
+  // ---- gather: lpr lanes per V row, 8 features each; R row groups
   const int lpr = (d + 7) / 8;
   const int R = kDecThreads / lpr;
   const int g = tid / lpr, li = tid - (tid / lpr) * lpr;
@@ -254,107 +398,66 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   for (int f = 0; f < 8; ++f) acc[f] = 0.0f;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
                                bh * static_cast<int64_t>(a.kstride) * d * (VF32 ? 4 : 2);
-  auto load8 = [&](int jj, float* x) {
+  constexpr int kRows = VF32 ? 4 : 6;  // rows per lane group in flight (<= 64 VGPRs for bf16)
+  if (g < R) {
     const int c0 = 8 * li;
-    if constexpr (VF32) {
-      const float* row = reinterpret_cast<const float*>(vbase) + static_cast<int64_t>(jj) * d;
-      if (kVec && c0 + 8 <= d) {
-        const float4 u0 = *reinterpret_cast<const float4*>(row + c0);
-        const float4 u1 = *reinterpret_cast<const float4*>(row + c0 + 4);
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-      } else {
+    for (int e0 = g; e0 < nl; e0 += kRows * R) {
+      uint32_t raw[kRows][VF32 ? 8 : 4];
+      float wr[kRows];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) x[f] = c0 + f < d ? row[c0 + f] : 0.0f;
-      }
-    } else {
-      const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + static_cast<int64_t>(jj) * d;
-      uint32_t w4[4];
-      if (kVec && c0 + 8 <= d) {
-        const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
-        w4[0] = u.x; w4[1] = u.y; w4[2] = u.z; w4[3] = u.w;
-      } else {
+      for (int r = 0; r < kRows; ++r) {
+        const int e = e0 + r * R;
+        const uint32_t ent = e < nl ? list[e] : list[e0];
+        // (clamps keep every access inside the visible keys and the table)
+        const int hb = min(max(static_cast<int>(ent & 0xFFFFu) - hmin, 0), d);
+        wr[r] = e < nl ? wtab[hb] : 0.0f;
+        const int64_t jj = min(k0 + static_cast<int>(ent >> 16), kend - 1);
+        if constexpr (VF32) {
+          const float* row = reinterpret_cast<const float*>(vbase) + jj * d;
+          if (kVec && c0 + 8 <= d) {
+            const uint4 u0 = *reinterpret_cast<const uint4*>(row + c0);
+            const uint4 u1 = *reinterpret_cast<const uint4*>(row + c0 + 4);
+            raw[r][0] = u0.x; raw[r][1] = u0.y; raw[r][2] = u0.z; raw[r][3] = u0.w;
+            raw[r][4] = u1.x; raw[r][5] = u1.y; raw[r][6] = u1.z; raw[r][7] = u1.w;
+          } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const uint32_t lo = c0 + 2 * f < d ? row[c0 + 2 * f] : 0u;
-          const uint32_t hi = c0 + 2 * f + 1 < d ? row[c0 + 2 * f + 1] : 0u;
-          w4[f] = lo | (hi << 16);
+            for (int f = 0; f < 8; ++f) raw[r][f] = c0 + f < d ? __builtin_bit_cast(uint32_t, row[c0 + f]) : 0u;
+          }
+        } else {
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + jj * d;
+          if (kVec && c0 + 8 <= d) {
+            const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
+            raw[r][0] = u.x; raw[r][1] = u.y; raw[r][2] = u.z; raw[r][3] = u.w;
+          } else {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              const uint32_t lo = c0 + 2 * f < d ? row[c0 + 2 * f] : 0u;
+              const uint32_t hi = c0 + 2 * f + 1 < d ? row[c0 + 2 * f + 1] : 0u;
+              raw[r][f] = lo | (hi << 16);
+            }
+          }
         }
       }
+      // rows e0, e0 + R, ... in order (entries past nl have weight 0)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        x[2 * f] = __builtin_bit_cast(float, w4[f] << 16);
-        x[2 * f + 1] = __builtin_bit_cast(float, w4[f] & 0xFFFF0000u);
-      }
-    }
-  };
-  // accumulate the buffered kept rows [0, nl), two rows per row group in flight
-  auto gather = [&](int nl) {
-    if (g >= R) return;
-    for (int e0 = g; e0 < nl; e0 += 2 * R) {
-      float x0[8], x1[8];
-      const int e1 = e0 + R;
-      const float w0 = list_w[e0];
-      const float w1 = e1 < nl ? list_w[e1] : 0.0f;
-      load8(list_j[e0], x0);
-      load8(e1 < nl ? list_j[e1] : list_j[e0], x1);
+      for (int r = 0; r < kRows; ++r) {
+        float x[8];
+        if constexpr (VF32) {
 #pragma unroll
-      for (int f = 0; f < 8; ++f) acc[f] = fmaf(w1, x1[f], fmaf(w0, x0[f], acc[f]));
-    }
-  };
-  if (k0 <= last) {
-    uint32_t run_ties = 0;
-    int nl = 0;
-    int it = 0;
-    for (int jb = k0; jb < k1; jb += kDecThreads, ++it) {
-      const int j = jb + tid;
-      const bool vis = j < k1 && j <= last;
-      uint32_t h = 0;
-      if (vis) {
-        const uint32_t* krow = a.kbits + (bh * a.kstride + j) * W;
+          for (int f = 0; f < 8; ++f) x[f] = __builtin_bit_cast(float, raw[r][f]);
+        } else {
 #pragma unroll
-        for (int w = 0; w < W; ++w) h += __builtin_popcount(krow[w] ^ qw[w]);
-      }
-      const bool tie = vis && h == T;
-      const bool strict = vis && h < T;
-      const int par = it & 1;
-      const uint64_t tm = __ballot(tie);
-      if (lane == 0) wcnt[par][0][wid] = static_cast<uint32_t>(__builtin_popcountll(tm));
-      __syncthreads();
-      uint32_t before = 0, tot = 0;
+          for (int f = 0; f < 4; ++f) {
+            x[2 * f] = __builtin_bit_cast(float, raw[r][f] << 16);
+            x[2 * f + 1] = __builtin_bit_cast(float, raw[r][f] & 0xFFFF0000u);
+          }
+        }
 #pragma unroll
-      for (int w = 0; w < kDecThreads / 64; ++w) {
-        const uint32_t c = wcnt[par][0][w];
-        before += w < wid ? c : 0u;
-        tot += c;
-      }
-      const uint32_t rank = run_ties + before + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
-      const bool keep = strict || (tie && rank < quota);
-      run_ties += tot;
-      const uint64_t km = __ballot(keep);
-      if (lane == 0) wcnt[par][1][wid] = static_cast<uint32_t>(__builtin_popcountll(km));
-      __syncthreads();
-      int kbefore = 0, ktot = 0;
-#pragma unroll
-      for (int w = 0; w < kDecThreads / 64; ++w) {
-        const int c = static_cast<int>(wcnt[par][1][w]);
-        kbefore += w < wid ? c : 0;
-        ktot += c;
-      }
-      if (keep) {
-        const int pos = nl + kbefore + __builtin_popcountll(km & lt_mask);
-        list_j[pos] = j;
-        list_w[pos] = expf(-2.0f * a.scale * static_cast<float>(static_cast<int>(h) - hmin));
-      }
-      nl += ktot;
-      if (nl > kDecList - kDecThreads || jb + kDecThreads >= k1) {
-        __syncthreads();  // the list is complete
-        gather(nl);
-        nl = 0;
-        __syncthreads();  // the list may be refilled
+        for (int f = 0; f < 8; ++f) acc[f] = fmaf(wr[r], x[f], acc[f]);
       }
     }
   }
+  __syncthreads();  // every group is done with the list: red reuses it
   // row-group partial sums, then a fixed-order sum over the groups
   if (g < R) {
 #pragma unroll
@@ -373,28 +476,36 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
 }
 
 // ---- 4. fixed-order sum over splits, normalized ------------------------------
-__global__ __launch_bounds__(64) void dec_reduce_kernel(DecArgs a) {
+// One thread per feature (blockDim = d rounded up to 64), 16 loads in flight.
+__global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
   const int64_t bhq = blockIdx.x;
+  const int c = threadIdx.x;
+  if (c >= a.d) return;
   const float Z = __builtin_bit_cast(float, a.stats[bhq * 4 + 2]);
   const float invZ = Z > 0.0f ? 1.0f / Z : 0.0f;
-  const float* p = a.part + bhq * a.splits * static_cast<int64_t>(a.d);
-  for (int c = threadIdx.x; c < a.d; c += 64) {
-    float sum = 0.0f;
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {  // 8 loads in flight, summed in order
-      float t[8];
+  const float* p = a.part + bhq * a.splits * static_cast<int64_t>(a.d) + c;
+  constexpr int kB = 16;
+  float sum = 0.0f;
+  for (int s0 = 0; s0 < a.splits; s0 += kB) {  // summed in split order
+    float t[kB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = s0 + u < a.splits ? p[(s0 + u) * static_cast<int64_t>(a.d) + c] : 0.0f;
+    for (int u = 0; u < kB; ++u) t[u] = s0 + u < a.splits ? p[(s0 + u) * static_cast<int64_t>(a.d)] : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += t[u];
-    }
-    a.out[bhq * a.d + c] = sum * invZ;
+    for (int u = 0; u < kB; ++u) sum += t[u];
   }
+  a.out[bhq * a.d + c] = sum * invZ;
 }
 
-// Work split and workspace layout, from the shape alone.
+// Work split and workspace layout, from the shape alone.  keys_per_split is
+// 256 times a power of two (at most 2048).  The per-(row, key) distance bins
+// are kept when n_q <= W (n_q bytes per key against the 4W bytes of key
+// words they replace in the gather; with more rows the key words, shared by
+// the rows and served from L2, are cheaper) and at most 1 GiB in all.
 struct DecPlan {
   int splits, keys_per_split;
-  size_t off_hist, off_stats, off_part, bytes;
+  bool bins;
+  int64_t nkp;
+  size_t off_hist, off_stats, off_part, off_bins, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -410,11 +521,15 @@ DecPlan plan_for(const had_decode_shape& s) {
   if (splits < min_by_keys) splits = min_by_keys;
   if (splits > kDecMaxSplits) splits = kDecMaxSplits;
   if (splits < 1) splits = 1;
-  int64_t per = (nk + splits - 1) / splits;
-  per = (per + kDecThreads - 1) / kDecThreads * kDecThreads;
+  const int64_t want = (nk + splits - 1) / splits;
+  int64_t per = kDecThreads;
+  while (per < want && per < kDecMaxKeysPerSplit) per *= 2;
   splits = (nk + per - 1) / per;
   p.splits = static_cast<int>(splits);
   p.keys_per_split = static_cast<int>(per);
+  p.nkp = splits * per;
+  const size_t bins_bytes = static_cast<size_t>(rows) * static_cast<size_t>(p.nkp);
+  p.bins = s.n_q <= words_per_row(s.dim) && bins_bytes <= (static_cast<size_t>(1) << 30);
   size_t off = 0;
   p.off_hist = off;
   off = align256(off + static_cast<size_t>(rows) * p.splits * (s.dim + 1) * sizeof(uint32_t));
@@ -422,6 +537,8 @@ DecPlan plan_for(const had_decode_shape& s) {
   off = align256(off + static_cast<size_t>(rows) * 4 * sizeof(int32_t));
   p.off_part = off;
   off = align256(off + static_cast<size_t>(rows) * p.splits * s.dim * sizeof(float));
+  p.off_bins = off;
+  if (p.bins) off = align256(off + bins_bytes);
   p.bytes = off;
   return p;
 }
@@ -440,20 +557,39 @@ had_status check_decode_shape(const had_decode_shape& s) {
 }
 
 template <int W>
-void launch_hist(const DecArgs& a, int64_t blocks, hipStream_t st) {
-  dec_hist_kernel<W><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+void launch_hist(const DecArgs& a, bool kvec, int64_t blocks, hipStream_t st) {
+  if (kvec && W % 2 == 0) dec_hist_kernel<W, true><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+  else dec_hist_kernel<W, false><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+}
+
+template <int W, bool kKVec, bool kBins, int kKPT>
+void launch_gather_kpt(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
+  const unsigned nb = static_cast<unsigned>(blocks);
+  const size_t lds = gather_lds_bytes(a.keys_per_split);
+  if (a.vf32) {
+    if (vec) dec_gather_kernel<W, true, true, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
+    else dec_gather_kernel<W, true, false, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
+  } else {
+    if (vec) dec_gather_kernel<W, false, true, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
+    else dec_gather_kernel<W, false, false, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
+  }
+}
+
+template <int W, bool kKVec, bool kBins>
+void launch_gather_k(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
+  switch (a.keys_per_split / kDecThreads) {
+    case 1: launch_gather_kpt<W, kKVec, kBins, 1>(a, vec, blocks, st); break;
+    case 2: launch_gather_kpt<W, kKVec, kBins, 2>(a, vec, blocks, st); break;
+    case 4: launch_gather_kpt<W, kKVec, kBins, 4>(a, vec, blocks, st); break;
+    default: launch_gather_kpt<W, kKVec, kBins, 8>(a, vec, blocks, st); break;  // 8
+  }
 }
 
 template <int W>
-void launch_gather(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
-  const unsigned nb = static_cast<unsigned>(blocks);
-  if (a.vf32) {
-    if (vec) dec_gather_kernel<W, true, true><<<nb, kDecThreads, 0, st>>>(a);
-    else dec_gather_kernel<W, true, false><<<nb, kDecThreads, 0, st>>>(a);
-  } else {
-    if (vec) dec_gather_kernel<W, false, true><<<nb, kDecThreads, 0, st>>>(a);
-    else dec_gather_kernel<W, false, false><<<nb, kDecThreads, 0, st>>>(a);
-  }
+void launch_gather(const DecArgs& a, bool vec, bool kvec, int64_t blocks, hipStream_t st) {
+  if (a.bins != nullptr) launch_gather_k<W, false, true>(a, vec, blocks, st);
+  else if (kvec && W % 2 == 0) launch_gather_k<W, true, false>(a, vec, blocks, st);
+  else launch_gather_k<W, false, false>(a, vec, blocks, st);
 }
 
 }  // namespace
@@ -509,6 +645,8 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   a.stats = reinterpret_cast<int32_t*>(ws + p.off_stats);
   a.part = reinterpret_cast<float*>(ws + p.off_part);
+  a.bins = p.bins ? ws + p.off_bins : nullptr;
+  a.nkp = p.nkp;
   a.splits = p.splits;
   a.keys_per_split = p.keys_per_split;
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -518,30 +656,33 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   const int64_t rows = a.bh_total * s.n_q;
   if (hist_blocks > 0x7FFFFFFF || gather_blocks > 0x7FFFFFFF || rows > 0x7FFFFFFF)
     return fail(HAD_ERR_UNSUPPORTED, "had_decode: grid too large");
+  // key rows of W words load as 16-byte (W % 4 == 0) or 8-byte (W % 2 == 0)
+  // vectors from an aligned base
+  const bool kvec = aligned(kbits, a.W % 4 == 0 ? 16 : 8);
   switch (a.W) {
-    case 1: launch_hist<1>(a, hist_blocks, hs); break;
-    case 2: launch_hist<2>(a, hist_blocks, hs); break;
-    case 3: launch_hist<3>(a, hist_blocks, hs); break;
-    case 4: launch_hist<4>(a, hist_blocks, hs); break;
-    case 5: launch_hist<5>(a, hist_blocks, hs); break;
-    case 6: launch_hist<6>(a, hist_blocks, hs); break;
-    case 7: launch_hist<7>(a, hist_blocks, hs); break;
-    default: launch_hist<8>(a, hist_blocks, hs); break;
+    case 1: launch_hist<1>(a, kvec, hist_blocks, hs); break;
+    case 2: launch_hist<2>(a, kvec, hist_blocks, hs); break;
+    case 3: launch_hist<3>(a, kvec, hist_blocks, hs); break;
+    case 4: launch_hist<4>(a, kvec, hist_blocks, hs); break;
+    case 5: launch_hist<5>(a, kvec, hist_blocks, hs); break;
+    case 6: launch_hist<6>(a, kvec, hist_blocks, hs); break;
+    case 7: launch_hist<7>(a, kvec, hist_blocks, hs); break;
+    default: launch_hist<8>(a, kvec, hist_blocks, hs); break;
   }
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
   // 16-byte row slices need 16-byte aligned rows
   const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
   switch (a.W) {
-    case 1: launch_gather<1>(a, vec, gather_blocks, hs); break;
-    case 2: launch_gather<2>(a, vec, gather_blocks, hs); break;
-    case 3: launch_gather<3>(a, vec, gather_blocks, hs); break;
-    case 4: launch_gather<4>(a, vec, gather_blocks, hs); break;
-    case 5: launch_gather<5>(a, vec, gather_blocks, hs); break;
-    case 6: launch_gather<6>(a, vec, gather_blocks, hs); break;
-    case 7: launch_gather<7>(a, vec, gather_blocks, hs); break;
-    default: launch_gather<8>(a, vec, gather_blocks, hs); break;
+    case 1: launch_gather<1>(a, vec, kvec, gather_blocks, hs); break;
+    case 2: launch_gather<2>(a, vec, kvec, gather_blocks, hs); break;
+    case 3: launch_gather<3>(a, vec, kvec, gather_blocks, hs); break;
+    case 4: launch_gather<4>(a, vec, kvec, gather_blocks, hs); break;
+    case 5: launch_gather<5>(a, vec, kvec, gather_blocks, hs); break;
+    case 6: launch_gather<6>(a, vec, kvec, gather_blocks, hs); break;
+    case 7: launch_gather<7>(a, vec, kvec, gather_blocks, hs); break;
+    default: launch_gather<8>(a, vec, kvec, gather_blocks, hs); break;
   }
   if ((st = check_launch("had_decode")) != HAD_OK) return st;
-  dec_reduce_kernel<<<static_cast<unsigned>(rows), 64, 0, hs>>>(a);
+  dec_reduce_kernel<<<static_cast<unsigned>(rows), (a.d + 63) / 64 * 64, 0, hs>>>(a);
   return check_launch("had_decode");
 }
