@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import sparse_attention_had_amd as had
-from had_workloads import make_inputs
+from had_workloads import DECODE_WORKLOADS, decode_inputs, make_inputs
 from parity_util import check_out, log
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +38,8 @@ CASES = [
     (1, 1, 2, 50, 50, 64, 80, 48, True, "bf16", 0.125),       # N > visible
     (1, 1, 2, 100, 100, 64, 10, 500, True, "f32", 0.3),       # every key visible
     (3, 1, 17, 777, 800, 33, 20, 760, False, "bf16", 0.25),   # two row batches
+    (1, 16, 64, 1000, 1000, 64, 100, 936, True, "bf16", 0.125),   # 2 splits of 512 keys, recomputed
+    (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 32 splits of 512 keys, bins
 ]
 
 
@@ -84,3 +86,35 @@ def test_decode_is_deterministic_and_reuses_its_workspace():
     o2 = had.decode(qb, kb, v_t, 300, 0.125, q_pos0=nk - nq, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_WORKLOADS))
+def test_decode_workload_sampled(name):
+    """The decode workloads at full size, in the launch configuration bench.py
+    times (the work split for 128 rows x 16384 keys is 16 splits of 1024 keys
+    with stored distance bins; for 2048 rows, 8 splits of 2048 keys with the
+    distances recomputed from the key words), checked against the oracle on
+    sampled (batch, head) slices, all new rows of each."""
+    w = DECODE_WORKLOADS[name]
+    log(f"decode workload {name}: B={w.batch} H={w.heads} n_k={w.n_k} n_q={w.n_q} d={w.dim} "
+        f"N={w.topn} seed={w.seed}")
+    inp = decode_inputs(w)
+    qn = torch.from_numpy(inp["q_new"]).cuda()
+    kc = torch.from_numpy(inp["k"]).cuda()
+    v_t = torch.from_numpy(inp["v"])
+    v_t = (v_t.to(torch.bfloat16) if w.v_dtype == "bf16" else v_t).cuda()
+    qb, _ = had.pack(qn, with_sigma=False)
+    kb, _ = had.pack(kc, with_sigma=False)
+    del kc
+    ws = torch.empty(had.decode_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.n_k, w.dim),
+                     dtype=torch.uint8, device="cuda")
+    out = had.decode(qb, kb, v_t, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal,
+                     workspace=ws).cpu().numpy()
+    log("  gpu done")
+    BH = w.batch * w.heads
+    rng = np.random.default_rng(66)
+    for bh in np.unique(np.r_[0, BH - 1, rng.integers(0, BH, 4)]):
+        b, h = divmod(int(bh), w.heads)
+        r = oracle.decode(inp["q_new"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                          q_pos0=w.q_pos0, causal=w.causal)
+        check_out(out[b, h], r["out"], r["E"], inp["v"], w.v_dtype, where=f"{name} slice {(b, h)}")
