@@ -275,8 +275,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(the path shards by (batch, head) slice with no communication).", file=sys.stderr)
+        print("bench.py: measures one GPU only; --gpus must be 1 (the path would shard by "
+              "(batch, head) slice with no communication, one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
