@@ -271,6 +271,8 @@ size_t had_decode_workspace_bytes(had_decode_shape s);
  *
  *  qbits  [B,H,n_q,W] uint32 sign words of the new rows (had_pack output).
  *  kbits  [B,H,k_stride,W] uint32 sign words of the cache; rows >= n_k unused.
+ *         4-byte aligned (with W even, 8- or 16-byte alignment lets key rows
+ *         load as vectors).
  *  v      [B,H,k_stride,d] float32 (HAD_F32) or bfloat16 (HAD_BF16) values;
  *         rows >= n_k unused.  4-byte aligned.
  *  q_pos0 position of the first new row (>= 0).  causal = 1: row i sees the
