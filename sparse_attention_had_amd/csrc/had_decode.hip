@@ -246,7 +246,7 @@ __device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, 
 }
 
 // ---- 3. selection and gather of the kept V rows, per (split, row) ------------
-// Thread t owns the keys k0 + t + 256*u (u < kKPT = keys_per_split / 256, a
+// Thread t owns the keys k0 + t + 256*u (u < kpt = keys_per_split / 256, a
 // power of two <= 8), so key order is (u, wave, lane) and every load below
 // is coalesced across the wave.  The Hamming distances come from the bins
 // the histogram launch wrote (kBins: one byte per key) or are recomputed
@@ -267,11 +267,13 @@ size_t gather_lds_bytes(int keys_per_split) {
   return list > red ? list : red;
 }
 
-template <int W, bool VF32, bool kVec, bool kKVec, bool kBins, int kKPT>
+constexpr int kDecMaxKPT = kDecMaxKeysPerSplit / kDecThreads;  // keys per thread, at most
+
+template <int W, bool VF32, bool kVec, bool kKVec, bool kBins>
 __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   extern __shared__ uint32_t dyn[];  // list, then red
   __shared__ float wtab[HAD_MAX_DIM + 1];
-  __shared__ uint32_t cnt[kKPT][kDecWaves];  // strict | ties << 16, per (u, wave)
+  __shared__ uint32_t cnt[kDecMaxKPT][kDecWaves];  // strict | ties << 16, per (u, wave)
   __shared__ RowStats rs_sh;
   uint32_t* list = dyn;
   float* red = reinterpret_cast<float*>(dyn);
@@ -288,12 +290,13 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk);  // keys j <= last
   const int kend = static_cast<int>(min(static_cast<int64_t>(k1), last + 1));  // visible: [k0, kend)
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int kpt = a.keys_per_split / kDecThreads;  // wave-uniform
 
   // ---- Hamming distances of this thread's keys (meaningless where a key is
   // not visible; never used there)
-  uint32_t hh[kKPT];
-  // keys per batch: a power of two (so it divides kKPT), about 16 key words in flight
-  constexpr int kGrp = cmin(kKPT, W <= 2 ? 8 : (W <= 4 ? 4 : 2));
+  uint32_t hh[kDecMaxKPT];
+  // keys per batch: about 16 key words in flight
+  constexpr int kGrp = cmin(kDecMaxKPT, W <= 2 ? 8 : (W <= 4 ? 4 : 2));
   uint32_t kw[kBins ? 1 : kGrp][W];
   const uint32_t* qw = a.qbits + bhq * W;
   const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
 #pragma unroll
       for (int g = 0; g < kGrp; ++g) {
         const int j = k0 + (u0 + g) * kDecThreads + tid;
-        if (j < kend) {
+        if (u0 + g < kpt && j < kend) {
           load_key_words<W, kKVec>(kb + static_cast<int64_t>(j) * W, kw[g]);
         } else {
 #pragma unroll
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
     // splits * keys_per_split entries, so every load stays inside it
     const uint8_t* brow = a.bins + bhq * a.nkp + k0 + tid;
 #pragma unroll
-    for (int u = 0; u < kKPT; ++u) hh[u] = brow[u * kDecThreads];
+    for (int u = 0; u < kDecMaxKPT; ++u) hh[u] = u < kpt ? brow[u * kDecThreads] : 0u;
   } else {
     load_batch(0);
   }
@@ -340,9 +343,11 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   if constexpr (!kBins) {
     finish_batch(0);
 #pragma unroll
-    for (int u0 = kGrp; u0 < kKPT; u0 += kGrp) {
-      load_batch(u0);
-      finish_batch(u0);
+    for (int u0 = kGrp; u0 < kDecMaxKPT; u0 += kGrp) {
+      if (u0 < kpt) {
+        load_batch(u0);
+        finish_batch(u0);
+      }
     }
   }
   __syncthreads();
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   // ---- per-(u, wave) counts of strict keys (h < T) and ties (h == T),
   // packed as strict | ties << 16 (a split holds at most 2048 keys)
 #pragma unroll
-  for (int u = 0; u < kKPT; ++u) {
+  for (int u = 0; u < kDecMaxKPT; ++u) {
+    if (u >= kpt) break;
     const bool vis = k0 + u * kDecThreads + tid < kend;
     const uint64_t sm = __ballot(vis && hh[u] < T);
     const uint64_t tm = __ballot(vis && hh[u] == T);
@@ -365,7 +371,8 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   // ---- ranks and the compacted list, in key order
   uint32_t run = 0;  // strict | ties << 16 in earlier u
 #pragma unroll
-  for (int u = 0; u < kKPT; ++u) {
+  for (int u = 0; u < kDecMaxKPT; ++u) {
+    if (u >= kpt) break;
     const int j = k0 + u * kDecThreads + tid;
     const bool vis = j < kend;
     const bool strict = vis && hh[u] < T;
@@ -558,38 +565,38 @@ had_status check_decode_shape(const had_decode_shape& s) {
 
 template <int W>
 void launch_hist(const DecArgs& a, bool kvec, int64_t blocks, hipStream_t st) {
-  if (kvec && W % 2 == 0) dec_hist_kernel<W, true><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
-  else dec_hist_kernel<W, false><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
-}
-
-template <int W, bool kKVec, bool kBins, int kKPT>
-void launch_gather_kpt(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
-  const unsigned nb = static_cast<unsigned>(blocks);
-  const size_t lds = gather_lds_bytes(a.keys_per_split);
-  if (a.vf32) {
-    if (vec) dec_gather_kernel<W, true, true, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
-    else dec_gather_kernel<W, true, false, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
-  } else {
-    if (vec) dec_gather_kernel<W, false, true, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
-    else dec_gather_kernel<W, false, false, kKVec, kBins, kKPT><<<nb, kDecThreads, lds, st>>>(a);
+  if constexpr (W % 2 == 0) {
+    if (kvec) {
+      dec_hist_kernel<W, true><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+      return;
+    }
   }
+  dec_hist_kernel<W, false><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
 }
 
 template <int W, bool kKVec, bool kBins>
 void launch_gather_k(const DecArgs& a, bool vec, int64_t blocks, hipStream_t st) {
-  switch (a.keys_per_split / kDecThreads) {
-    case 1: launch_gather_kpt<W, kKVec, kBins, 1>(a, vec, blocks, st); break;
-    case 2: launch_gather_kpt<W, kKVec, kBins, 2>(a, vec, blocks, st); break;
-    case 4: launch_gather_kpt<W, kKVec, kBins, 4>(a, vec, blocks, st); break;
-    default: launch_gather_kpt<W, kKVec, kBins, 8>(a, vec, blocks, st); break;  // 8
+  const unsigned nb = static_cast<unsigned>(blocks);
+  const size_t lds = gather_lds_bytes(a.keys_per_split);
+  if (a.vf32) {
+    if (vec) dec_gather_kernel<W, true, true, kKVec, kBins><<<nb, kDecThreads, lds, st>>>(a);
+    else dec_gather_kernel<W, true, false, kKVec, kBins><<<nb, kDecThreads, lds, st>>>(a);
+  } else {
+    if (vec) dec_gather_kernel<W, false, true, kKVec, kBins><<<nb, kDecThreads, lds, st>>>(a);
+    else dec_gather_kernel<W, false, false, kKVec, kBins><<<nb, kDecThreads, lds, st>>>(a);
   }
 }
 
 template <int W>
 void launch_gather(const DecArgs& a, bool vec, bool kvec, int64_t blocks, hipStream_t st) {
-  if (a.bins != nullptr) launch_gather_k<W, false, true>(a, vec, blocks, st);
-  else if (kvec && W % 2 == 0) launch_gather_k<W, true, false>(a, vec, blocks, st);
-  else launch_gather_k<W, false, false>(a, vec, blocks, st);
+  if (a.bins != nullptr) {
+    launch_gather_k<W, false, true>(a, vec, blocks, st);
+  } else if constexpr (W % 2 == 0) {
+    if (kvec) launch_gather_k<W, true, false>(a, vec, blocks, st);
+    else launch_gather_k<W, false, false>(a, vec, blocks, st);
+  } else {
+    launch_gather_k<W, false, false>(a, vec, blocks, st);
+  }
 }
 
 }  // namespace

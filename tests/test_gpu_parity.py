@@ -236,6 +236,27 @@ def test_attention_invariants():
         np.testing.assert_allclose(o[0, h], mean, rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_at_the_sequence_limit(causal):
+    """n = 65536 (the limit) with d = 5: six possible logits, so the threshold
+    bin holds thousands of ties, each lane-half's 16-bit histogram counter
+    sees up to 32768 keys and the tie count in the selection key reaches its
+    bound.  Sampled rows against the oracle: indices bit-exact, outputs within
+    the bf16 tolerance."""
+    B, H, n, d, topn, scale = 1, 1, 65536, 5, 300, 0.3
+    log(f"attention at the limit {(B, H, n, d, topn, causal)}")
+    inp = make_inputs(B, H, n, d, rank=4, noise="normal", seed=99, v_dtype="bf16")
+    q, k, v = to_dev(inp)
+    qb, _ = had.pack(q, with_sigma=False)
+    kb, _ = had.pack(k, with_sigma=False)
+    out = had.attention(qb, kb, v, topn, scale, causal).cpu().numpy()
+    idx = had.select(qb, kb, d, topn, causal)[0].cpu().numpy()
+    rows = np.array([0, 1, 2, 37, 299, 300, 32767, 32768, 40000, 65534, 65535])
+    r = oracle_head(inp, 0, 0, topn, scale, causal, rows=rows)
+    assert np.array_equal(idx[r["rows"]].astype(np.int64), r["idx"])
+    check_out(out[0, 0][r["rows"]], r["out"], r["E"], inp["v"], "bf16", where=f"n={n} causal={causal}")
+
+
 # --------------------------------------------------------------- workloads
 def _workload_check(name, sample_rows=None, select_heads=None):
     w = WORKLOADS[name]
