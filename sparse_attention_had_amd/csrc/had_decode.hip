@@ -11,21 +11,25 @@
 // causal masking it sees keys j <= q_pos0 + i.
 //
 // GPU design.  With n_q << n_k the work is a scan of the key cache, so it is
-// split over (key range, slice) work-groups and runs in three launches:
+// split over (key range, slice) work-groups (256 * 2^m keys per split, at
+// most 2048) and runs in three launches:
 //  1. dec_hist: per split and batch of up to 16 rows, h of every (row, key)
 //     pair by XOR + popcount on the vector ALU (the query words are
-//     wave-uniform scalars) into a per-split (d+1)-bin histogram per row
-//     (LDS atomics).
-//  2. dec_gather: one 256-thread work-group per (split, row).  Wave 0 sums
-//     the row's split histograms, finds the threshold bin T and the tie
-//     quota r (as in had_attention) and this split's share of the r ties
-//     (lower splits first); the split-0 work-group also writes the softmax
-//     denominator Z.  Then h is recomputed from the key words (L2-resident
-//     after step 1), h < T and the first quota keys with h == T are kept in
-//     key order (wave ballots plus a work-group prefix over the waves), the
-//     kept keys and their weights exp(-2*scale*(h - h_min)) are compacted in
-//     LDS, and only the kept V rows are read, 16 bytes of a row per lane,
-//     accumulating in fp32; the row groups are summed in a fixed order.
+//     wave-uniform scalars; key rows as vector loads) into a per-split
+//     (d+1)-bin histogram per row (LDS atomics).  With n_q <= W it also
+//     stores h of every (row, key) as one byte ("bins").
+//  2. dec_gather: one 256-thread work-group per (split, row).  Its keys'
+//     distances are requested first (the bins, or the key words again,
+//     L2-resident after step 1), and meanwhile wave 0 sums the row's split
+//     histograms, finds the threshold bin T and the tie quota r (as in
+//     had_attention) and this split's share of the r ties (lower splits
+//     first); the split-0 work-group also writes the softmax denominator Z.
+//     h < T and the first quota keys with h == T are kept in key order (wave
+//     ballots plus one work-group prefix over (key step, wave) counts), the
+//     kept keys and their distances are compacted in LDS, and only the kept
+//     V rows are read, 16 bytes of a row per lane, with weights
+//     exp(-2*scale*(h - h_min)) from a table, accumulating in fp32; the row
+//     groups are summed in a fixed order.
 //  3. dec_reduce: out = (sum over splits, in split order) / Z.
 // HBM bytes per slice: the key words (d/8 bytes per key), and per row the
 // 2d bytes (bf16) of each kept key; everything else is small.

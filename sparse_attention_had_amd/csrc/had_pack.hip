@@ -12,11 +12,16 @@
 //    onto the flat word stream (word = element / 32).  With x 16-byte
 //    aligned, lane L of a wave loads floats 4L..4L+3 of a 256-float segment;
 //    the 8 lanes that cover one word OR their sign nibbles together and one
-//    of them stores the word.  The waves of a tensor sweep it together (wave
-//    w of nw takes segments w, w + nw, ...), kUnroll 1 KiB loads in flight
-//    each: at any moment all waves read neighbouring addresses, which streams
-//    from HBM faster than giving each wave a far-apart contiguous run.  Unaligned x falls back to one 64-float ballot per load.
-//    The 8-lane OR runs on DPP lane moves (no LDS round trip).
+//    of them stores the word (the 8-lane OR runs on DPP lane moves, no LDS
+//    round trip).  The waves of a tensor sweep it together (wave w of nw
+//    takes segments w, w + nw, ...): at any moment all waves read
+//    neighbouring addresses, which streams from HBM faster than giving each
+//    wave a far-apart contiguous run.  Each wave keeps two batches of
+//    kUnroll 1 KiB loads in flight (the next batch is requested before the
+//    current one is processed), through raw buffer resources whose range
+//    check zeroes past-the-end loads and drops past-the-end word stores, so
+//    the loop has no bounds branches.  Unaligned x falls back to one
+//    64-float ballot per load.
 //  * other d: one thread per output word (pad bits stay 0).
 //  * One launch packs one tensor, or two tensors of the same shape (Q and K
 //    of the fused forward call): blocks [0, nb0) work on the first, the rest
@@ -27,10 +32,10 @@
 //    block's partial pair (no end-of-block barrier, so a wave that is done
 //    leaves at once).  One wave (a finalize kernel on the same stream, or a
 //    wave of the attention launch in the fused call) sums the partials in a
-//    fixed order and writes sigma.  (A
-//    "last block finalizes" scheme needs an agent-scope release per block,
-//    which writes back L2 and costs more than the whole pack.)  No
-//    floating-point atomics, so sigma is bit-identical from run to run.
+//    fixed order and writes sigma.  (A "last block finalizes" scheme needs
+//    an agent-scope release per block, which writes back L2 and costs more
+//    than the whole pack.)  No floating-point atomics, so sigma is
+//    bit-identical from run to run.
 //  * NaN: with sigma, a NaN anywhere in a lane's elements makes its float64
 //    sum of squares NaN (squares of +-inf stay +inf), so the status flag is
 //    read off that sum; without sigma each element is compared.
