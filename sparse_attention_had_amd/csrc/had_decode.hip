@@ -110,18 +110,22 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   const int nb = a.d + 1;
   const int k0 = s * a.keys_per_split;
   const int k1 = min(a.nk, k0 + a.keys_per_split);
-  for (int t = threadIdx.x; t < nqh * nb; t += kDecThreads) hl[t] = 0u;
-  __syncthreads();
   const uint32_t* qrow = a.qbits + (bh * a.nq + q0) * W;
   constexpr int kU = 4;  // keys per thread in flight
-  for (int jb = k0; jb < k1; jb += kU * kDecThreads) {
-    uint32_t kw[kU][W];
-    int j[kU];
+  uint32_t kw[kU][W];
+  int j[kU];
+  auto load = [&](int jb) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       j[u] = jb + u * kDecThreads + static_cast<int>(threadIdx.x);
       load_key_words<W, kKVec>(a.kbits + (bh * a.kstride + (j[u] < k1 ? j[u] : 0)) * W, kw[u]);
     }
+  };
+  load(k0);  // the first keys are in flight while the histogram is cleared
+  for (int t = threadIdx.x; t < nqh * nb; t += kDecThreads) hl[t] = 0u;
+  __syncthreads();
+  for (int jb = k0; jb < k1; jb += kU * kDecThreads) {
+    if (jb != k0) load(jb);
     for (int q = 0; q < nqh; ++q) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
