@@ -48,6 +48,8 @@
 //    and are stored transposed.  Groups are large (pass 1: 4 KB of key words;
 //    pass 2: about 16 KB of V) so that the compute of one group hides the load
 //    latency of the next.
+#include <atomic>
+
 #include "had_internal.h"
 
 namespace had {
@@ -141,6 +143,23 @@ __device__ inline uint32_t lds_addr(const unsigned char* p) {
 __device__ inline uint32_t lds_load_u32(uint32_t addr) {
   return *(lds_cu32*)(static_cast<uintptr_t>(addr));
 }
+// Issue priority of the calling wave (0..3, higher issues first).  When the
+// whole grid is resident at once, the work-groups that share a CU start
+// together and have equal work, but the instruction arbiter favours the
+// oldest waves: without help the first work-group races ahead and the last
+// one finishes alone, with a third of the waves to hide its latencies.
+// Lowering a wave's priority as it progresses (3 in pass 1, then 2, 1 and,
+// for the last key group only, 0) lets the ones behind issue first; within
+// one level the oldest still goes first, so the last level is kept short.
+__device__ inline void set_priority(int p) {
+  switch (p) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // Keeps a per-lane value in a VGPR as computed (stops re-association that
 // would split an LDS base back out of it).
 __device__ inline uint32_t opaque(uint32_t v) {
@@ -313,6 +332,7 @@ void had_attn_kernel(AttnArgs a) {
     copies_done();
     for (int gi = 0; gi < ngroups; ++gi) {
       const int buf = gi & 1;
+      if (a.balance && gi == 0) set_priority(3);
       if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, std::integral_constant<int, C::kCH1>{}, buf ^ 1);
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
@@ -790,6 +810,8 @@ void had_attn_kernel(AttnArgs a) {
   copies_done();
   for (int gi = 0; gi < ngroups2; ++gi) {
     const int buf = gi & 1;
+    if (a.balance && (gi == 0 || gi == ngroups2 / 2 || gi == ngroups2 - 1))
+      set_priority(gi == ngroups2 - 1 ? 0 : (gi < ngroups2 / 2 ? 2 : 1));
     if (gi + 1 < ngroups2) {
       k_issue((gi + 1) * C::kCH2, std::integral_constant<int, C::kCH2>{}, buf ^ 1);
       v_issue((gi + 1) * C::kCH2, buf ^ 1);
@@ -822,14 +844,39 @@ void had_attn_kernel(AttnArgs a) {
   }
 }
 
+// Work-groups of this kernel the device holds at once (occupancy x CUs), per
+// device and cached; 0 if the runtime cannot say.
+template <int W, bool VF32, int MODE, bool VDIRECT>
+int64_t resident_capacity() {
+  static std::atomic<int64_t> cache[64];  // 0: not known yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    using C = Cfg<W, VF32, VDIRECT>;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, had_attn_kernel<W, VF32, MODE, VDIRECT>,
+                                                     C::kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cap = static_cast<int64_t>(per_cu) * cus;
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
 template <int W, bool VF32, int MODE, bool VDIRECT = false>
-had_status launch_one(const AttnArgs& a, hipStream_t st) {
+had_status launch_one(const AttnArgs& args, hipStream_t st) {
   using C = Cfg<W, VF32, VDIRECT>;
-  const int qrows = (MODE == 2) ? a.row_count : a.n;
+  const int qrows = (MODE == 2) ? args.row_count : args.n;
   const int64_t ntq = (qrows + C::kQB - 1) / C::kQB;
-  const int64_t blocks = ntq * a.bh_count;
+  const int64_t blocks = ntq * args.bh_count;
   if (blocks <= 0) return HAD_OK;
   if (blocks > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "grid too large");
+  AttnArgs a = args;
+  a.balance = blocks <= resident_capacity<W, VF32, MODE, VDIRECT>() ? 1 : 0;
   had_attn_kernel<W, VF32, MODE, VDIRECT><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
   return check_launch(MODE == 0 ? "had_attention"
                       : (MODE == 1 ? "had_select" : (MODE == 2 ? "had_logits" : "had_topn_mass")));

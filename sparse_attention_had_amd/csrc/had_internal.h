@@ -151,6 +151,7 @@ struct AttnArgs {
   int16_t* logits;   // Logits output [bh_count, row_count, n]
   double mass;       // Mass: softmax mass to reach
   int32_t* nmass;    // Mass output [bh_count, n]
+  int balance;       // set by the launcher: the whole grid is resident at once
   // Optional sigma finalize (fused forward call): wave 0 of the last block
   // turns the partials of a preceding pack launch into sigma_out[t].
   const double2* sigma_partials[2];
