@@ -433,35 +433,42 @@ void had_attn_kernel(AttnArgs a) {
 
   // =========================================================== per-row statistics
   const int Ni = qvalid ? min(a.topn, lim) : 0;
-  int T = 0, hmin = 0, below0 = 0, ties0 = 0, below = 0;
   const uint32_t* hq = reinterpret_cast<const uint32_t*>(region) + wid * (d + 1) * 32 + ql;
+  int T, hmin, below0, ties0, below;
   {
-    // scan bins upward, 8 independent LDS reads at a time; every lane stops
-    // at its threshold (the visible count is >= Ni, so each lane finds one)
-    int cum = 0, cum0 = 0;
-    bool have_min = false, found = false;
-    for (int b0 = 0; !found; b0 += 8) {
+    // Scan the bins upward, 8 independent LDS reads at a time, keeping the
+    // running counts packed as the histogram stores them (half 0 | half 1
+    // << 16; each stays below 2^16): one add per bin, the total by a dot
+    // product with (1, 1).  The running total never decreases, so T is the
+    // number of bins whose running total is still below Ni, h_min the number
+    // whose running total is 0, and the counts below T are the running
+    // counts at the last bin below Ni.  The wave stops once every lane has
+    // passed its Ni (the visible count is >= Ni, so every lane does).
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    const v2u16 ones = {1, 1};
+    const uint32_t ni = static_cast<uint32_t>(Ni);
+    uint32_t cumx = 0, cumx_lt = 0;
+    int nlt = 0, nzero = 0;
+    for (int b0 = 0; b0 <= d; b0 += 8) {
       uint32_t x[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) x[k] = (b0 + k <= d) ? hq[(b0 + k) * 32] : 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int c0 = static_cast<int>(x[k] & 0xFFFFu);
-        const int cnt = c0 + static_cast<int>(x[k] >> 16);
-        if (!have_min && cnt > 0) hmin = b0 + k;
-        have_min |= cnt > 0;
-        const bool hit = !found && b0 + k <= d && cum + cnt >= Ni;
-        if (hit) {
-          T = b0 + k;
-          below = cum;
-          below0 = cum0;
-          ties0 = c0;
-        }
-        found |= hit;
-        cum += cnt;
-        cum0 += c0;
+        cumx += x[k];
+        const uint32_t tot = __builtin_amdgcn_udot2(__builtin_bit_cast(v2u16, cumx), ones, 0u, false);
+        const bool lt = tot < ni;
+        nlt += lt ? 1 : 0;
+        cumx_lt = lt ? cumx : cumx_lt;
+        nzero += tot == 0u ? 1 : 0;
       }
+      if (__all(__builtin_amdgcn_udot2(__builtin_bit_cast(v2u16, cumx), ones, 0u, false) >= ni)) break;
     }
+    T = min(nlt, d);
+    hmin = cumx == 0u ? 0 : nzero;  // an empty histogram (no visible key) keeps 0
+    below0 = static_cast<int>(cumx_lt & 0xFFFFu);
+    below = below0 + static_cast<int>(cumx_lt >> 16);
+    ties0 = static_cast<int>(hq[T * 32] & 0xFFFFu);
   }
   const int r_tie = Ni - below;
   const int quota0 = min(r_tie, ties0);
