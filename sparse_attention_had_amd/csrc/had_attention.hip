@@ -180,7 +180,7 @@ void had_attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;
   const int ql = lane & 31;
   const int n = a.n;
@@ -300,24 +300,37 @@ void had_attn_kernel(AttnArgs a) {
   };
 
   // cin + k*u, u = -logit, for (query ql, key half*Hh + 16*gc + i),
-  // i = 0..15, chunk c of the key-word buffer buf (k set by make_q).
-  auto logits_tile = [&](int buf, int c, uint32_t cin) {
+  // i = 0..15, chunk c of the key-word buffer buf (k set by make_q), in
+  // three steps that a caller can spread out to hide their LDS latency:
+  // the key words, their +-1 bytes (table reads), the products.
+  auto k_words = [&](int buf, int c, uint32_t (&words)[W]) {
     const uint32_t* krow = reinterpret_cast<const uint32_t*>(lds + kKbOff + buf * C::kKbBuf) + (c * 32 + ql) * W;
-    uint32_t words[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) words[w] = krow[w];
-    v16i acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = static_cast<int>(cin);
+  };
+  auto k_expand = [&](const uint32_t (&words)[W], v4i (&kv)[W]) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const uint32_t b16 = words[w] >> (16 * half);
       const uint2 lo = byte_lut[b16 & 0xFFu];
       const uint2 hi = byte_lut[(b16 >> 8) & 0xFFu];
-      const v4i kv = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y)};
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qx[w], acc, 0, 0, 0);
+      kv[w] = v4i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y)};
     }
+  };
+  auto k_product = [&](const v4i (&kv)[W], uint32_t cin) {
+    v16i acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = static_cast<int>(cin);
+#pragma unroll
+    for (int w = 0; w < W; ++w) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv[w], qx[w], acc, 0, 0, 0);
     return acc;
+  };
+  auto logits_tile = [&](int buf, int c, uint32_t cin) {
+    uint32_t words[W];
+    v4i kv[W];
+    k_words(buf, c, words);
+    k_expand(words, kv);
+    return k_product(kv, cin);
   };
 
   // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
@@ -336,7 +349,33 @@ void had_attn_kernel(AttnArgs a) {
       if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, std::integral_constant<int, C::kCH1>{}, buf ^ 1);
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
-      if (cend > 0) {
+      if (cend == C::kCH1) {
+        // A full group, software-pipelined and straight-line: step c takes
+        // the products of chunk c, expands the key bytes of chunk c + 1,
+        // reads the key words of chunk c + 2 and hands chunk c - 1 to the
+        // body.  The LDS reads are queued ahead of the body's LDS traffic,
+        // and with no branch in between the waits stop at exactly the reads
+        // that a product needs.
+        constexpr int K = C::kCH1;
+        uint32_t kw[W];
+        v4i kv[W];
+        v16i ta, tb;
+        auto step = [&](v16i& cur, const v16i& prev, int c) {
+          cur = k_product(kv, cin);
+          if (c + 1 < K) k_expand(kw, kv);
+          if (c + 2 < K) k_words(buf, c + 2, kw);
+          if (c > 0) body(prev, g0 + c - 1);
+        };
+        k_words(buf, 0, kw);
+        k_expand(kw, kv);
+        k_words(buf, 1, kw);
+#pragma unroll
+        for (int c = 0; c < K; c += 2) {
+          step(ta, tb, c);
+          if (c + 1 < K) step(tb, ta, c + 1);
+        }
+        body((K & 1) ? ta : tb, g0 + K - 1);
+      } else if (cend > 0) {
         v16i u_next = logits_tile(buf, 0, cin);
         for (int c = 0; c < cend; ++c) {
           const v16i u = u_next;
@@ -379,10 +418,12 @@ void had_attn_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i)
         __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
     } else {
+      // hidden elements add 0 (their tile entry is a valid bin address):
+      // every chunk issues the same 16 LDS operations, without branches
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (i < L)
-          __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
+        __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), i < L ? addend : 0u,
+                           __ATOMIC_RELAXED);
     }
   });
 
