@@ -334,7 +334,8 @@ void had_attn_kernel(AttnArgs a) {
   };
 
   // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
-  // body(u, gc) runs per chunk with a one-chunk logit lookahead.
+  // body(u, gc, full) runs per chunk; full (a compile-time tag) says that
+  // every lane of the wave sees all 16 keys of the chunk.
   // first_issued: group 0 was copied at kernel entry.
   auto k_sweep = [&](uint32_t cin, bool first_issued, auto&& body) {
     const int ngroups = (nchunk + C::kCH1 - 1) / C::kCH1;
@@ -349,38 +350,44 @@ void had_attn_kernel(AttnArgs a) {
       if (gi + 1 < ngroups) k_issue((gi + 1) * C::kCH1, std::integral_constant<int, C::kCH1>{}, buf ^ 1);
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
-      if (cend == C::kCH1) {
+      // every lane sees every key of the group: keys up to half*Hh + 16*(g0 + kCH1)
+      const bool whole = cend == C::kCH1 && __all(lim >= half * Hh + 16 * (g0 + C::kCH1));
+      if (whole) {
         // A full group, software-pipelined and straight-line: step c takes
-        // the products of chunk c, expands the key bytes of chunk c + 1,
-        // reads the key words of chunk c + 2 and hands chunk c - 1 to the
-        // body.  The LDS reads are queued ahead of the body's LDS traffic,
-        // and with no branch in between the waits stop at exactly the reads
-        // that a product needs.
+        // the products of chunk c, expands the key bytes of chunk c + 2,
+        // reads the key words of chunk c + 3 and hands chunk c - 1 to the
+        // body.  A product's operands were read a whole step (and one
+        // body's worth of LDS atomics) before it, and with no branch in
+        // between the compiler's waits stop at exactly those reads.
         constexpr int K = C::kCH1;
         uint32_t kw[W];
-        v4i kv[W];
+        v4i kv0[W], kv1[W];
         v16i ta, tb;
-        auto step = [&](v16i& cur, const v16i& prev, int c) {
+        auto step = [&](v16i& cur, const v16i& prev, v4i (&kv)[W], int c) {
           cur = k_product(kv, cin);
-          if (c + 1 < K) k_expand(kw, kv);
-          if (c + 2 < K) k_words(buf, c + 2, kw);
-          if (c > 0) body(prev, g0 + c - 1);
+          if (c + 2 < K) k_expand(kw, kv);
+          if (c + 3 < K) k_words(buf, c + 3, kw);
+          if (c > 0) body(prev, g0 + c - 1, std::true_type{});
         };
         k_words(buf, 0, kw);
-        k_expand(kw, kv);
-        k_words(buf, 1, kw);
+        k_expand(kw, kv0);
+        if (K > 1) {
+          k_words(buf, 1, kw);
+          k_expand(kw, kv1);
+        }
+        if (K > 2) k_words(buf, 2, kw);
 #pragma unroll
         for (int c = 0; c < K; c += 2) {
-          step(ta, tb, c);
-          if (c + 1 < K) step(tb, ta, c + 1);
+          step(ta, tb, kv0, c);
+          if (c + 1 < K) step(tb, ta, kv1, c + 1);
         }
-        body((K & 1) ? ta : tb, g0 + K - 1);
+        body((K & 1) ? ta : tb, g0 + K - 1, std::true_type{});
       } else if (cend > 0) {
         v16i u_next = logits_tile(buf, 0, cin);
         for (int c = 0; c < cend; ++c) {
           const v16i u = u_next;
           if (c + 1 < cend) u_next = logits_tile(buf, c + 1, cin);
-          body(u, g0 + c);
+          body(u, g0 + c, std::false_type{});
         }
       }
       copies_done();
@@ -391,7 +398,7 @@ void had_attn_kernel(AttnArgs a) {
   if (MODE == 2) {
     int16_t* dst = a.logits + (bh_local * a.row_count + (qvalid ? i_row - a.row_begin : 0)) * static_cast<int64_t>(n);
     make_q(0x01u, 0xFEu);  // +-1: the tile holds u itself
-    k_sweep(0u, true, [&](const v16i& u, int gc) {
+    k_sweep(0u, true, [&](const v16i& u, int gc, auto) {
       if (!qvalid) return;
       const int kbase = half * Hh + 16 * gc;
 #pragma unroll
@@ -411,15 +418,15 @@ void had_attn_kernel(AttnArgs a) {
   // what the tile holds with k = 64 and cin = hb
   const uint32_t hb = lds_addr(region + (wid * (d + 1) * 32 + ql) * 4 + 64 * d);
   make_q(0x40u, 0x80u);  // +-64
-  k_sweep(hb, true, [&](const v16i& t, int gc) {
-    const int L = lim - (half * Hh + 16 * gc);  // element i visible iff i < L
-    if (__all(L >= 16)) {
+  k_sweep(hb, true, [&](const v16i& t, int gc, auto full) {
+    if constexpr (decltype(full)::value) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), addend, __ATOMIC_RELAXED);
     } else {
-      // hidden elements add 0 (their tile entry is a valid bin address):
-      // every chunk issues the same 16 LDS operations, without branches
+      // element i visible iff i < L; hidden ones add 0 (their tile entry is
+      // a valid bin address)
+      const int L = lim - (half * Hh + 16 * gc);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         __atomic_fetch_add((lds_u32*)(static_cast<uintptr_t>(static_cast<uint32_t>(t[i]))), i < L ? addend : 0u,
@@ -532,7 +539,7 @@ void had_attn_kernel(AttnArgs a) {
     int pos = half ? (below0 + quota0) : 0;
     int32_t* dst = a.idx + (bh_local * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(a.topn);
     make_q(0x02u, 0xFCu);  // +-2
-    k_sweep(lutc, false, [&](const v16i& t, int gc) {
+    k_sweep(lutc, false, [&](const v16i& t, int gc, auto) {
       const int kbase = half * Hh + 16 * gc;
       const int L = lim - kbase;
 #pragma unroll
