@@ -84,9 +84,10 @@ struct Cfg {
   static constexpr int kThreads = threads_for(W);
   static constexpr int kQB = 32 * kWaves;  // query rows per block
   static constexpr int kDP = 32 * W;       // padded feature count
-  // 16-key chunks per half in one key group: K-only loops (2 KB of key
-  // words) and the attend loop (V tile of about 16 KB)
-  static constexpr int kCH1 = W <= 2 ? 16 / W : 32 / W;
+  // 16-key chunks per half in one key group: K-only loops (4 KB of key
+  // words; fewer groups mean fewer barriers and pipeline refills) and the
+  // attend loop (V tile of about 16 KB)
+  static constexpr int kCH1 = 32 / W;
   static constexpr int kCH2 = VF32 ? (W <= 2 ? 2 : 1) : (W <= 2 ? 4 : (W <= 4 ? 2 : 1));
   static constexpr int kKb1 = kCH1 * 32 * W * 4;  // bytes of key words per group
   static constexpr int kKb2 = kCH2 * 32 * W * 4;
