@@ -42,7 +42,11 @@ had_status check_shape(const had_shape& s, int64_t max_seq = HAD_MAX_SEQ);
 
 // ---- pack (had_pack.hip) ----
 constexpr int kPackThreads = 256;    // threads per pack block
-constexpr int kPackMaxBlocks = 512;  // pack blocks per tensor, at most
+// Pack blocks per tensor, at most.  256 blocks x 4 waves, each with two
+// batches of 4 KiB of loads in flight, keep about 64 KiB of reads in flight
+// per CU on a fused Q+K launch: a measured optimum for streaming fp32 Q and
+// K (twice that or half of it is 5-10 % slower).
+constexpr int kPackMaxBlocks = 256;
 constexpr int kPackWavesPerBlock = kPackThreads / 64;
 
 int pack_grid_blocks(const had_shape& s);
