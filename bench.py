@@ -109,10 +109,10 @@ def cpu_baseline(w, inp, budget_s):
                       f"{dt:.1f} s wall, numpy float64, 1 thread"}
 
 
-def decode_model(w):
+def decode_model(w, fp32_rows=False):
     """Algorithmic HBM bytes of one had_decode call on decode workload w: the
     cached key words once, the kept V rows of every new row, the new rows'
-    query words and outputs."""
+    query words (float32 rows for had_decode_forward) and outputs."""
     W = (w.dim + 31) // 32
     bh = w.batch * w.heads
     vbytes = 2 if w.v_dtype == "bf16" else 4
@@ -120,7 +120,8 @@ def decode_model(w):
     for i in range(w.n_q):
         vis = min(w.n_k, w.q_pos0 + i + 1) if w.causal else w.n_k
         kept += min(w.topn, vis)
-    per_slice = w.n_k * W * 4 + kept * w.dim * vbytes + w.n_q * (W * 4 + w.dim * 4)
+    qbytes = w.dim * 4 if fp32_rows else W * 4
+    per_slice = w.n_k * W * 4 + kept * w.dim * vbytes + w.n_q * (qbytes + w.dim * 4)
     return {"kept": bh * kept, "hbm_bytes": bh * per_slice}
 
 
@@ -175,8 +176,10 @@ def settle(step, seconds):
 
 
 def bench_decode(args, w):
-    """One step = had_pack of the new rows' queries + had_decode against the
-    packed cache (packed once, outside the timed region)."""
+    """One step = had_decode_forward: the new rows' float32 queries against the
+    packed cache (packed once, outside the timed region); their sign words are
+    built inside the first of its three launches.  --separate-calls times
+    had_pack of the new rows + had_decode instead."""
     import torch
     import sparse_attention_had_amd as had
     from had_workloads import decode_inputs
@@ -196,10 +199,18 @@ def bench_decode(args, w):
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    def decode_call():
+        if args.separate_calls:
+            had.decode(qb, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal, out=out,
+                       workspace=ws)
+        else:
+            had.decode_forward(qn, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal,
+                               out=out, workspace=ws)
+
     def step():
-        had.pack(qn, out=qb, with_sigma=False)
-        had.decode(qb, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal, out=out,
-                   workspace=ws)
+        if args.separate_calls:
+            had.pack(qn, out=qb, with_sigma=False)
+        decode_call()
 
     for _ in range(args.warmup):
         step()
@@ -216,13 +227,14 @@ def bench_decode(args, w):
     d0 = torch.cuda.Event(enable_timing=True)
     d1 = torch.cuda.Event(enable_timing=True)
     d0.record(stream)
+    if args.separate_calls:
+        had.pack(qn, out=qb, with_sigma=False)
     for _ in range(args.steps):
-        had.decode(qb, kb, v, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal, out=out,
-                   workspace=ws)
+        decode_call()
     d1.record(stream)
     torch.cuda.synchronize()
     dec_s = d0.elapsed_time(d1) / args.steps / 1e3
-    model = decode_model(w)
+    model = decode_model(w, fp32_rows=not args.separate_calls)
     achieved = model["hbm_bytes"] / dec_s
     rec = {
         "metric": f"query rows/sec of HAD decode against a {w.n_k}-key cache; % of HBM roofline",
@@ -241,11 +253,14 @@ def bench_decode(args, w):
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_k": w.n_k,
                    "n_q": w.n_q, "dim": w.dim, "topn": w.topn, "causal": w.causal,
                    "v_dtype": w.v_dtype, "scale": w.scale,
-                   "step": "had_pack(new rows' Q) + had_decode (3 launches)"},
+                   "step": ("had_pack(new rows' Q) + had_decode (4 launches)" if args.separate_calls
+                            else "had_decode_forward (3 launches; the new rows' sign words are built "
+                                 "inside the first)")},
         "decode_us": dec_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "had_decode (dec_hist, dec_gather, dec_reduce)",
+                     "kernel": "had_decode%s (dec_hist, dec_gather, dec_reduce)"
+                               % ("" if args.separate_calls else "_forward"),
                      "work_per_launch": {k2: float(v2) for k2, v2 in model.items()}},
     }
     if not args.no_cpu_baseline:
@@ -268,7 +283,8 @@ def main():
                     help="time only had_attention launches (for profiling runs)")
     ap.add_argument("--separate-calls", action="store_true",
                     help="step = had_pack(Q), had_pack(K), had_attention (5 launches) "
-                         "instead of had_forward (2 launches)")
+                         "instead of had_forward (2 launches); for a decode workload, "
+                         "had_pack(new rows) + had_decode instead of had_decode_forward")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for HBM counter runs: 3 attention launches, then one plain "
                          "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")

@@ -295,6 +295,31 @@ had_status had_decode(const uint32_t* qbits, const uint32_t* kbits,
                       float* out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * had_decode_forward - had_decode with the new rows given as float32: the
+ * step "sign-binarize the new queries, then attend against the cache" in the
+ * launches of had_decode (the first launch builds the rows' sign words).
+ *
+ * Defined by: the passages cited for had_pack (the sign of a standardized
+ * row; no sigma is formed, since dividing by it changes no sign) and for
+ * had_decode.
+ *
+ *  q      [B,H,n_q,d] float32 new rows, contiguous, 4-byte aligned.  Bit c of
+ *         word w of a row is [q_{32w+c} < 0], pad bits 0: exactly the words
+ *         had_pack writes, so the result equals had_pack followed by
+ *         had_decode, bit for bit.  A NaN element gives a 0 bit and is not
+ *         reported (call had_pack to have NaN input flagged).
+ *  Every other argument, the workspace (the same had_decode_workspace_bytes;
+ *  it also holds the rows' words), the precision and the errors are those of
+ *  had_decode.
+ */
+had_status had_decode_forward(const float* q, const uint32_t* kbits,
+                              const void* v, had_dtype v_dtype,
+                              had_decode_shape s, int64_t q_pos0,
+                              int64_t topn, float scale, int causal,
+                              float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* had_status_string(had_status st);
 

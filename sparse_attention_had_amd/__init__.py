@@ -119,6 +119,9 @@ def load_library():
         lib.had_decode.argtypes = [P, P, P, I, DecodeShape, I64, I64, ctypes.c_float, I, P, P,
                                    ctypes.c_size_t, P]
         lib.had_decode.restype = I
+        lib.had_decode_forward.argtypes = [P, P, P, I, DecodeShape, I64, I64, ctypes.c_float, I, P, P,
+                                   ctypes.c_size_t, P]
+        lib.had_decode_forward.restype = I
         lib.had_status_string.argtypes = [I]
         lib.had_status_string.restype = ctypes.c_char_p
         lib.had_last_error.argtypes = []
@@ -334,15 +337,36 @@ def decode(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int,
     int32, v [B,H,k_stride,d] float32 or bfloat16; the first n_k cache rows are
     valid (default: all).  Returns out [B,H,n_q,d] float32.
     """
+    return _decode_call("had_decode", qbits, kbits, v, topn, scale, q_pos0, causal, n_k, out,
+                        workspace, stream)
+
+
+def decode_forward(q: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int, scale: float,
+                   q_pos0: int = 0, causal: bool = True, *, n_k: int | None = None,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """had_decode_forward: as decode(), with the new rows q [B,H,n_q,d] float32
+    (their sign words are built inside the first launch; equal to pack + decode)."""
+    return _decode_call("had_decode_forward", q, kbits, v, topn, scale, q_pos0, causal, n_k, out,
+                        workspace, stream)
+
+
+def _decode_call(name, qarg, kbits, v, topn, scale, q_pos0, causal, n_k, out, workspace, stream):
     lib = load_library()
-    _need_cuda(qbits, "qbits", torch.int32)
     _need_cuda(kbits, "kbits", torch.int32)
     _need_cuda(v, "v")
     B, H, ks, d = _shape4(v, "v")
     W = words_per_row(d)
-    nq = qbits.shape[2]
-    if qbits.dim() != 4 or tuple(qbits.shape) != (B, H, nq, W):
-        raise ValueError("qbits must have shape [B, H, n_q, ceil(d/32)]")
+    if name == "had_decode":
+        _need_cuda(qarg, "qbits", torch.int32)
+        nq = qarg.shape[2]
+        if qarg.dim() != 4 or tuple(qarg.shape) != (B, H, nq, W):
+            raise ValueError("qbits must have shape [B, H, n_q, ceil(d/32)]")
+    else:
+        _need_cuda(qarg, "q", torch.float32)
+        nq = qarg.shape[2]
+        if qarg.dim() != 4 or tuple(qarg.shape) != (B, H, nq, d):
+            raise ValueError("q must have shape [B, H, n_q, d]")
     if tuple(kbits.shape) != (B, H, ks, W):
         raise ValueError("kbits must have shape [B, H, k_stride, ceil(d/32)]")
     nk = ks if n_k is None else int(n_k)
@@ -357,8 +381,8 @@ def decode(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, topn: int,
     if workspace is None:
         workspace = _workspace(v.device, sh, need)
     _need_cuda(workspace, "workspace")
-    _check("had_decode", lib.had_decode(
-        qbits.data_ptr(), kbits.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(q_pos0),
+    _check(name, getattr(lib, name)(
+        qarg.data_ptr(), kbits.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(q_pos0),
         int(topn), float(scale), int(bool(causal)), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), sh))
     return out

@@ -47,7 +47,8 @@ constexpr int kDecMinKeysPerSplit = 256;
 constexpr int kDecMaxKeysPerSplit = 2048;
 
 struct DecArgs {
-  const uint32_t* qbits;  // [BH, nq, W]
+  const uint32_t* qbits;  // [BH, nq, W] (had_decode_forward: written by the histogram launch)
+  const float* qf;        // [BH, nq, d] float32 new rows (had_decode_forward), else null
   const uint32_t* kbits;  // [BH, kstride, W]
   const void* v;          // [BH, kstride, d]
   int vf32;
@@ -97,9 +98,13 @@ __device__ inline void load_key_words(const uint32_t* krow, uint32_t* kw) {
 }
 
 // ---- 1. logits and per-split histograms -------------------------------------
-template <int W, bool kKVec>
+// kQF: the new rows arrive as float32 (had_decode_forward); each work-group
+// builds their sign words itself (bit c of word w is [x_{32w+c} < 0], pad bits
+// 0, as had_pack), and the split-0 work-groups store them for the gather.
+template <int W, bool kKVec, bool kQF>
 __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   __shared__ uint32_t hl[kDecQBatch * (HAD_MAX_DIM + 1)];
+  __shared__ uint32_t qs[kQF ? kDecQBatch * W : 1];
   const int nqb = (a.nq + kDecQBatch - 1) / kDecQBatch;
   const int64_t bid = blockIdx.x;
   const int s = static_cast<int>(bid % a.splits);
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   const int nb = a.d + 1;
   const int k0 = s * a.keys_per_split;
   const int k1 = min(a.nk, k0 + a.keys_per_split);
-  const uint32_t* qrow = a.qbits + (bh * a.nq + q0) * W;
+  const uint32_t* qrow = kQF ? qs : a.qbits + (bh * a.nq + q0) * W;
   constexpr int kU = 4;  // keys per thread in flight
   uint32_t kw[kU][W];
   int j[kU];
@@ -123,6 +128,23 @@ __global__ __launch_bounds__(kDecThreads) void dec_hist_kernel(DecArgs a) {
   };
   load(k0);  // the first keys are in flight while the histogram is cleared
   for (int t = threadIdx.x; t < nqh * nb; t += kDecThreads) hl[t] = 0u;
+  if constexpr (kQF) {
+    // wave w packs rows w, w + 4, ...: one ballot per 64 elements = 2 words
+    const int lane = threadIdx.x & 63;
+    for (int q = static_cast<int>(threadIdx.x >> 6); q < nqh; q += kDecThreads / 64) {
+      const float* xr = a.qf + (bh * a.nq + q0 + q) * static_cast<int64_t>(a.d);
+#pragma unroll
+      for (int w2 = 0; w2 < W; w2 += 2) {
+        const int e = 32 * w2 + lane;
+        const uint64_t m = __ballot(e < a.d && xr[e < a.d ? e : 0] < 0.0f);
+        if (lane < 2 && w2 + lane < W) {
+          const uint32_t word = static_cast<uint32_t>(m >> (32 * lane));
+          qs[q * W + w2 + lane] = word;
+          if (s == 0) const_cast<uint32_t*>(a.qbits)[(bh * a.nq + q0 + q) * W + w2 + lane] = word;
+        }
+      }
+    }
+  }
   __syncthreads();
   for (int jb = k0; jb < k1; jb += kU * kDecThreads) {
     if (jb != k0) load(jb);
@@ -520,7 +542,7 @@ struct DecPlan {
   int splits, keys_per_split;
   bool bins;
   int64_t nkp;
-  size_t off_hist, off_stats, off_part, off_bins, bytes;
+  size_t off_hist, off_stats, off_part, off_bins, off_qbits, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -554,6 +576,8 @@ DecPlan plan_for(const had_decode_shape& s) {
   off = align256(off + static_cast<size_t>(rows) * p.splits * s.dim * sizeof(float));
   p.off_bins = off;
   if (p.bins) off = align256(off + bins_bytes);
+  p.off_qbits = off;  // the new rows' sign words (had_decode_forward)
+  off = align256(off + static_cast<size_t>(rows) * words_per_row(s.dim) * sizeof(uint32_t));
   p.bytes = off;
   return p;
 }
@@ -571,15 +595,21 @@ had_status check_decode_shape(const had_decode_shape& s) {
   return HAD_OK;
 }
 
-template <int W>
-void launch_hist(const DecArgs& a, bool kvec, int64_t blocks, hipStream_t st) {
+template <int W, bool kQF>
+void launch_hist_q(const DecArgs& a, bool kvec, int64_t blocks, hipStream_t st) {
   if constexpr (W % 2 == 0) {
     if (kvec) {
-      dec_hist_kernel<W, true><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+      dec_hist_kernel<W, true, kQF><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
       return;
     }
   }
-  dec_hist_kernel<W, false><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+  dec_hist_kernel<W, false, kQF><<<static_cast<unsigned>(blocks), kDecThreads, 0, st>>>(a);
+}
+
+template <int W>
+void launch_hist(const DecArgs& a, bool kvec, int64_t blocks, hipStream_t st) {
+  if (a.qf != nullptr) launch_hist_q<W, true>(a, kvec, blocks, st);
+  else launch_hist_q<W, false>(a, kvec, blocks, st);
 }
 
 template <int W, bool kKVec, bool kBins>
@@ -617,32 +647,39 @@ extern "C" size_t had_decode_workspace_bytes(had_decode_shape s) {
   return plan_for(s).bytes;
 }
 
-extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, const void* v,
-                                 had_dtype v_dtype, had_decode_shape s, int64_t q_pos0,
-                                 int64_t topn, float scale, int causal, float* out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
+namespace had {
+namespace {
+
+// had_decode (qbits given) and had_decode_forward (float32 rows qf, whose
+// sign words the histogram launch builds into the workspace).
+had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, const uint32_t* kbits,
+                       const void* v, had_dtype v_dtype, had_decode_shape s, int64_t q_pos0,
+                       int64_t topn, float scale, int causal, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   had_status st = check_decode_shape(s);
   if (st != HAD_OK) return st;
-  if (qbits == nullptr || kbits == nullptr || v == nullptr || out == nullptr)
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: null qbits, kbits, v or out");
-  if (!aligned(qbits, 4) || !aligned(kbits, 4) || !aligned(v, 4) || !aligned(out, 4))
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: qbits, kbits, v and out must be 4-byte aligned");
-  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, "had_decode: unknown v_dtype");
-  if (topn < 1) return fail(HAD_ERR_INVALID_ARG, "had_decode: topn must be >= 1");
+  const void* q = qf != nullptr ? static_cast<const void*>(qf) : static_cast<const void*>(qbits);
+  if (q == nullptr || kbits == nullptr || v == nullptr || out == nullptr)
+    return failf(HAD_ERR_INVALID_ARG, "%s: null queries, kbits, v or out", who);
+  if (!aligned(q, 4) || !aligned(kbits, 4) || !aligned(v, 4) || !aligned(out, 4))
+    return failf(HAD_ERR_INVALID_ARG, "%s: queries, kbits, v and out must be 4-byte aligned", who);
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", who);
+  if (topn < 1) return failf(HAD_ERR_INVALID_ARG, "%s: topn must be >= 1", who);
   if (!std::isfinite(scale) || !(scale > 0.0f))
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: scale must be finite and > 0");
-  if (causal != 0 && causal != 1) return fail(HAD_ERR_INVALID_ARG, "had_decode: causal must be 0 or 1");
+    return failf(HAD_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
+  if (causal != 0 && causal != 1) return failf(HAD_ERR_INVALID_ARG, "%s: causal must be 0 or 1", who);
   if (q_pos0 < 0 || q_pos0 > HAD_MAX_DECODE_KEYS)
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: q_pos0 must be in [0, HAD_MAX_DECODE_KEYS]");
+    return failf(HAD_ERR_INVALID_ARG, "%s: q_pos0 must be in [0, HAD_MAX_DECODE_KEYS]", who);
   const DecPlan p = plan_for(s);
   if (workspace == nullptr || !aligned(workspace, 256))
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: workspace must be non-null and 256-byte aligned");
+    return failf(HAD_ERR_INVALID_ARG, "%s: workspace must be non-null and 256-byte aligned", who);
   if (workspace_bytes < p.bytes)
-    return fail(HAD_ERR_INVALID_ARG, "had_decode: workspace smaller than had_decode_workspace_bytes()");
+    return failf(HAD_ERR_INVALID_ARG, "%s: workspace smaller than had_decode_workspace_bytes()", who);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   DecArgs a{};
-  a.qbits = qbits;
+  // the forward call builds the rows' words into the workspace
+  a.qbits = qf != nullptr ? reinterpret_cast<const uint32_t*>(ws + p.off_qbits) : qbits;
+  a.qf = qf;
   a.kbits = kbits;
   a.v = v;
   a.vf32 = v_dtype == HAD_F32;
@@ -670,7 +707,7 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
   const int64_t gather_blocks = a.bh_total * s.n_q * p.splits;
   const int64_t rows = a.bh_total * s.n_q;
   if (hist_blocks > 0x7FFFFFFF || gather_blocks > 0x7FFFFFFF || rows > 0x7FFFFFFF)
-    return fail(HAD_ERR_UNSUPPORTED, "had_decode: grid too large");
+    return failf(HAD_ERR_UNSUPPORTED, "%s: grid too large", who);
   // key rows of W words load as 16-byte (W % 4 == 0) or 8-byte (W % 2 == 0)
   // vectors from an aligned base
   const bool kvec = aligned(kbits, a.W % 4 == 0 ? 16 : 8);
@@ -684,7 +721,7 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
     case 7: launch_hist<7>(a, kvec, hist_blocks, hs); break;
     default: launch_hist<8>(a, kvec, hist_blocks, hs); break;
   }
-  if ((st = check_launch("had_decode")) != HAD_OK) return st;
+  if ((st = check_launch(who)) != HAD_OK) return st;
   // 16-byte row slices need 16-byte aligned rows
   const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
   switch (a.W) {
@@ -697,7 +734,30 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
     case 7: launch_gather<7>(a, vec, kvec, gather_blocks, hs); break;
     default: launch_gather<8>(a, vec, kvec, gather_blocks, hs); break;
   }
-  if ((st = check_launch("had_decode")) != HAD_OK) return st;
+  if ((st = check_launch(who)) != HAD_OK) return st;
   dec_reduce_kernel<<<static_cast<unsigned>(rows), (a.d + 63) / 64 * 64, 0, hs>>>(a);
-  return check_launch("had_decode");
+  return check_launch(who);
+}
+
+}  // namespace
+}  // namespace had
+
+extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, const void* v,
+                                 had_dtype v_dtype, had_decode_shape s, int64_t q_pos0,
+                                 int64_t topn, float scale, int causal, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (qbits == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_decode: null qbits");
+  return decode_impl("had_decode", qbits, nullptr, kbits, v, v_dtype, s, q_pos0, topn, scale, causal, out,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" had_status had_decode_forward(const float* q, const uint32_t* kbits, const void* v,
+                                         had_dtype v_dtype, had_decode_shape s, int64_t q_pos0,
+                                         int64_t topn, float scale, int causal, float* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (q == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_decode_forward: null q");
+  return decode_impl("had_decode_forward", nullptr, q, kbits, v, v_dtype, s, q_pos0, topn, scale, causal,
+                     out, workspace, workspace_bytes, stream);
 }

@@ -164,6 +164,16 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(s=D(1, 2, 4, 1000, (1 << 22) + 1, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
 
+    def fwd(q=A16, k=A16B, wsb=ws_bytes, s=ok):
+        return lib.had_decode_forward(q, k, A16C, 1, s, 996, 8, 0.125, 1, 0x40000, 0x100000, wsb, None)
+
+    assert fwd(q=None) == INVALID
+    assert fwd(q=A16 + 2) == INVALID
+    assert fwd(k=None) == INVALID
+    assert fwd(wsb=ws_bytes - 1) == INVALID
+    assert fwd(s=D(1, 2, 65, 1000, 1024, 64)) == UNSUPPORTED
+    assert lib.had_last_error() != b""
+
 
 def test_topn_mass_rejects_bad_arguments(lib):
     s = Shape(2, 3, 100, 64)

@@ -1,5 +1,7 @@
 """GPU parity of had_decode (new query rows against a key/value cache)
-through the C ABI, against the CPU oracle's decode().
+through the C ABI, against the CPU oracle's decode(); had_decode_forward
+(float32 new rows, sign words built inside the first launch) must equal
+had_pack + had_decode bit for bit.
 
 Cache rows past n_k hold large finite garbage so that a read of an unused
 row shows up in the outputs.  Outputs must be within 1e-5 * sum(p|V|) (fp32
@@ -63,7 +65,11 @@ def test_decode_matches_oracle(case):
     v_t = (v_t.to(torch.bfloat16) if vdt == "bf16" else v_t).cuda()
     qb, _ = had.pack(q_t, with_sigma=False)
     kb, _ = had.pack(k_t, with_sigma=False)
-    out = had.decode(qb, kb, v_t, topn, scale, q_pos0=p0, causal=causal, n_k=nk).cpu().numpy()
+    out_t = had.decode(qb, kb, v_t, topn, scale, q_pos0=p0, causal=causal, n_k=nk)
+    fwd_t = had.decode_forward(q_t, kb, v_t, topn, scale, q_pos0=p0, causal=causal, n_k=nk)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, fwd_t), "decode_forward differs from pack + decode"
+    out = out_t.cpu().numpy()
     vvalid = inp["v"][:, :, :nk]
     for b in range(B):
         for h in range(H):
@@ -108,8 +114,12 @@ def test_decode_workload_sampled(name):
     del kc
     ws = torch.empty(had.decode_workspace_bytes(w.batch, w.heads, w.n_q, w.n_k, w.n_k, w.dim),
                      dtype=torch.uint8, device="cuda")
-    out = had.decode(qb, kb, v_t, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal,
-                     workspace=ws).cpu().numpy()
+    out_t = had.decode_forward(qn, kb, v_t, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal,
+                               workspace=ws)
+    ref_t = had.decode(qb, kb, v_t, w.topn, w.scale, q_pos0=w.q_pos0, causal=w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, ref_t), "decode_forward differs from pack + decode"
+    out = out_t.cpu().numpy()
     log("  gpu done")
     BH = w.batch * w.heads
     rng = np.random.default_rng(66)
