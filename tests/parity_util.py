@@ -1,5 +1,6 @@
-"""Helpers shared by the GPU parity tests (no method arithmetic here: they
-move data and call either the oracle or the GPU library)."""
+"""Helpers shared by the GPU parity tests: they move data, call the oracle or
+the GPU library, and compare (tolerances, and for the top-N mass the float64
+prefix sums that show a decision lies within rounding)."""
 
 import sys
 
@@ -47,3 +48,21 @@ def check_out(got, ref, E, v_all, v_dtype, where=""):
             f"{where}: {int(bad.sum())} outputs outside tolerance; first at {tuple(i)}: "
             f"got {got[tuple(i)]!r} want {ref[tuple(i)]!r} tol {np.broadcast_to(tol, err.shape)[tuple(i)]!r}")
     return float(err.max()) if err.size else 0.0
+
+
+def check_topn_mass(got, S, scale, mass, causal, where=""):
+    """got [rows] against oracle.topn_mass(S, scale, mass, causal); a row may
+    differ by one only where a prefix sum lies within 1e-12 of mass (a
+    decision inside the rounding of the float64 sums)."""
+    want = oracle.topn_mass(S, scale, mass, causal)
+    got = np.asarray(got, dtype=np.int64)
+    n = S.shape[1]
+    for r in np.nonzero(got != want)[0]:
+        nv = oracle.visible_count(int(r), n, causal)
+        z = scale * S[r, :nv].astype(np.float64)
+        e = np.exp(z - z.max())
+        c = np.cumsum(np.sort(e / e.sum())[::-1])
+        margin = min(abs(c[want[r] - 1] - mass), abs(c[want[r] - 2] - mass) if want[r] >= 2 else 1.0)
+        assert abs(int(got[r]) - int(want[r])) == 1 and margin < 1e-12, \
+            f"{where}: mass {mass} row {r}: got {got[r]} want {want[r]}"
+

@@ -12,7 +12,7 @@ import torch
 import oracle
 import sparse_attention_had_amd as had
 from had_workloads import WORKLOADS, make_inputs, workload_inputs
-from parity_util import bits_np, check_out, log, oracle_head, to_dev
+from parity_util import bits_np, check_out, check_topn_mass, log, oracle_head, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -342,19 +342,7 @@ def test_topn_mass_matches_oracle(case):
         for b in range(B):
             for h in range(H):
                 S = oracle.logits(oracle.binarize(inp["q"][b, h]), oracle.binarize(inp["k"][b, h]))
-                want = oracle.topn_mass(S, sc, mass, causal)
-                g = got[b * H + h]
-                bad = np.nonzero(g != want)[0]
-                for r in bad:
-                    # only a decision within rounding of the float64 sums may differ
-                    nv = oracle.visible_count(int(r), n, causal)
-                    z = sc * S[r, :nv].astype(np.float64)
-                    p = np.sort(np.exp(z - z.max()) / np.exp(z - z.max()).sum())[::-1]
-                    c = np.cumsum(p)
-                    margin = min(abs(c[want[r] - 1] - mass),
-                                 abs(c[want[r] - 2] - mass) if want[r] >= 2 else 1.0)
-                    assert abs(int(g[r]) - int(want[r])) == 1 and margin < 1e-12, \
-                        f"mass {mass} slice {(b, h)} row {r}: got {g[r]} want {want[r]}"
+                check_topn_mass(got[b * H + h], S, sc, mass, causal, where=f"slice {(b, h)}")
 
 
 # ------------------------------------------------------- sigma calibration

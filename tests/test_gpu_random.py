@@ -1,11 +1,14 @@
 """GPU: a seeded sweep of random small shapes through every compute call of
-the C ABI (had_forward, had_attention, had_select, had_pack, had_decode),
-each compared with the oracle: packed bits and kept indices bit-exact, sigma
-within 1e-6 relative, outputs within the fp32 / bf16 tolerances.  The shapes
-mix feature counts around the 32-bit word boundaries (1 ... 256), sequence
-lengths around the 16-key chunk and 128-row tile boundaries, N from 1 to
-beyond n, both masks, both V types, sharp and flat softmax scales and both
-noise families.  Every case prints its parameters first.
+the C ABI (had_forward, had_attention, had_select, had_logits, had_pack,
+had_decode, had_decode_forward, had_topn_mass), each compared with the
+oracle: packed bits, logits and kept indices bit-exact, sigma within 1e-6
+relative, outputs within the fp32 / bf16 tolerances, top-N mass exact up to
+decisions within rounding; had_decode_forward equal to had_pack + had_decode
+bit for bit.  The shapes mix feature counts around the 32-bit word
+boundaries (1 ... 256), sequence lengths around the 16-key chunk and 128-row
+tile boundaries, N from 1 to beyond n, both masks, both V types, sharp and
+flat softmax scales and both noise families.  Every case prints its
+parameters first.
 """
 
 import numpy as np
@@ -15,7 +18,7 @@ import torch
 import oracle
 import sparse_attention_had_amd as had
 from had_workloads import make_inputs
-from parity_util import bits_np, check_out, log
+from parity_util import bits_np, check_out, check_topn_mass, log
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +46,16 @@ def _cases(seed, count):
         scale = float(rng.choice([0.01, 0.1, 1 / np.sqrt(d), 0.5, 2.0]))
         noise = str(rng.choice(["normal", "t3"]))
         nq = int(min(n, rng.integers(1, 5)))
-        out.append((B, H, n, d, topn, causal, vdt, scale, noise, nq, int(rng.integers(0, 1 << 30))))
+        seed = int(rng.integers(0, 1 << 30))
+        mass = float(rng.choice([0.5, 0.9, 0.99]))
+        out.append((B, H, n, d, topn, causal, vdt, scale, noise, nq, seed, mass))
     return out
 
 
 @pytest.mark.parametrize("block", range(6))
 def test_random_shapes_against_the_oracle(block):
     for case in _cases(7000 + block, 50):
-        B, H, n, d, topn, causal, vdt, scale, noise, nq, seed = case
+        B, H, n, d, topn, causal, vdt, scale, noise, nq, seed, mass = case
         log(f"random {case}")
         inp = make_inputs(B, H, n, d, rank=min(4, d), noise=noise, seed=seed, v_dtype=vdt)
         q = torch.from_numpy(inp["q"]).cuda()
@@ -63,9 +68,14 @@ def test_random_shapes_against_the_oracle(block):
         p0 = n - nq
         qn = np.ascontiguousarray(inp["q"][:, :, p0:])
         qnb, _ = had.pack(torch.from_numpy(qn).cuda(), with_sigma=False)
-        od = had.decode(qnb, kb, v, topn, scale, q_pos0=p0, causal=causal).cpu().numpy()
+        odt = had.decode(qnb, kb, v, topn, scale, q_pos0=p0, causal=causal)
+        odf = had.decode_forward(torch.from_numpy(qn).cuda(), kb, v, topn, scale, q_pos0=p0, causal=causal)
+        lg = had.logits(qb, kb, d).cpu().numpy()
+        nm = had.topn_mass(qb, kb, d, scale, mass, causal).cpu().numpy()
         torch.cuda.synchronize()
         assert torch.equal(out, out2), f"{case}: had_forward and had_attention differ"
+        assert torch.equal(odt, odf), f"{case}: had_decode_forward and had_pack + had_decode differ"
+        od = odt.cpu().numpy()
         assert np.array_equal(bits_np(qb), oracle.pack_bits(oracle.binarize(inp["q"]))), f"{case}: bits"
         ref_sigma = oracle.sigma(inp["q"])
         assert abs(float(sq.item()) - ref_sigma) <= 1e-6 * ref_sigma, f"{case}: sigma"
@@ -75,6 +85,9 @@ def test_random_shapes_against_the_oracle(block):
                 r = oracle.forward(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], topn, scale,
                                    causal=causal)
                 assert np.array_equal(idx[b * H + h].astype(np.int64), r["idx"]), f"{case}: select {(b, h)}"
+                S = oracle.logits(oracle.binarize(inp["q"][b, h]), oracle.binarize(inp["k"][b, h]))
+                assert np.array_equal(lg[b * H + h].astype(np.int64), S.astype(np.int64)), f"{case}: logits {(b, h)}"
+                check_topn_mass(nm[b * H + h], S, float(np.float32(scale)), mass, causal, where=f"{case} {(b, h)}")
                 check_out(o[b, h], r["out"], r["E"], inp["v"], vdt, where=f"{case} slice {(b, h)}")
                 rd = oracle.decode(qn[b, h], inp["k"][b, h], inp["v"][b, h], topn, scale,
                                    q_pos0=p0, causal=causal)
