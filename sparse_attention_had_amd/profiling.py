@@ -3,6 +3,8 @@
     python -m sparse_attention_had_amd.profiling stats  <kernel_stats.csv> <out.md> --cmd "..."
     python -m sparse_attention_had_amd.profiling traffic --fetch <fetch csv> --write <write csv> \
         --workload NAME --out profiles/traffic_had_attention_NAME.json --cmd "..."
+    python -m sparse_attention_had_amd.profiling counters --csv <pass 1 csv> --cmd "..." \
+        [--csv <pass 2 csv> --cmd "..."] --kernel had_attn_kernel --workload NAME --out <out.md>
 
 The traffic run profiles `bench.py --traffic-probe`, which launches the
 attention kernel a few times and then one plain device-to-device copy of
@@ -98,6 +100,35 @@ def stats(stats_csv, out_md, cmd, title):
     print("\n".join(lines))
 
 
+def counters(csvs, cmds, kernel, workload, out_md):
+    """SQ counters of one kernel, one rocprofv3 --pmc pass per CSV: the mean
+    over its dispatches of each counter (summed over the counter's instances
+    within a dispatch), and that mean divided by SQ_WAVES (waves per dispatch)."""
+    means, ndisp = {}, {}
+    for path in csvs:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for name in sorted({c for d in per.values() for c in d}):
+            vals = [d[name] for d in per.values() if name in d]
+            means[name] = statistics.fmean(vals)
+            ndisp[name] = len(vals)
+    waves = means.get("SQ_WAVES")
+    lines = [f"# SQ counters, `{kernel}`, {workload}", "",
+             f"Kernel sources: sha256 prefix `{source_hash()}` of `sparse_attention_had_amd/csrc`.", "",
+             "Commands (one counter pass each):", "", "```"] + list(cmds) + ["```", "",
+             "| counter | mean per dispatch | per wave | dispatches |", "|---|---|---|---|"]
+    for name, v in means.items():
+        pw = f"{v / waves:.4g}" if waves else "—"
+        lines.append(f"| `{name}` | {v:.6g} | {pw} | {ndisp[name]} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -112,9 +143,17 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", action="append", required=True)
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--kernel", default="had_attn_kernel")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
         stats(a.csv, a.out, a.cmd, a.title)
+    elif a.cmd_name == "counters":
+        counters(a.csv, a.cmd, a.kernel, a.workload, a.out)
     else:
         traffic(a.fetch, a.write, a.workload, a.out, a.cmd)
 
