@@ -199,27 +199,38 @@ struct RowStats {
   uint32_t quota;
 };
 
+template <int W>
 __device__ RowStats row_stats(const DecArgs& a, int64_t bhq, int q, int s_self, bool write_stats) {
   const int lane = threadIdx.x & 63;
   const int nb = a.d + 1;
   const uint32_t* hp = a.hist + bhq * a.splits * nb;
   const int Ni = min(a.topn, visible_keys(a, q));
-  constexpr int kR = (HAD_MAX_DIM + 1 + 63) / 64;
+  constexpr int kR = (32 * W + 1 + 63) / 64;  // 64-bin rows of the d + 1 <= 32W + 1 bins
   uint32_t cnt[kR];
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int b = 64 * r + lane;
-    uint32_t c = 0;
-    if (b < nb) {
-      for (int s0 = 0; s0 < a.splits; s0 += 8) {  // 8 loads in flight
-        uint32_t t[8];
+  for (int r = 0; r < kR; ++r) cnt[r] = 0u;
+  // up to three rows of 8 splits in flight at once: one round trip per 8
+  // splits for d < 192, two above (24 loads keep the gather at 8 waves per SIMD)
+  constexpr int kRB = kR < 3 ? kR : 3;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = s0 + u < a.splits ? hp[(s0 + u) * nb + b] : 0u;
+  for (int r0 = 0; r0 < kR; r0 += kRB) {
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      uint32_t t[kRB][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c += t[u];
+      for (int r = 0; r < kRB; ++r) {
+        const int b = 64 * (r0 + r) + lane;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          t[r][u] = (r0 + r < kR && b < nb && s0 + u < a.splits) ? hp[(s0 + u) * nb + b] : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        if (r0 + r < kR) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cnt[r0 + r] += t[r][u];
+        }
       }
     }
-    cnt[r] = c;
   }
   int T = -1, hmin = -1;
   uint32_t below = 0, run = 0;
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_gather_kernel(DecArgs a) {
   for (int t = tid; t <= d; t += kDecThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
   // the row's threshold and this split's tie quota (wave 0), shared through LDS
   if (wid == 0) {
-    const RowStats r0 = row_stats(a, bhq, q, s, s == 0);
+    const RowStats r0 = row_stats<W>(a, bhq, q, s, s == 0);
     if (lane == 0) rs_sh = r0;
   }
   if constexpr (!kBins) {
