@@ -40,8 +40,9 @@ CASES = [
     (1, 1, 2, 50, 50, 64, 80, 48, True, "bf16", 0.125),       # N > visible
     (1, 1, 2, 100, 100, 64, 10, 500, True, "f32", 0.3),       # every key visible
     (3, 1, 17, 777, 800, 33, 20, 760, False, "bf16", 0.25),   # two row batches
-    (1, 16, 64, 1000, 1000, 64, 100, 936, True, "bf16", 0.125),   # 2 splits of 512 keys, recomputed
-    (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 32 splits of 512 keys, bins
+    (1, 8, 64, 1000, 1000, 64, 100, 936, True, "bf16", 0.125),    # 2 splits of 512 keys, recomputed
+    (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 16 splits of 1024 keys, bins
+    (1, 32, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 32 splits of 512 keys, bins
 ]
 
 
@@ -97,7 +98,7 @@ def test_decode_is_deterministic_and_reuses_its_workspace():
 @pytest.mark.parametrize("name", sorted(DECODE_WORKLOADS))
 def test_decode_workload_sampled(name):
     """The decode workloads at full size, in the launch configuration bench.py
-    times (the work split for 128 rows x 16384 keys is 16 splits of 1024 keys
+    times (the work split for 128 rows x 16384 keys is 8 splits of 2048 keys
     with stored distance bins; for 2048 rows, 8 splits of 2048 keys with the
     distances recomputed from the key words), checked against the oracle on
     sampled (batch, head) slices, all new rows of each."""
