@@ -36,7 +36,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "query rows/sec of HAD attention at n=1024,N=256; % of HBM/VALU roofline"
+METRIC = "query rows/sec of HAD attention at n={n},N={topn}; % of HBM/VALU roofline"  # headline: n=1024, N=256
 VALU_PEAK = 256 * 4 * 16 * 2.4e9  # int32 lane-ops/s
 HBM_PEAK = 8.0e12  # B/s
 
@@ -382,7 +382,7 @@ def main():
     achieved = model["lane_ops"] / attn_avg_s
     traffic = traffic_for(name)
     rec = {
-        "metric": METRIC,
+        "metric": METRIC.format(n=w.seq, topn=w.topn),
         "value": rows / (ms_step / 1e3),
         "unit": "query rows/s",
         "n_gpus": 1,

@@ -1,4 +1,7 @@
-"""Build libhad.so (gfx950) in-tree with hipcc.
+"""Build libhad.so (gfx950) in-tree with hipcc, and libhad_popcount.so: the
+same library with the attention kernel's logit stage on the vector ALU (XOR +
+popcount) instead of the int8 matrix cores, kept to measure that choice
+(load it with HAD_LIBRARY=.../libhad_popcount.so).
 
 Usage: python -m sparse_attention_had_amd.build   (or __graft_entry__.build())
 """
@@ -15,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhad.so")
+LIB_POPCOUNT = os.path.join(PKG, "libhad_popcount.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip"]
@@ -37,28 +41,39 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, tag, defs = job
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libhad.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950, link libhad.so and libhad_popcount.so;
+    returns the path of libhad.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = [(src, "", []) for src in SOURCES]
+    jobs.append(("had_attention.hip", "_popcount", ["-DHAD_LOGITS_POPCOUNT=1"]))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    main_objs = objs[:len(SOURCES)]
+    _link(main_objs, LIB)
+    pop_objs = [objs[-1] if src == "had_attention.hip" else o for src, o in zip(SOURCES, main_objs)]
+    _link(pop_objs, LIB_POPCOUNT)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LIB_POPCOUNT}")
     return LIB
 
 

@@ -61,6 +61,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// Build option: the logit tiles from XOR + popcount on the vector ALU instead
+// of the int8 matrix cores (the same tile values, so the same results; the
+// K-only sweeps then take their plain loop).  It builds libhad_popcount.so,
+// the comparison that keeps the matrix-core stage in libhad.so.
+#ifndef HAD_LOGITS_POPCOUNT
+#define HAD_LOGITS_POPCOUNT 0
+#endif
+constexpr bool kPopcountLogits = HAD_LOGITS_POPCOUNT != 0;
+
 // weight table: d+1 weights, then a zero slot in the last bank of its
 // 64-dword row, away from the low entries every row uses
 constexpr int kLutEntries = 320;
@@ -288,7 +297,9 @@ void had_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < W; ++w) qwords[w] = qvalid ? ~qrow[w] : ~0u;  // complement: the product is -s
   }
+  int kmag = 0;  // k of the tile entries cin + k*u (the popcount build uses it)
   auto make_q = [&](uint32_t pos, uint32_t flip) {
+    kmag = static_cast<int>(pos);
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const uint32_t b16 = (qwords[w] >> (16 * half)) & 0xFFFFu;
@@ -327,11 +338,29 @@ void had_attn_kernel(AttnArgs a) {
     return acc;
   };
   auto logits_tile = [&](int buf, int c, uint32_t cin) {
-    uint32_t words[W];
-    v4i kv[W];
-    k_words(buf, c, words);
-    k_expand(words, kv);
-    return k_product(kv, cin);
+    if constexpr (kPopcountLogits) {
+      // u = 2h - d with h = sum over words of popcount(q XOR k) (pad bits are
+      // 0 in both), for the keys of this lane's registers (MFMA rows m)
+      const uint32_t* kb = reinterpret_cast<const uint32_t*>(lds + kKbOff + buf * C::kKbBuf) + c * 32 * W;
+      const uint32_t base = cin - static_cast<uint32_t>(kmag * d);
+      const uint32_t k2 = static_cast<uint32_t>(2 * kmag);
+      v16i t;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = ((i >> 2) << 3) | (half << 2) | (i & 3);
+        uint32_t h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h = __builtin_popcount(~qwords[w] ^ kb[m * W + w]) + h;
+        t[i] = static_cast<int>(base + k2 * h);
+      }
+      return t;
+    } else {
+      uint32_t words[W];
+      v4i kv[W];
+      k_words(buf, c, words);
+      k_expand(words, kv);
+      return k_product(kv, cin);
+    }
   };
 
   // K-only sweep over all chunks this wave sees, kCH1 chunks per group;
@@ -352,7 +381,7 @@ void had_attn_kernel(AttnArgs a) {
       const int g0 = gi * C::kCH1;
       const int cend = min(C::kCH1, wchunks - g0);
       // every lane sees every key of the group: keys up to half*Hh + 16*(g0 + kCH1)
-      const bool whole = cend == C::kCH1 && __all(lim >= half * Hh + 16 * (g0 + C::kCH1));
+      const bool whole = !kPopcountLogits && cend == C::kCH1 && __all(lim >= half * Hh + 16 * (g0 + C::kCH1));
       if (whole) {
         // A full group, software-pipelined and straight-line: step c takes
         // the products of chunk c, expands the key bytes of chunk c + 2,

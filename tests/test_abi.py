@@ -40,6 +40,16 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, fn), fn
 
 
+def test_popcount_logit_build_exports_every_declared_symbol():
+    """libhad_popcount.so (the build with the vector-ALU logit stage) is the
+    same C ABI."""
+    path = os.path.join(ROOT, "sparse_attention_had_amd", "libhad_popcount.so")
+    assert os.path.exists(path), "libhad_popcount.so not built"
+    alt = ctypes.CDLL(path)
+    for fn in declared_functions():
+        assert hasattr(alt, fn), fn
+
+
 def test_words_per_row_and_status_strings(lib):
     assert [lib.had_words_per_row(d) for d in (1, 31, 32, 33, 64, 128, 256)] == [1, 1, 1, 2, 2, 4, 8]
     assert lib.had_status_string(0) == b"HAD_OK"
