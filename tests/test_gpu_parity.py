@@ -187,6 +187,8 @@ ATTN_CASES = [
     (2, 2, 177, 32, 20, True, "bf16", 0.2),    # d = 32: one word per row
     (1, 2, 160, 96, 30, False, "bf16", 0.1),   # d = 96: three words per row
     (1, 1, 90, 256, 40, True, "f32", 1 / 16),  # fp32 V at d = 256
+    (1, 1, 100, 64, 16, False, "f32", 60.0),   # weights past the first bin underflow to 0
+    (1, 2, 150, 128, 30, True, "bf16", 60.0),
 ]
 
 
