@@ -1,0 +1,90 @@
+"""CPU: the host logic of bench.py.  The work models that turn a measured
+launch time into a roofline fraction are checked against counts written out
+by hand for the headline workload and against enumeration over rows on small
+shapes; the HBM traffic record is used only while the kernel sources are the
+ones it was taken on; the headline metric string is the one its numbers are
+quoted under; more than one GPU is refused with a message.
+"""
+
+import os
+import subprocess
+import sys
+import types
+
+import pytest
+
+import bench
+from had_workloads import DECODE_WORKLOADS, WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_headline_work_model_by_hand():
+    # 8 x 12 slices, n = 1024, d = 64 (W = 2 words), N = 256, bf16 V, not causal
+    m = bench.work_model(WORKLOADS["t5-base-n1024"])
+    slices, n, d, N = 96, 1024, 64, 256
+    assert m["visible_pairs"] == slices * n * n == 100_663_296
+    assert m["kept"] == slices * n * N == 25_165_824
+    # XOR + popcount per word (2 x 2) and histogram + compaction (2) per pair,
+    # weight + index per kept pair (2)
+    assert m["int_ops"] == 100_663_296 * 6 + 25_165_824 * 2
+    assert m["flops"] == 2 * 25_165_824 * d
+    assert m["lane_ops"] == m["int_ops"] + m["flops"] / 4
+    # bits of Q and K (2 words each), bf16 V, fp32 out
+    assert m["hbm_bytes"] == slices * n * (2 * 2 * 4 + d * 2 + d * 4) == 39_321_600
+
+
+@pytest.mark.parametrize("n,N,causal,d,vdt", [(1, 1, False, 1, "f32"), (7, 3, True, 33, "bf16"),
+                                              (16, 20, True, 64, "f32"), (50, 8, False, 100, "bf16"),
+                                              (129, 128, True, 256, "bf16")])
+def test_work_model_against_enumeration(n, N, causal, d, vdt):
+    w = types.SimpleNamespace(batch=2, heads=3, seq=n, dim=d, topn=N, causal=causal, v_dtype=vdt)
+    W = -(-d // 32)
+    vis = kept = 0
+    for i in range(n):
+        v = i + 1 if causal else n
+        vis += v
+        kept += min(N, v)
+    m = bench.work_model(w)
+    assert m["visible_pairs"] == 6 * vis
+    assert m["kept"] == 6 * kept
+    assert m["int_ops"] == 6 * (vis * (2 * W + 2) + 2 * kept)
+    assert m["flops"] == 6 * 2 * kept * d
+    assert m["hbm_bytes"] == 6 * n * (2 * W * 4 + d * (2 if vdt == "bf16" else 4) + d * 4)
+
+
+def test_decode_model_by_hand():
+    w = DECODE_WORKLOADS["decode-n16384"]
+    # 4 x 32 slices, one new row seeing all 16384 keys, d = 128 (4 words), N = 2048, bf16 V
+    slices, nk, d, N = 128, 16384, 128, 2048
+    assert (w.batch * w.heads, w.n_k, w.dim, w.topn, w.n_q) == (slices, nk, d, N, 1)
+    key_words = slices * nk * 4 * 4
+    kept_rows = slices * N * d * 2
+    m = bench.decode_model(w, fp32_rows=True)
+    assert m["kept"] == slices * N
+    assert m["hbm_bytes"] == key_words + kept_rows + slices * (d * 4 + d * 4) == 100_794_368
+    # with packed new rows: their words instead of float32 rows
+    assert bench.decode_model(w)["hbm_bytes"] == key_words + kept_rows + slices * (4 * 4 + d * 4)
+
+
+def test_traffic_record_only_on_matching_sources(monkeypatch):
+    import sparse_attention_had_amd.profiling as prof
+
+    got = bench.traffic_for("t5-base-n1024")
+    assert got is not None and got > 0, "the committed traffic record is stale for these kernel sources"
+    monkeypatch.setattr(prof, "source_hash", lambda: "0" * 16)
+    assert bench.traffic_for("t5-base-n1024") is None
+    assert bench.traffic_for("no-such-workload") is None
+
+
+def test_headline_metric_string():
+    w = WORKLOADS["t5-base-n1024"]
+    assert bench.METRIC.format(n=w.seq, topn=w.topn) == \
+        "query rows/sec of HAD attention at n=1024,N=256; % of HBM/VALU roofline"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
