@@ -113,19 +113,21 @@ had_status had_pack(const float* x, had_shape s, uint32_t* xbits, float* sigma,
  * minibatches described for Eq. 12: Pith review, referee minor comment 6 and
  * "Assumptions & free parameters").  A had_sigma_state lives in device
  * memory; set it to zero (e.g. hipMemsetAsync) to start a calibration.
+ * Each call merges its elements with the parallel-variance update, so the
+ * state never differences large sums of squares.
  */
 typedef struct {
-  double count;  /* elements seen */
-  double sum;    /* sum of x */
-  double sum_sq; /* sum of x*x */
+  double count; /* elements seen */
+  double mean;  /* their mean */
+  double m2;    /* sum of squared deviations from the mean */
   double reserved;
 } had_sigma_state;
 
 /*
  * had_pack_calibrate - had_pack without a per-call sigma: packs x into xbits
- * and adds the element count, sum and sum of squares of x to *state (device,
- * 8-byte aligned).  Calls on one stream add in stream order, so the state is
- * the same on every run.  workspace: had_pack_workspace_bytes(s) bytes,
+ * and merges the element count, mean and squared deviations of x into *state
+ * (device, 8-byte aligned).  Calls on one stream merge in stream order, so
+ * the state is the same on every run.  workspace: had_pack_workspace_bytes(s) bytes,
  * 16-byte aligned.  Calls that may overlap need distinct workspaces and must
  * not share a state.
  */

@@ -138,10 +138,12 @@ def _check(fn: str, status: int) -> None:
         raise HadError(fn, status, name, detail)
 
 
+def _stream_of(device: torch.device, stream):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def _stream_handle(device: torch.device, stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return int(stream.cuda_stream)
+    return int(_stream_of(device, stream).cuda_stream)
 
 
 def _need_cuda(t: torch.Tensor, name: str, dtype=None):
@@ -170,11 +172,17 @@ def pack_workspace_bytes(shape) -> int:
 _ws_cache = {}
 
 
-def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor:
-    key = (device.index, stream_handle)
+def _workspace(device: torch.device, stream, nbytes: int) -> torch.Tensor:
+    """A cached workspace of at least nbytes for calls on `stream` (None: the
+    current stream).  It is allocated while that stream is current, so the
+    caching allocator orders its reuse after the stream's work; no initial
+    contents are needed by any call."""
+    s = _stream_of(device, stream)
+    key = (device.index, int(s.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 
@@ -207,7 +215,7 @@ def pack(x: torch.Tensor, *, with_sigma: bool = True, out: torch.Tensor | None =
         _need_cuda(sigma, "sigma", torch.float32)
         need = int(lib.had_pack_workspace_bytes(shape))
         if workspace is None:
-            workspace = _workspace(x.device, sh, need)
+            workspace = _workspace(x.device, stream, need)
         _need_cuda(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
         sig_ptr = sigma.data_ptr()
@@ -304,7 +312,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale:
         _need_cuda(sigma_k, "sigma_k", torch.float32)
         need = int(lib.had_forward_workspace_bytes(shape))
         if workspace is None:
-            workspace = _workspace(dev, sh, need)
+            workspace = _workspace(dev, stream, need)
         _need_cuda(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
         sq_ptr, sk_ptr, ws_ptr = sigma_q.data_ptr(), sigma_k.data_ptr(), workspace.data_ptr()
@@ -379,7 +387,7 @@ def _decode_call(name, qarg, kbits, v, topn, scale, q_pos0, causal, n_k, out, wo
     sh = _stream_handle(v.device, stream)
     need = int(lib.had_decode_workspace_bytes(shape))
     if workspace is None:
-        workspace = _workspace(v.device, sh, need)
+        workspace = _workspace(v.device, stream, need)
     _need_cuda(workspace, "workspace")
     _check(name, getattr(lib, name)(
         qarg.data_ptr(), kbits.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(q_pos0),
@@ -431,7 +439,7 @@ def pack_calibrate(x: torch.Tensor, state: torch.Tensor, *, out: torch.Tensor | 
     sh = _stream_handle(x.device, stream)
     need = int(lib.had_pack_workspace_bytes(shape))
     if workspace is None:
-        workspace = _workspace(x.device, sh, need)
+        workspace = _workspace(x.device, stream, need)
     st_ptr = None
     if dev_status is not None:
         _need_cuda(dev_status, "dev_status", torch.int32)

@@ -548,7 +548,9 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
 // 256 times a power of two (at most 2048).  The per-(row, key) distance bins
 // are kept when n_q <= W (n_q bytes per key against the 4W bytes of key
 // words they replace in the gather; with more rows the key words, shared by
-// the rows and served from L2, are cheaper) and at most 1 GiB in all.
+// the rows and served from L2, are cheaper), when every distance fits a byte
+// (d <= 255: at d = 256 a key whose signs all differ from the row's has
+// h = 256) and at most 1 GiB in all.
 struct DecPlan {
   int splits, keys_per_split;
   bool bins;
@@ -580,7 +582,7 @@ DecPlan plan_for(const had_decode_shape& s) {
   p.keys_per_split = static_cast<int>(per);
   p.nkp = splits * per;
   const size_t bins_bytes = static_cast<size_t>(rows) * static_cast<size_t>(p.nkp);
-  p.bins = s.n_q <= words_per_row(s.dim) && bins_bytes <= (static_cast<size_t>(1) << 30);
+  p.bins = s.n_q <= words_per_row(s.dim) && s.dim <= 255 && bins_bytes <= (static_cast<size_t>(1) << 30);
   size_t off = 0;
   p.off_hist = off;
   off = align256(off + static_cast<size_t>(rows) * p.splits * (s.dim + 1) * sizeof(uint32_t));

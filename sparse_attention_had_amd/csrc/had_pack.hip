@@ -26,7 +26,11 @@
 //  * One launch packs one tensor, or two tensors of the same shape (Q and K
 //    of the fused forward call): blocks [0, nb0) work on the first, the rest
 //    on the second, each exactly as a launch of its own would.
-//  * sigma: every thread sums x and x*x in float64; each wave reduces its
+//  * sigma: every thread sums y = x - c and y*y in float64, where the shift c
+//    is the tensor's first element (0 if that is not finite): the variance
+//    is the same for y as for x, and with c near the data the one-pass
+//    formula sum(y^2)/M - (sum(y)/M)^2 does not cancel away its digits when
+//    the mean is large against the spread.  Each wave reduces its
 //    lanes in a fixed order into an LDS slot and bumps an LDS counter; the
 //    wave that arrives last adds the slots in index order and stores the
 //    block's partial pair (no end-of-block barrier, so a wave that is done
@@ -126,22 +130,42 @@ __device__ inline void flag_nan(bool nan_seen, uint32_t* dev_status) {
     atomicOr(dev_status, HAD_DEV_NAN_INPUT);
 }
 
+// Shift subtracted from every element before the sigma sums: the tensor's
+// first element, or 0 when that is infinite or NaN.  Every thread of a
+// tensor reads the same value, so the sums of all blocks share it.
+__device__ inline float sigma_shift(const float* x) {
+  const float c = x[0];
+  return __builtin_isfinite(c) ? c : 0.0f;
+}
+
 // One wave: sigma from the partial pairs.
 __global__ __launch_bounds__(64) void sigma_finalize_kernel(const double2* partials, int nparts,
                                                             double count, float* sigma) {
   sigma_from_partials(partials, nparts, count, sigma);
 }
 
-// One wave: adds this call's element count, sum and sum of squares to a
-// running calibration state (calls on one stream add in stream order).
+// One wave: merges this call's elements into a running calibration state of
+// (count, mean, M2 = sum of squared deviations from the mean), in stream
+// order.  The call's own mean and M2 come from its shifted partial sums
+// (S1 = sum(x - c), S2 = sum((x - c)^2)): mean_b = c + S1/n_b, M2_b = S2 -
+// S1^2/n_b; the pair is merged with the parallel-variance update, so no sum
+// of raw squares is ever differenced.
 __global__ __launch_bounds__(64) void sigma_accumulate_kernel(const double2* partials, int nparts,
-                                                              double count, had_sigma_state* state) {
+                                                              double count, const float* x,
+                                                              had_sigma_state* state) {
   double a, b;
   partials_total(partials, nparts, a, b);
   if ((threadIdx.x & 63) == 63) {
-    state->count += count;
-    state->sum += a;
-    state->sum_sq += b;
+    const double c = static_cast<double>(sigma_shift(x));
+    const double mean_b = c + a / count;
+    double m2_b = b - a * (a / count);
+    if (!(m2_b > 0.0)) m2_b = 0.0;
+    const double n = state->count;
+    const double tot = n + count;
+    const double delta = mean_b - state->mean;
+    state->mean += delta * (count / tot);
+    state->m2 += m2_b + delta * delta * (n * count / tot);
+    state->count = tot;
   }
 }
 
@@ -150,8 +174,7 @@ __global__ __launch_bounds__(64) void sigma_from_state_kernel(const had_sigma_st
     const double n = state->count;
     double var = 0.0;
     if (n > 0.0) {
-      const double mean = state->sum / n;
-      var = state->sum_sq / n - mean * mean;
+      var = state->m2 / n;
       if (!(var > 0.0)) var = 0.0;
     }
     *sigma = static_cast<float>(sqrt(var));
@@ -180,11 +203,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
   const int64_t nseg = (p.elems + 255) >> 8;
   const int64_t nwords = p.elems >> 5;
   const int shift = 4 * (lane & 7);
+  const float csh = kSigma ? sigma_shift(x) : 0.0f;
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
   // A batch is segments s0 + u * nw (u < kUnroll), addressed through buffer
   // resources based at segment s0, so past-the-end segments read as zeros
-  // (adding nothing to the sums) and their words are not stored.  Two batch
+  // (their shift is taken as 0 too, so they add nothing to the sums) and
+  // their words are not stored.  Two batch
   // buffers alternate: the next batch's loads are issued before the current
   // one is processed, so every wave keeps loads in flight.
   auto load_batch = [&](int64_t s0, f32x4 (&v)[kUnroll]) {
@@ -209,7 +234,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_vec_kernel(PackJobs p) {
         __builtin_amdgcn_raw_buffer_store_b32(w, r, static_cast<int>((u * nw * 8 + (lane >> 3)) * 4), 0, 0);
       if (!kSigma) nan_seen |= (e.x != e.x) | (e.y != e.y) | (e.z != e.z) | (e.w != e.w);
       if (kSigma) {
-        const double a = e.x, b = e.y, c = e.z, d = e.w;
+        // the 4 elements of a lane are all in range or all past the end (d % 32 == 0)
+        const float cu = (s0 + u * nw) * 256 + lane * 4 < p.elems ? csh : 0.0f;
+        const double a = e.x - cu, b = e.y - cu, c = e.z - cu, d = e.w - cu;
         s1 += (a + b) + (c + d);
         s2 += fma(a, a, b * b) + fma(c, c, d * d);
       }
@@ -241,6 +268,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(PackJobs p) {
   const int64_t nwaves = bj.nblk * kWavesPerBlock;
   const int64_t nchunks = (p.elems + 63) >> 6;
   const int64_t nwords = p.elems >> 5;
+  const float csh = kSigma ? sigma_shift(x) : 0.0f;
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
   for (int64_t c0 = wave * kUnroll; c0 < nchunks; c0 += nwaves * kUnroll) {
@@ -255,7 +283,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_stream_kernel(PackJobs p) {
       const uint64_t m = __ballot(v[u] < 0.0f);
       nan_seen |= (v[u] != v[u]);
       if (kSigma) {
-        const double dv = static_cast<double>(v[u]);
+        const double dv = (c0 + u) * 64 + lane < p.elems ? static_cast<double>(v[u] - csh) : 0.0;
         s1 += dv;
         s2 = fma(dv, dv, s2);
       }
@@ -277,6 +305,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(PackJobs p) {
   const int d = p.d, W = p.W;
   const int64_t nwords = p.rows * W;
   const int64_t stride = bj.nblk * kPackThreads;
+  const float csh = kSigma ? sigma_shift(x) : 0.0f;
   double s1 = 0.0, s2 = 0.0;
   bool nan_seen = false;
   for (int64_t wi = bj.blk * kPackThreads + threadIdx.x; wi < nwords; wi += stride) {
@@ -290,7 +319,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(PackJobs p) {
       word |= static_cast<uint32_t>(v < 0.0f) << (c - 32 * w);
       nan_seen |= (v != v);
       if (kSigma) {
-        const double dv = static_cast<double>(v);
+        const double dv = static_cast<double>(v - csh);
         s1 += dv;
         s2 = fma(dv, dv, s2);
       }
@@ -439,7 +468,7 @@ extern "C" had_status had_pack_calibrate(const float* x, had_shape s, uint32_t* 
   if ((st = launch_pack(&job, 1, s, dev_status, hs)) != HAD_OK) return st;
   const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
   sigma_accumulate_kernel<<<1, 64, 0, hs>>>(reinterpret_cast<const double2*>(partials),
-                                            pack_partials(s), count, state);
+                                            pack_partials(s), count, x, state);
   return check_launch("had_pack_calibrate");
 }
 

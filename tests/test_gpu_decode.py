@@ -79,6 +79,31 @@ def test_decode_matches_oracle(case):
             check_out(out[b, h], r["out"], r["E"], vvalid, vdt, where=f"slice {(b, h)}")
 
 
+@pytest.mark.parametrize("nq", [1, 3])
+def test_decode_d256_key_opposite_to_every_query_sign(nq):
+    """d = 256: a key whose signs all differ from a row's has Hamming distance
+    256, which does not fit the per-key distance byte of the few-row path; the
+    row's output must still match the oracle (that key is the least similar
+    one, weight exp(-2 * scale * 256) relative to an equal key)."""
+    B, H, nk, d, topn = 1, 2, 600, 256, 599
+    log(f"decode d=256 opposite key nq={nq}")
+    inp = make_inputs(B, H, nk, d, v_dtype="f32", rank=4, noise="normal", seed=256 + nq)
+    qn = np.ascontiguousarray(inp["q"][:, :, nk - nq:])
+    k = inp["k"].copy()
+    for i in range(nq):
+        k[:, :, 10 + i] = -np.where(qn[:, :, i] >= 0, 1.0, -1.0) * (1.0 + np.abs(k[:, :, 10 + i]))
+        k[:, :, 20 + i] = np.where(qn[:, :, i] >= 0, 1.0, -1.0)
+    kb, _ = had.pack(torch.from_numpy(k).cuda(), with_sigma=False)
+    v = torch.from_numpy(inp["v"]).cuda()
+    for scale in (1e-3, 0.01):
+        out = had.decode_forward(torch.from_numpy(qn).cuda(), kb, v, topn, scale, q_pos0=nk - nq,
+                                 causal=True).cpu().numpy()
+        for h in range(H):
+            r = oracle.decode(qn[0, h], k[0, h], inp["v"][0, h], topn, scale, q_pos0=nk - nq, causal=True)
+            assert (r["S"][np.arange(nq), 10 + np.arange(nq)] == -d).all()
+            check_out(out[0, h], r["out"], r["E"], inp["v"], "f32", where=f"head {h} scale {scale}")
+
+
 def test_decode_is_deterministic_and_reuses_its_workspace():
     B, H, nq, nk, d = 2, 4, 8, 3000, 64
     log(f"decode determinism {(B, H, nq, nk, d)}")
