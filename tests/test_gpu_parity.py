@@ -55,6 +55,33 @@ def test_pack_bits_and_sigma(shape):
     assert abs(float(sig2.item()) - ref) <= 1e-6 * ref + 1e-30
 
 
+@pytest.mark.parametrize("shape,offset,spread", [((2, 3, 77, 64), 1.0e4, 1.0), ((1, 4, 1000, 128), -3.0e5, 2.0),
+                                                  ((3, 1, 9, 33), 2.5e4, 0.5), ((2, 2, 300, 64), 1.0e4, 1.0e-2)])
+def test_pack_sigma_with_a_large_common_offset(shape, offset, spread):
+    """x = offset + spread * N(0, 1): the mean is 1e4 to 1e6 times the spread,
+    where a one-pass sum of raw squares would lose the digits sigma needs.
+    Sigma must still be within 1e-6 relative of the oracle's two-pass value,
+    through had_pack, had_forward and the running calibration."""
+    log(f"pack sigma offset {shape} {offset} {spread}")
+    rng = np.random.default_rng(int(abs(offset)) + shape[2])
+    x = (offset + spread * rng.standard_normal(shape)).astype(np.float32)
+    ref = oracle.sigma(x)
+    xt = torch.from_numpy(x).cuda()
+    _, sig = had.pack(xt)
+    assert abs(float(sig.item()) - ref) <= 1e-6 * ref, (float(sig.item()), ref)
+    v = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    _, _, _, sq, _ = had.forward(xt, xt, v, 4, 0.1, False)
+    assert abs(float(sq.item()) - ref) <= 1e-6 * ref, (float(sq.item()), ref)
+    # calibration over two halves of the batch, then the whole tensor
+    state = had.sigma_state()
+    half = shape[0] // 2 or 1
+    parts = [x[:half], x[half:]] if shape[0] > 1 else [x]
+    for part in parts:
+        had.pack_calibrate(torch.from_numpy(np.ascontiguousarray(part)).cuda(), state)
+    sc = float(had.sigma_from_state(state).item())
+    assert abs(sc - ref) <= 1e-6 * ref, (sc, ref)
+
+
 @pytest.mark.parametrize("shape", [(2, 3, 77, 64), (1, 1, 999, 32)])
 def test_pack_unaligned_input(shape):
     """x at a 4-byte but not 16-byte aligned address takes the scalar path."""
@@ -236,6 +263,32 @@ def test_attention_invariants():
     for h in range(2):
         mean = inp["v"][0, h][idx[h]].mean(axis=1)
         np.testing.assert_allclose(o[0, h], mean, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 64, 64, 20, False, 0.3), (1, 1, 200, 256, 37, True, 0.2),
+                                  (2, 1, 128, 128, 128, False, 0.05), (1, 1, 100, 100, 1, True, 1.0)])
+def test_attention_onehot_v_gives_the_weight_row(case):
+    """V = identity rows (n <= d, fp32): out_i is row i of the sparse softmax
+    matrix itself, so its non-zero positions are exactly the kept set the
+    attend path chose (N_i of them) and its values the oracle's weights."""
+    B, H, n, d, topn, causal, scale = case
+    log(f"attention one-hot V {case}")
+    inp = make_inputs(B, H, n, d, rank=4, noise="t3", seed=n + d + topn)
+    q, k, _ = to_dev(inp)
+    qb, _ = had.pack(q, with_sigma=False)
+    kb, _ = had.pack(k, with_sigma=False)
+    eye = np.zeros((B, H, n, d), dtype=np.float32)
+    eye[:, :, np.arange(n), np.arange(n)] = 1.0
+    out = had.attention(qb, kb, torch.from_numpy(eye).cuda(), topn, scale, causal).cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            r = oracle.forward(inp["q"][b, h], inp["k"][b, h], eye[b, h], topn, scale, causal=causal)
+            check_out(out[b, h], r["out"], r["E"], eye, "f32", where=f"slice {(b, h)}")
+            for i in range(n):
+                kept = r["idx"][i][r["idx"][i] >= 0]
+                nz = np.nonzero(out[b, h, i])[0]
+                assert np.array_equal(nz, kept), f"slice {(b, h)} row {i}: non-zeros {nz[:10]} kept {kept[:10]}"
+                assert nz.size == min(topn, i + 1 if causal else n)
 
 
 @pytest.mark.parametrize("causal", [False, True])
