@@ -19,8 +19,16 @@ Roofline of the dominant kernel (had_attention), algorithmic work only:
     lane-op equivalents = int ops + flops / 4        (a packed fp32 FMA lane
               does 4 flops per lane-op issue)
     peak    = 256 CU * 4 SIMD * 16 lanes * 2.4 GHz = 39.32 T lane-ops/s
+This "frac" is VALU-equivalent: the method's work priced at vector-ALU rates.
 The kernel puts the logits and the V product on the matrix cores, so it can
-run faster than this vector-unit bound (frac > 1).
+run faster than this vector-unit bound (frac > 1).  Beside it, roofline.mfma
+gives the matrix-core work the kernel actually issues (dense-masked tiles,
+counted from its tiling: int8 logit tiles in both passes, bf16 hi/lo weight
+products in pass 2) against the dense peaks (int8 5.0 POP/s, bf16
+2.5 PFLOP/s), i.e. how busy the matrix cores would be if nothing else ran.
+
+The kernel time is the median over 50 timed groups of 5 back-to-back
+launches, each group bracketed by HIP events on the stream it runs on.
 """
 
 from __future__ import annotations
@@ -39,6 +47,9 @@ sys.path.insert(0, ROOT)
 METRIC = "query rows/sec of HAD attention at n={n},N={topn}; % of HBM/VALU roofline"  # headline: n=1024, N=256
 VALU_PEAK = 256 * 4 * 16 * 2.4e9  # int32 lane-ops/s
 HBM_PEAK = 8.0e12  # B/s
+INT8_MFMA_PEAK = 5.0e15  # dense int8 matrix-core ops/s
+BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core flops/s
+FP32_MFMA_PEAK = 157.3e12  # dense fp32 matrix-core flops/s
 
 
 def work_model(w):
@@ -63,6 +74,75 @@ def work_model(w):
             "lane_ops": lane_ops, "hbm_bytes": hbm}
 
 
+def mfma_model(w):
+    """Matrix-core instructions one had_attention launch issues on workload w,
+    from the kernel's tiling (it never reads the data).  A work-group is 4 waves
+    of 32 query rows (2 waves for d > 128); its visible keys [0, kend) split at
+    Hh into two halves, and one 16-key chunk per half is one 32 x 32 logit tile
+    of W int8 instructions (v_mfma_i32_32x32x32_i8, 65536 ops each).  Pass 1
+    runs the chunks a wave sees; pass 2 runs whole groups of kCH2 chunks up to
+    the last group with a visible chunk, each chunk one logit tile plus 4W bf16
+    products (v_mfma_f32_32x32x16_bf16, hi and lo weights, 32768 flops each),
+    or, with fp32 V, 16W fp32 products (v_mfma_f32_32x32x2f32, 4096 flops each)."""
+    W = (w.dim + 31) // 32
+    waves = 4 if W <= 4 else 2
+    qb = 32 * waves
+    vf32 = w.v_dtype == "f32"
+    kch2 = (2 if W <= 2 else 1) if vf32 else (4 if W <= 2 else (2 if W <= 4 else 1))
+    n = w.seq
+    int8 = bf16 = fp32 = 0
+    for t in range((n + qb - 1) // qb):
+        q0 = t * qb
+        kend = min(n, q0 + qb) if w.causal else n
+        hh = ((kend + 1) // 2 + 15) & ~15
+        nchunk = hh // 16
+        for wv in range(waves):
+            wq0 = q0 + 32 * wv
+            if wq0 >= n:
+                continue
+            wlim = min(n, wq0 + 32) if w.causal else n
+            wch = min(nchunk, (wlim + 15) // 16)
+            p2 = ((wch + kch2 - 1) // kch2) * kch2  # whole groups in pass 2
+            int8 += (wch + p2) * W
+            if vf32:
+                fp32 += p2 * 16 * W
+            else:
+                bf16 += p2 * 4 * W
+    bh = w.batch * w.heads
+    return {"int8_instr": bh * int8, "bf16_instr": bh * bf16, "fp32_instr": bh * fp32,
+            "int8_ops": bh * int8 * 65536.0, "bf16_flops": bh * bf16 * 32768.0,
+            "fp32_flops": bh * fp32 * 4096.0}
+
+
+def mfma_roofline(w, seconds):
+    m = mfma_model(w)
+    busy = (m["int8_ops"] / INT8_MFMA_PEAK + m["bf16_flops"] / BF16_MFMA_PEAK
+            + m["fp32_flops"] / FP32_MFMA_PEAK)
+    return {"int8_tops": m["int8_ops"] / seconds / 1e12, "bf16_tflops": m["bf16_flops"] / seconds / 1e12,
+            "fp32_tflops": m["fp32_flops"] / seconds / 1e12,
+            "peaks": {"int8_tops": INT8_MFMA_PEAK / 1e12, "bf16_tflops": BF16_MFMA_PEAK / 1e12,
+                      "fp32_tflops": FP32_MFMA_PEAK / 1e12},
+            "frac": busy / seconds, "busy_us_at_peak": busy * 1e6,
+            "instructions_per_launch": {k: float(m[k]) for k in ("int8_instr", "bf16_instr", "fp32_instr")}}
+
+
+def timed_launches(launch, stream, groups, per_group=5):
+    """groups x per_group back-to-back launches on `stream`, with a HIP event
+    recorded on it between groups; returns the per-launch time of each group
+    in seconds.  (An event between every two launches would add its own
+    drain-and-timestamp, about 2 us, to each launch.)"""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    for g in range(groups):
+        ev[g].record(stream)
+        for _ in range(per_group):
+            launch()
+    ev[groups].record(stream)
+    torch.cuda.synchronize()
+    return [ev[g].elapsed_time(ev[g + 1]) / 1e3 / per_group for g in range(groups)]
+
+
 def traffic_for(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
@@ -77,36 +157,119 @@ def traffic_for(workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s):
-    """The plain oracle on a bounded sample of the same workload, one thread."""
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
+_TASKS = None  # task list of the running baseline, inherited by forked workers
+
+
+def _oracle_slice(i):
+    """Task i of the running baseline through the oracle (one (batch, head)
+    slice: sign, pack and sigma of the slice, logits, stable-sort top-N,
+    softmax, AV).  Returns the query rows done."""
     import oracle
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    rows = 0
-    heads = 0
-    t0 = time.perf_counter()
+    kind, q, k, v, topn, scale, causal, q_pos0 = _TASKS[i]
+    if kind == "decode":
+        oracle.decode(q, k, v, topn, scale, q_pos0=q_pos0, causal=causal)
+    else:
+        oracle.sigma(q)
+        oracle.forward(q, k, v, topn, scale, causal=causal)
+    return q.shape[0]
+
+
+def _worker_init():
     try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def host_workers():
+    """Worker processes for the oracle: the cores this process may run on,
+    at most 16 (a one-GPU machine's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _run_oracle(tasks, budget_s, workers):
+    """Runs tasks (one per slice, in order) until budget_s of wall time has
+    passed; returns (rows, slices, seconds).  workers == 1 runs in-process with
+    one BLAS thread; otherwise forked worker processes (this runs before the
+    process touches the GPU) share the inputs copy-on-write."""
+    global _TASKS
+    _TASKS = list(tasks)
+    rows = done = 0
+    try:
+        if workers == 1:
+            try:
+                from threadpoolctl import threadpool_limits
+                ctx = threadpool_limits(limits=1)
+            except Exception:  # pragma: no cover
+                ctx = None
+            t0 = time.perf_counter()
+            try:
+                for i in range(len(_TASKS)):
+                    rows += _oracle_slice(i)
+                    done += 1
+                    if time.perf_counter() - t0 > budget_s:
+                        break
+            finally:
+                if ctx is not None:
+                    ctx.__exit__(None, None, None)
+            return rows, done, time.perf_counter() - t0
+        import multiprocessing as mp
+
+        with mp.get_context("fork").Pool(workers, initializer=_worker_init) as pool:
+            pool.map(abs, range(workers))  # the workers are up before the clock starts
+            t0 = time.perf_counter()
+            pending, nxt = [], 0
+            while True:
+                while (len(pending) < 2 * workers and nxt < len(_TASKS)
+                       and time.perf_counter() - t0 <= budget_s):
+                    pending.append(pool.apply_async(_oracle_slice, (nxt,)))
+                    nxt += 1
+                if not pending:
+                    break
+                rows += pending.pop(0).get()
+                done += 1
+            return rows, done, time.perf_counter() - t0
+    finally:
+        _TASKS = None
+
+
+def cpu_baseline(w, inp, budget_s, single_budget_s=None):
+    """The plain oracle on a bounded sample of the same workload: (batch, head)
+    slices spread over worker processes on the host cores, and beside it the
+    same oracle on one core."""
+    def tasks():
         for bh in range(w.batch * w.heads):
             b, h = divmod(bh, w.heads)
-            oracle.sigma(inp["q"][b, h])
-            oracle.forward(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
-                           causal=w.causal)
-            rows += w.seq
-            heads += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "query rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {w.batch * w.heads} (batch, head) slices, all {w.seq} rows each "
-                      f"(sign, pack, sigma of the slice, logits, stable-sort top-N, softmax, AV), "
-                      f"{dt:.1f} s wall, numpy float64, 1 thread"}
+            yield ("forward", inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                   w.causal, 0)
+
+    return _baseline(w.batch * w.heads, f"all {w.seq} rows each (sign, pack, sigma of the slice, "
+                     "logits, stable-sort top-N, softmax, AV)", tasks, budget_s, single_budget_s)
+
+
+def _baseline(nslices, what, tasks, budget_s, single_budget_s):
+    workers = host_workers()
+    single_budget_s = budget_s / 3 if single_budget_s is None else single_budget_s
+    r1, s1, t1 = _run_oracle(tasks(), single_budget_s, 1)
+    rec = {"value": r1 / t1, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+           "sample": f"{s1} of {nslices} (batch, head) slices, {what}, {t1:.1f} s wall, "
+                     f"numpy float64, 1 thread"}
+    if workers > 1:
+        rn, sn, tn = _run_oracle(tasks(), budget_s, workers)
+        rec = {"value": rn / tn, "unit": "query rows/s", "cores": workers, "kind": "oracle",
+               "sample": f"{sn} of {nslices} (batch, head) slices, {what}, {tn:.1f} s wall, "
+                         f"numpy float64, {workers} worker processes of one BLAS thread each "
+                         f"(os.cpu_count() = {os.cpu_count()})",
+               "single_core": rec}
+    rec["os_cpu_count"] = os.cpu_count()
+    rec["workers"] = workers
+    return rec
 
 
 def decode_model(w, fp32_rows=False):
@@ -125,33 +288,16 @@ def decode_model(w, fp32_rows=False):
     return {"kept": bh * kept, "hbm_bytes": bh * per_slice}
 
 
-def decode_cpu_baseline(w, inp, budget_s):
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    import oracle
-
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    rows = heads = 0
-    t0 = time.perf_counter()
-    try:
+def decode_cpu_baseline(w, inp, budget_s, single_budget_s=None):
+    def tasks():
         for bh in range(w.batch * w.heads):
             b, h = divmod(bh, w.heads)
-            oracle.decode(inp["q_new"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
-                          q_pos0=w.q_pos0, causal=w.causal)
-            rows += w.n_q
-            heads += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "query rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {w.batch * w.heads} (batch, head) slices, {w.n_q} new rows "
-                      f"each against {w.n_k} cached keys (sign, pack, logits, stable-sort "
-                      f"top-N, softmax, AV), {dt:.1f} s wall, numpy float64, 1 thread"}
+            yield ("decode", inp["q_new"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                   w.causal, w.q_pos0)
+
+    return _baseline(w.batch * w.heads, f"{w.n_q} new rows each against {w.n_k} cached keys "
+                     "(sign, pack, logits, stable-sort top-N, softmax, AV)", tasks, budget_s,
+                     single_budget_s)
 
 
 def settle(step, seconds):
@@ -185,6 +331,8 @@ def bench_decode(args, w):
     from had_workloads import decode_inputs
 
     inp = decode_inputs(w)
+    # the oracle baseline runs first, before this process touches the GPU
+    cpu = None if args.no_cpu_baseline else decode_cpu_baseline(w, inp, args.cpu_budget)
     dev = torch.device("cuda:0")
     qn = torch.from_numpy(inp["q_new"]).to(dev)
     kc = torch.from_numpy(inp["k"]).to(dev)
@@ -224,16 +372,10 @@ def bench_decode(args, w):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
     if args.separate_calls:
         had.pack(qn, out=qb, with_sigma=False)
-    for _ in range(args.steps):
-        decode_call()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_s = d0.elapsed_time(d1) / args.steps / 1e3
+    durs = timed_launches(decode_call, stream, 50)
+    dec_s = float(np.median(durs))
     model = decode_model(w, fp32_rows=not args.separate_calls)
     achieved = model["hbm_bytes"] / dec_s
     rec = {
@@ -257,14 +399,16 @@ def bench_decode(args, w):
                             else "had_decode_forward (3 launches; the new rows' sign words are built "
                                  "inside the first)")},
         "decode_us": dec_s * 1e6,
+        "decode_us_mean": float(np.mean(durs)) * 1e6,
+        "timed_calls": f"median over {len(durs)} groups of 5 back-to-back calls",
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
                      "kernel": "had_decode%s (dec_hist, dec_gather, dec_reduce)"
                                % ("" if args.separate_calls else "_forward"),
                      "work_per_launch": {k2: float(v2) for k2, v2 in model.items()}},
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = decode_cpu_baseline(w, inp, args.cpu_budget)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 
@@ -304,6 +448,8 @@ def main():
         return bench_decode(args, DECODE_WORKLOADS[name])
     w = WORKLOADS[name]
     inp = workload_inputs(w)
+    # the oracle baseline runs first, before this process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget)
     dev = torch.device("cuda:0")
     q = torch.from_numpy(inp["q"]).to(dev)
     k = torch.from_numpy(inp["k"]).to(dev)
@@ -366,16 +512,12 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # timed region 2: back-to-back had_attention launches on the same stream,
-    # bracketed by HIP events, for the dominant kernel's average duration
-    a_start = torch.cuda.Event(enable_timing=True)
-    a_end = torch.cuda.Event(enable_timing=True)
-    a_start.record(stream)
-    for _ in range(args.steps):
-        had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out)
-    a_end.record(stream)
-    torch.cuda.synchronize()
-    attn_avg_s = a_start.elapsed_time(a_end) / args.steps / 1e3
+    # timed region 2: had_attention launches on the same stream, 50 groups of 5
+    # back-to-back launches bracketed by HIP events; the median is the kernel's
+    # duration
+    durs = timed_launches(lambda: had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out),
+                          stream, 50)
+    attn_avg_s = float(np.median(durs))
 
     rows = w.rows
     model = work_model(w)
@@ -405,6 +547,8 @@ def main():
                           "as bf16 hi+lo, bf16 matrix-core V product with fp32 accumulation",
         },
         "attention_us": attn_avg_s * 1e6,
+        "attention_us_mean": float(np.mean(durs)) * 1e6,
+        "attention_timing": f"median over {len(durs)} groups of 5 back-to-back launches",
         "attention_rows_per_s": rows / attn_avg_s,
         "roofline": {
             "bound": "alu",
@@ -412,15 +556,19 @@ def main():
             "peak": VALU_PEAK / 1e12,
             "unit": "Tops/s",
             "frac": achieved / VALU_PEAK,
+            "frac_kind": "VALU-equivalent: the method's algorithmic int ops and fp32 flops at "
+                         "vector-ALU peak rates (the kernel itself runs both contractions on the "
+                         "matrix cores; see mfma)",
             "traffic": traffic,
             "kernel": "had_attn_kernel",
             "work_per_launch": {k2: float(v2) for k2, v2 in model.items()},
             "hbm_frac": (model["hbm_bytes"] / attn_avg_s) / HBM_PEAK,
+            "mfma": mfma_roofline(w, attn_avg_s),
         },
         "wall_s_timed_region": wall,
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 

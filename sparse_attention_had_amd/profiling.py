@@ -27,10 +27,16 @@ COPY_BYTES = 64 << 20
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def source_hash() -> str:
+# The sources the attention kernel is compiled from: a counter record taken on
+# them stays valid while they are unchanged.
+ATTENTION_SOURCES = ("had_attention.hip", "had_internal.h")
+
+
+def source_hash(files=ATTENTION_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_had_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files):
+        h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -118,7 +124,8 @@ def counters(csvs, cmds, kernel, workload, out_md):
             ndisp[name] = len(vals)
     waves = means.get("SQ_WAVES")
     lines = [f"# SQ counters, `{kernel}`, {workload}", "",
-             f"Kernel sources: sha256 prefix `{source_hash()}` of `sparse_attention_had_amd/csrc`.", "",
+             f"Kernel sources: sha256 prefix `{source_hash()}` of "
+             f"{', '.join('`' + f + '`' for f in ATTENTION_SOURCES)}.", "",
              "Commands (one counter pass each):", "", "```"] + list(cmds) + ["```", "",
              "| counter | mean per dispatch | per wave | dispatches |", "|---|---|---|---|"]
     for name, v in means.items():

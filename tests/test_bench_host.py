@@ -11,6 +11,8 @@ import subprocess
 import sys
 import types
 
+import numpy as np
+
 import pytest
 
 import bench
@@ -88,3 +90,59 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_mfma_model_at_the_headline_workload():
+    """384 matrix-core instructions per wave at t5-base-n1024 (the SQ_INSTS_MFMA
+    count the counter pass reads): 32 int8 logit tiles of 2 instructions in each
+    pass, and 8 bf16 products (hi and lo weights, 2 K-steps, 2 feature tiles) per
+    pass-2 tile."""
+    w = WORKLOADS["t5-base-n1024"]
+    m = bench.mfma_model(w)
+    waves = 96 * (1024 // 32)
+    assert m["int8_instr"] == waves * (32 * 2 + 32 * 2)
+    assert m["bf16_instr"] == waves * 32 * 8
+    assert (m["int8_instr"] + m["bf16_instr"]) / waves == 384
+    assert m["fp32_instr"] == 0
+    r = bench.mfma_roofline(w, 51.6e-6)
+    busy = m["int8_ops"] / 5.0e15 + m["bf16_flops"] / 2.5e15
+    assert abs(r["frac"] - busy / 51.6e-6) < 1e-12
+    assert 0.25 < r["frac"] < 0.35
+
+
+def test_mfma_model_causal_counts_only_visible_chunks():
+    # one slice, n = 256, causal, d = 64: work-group t (128 rows) sees keys [0, 128(t+1))
+    w = types.SimpleNamespace(batch=1, heads=1, seq=256, dim=64, topn=16, causal=True, v_dtype="bf16")
+    m = bench.mfma_model(w)
+    int8 = bf16 = 0
+    for t in range(2):
+        kend = 128 * (t + 1)
+        nchunk = (((kend + 1) // 2 + 15) & ~15) // 16
+        for wv in range(4):
+            wch = min(nchunk, (min(256, 128 * t + 32 * wv + 32) + 15) // 16)
+            p2 = -(-wch // 4) * 4
+            int8 += 2 * (wch + p2)
+            bf16 += 8 * p2
+    assert (m["int8_instr"], m["bf16_instr"]) == (int8, bf16)
+
+
+def test_host_workers_and_baseline_record(monkeypatch):
+    assert 1 <= bench.host_workers() <= 16
+    w = types.SimpleNamespace(batch=1, heads=2, seq=40, dim=8, topn=5, causal=False, scale=0.3)
+    rng = np.random.default_rng(0)
+    inp = {"q": rng.standard_normal((1, 2, 40, 8)), "k": rng.standard_normal((1, 2, 40, 8)),
+           "v": rng.standard_normal((1, 2, 40, 8))}
+    monkeypatch.setattr(bench, "host_workers", lambda: 1)
+    rec = bench.cpu_baseline(w, inp, 0.5)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["workers"] == 1
+    assert rec["value"] > 0 and rec["os_cpu_count"] == os.cpu_count()
+
+
+def test_forked_workers_run_every_slice(monkeypatch):
+    w = types.SimpleNamespace(batch=2, heads=3, seq=30, dim=8, topn=4, causal=True, scale=0.3)
+    rng = np.random.default_rng(1)
+    inp = {x: rng.standard_normal((2, 3, 30, 8)) for x in ("q", "k", "v")}
+    monkeypatch.setattr(bench, "host_workers", lambda: 2)
+    rec = bench.cpu_baseline(w, inp, 30.0, 30.0)
+    assert rec["cores"] == 2 and rec["workers"] == 2
+    assert rec["sample"].startswith("6 of 6 ") and rec["single_core"]["sample"].startswith("6 of 6 ")
