@@ -209,6 +209,34 @@ had_status had_forward(const float* q, const float* k, const void* v,
                        void* stream);
 
 /*
+ * had_forward_noalloc - had_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same two launches and the same results bit for bit,
+ * with the sigma partials in a fixed device array inside the library instead
+ * of a caller workspace.  The call allocates nothing; the caller still owns
+ * q, k, v, qbits, kbits, out, sigma_q, sigma_k and dev_status (meanings as
+ * had_forward).
+ *
+ *  Scratch: HAD_FORWARD_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the
+ *  first call on that GPU until the process ends.  Shapes whose
+ *  had_forward_workspace_bytes() exceeds it are rejected with
+ *  HAD_ERR_UNSUPPORTED (the partials are capped at 256 pairs per tensor, so
+ *  no valid shape needs more).  The array keeps the last call's contents and
+ *  needs no initial contents.  All calls on one GPU share it: two calls that
+ *  may overlap on the same GPU (different streams, or threads without
+ *  ordering) race and may produce a wrong sigma.
+ *  Errors: those of had_forward, and HAD_ERR_HIP if the array's device
+ *  address cannot be looked up.
+ */
+#define HAD_FORWARD_NOALLOC_SCRATCH_BYTES 8192
+had_status had_forward_noalloc(const float* q, const float* k, const void* v,
+                               had_dtype v_dtype, had_shape s, int64_t topn,
+                               float scale, int causal, uint32_t* qbits,
+                               uint32_t* kbits, float* out, float* sigma_q,
+                               float* sigma_k, uint32_t* dev_status,
+                               void* stream);
+
+/*
  * had_logits - inspection export of the integer logits s = d - 2*Hamming
  * computed by the same logit stage as had_attention (no mask, every key).
  *

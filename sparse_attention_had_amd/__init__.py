@@ -108,6 +108,9 @@ def load_library():
         lib.had_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P,
                                     ctypes.c_size_t, P, P]
         lib.had_forward.restype = I
+        lib.had_forward_noalloc.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P,
+                                            P, P]
+        lib.had_forward_noalloc.restype = I
         lib.had_pack_calibrate.argtypes = [P, Shape, P, P, P, ctypes.c_size_t, P, P]
         lib.had_pack_calibrate.restype = I
         lib.had_sigma_from_state.argtypes = [P, P, P]
@@ -324,6 +327,54 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale:
         q.data_ptr(), k.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(topn), float(scale),
         int(bool(causal)), qbits.data_ptr(), kbits.data_ptr(), out.data_ptr(), sq_ptr, sk_ptr,
         ws_ptr, ws_bytes, st_ptr, sh))
+    if not with_sigma:
+        return out, qbits, kbits, None, None
+    return out, qbits, kbits, sigma_q, sigma_k
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale: float,
+                    causal: bool = False, *, with_sigma: bool = True, out: torch.Tensor | None = None,
+                    qbits: torch.Tensor | None = None, kbits: torch.Tensor | None = None,
+                    sigma_q: torch.Tensor | None = None, sigma_k: torch.Tensor | None = None,
+                    dev_status: torch.Tensor | None = None, stream=None):
+    """had_forward_noalloc: forward() without a workspace (the sigma partials
+    live in the library's own device array; calls that overlap on one GPU
+    race).  The library allocates nothing; tensors not passed in are
+    allocated here by torch.  Returns (out, qbits, kbits, sigma_q, sigma_k)."""
+    lib = load_library()
+    _need_cuda(q, "q", torch.float32)
+    _need_cuda(k, "k", torch.float32)
+    _need_cuda(v, "v")
+    B, H, n, d = _shape4(q, "q")
+    if tuple(k.shape) != (B, H, n, d) or tuple(v.shape) != (B, H, n, d):
+        raise ValueError("q, k and v must have the same shape [B, H, n, d]")
+    W = words_per_row(d)
+    dev = q.device
+    qbits = torch.empty((B, H, n, W), dtype=torch.int32, device=dev) if qbits is None else qbits
+    kbits = torch.empty((B, H, n, W), dtype=torch.int32, device=dev) if kbits is None else kbits
+    for t, name in ((qbits, "qbits"), (kbits, "kbits")):
+        _need_cuda(t, name, torch.int32)
+        if tuple(t.shape) != (B, H, n, W):
+            raise ValueError(f"{name} must have shape [B, H, n, ceil(d/32)]")
+    out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev) if out is None else out
+    _need_cuda(out, "out", torch.float32)
+    if tuple(out.shape) != (B, H, n, d):
+        raise ValueError("out must have the shape of v")
+    sq_ptr = sk_ptr = None
+    if with_sigma:
+        sigma_q = torch.empty(1, dtype=torch.float32, device=dev) if sigma_q is None else sigma_q
+        sigma_k = torch.empty(1, dtype=torch.float32, device=dev) if sigma_k is None else sigma_k
+        _need_cuda(sigma_q, "sigma_q", torch.float32)
+        _need_cuda(sigma_k, "sigma_k", torch.float32)
+        sq_ptr, sk_ptr = sigma_q.data_ptr(), sigma_k.data_ptr()
+    st_ptr = None
+    if dev_status is not None:
+        _need_cuda(dev_status, "dev_status", torch.int32)
+        st_ptr = dev_status.data_ptr()
+    _check("had_forward_noalloc", lib.had_forward_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _v_dtype(v), Shape(B, H, n, d), int(topn),
+        float(scale), int(bool(causal)), qbits.data_ptr(), kbits.data_ptr(), out.data_ptr(),
+        sq_ptr, sk_ptr, st_ptr, _stream_handle(dev, stream)))
     if not with_sigma:
         return out, qbits, kbits, None, None
     return out, qbits, kbits, sigma_q, sigma_k

@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstring>
+#include <mutex>
 
 #include "had_internal.h"
 
@@ -116,32 +117,27 @@ extern "C" size_t had_forward_workspace_bytes(had_shape s) {
   return 2 * had_pack_workspace_bytes(s);
 }
 
-extern "C" had_status had_forward(const float* q, const float* k, const void* v, had_dtype v_dtype,
-                                  had_shape s, int64_t topn, float scale, int causal,
-                                  uint32_t* qbits, uint32_t* kbits, float* out, float* sigma_q,
-                                  float* sigma_k, void* workspace, size_t workspace_bytes,
-                                  uint32_t* dev_status, void* stream) {
-  clear_error();
-  had_status st = check_shape(s);
-  if (st != HAD_OK) return st;
-  if ((st = check_pack_args(q, qbits, sigma_q, "had_forward")) != HAD_OK) return st;
-  if ((st = check_pack_args(k, kbits, sigma_k, "had_forward")) != HAD_OK) return st;
+namespace had {
+namespace {
+
+// The two launches of the forward call; ws holds 2 * pack_partials(s) partial
+// pairs per tensor that asks for sigma (checked by the caller).
+had_status forward_launch(const float* q, const float* k, const void* v, had_dtype v_dtype,
+                          const had_shape& s, int64_t topn, float scale, int causal,
+                          uint32_t* qbits, uint32_t* kbits, float* out, float* sigma_q,
+                          float* sigma_k, double* ws, uint32_t* dev_status, hipStream_t hs,
+                          const char* who) {
+  had_status st;
+  if ((st = check_pack_args(q, qbits, sigma_q, who)) != HAD_OK) return st;
+  if ((st = check_pack_args(k, kbits, sigma_k, who)) != HAD_OK) return st;
   if (dev_status != nullptr && !aligned(dev_status, 4))
-    return fail(HAD_ERR_INVALID_ARG, "had_forward: dev_status must be 4-byte aligned");
+    return failf(HAD_ERR_INVALID_ARG, "%s: dev_status must be 4-byte aligned", who);
   AttnArgs a;
-  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_forward", a)) != HAD_OK)
+  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, who, a)) != HAD_OK)
     return st;
   double* part[2] = {nullptr, nullptr};
-  if (sigma_q != nullptr || sigma_k != nullptr) {
-    if (workspace == nullptr || !aligned(workspace, 16))
-      return fail(HAD_ERR_INVALID_ARG, "had_forward: sigma requested but workspace is null or unaligned");
-    if (workspace_bytes < had_forward_workspace_bytes(s))
-      return fail(HAD_ERR_INVALID_ARG, "had_forward: workspace smaller than had_forward_workspace_bytes()");
-    double* ws = static_cast<double*>(workspace);
-    if (sigma_q != nullptr) part[0] = ws;
-    if (sigma_k != nullptr) part[1] = ws + 2 * pack_partials(s);
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (sigma_q != nullptr) part[0] = ws;
+  if (sigma_k != nullptr) part[1] = ws + 2 * pack_partials(s);
   const PackJob jobs[2] = {{q, qbits, part[0]}, {k, kbits, part[1]}};
   if ((st = launch_pack(jobs, 2, s, dev_status, hs)) != HAD_OK) return st;
   a.sigma_partials[0] = reinterpret_cast<const double2*>(part[0]);
@@ -151,6 +147,103 @@ extern "C" had_status had_forward(const float* q, const float* k, const void* v,
   a.sigma_nparts = pack_partials(s);
   a.sigma_count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
   return launch_attention_family(AttnMode::Attend, a, hs);
+}
+
+}  // namespace
+}  // namespace had
+
+extern "C" had_status had_forward(const float* q, const float* k, const void* v, had_dtype v_dtype,
+                                  had_shape s, int64_t topn, float scale, int causal,
+                                  uint32_t* qbits, uint32_t* kbits, float* out, float* sigma_q,
+                                  float* sigma_k, void* workspace, size_t workspace_bytes,
+                                  uint32_t* dev_status, void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if (sigma_q != nullptr || sigma_k != nullptr) {
+    if (workspace == nullptr || !aligned(workspace, 16))
+      return fail(HAD_ERR_INVALID_ARG, "had_forward: sigma requested but workspace is null or unaligned");
+    if (workspace_bytes < had_forward_workspace_bytes(s))
+      return fail(HAD_ERR_INVALID_ARG, "had_forward: workspace smaller than had_forward_workspace_bytes()");
+  }
+  return forward_launch(q, k, v, v_dtype, s, topn, scale, causal, qbits, kbits, out, sigma_q, sigma_k,
+                        static_cast<double*>(workspace), dev_status, static_cast<hipStream_t>(stream),
+                        "had_forward");
+}
+
+// ---- had_forward_noalloc: the forward call with its sigma partials in a
+// file-scope device array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy of the array until the process ends;
+// its address on each device is looked up once (hipGetSymbolAddress, with
+// that device current) and kept.  The array's name is only a host-side stand-in for
+// the symbol: host code passes the looked-up address, never the name.
+namespace had {
+namespace {
+
+constexpr size_t kScratchBytes = HAD_FORWARD_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes >= 2 * kPackMaxBlocks * 2 * sizeof(double),
+              "scratch must hold the sigma partials of the largest pack grid");
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // guarded by g_scratch_mu; null until looked up
+
+// Device address of this device's scratch array for work on stream st.
+had_status scratch_address(hipStream_t st, void** ptr) {
+  int dev = -1;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return failf(HAD_ERR_HIP, "had_forward_noalloc: device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HAD_ERR_UNSUPPORTED, "had_forward_noalloc: device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess)
+      return failf(HAD_ERR_HIP, "had_forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return failf(HAD_ERR_HIP, "had_forward_noalloc: hipSetDevice: %s", hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return failf(HAD_ERR_HIP, "had_forward_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return HAD_OK;
+}
+
+}  // namespace
+}  // namespace had
+
+extern "C" had_status had_forward_noalloc(const float* q, const float* k, const void* v,
+                                          had_dtype v_dtype, had_shape s, int64_t topn, float scale,
+                                          int causal, uint32_t* qbits, uint32_t* kbits, float* out,
+                                          float* sigma_q, float* sigma_k, uint32_t* dev_status,
+                                          void* stream) {
+  clear_error();
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  const size_t need = had_forward_workspace_bytes(s);
+  if (need > kScratchBytes)
+    return failf(HAD_ERR_UNSUPPORTED, "had_forward_noalloc: needs %zu bytes of scratch, above the %zu-byte limit",
+                 need, kScratchBytes);
+  // every argument check runs before the scratch address is looked up
+  if ((st = check_pack_args(q, qbits, sigma_q, "had_forward_noalloc")) != HAD_OK) return st;
+  if ((st = check_pack_args(k, kbits, sigma_k, "had_forward_noalloc")) != HAD_OK) return st;
+  if (dev_status != nullptr && !aligned(dev_status, 4))
+    return fail(HAD_ERR_INVALID_ARG, "had_forward_noalloc: dev_status must be 4-byte aligned");
+  AttnArgs unused;
+  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_forward_noalloc",
+                        unused)) != HAD_OK)
+    return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (sigma_q != nullptr || sigma_k != nullptr) {
+    if ((st = scratch_address(hs, &ws)) != HAD_OK) return st;
+  }
+  return forward_launch(q, k, v, v_dtype, s, topn, scale, causal, qbits, kbits, out, sigma_q, sigma_k,
+                        static_cast<double*>(ws), dev_status, hs, "had_forward_noalloc");
 }
 
 extern "C" had_status had_select(const uint32_t* qbits, const uint32_t* kbits, had_shape s,

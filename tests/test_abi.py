@@ -230,3 +230,26 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(had, "_lib", None)
     with pytest.raises(RuntimeError, match="libhad.so not found"):
         had.load_library()
+
+
+def test_forward_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
+    s = Shape(1, 2, 128, 64)
+
+    def f(q=A16, k=A16B, v=A16C, vdt=1, shape=s, topn=8, scale=0.125, causal=0, qb=0x50000,
+          kb=0x60000, out=0x40000, sq=0x70000, sk=0x70010, st=None):
+        return lib.had_forward_noalloc(q, k, v, vdt, shape, topn, scale, causal, qb, kb, out, sq, sk,
+                                       st, None)
+
+    assert f(q=None) == INVALID
+    assert f(k=A16B + 2) == INVALID
+    assert f(qb=None) == INVALID
+    assert f(out=0x40004) == INVALID
+    assert f(vdt=9) == INVALID
+    assert f(topn=0) == INVALID
+    assert f(scale=-1.0) == INVALID
+    assert f(causal=2) == INVALID
+    assert f(sq=0x70002) == INVALID
+    assert f(st=0x80002) == INVALID
+    assert f(shape=Shape(1, 2, 128, 0)) == INVALID
+    assert f(shape=Shape(1, 2, 70000, 64)) == UNSUPPORTED
+    assert lib.had_last_error() != b""
