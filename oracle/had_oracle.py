@@ -40,6 +40,8 @@ __all__ = [
     "forward",
     "decode",
     "topn_mass",
+    "sparse_softmax_av_backward",
+    "backward",
 ]
 
 
@@ -313,3 +315,105 @@ def topn_mass(S, scale: float, mass: float, causal: bool = False, row_index=None
         c = np.cumsum(np.sort(p)[::-1])
         out[r] = min(int(np.searchsorted(c, mass, side="left")) + 1, nv)
     return out
+
+
+# ---------------------------------------------------------------------------
+# training-side variant: straight-through backward of the path
+# ---------------------------------------------------------------------------
+def sparse_softmax_av_backward(S, idx, v, dout, scale: float):
+    """Gradients of L = sum_i dout_i . out_i through softmax-over-the-kept-set and AV.
+
+    [review] "What carries the argument": training runs a four-stage annealing
+    schedule whose later stages finish the binarization with a
+    straight-through estimator, i.e. the forward pass is this path and the
+    backward pass treats sign() as the identity.  The top-N selection is a
+    discrete choice; its gradient is taken with the kept sets held fixed, so
+    for row i with kept set K_i and p_ij = softmax over K_i of scale * S_ij:
+
+        dP_ij = dout_i . V_j                      (j in K_i)
+        D_i   = sum_{j in K_i} p_ij dP_ij
+        dS_ij = scale * p_ij * (dP_ij - D_i)      (0 outside K_i)
+        dV_j  = sum_i p_ij dout_i
+
+    All in float64.  Returns (ds, dv, e_ds, e_dv): ds [rows, topn] aligned with
+    idx (0 where idx == -1), dv [n_keys, d], and the magnitudes used for
+    tolerances, e_ds_ij = scale * p_ij * (a_ij + A_i) with a_ij = sum_c
+    |dout_ic| |V_jc| and A_i = sum_j p_ij a_ij (what the terms of dS_ij add up
+    to in absolute value), and e_dv_jc = sum_i p_ij |dout_ic|.
+    """
+    S = np.asarray(S)
+    idx = np.asarray(idx)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    rows = S.shape[0]
+    ds = np.zeros(idx.shape, dtype=np.float64)
+    e_ds = np.zeros(idx.shape, dtype=np.float64)
+    dv = np.zeros_like(v)
+    e_dv = np.zeros_like(v)
+    for r in range(rows):
+        m = int(np.count_nonzero(idx[r] >= 0))
+        kept = idx[r, :m]
+        if m == 0:
+            continue
+        z = float(scale) * S[r, kept].astype(np.float64)
+        e = np.exp(z - z.max())
+        p = e / e.sum()
+        dp = v[kept] @ dout[r]
+        D = float(p @ dp)
+        ds[r, :m] = float(scale) * p * (dp - D)
+        dv[kept] += np.outer(p, dout[r])
+        a = np.abs(v[kept]) @ np.abs(dout[r])
+        e_ds[r, :m] = float(scale) * p * (a + float(p @ a))
+        e_dv[kept] += np.outer(p, np.abs(dout[r]))
+    return ds, dv, e_ds, e_dv
+
+
+def backward(q, k, v, dout, topn: int, scale: float, causal: bool = False,
+             sigma_q: float = 1.0, sigma_k: float = 1.0, block: int = 2048):
+    """Straight-through backward of the whole path on one head.
+
+    Forward: Bq = sign(q / sigma_q), Bk = sign(k / sigma_k) (binarize()),
+    S = Bq Bk^T, top-N per row (select_topn()), out = softmax over the kept
+    set of scale * S, times V.  Backward with the straight-through estimator
+    ([review] "What carries the argument": the estimator finishes the
+    binarization; read as d sign(u)/du = 1, the plain identity form, on the
+    standardized input u = x / sigma with sigma a calibrated constant):
+
+        dBq = dS Bk,  dBk = dS^T Bq,  dq = dBq / sigma_q,  dk = dBk / sigma_k,
+
+    with dS and dV from sparse_softmax_av_backward().  Rows are processed in
+    blocks of `block` (the logits of one block at a time).  Returns dq, dk,
+    dv and their tolerance magnitudes e_dq, e_dk, e_dv (the sums of the
+    absolute values of the terms, |Bk| = |Bq| = 1), plus idx.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    n, d = q.shape
+    bq = binarize(q).astype(np.float64)
+    bk = binarize(k).astype(np.float64)
+    dq = np.zeros((n, d))
+    dk = np.zeros((k.shape[0], d))
+    dv = np.zeros_like(v)
+    e_dq = np.zeros((n, d))
+    e_dk = np.zeros((k.shape[0], d))
+    e_dv = np.zeros_like(v)
+    idx_all = np.full((n, topn), -1, dtype=np.int64)
+    for r0 in range(0, n, block):
+        rows = np.arange(r0, min(n, r0 + block))
+        S = logits(bq[rows], bk)
+        idx = select_topn(S, topn, causal, row_index=rows)
+        idx_all[rows] = idx
+        ds, dvb, e_ds, e_dvb = sparse_softmax_av_backward(S, idx, v, dout[rows], scale)
+        dv += dvb
+        e_dv += e_dvb
+        for t, r in enumerate(rows):
+            m = int(np.count_nonzero(idx[t] >= 0))
+            kept = idx[t, :m]
+            dq[r] = ds[t, :m] @ bk[kept]
+            e_dq[r] = e_ds[t, :m].sum()
+            dk[kept] += np.outer(ds[t, :m], bq[r])
+            e_dk[kept] += e_ds[t, :m][:, None]
+    return {"dq": dq / sigma_q, "dk": dk / sigma_k, "dv": dv,
+            "e_dq": e_dq / sigma_q, "e_dk": e_dk / sigma_k, "e_dv": e_dv, "idx": idx_all}

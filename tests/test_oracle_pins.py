@@ -372,3 +372,116 @@ def test_topn_mass_brute_force_and_limits():
             assert got[r] == best
     assert oracle.topn_mass(S, 0.6, 1.0).tolist() == [7] * 6
     assert oracle.topn_mass(S, 0.6, 1.0, causal=True).tolist() == [1, 2, 3, 4, 5, 6]
+
+
+# ------------------------------------------------- straight-through backward ----
+def _pm1(x):
+    # {-1, +1} with x >= 0 -> +1, written here independently of oracle.binarize
+    return np.where(np.asarray(x) >= 0, 1.0, -1.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_with_every_key_kept_matches_torch_autograd(causal):
+    """N >= n keeps every visible key, so the path is dense (masked) softmax
+    attention on the +-1 matrices; with the straight-through estimator on the
+    standardized inputs (sign's derivative taken as 1, sigma constant) its
+    gradients are what torch's float64 autograd gives for
+    u = x / sigma;  b = u + (sign(u) - u).detach().  Catches a dropped -D_i
+    term, a transposed dS, a missing scale or 1/sigma, and dV from the wrong
+    weights."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(31 + causal)
+    n, d, scale, sq, sk = 9, 7, 0.37, 1.7, 0.6
+    q, k, v, dout = (rng.standard_normal((n, d)) for _ in range(4))
+    r = oracle.backward(q, k, v, dout, n + 3, scale, causal, sigma_q=sq, sigma_k=sk)
+    tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    uq, uk = tq / sq, tk / sk
+    bq = uq + (torch.where(uq >= 0, 1.0, -1.0) - uq).detach()
+    bk = uk + (torch.where(uk >= 0, 1.0, -1.0) - uk).detach()
+    z = scale * (bq @ bk.T)
+    if causal:
+        z = z.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    out = torch.softmax(z, dim=-1) @ tv
+    (out * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(r["dq"], tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("d,n,topn,causal", [(5, 11, 4, False), (5, 11, 4, True), (3, 8, 2, False),
+                                              (33, 10, 5, True)])
+def test_backward_matches_finite_differences_with_the_kept_sets_fixed(d, n, topn, causal):
+    """Central differences (float64) of f = sum(dout * out) with the kept
+    sets held at the oracle's choice, the +-1 matrices and V perturbed as real
+    numbers.  f is written here as a masked dense softmax (keep mask -> -inf
+    elsewhere), not with the oracle's per-row loop; few feature values (small
+    d) make ties at the threshold common."""
+    rng = np.random.default_rng(100 * d + n + topn + causal)
+    q, k, v, dout = (rng.standard_normal((n, d)) for _ in range(4))
+    scale = 0.45
+    r = oracle.backward(q, k, v, dout, topn, scale, causal)
+    keep = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        keep[i, r["idx"][i][r["idx"][i] >= 0]] = True
+
+    def f(bq, bk, vv):
+        z = np.where(keep, scale * (bq @ bk.T), -np.inf)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return float(np.sum(dout * (p @ vv)))
+
+    bq0, bk0 = _pm1(q), _pm1(k)
+    h = 1e-6
+    for name, base, grad in (("bq", bq0, r["dq"]), ("bk", bk0, r["dk"]), ("v", v, r["dv"])):
+        for i, c in [(0, 0), (n // 2, d - 1), (n - 1, d // 2), (1, 1 % d)]:
+            plus, minus = base.copy(), base.copy()
+            plus[i, c] += h
+            minus[i, c] -= h
+            args_p = {"bq": (plus, bk0, v), "bk": (bq0, plus, v), "v": (bq0, bk0, plus)}[name]
+            args_m = {"bq": (minus, bk0, v), "bk": (bq0, minus, v), "v": (bq0, bk0, minus)}[name]
+            fd = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(fd - grad[i, c]) <= 1e-7 * (1 + abs(fd)), (name, i, c, fd, grad[i, c])
+
+
+def test_backward_two_kept_keys_closed_form():
+    """One row keeping two keys with logits s1 > s2: p1 = logistic(scale (s1 - s2)),
+    dS_1 = -dS_2 = scale p1 p2 dout.(V1 - V2), dV_1 = p1 dout, dV_2 = p2 dout,
+    and the dropped key gets nothing."""
+    q = np.array([[1.0, 1.0, 1.0, 1.0]])
+    k = np.array([[1.0, 1.0, 1.0, 1.0],      # s = 4
+                  [1.0, 1.0, 1.0, -1.0],     # s = 2
+                  [-1.0, -1.0, -1.0, -1.0]])  # s = -4, dropped
+    v = np.array([[0.5, -1.0, 2.0, 0.0], [1.5, 0.25, -1.0, 3.0], [9.0, 9.0, 9.0, 9.0]])
+    dout = np.array([[1.0, -2.0, 0.5, 1.0]])
+    scale = 0.3
+    p1 = 1.0 / (1.0 + math.exp(-scale * 2.0))
+    p2 = 1.0 - p1
+    g = scale * p1 * p2 * float(dout[0] @ (v[0] - v[1]))
+    r = oracle.backward(q, k, v, dout, 2, scale)
+    np.testing.assert_allclose(r["dv"], [p1 * dout[0], p2 * dout[0], np.zeros(4)], rtol=1e-14, atol=1e-15)
+    # dq = dS_1 Bk_1 + dS_2 Bk_2;  dk_j = dS_j Bq
+    np.testing.assert_allclose(r["dq"][0], g * k[0] - g * k[1], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(r["dk"], [g * q[0], -g * q[0], np.zeros(4)], rtol=1e-13, atol=1e-15)
+
+
+def test_backward_invariants():
+    """Softmax gradients sum to zero over a row's kept keys (so sum_i dq_i .
+    1-direction checks hold), dV sums to sum_i dout_i over the keys, the
+    gradient is linear in dout, and the row-block size changes nothing."""
+    rng = np.random.default_rng(5)
+    n, d, topn = 40, 6, 9
+    q, k, v, dout = (rng.standard_normal((n, d)) for _ in range(4))
+    bq, bk = oracle.binarize(q), oracle.binarize(k)
+    S = oracle.logits(bq, bk)
+    idx = oracle.select_topn(S, topn, True)
+    ds, dv, e_ds, _ = oracle.sparse_softmax_av_backward(S, idx, v, dout, 0.5)
+    assert np.all(np.abs(ds.sum(axis=1)) <= 1e-13 * (1 + e_ds.sum(axis=1)))
+    assert np.all(ds[idx < 0] == 0)
+    np.testing.assert_allclose(dv.sum(axis=0), dout.sum(axis=0), rtol=0, atol=1e-12)
+    r1 = oracle.backward(q, k, v, dout, topn, 0.5, True)
+    r2 = oracle.backward(q, k, v, 2.5 * dout, topn, 0.5, True, block=7)
+    for x in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(r2[x], 2.5 * r1[x], rtol=1e-12, atol=1e-13)
+    assert np.all(r1["e_dq"] >= np.abs(r1["dq"])) and np.all(r1["e_dv"] >= np.abs(r1["dv"]))
