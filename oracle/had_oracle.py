@@ -327,49 +327,45 @@ def sparse_softmax_av_backward(S, idx, v, dout, scale: float):
     schedule whose later stages finish the binarization with a
     straight-through estimator, i.e. the forward pass is this path and the
     backward pass treats sign() as the identity.  The top-N selection is a
-    discrete choice; its gradient is taken with the kept sets held fixed, so
-    for row i with kept set K_i and p_ij = softmax over K_i of scale * S_ij:
+    discrete choice; its gradient is taken with the kept sets held fixed.  In
+    matrix form, with M the keep mask of idx and P the softmax of scale * S
+    over each row's kept keys (0 elsewhere):
 
-        dP_ij = dout_i . V_j                      (j in K_i)
-        D_i   = sum_{j in K_i} p_ij dP_ij
-        dS_ij = scale * p_ij * (dP_ij - D_i)      (0 outside K_i)
-        dV_j  = sum_i p_ij dout_i
+        dP = dout V^T,   D = rowsum(P * dP),   dS = scale * P * (dP - D),
+        dV = P^T dout
 
-    All in float64.  Returns (ds, dv, e_ds, e_dv): ds [rows, topn] aligned with
-    idx (0 where idx == -1), dv [n_keys, d], and the magnitudes used for
-    tolerances, e_ds_ij = scale * p_ij * (a_ij + A_i) with a_ij = sum_c
-    |dout_ic| |V_jc| and A_i = sum_j p_ij a_ij (what the terms of dS_ij add up
-    to in absolute value), and e_dv_jc = sum_i p_ij |dout_ic|.
+    (dS is 0 outside the kept sets because P is).  All in float64.  Returns
+    dense (dS, dV, e_ds, e_dv): e_ds = scale * P * (a + A) with a = |dout|
+    |V|^T and A = rowsum(P * a) is what the terms of dS add up to in absolute
+    value, e_dv = P^T |dout|; they set the tolerances.
     """
-    S = np.asarray(S)
+    S = np.asarray(S, dtype=np.float64)
     idx = np.asarray(idx)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
-    rows = S.shape[0]
-    ds = np.zeros(idx.shape, dtype=np.float64)
-    e_ds = np.zeros(idx.shape, dtype=np.float64)
-    dv = np.zeros_like(v)
-    e_dv = np.zeros_like(v)
-    for r in range(rows):
-        m = int(np.count_nonzero(idx[r] >= 0))
-        kept = idx[r, :m]
-        if m == 0:
-            continue
-        z = float(scale) * S[r, kept].astype(np.float64)
-        e = np.exp(z - z.max())
-        p = e / e.sum()
-        dp = v[kept] @ dout[r]
-        D = float(p @ dp)
-        ds[r, :m] = float(scale) * p * (dp - D)
-        dv[kept] += np.outer(p, dout[r])
-        a = np.abs(v[kept]) @ np.abs(dout[r])
-        e_ds[r, :m] = float(scale) * p * (a + float(p @ a))
-        e_dv[kept] += np.outer(p, np.abs(dout[r]))
-    return ds, dv, e_ds, e_dv
+    rows, n_keys = S.shape
+    keep = np.zeros((rows, n_keys), dtype=bool)
+    r_of, c_of = np.nonzero(idx >= 0)
+    keep[r_of, idx[r_of, c_of]] = True
+    z = np.where(keep, float(scale) * S, -np.inf)
+    zmax = np.max(z, axis=1, keepdims=True)
+    zmax[~np.isfinite(zmax)] = 0.0
+    e = np.where(keep, np.exp(z - zmax), 0.0)
+    tot = e.sum(axis=1, keepdims=True)
+    P = e / np.where(tot > 0, tot, 1.0)
+    dP = dout @ v.T
+    D = np.sum(P * dP, axis=1, keepdims=True)
+    dS = float(scale) * P * (dP - D)
+    dV = P.T @ dout
+    a = np.abs(dout) @ np.abs(v).T
+    A = np.sum(P * a, axis=1, keepdims=True)
+    e_ds = float(scale) * P * (a + A)
+    e_dv = P.T @ np.abs(dout)
+    return dS, dV, e_ds, e_dv
 
 
 def backward(q, k, v, dout, topn: int, scale: float, causal: bool = False,
-             sigma_q: float = 1.0, sigma_k: float = 1.0, block: int = 2048):
+             sigma_q: float = 1.0, sigma_k: float = 1.0, block: int = 512):
     """Straight-through backward of the whole path on one head.
 
     Forward: Bq = sign(q / sigma_q), Bk = sign(k / sigma_k) (binarize()),
@@ -405,15 +401,12 @@ def backward(q, k, v, dout, topn: int, scale: float, causal: bool = False,
         S = logits(bq[rows], bk)
         idx = select_topn(S, topn, causal, row_index=rows)
         idx_all[rows] = idx
-        ds, dvb, e_ds, e_dvb = sparse_softmax_av_backward(S, idx, v, dout[rows], scale)
-        dv += dvb
+        dS, dVb, e_ds, e_dvb = sparse_softmax_av_backward(S, idx, v, dout[rows], scale)
+        dq[rows] = dS @ bk
+        dk += dS.T @ bq[rows]
+        dv += dVb
+        e_dq[rows] = e_ds.sum(axis=1, keepdims=True)
+        e_dk += e_ds.sum(axis=0)[:, None]
         e_dv += e_dvb
-        for t, r in enumerate(rows):
-            m = int(np.count_nonzero(idx[t] >= 0))
-            kept = idx[t, :m]
-            dq[r] = ds[t, :m] @ bk[kept]
-            e_dq[r] = e_ds[t, :m].sum()
-            dk[kept] += np.outer(ds[t, :m], bq[r])
-            e_dk[kept] += e_ds[t, :m][:, None]
     return {"dq": dq / sigma_q, "dk": dk / sigma_k, "dv": dv,
             "e_dq": e_dq / sigma_q, "e_dk": e_dk / sigma_k, "e_dv": e_dv, "idx": idx_all}

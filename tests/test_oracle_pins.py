@@ -478,7 +478,11 @@ def test_backward_invariants():
     idx = oracle.select_topn(S, topn, True)
     ds, dv, e_ds, _ = oracle.sparse_softmax_av_backward(S, idx, v, dout, 0.5)
     assert np.all(np.abs(ds.sum(axis=1)) <= 1e-13 * (1 + e_ds.sum(axis=1)))
-    assert np.all(ds[idx < 0] == 0)
+    kept = np.zeros(ds.shape, dtype=bool)
+    for i in range(n):
+        kept[i, idx[i][idx[i] >= 0]] = True
+    assert np.all(ds[~kept] == 0) and np.count_nonzero(kept, axis=1).tolist() == \
+        [min(topn, i + 1) for i in range(n)]
     np.testing.assert_allclose(dv.sum(axis=0), dout.sum(axis=0), rtol=0, atol=1e-12)
     r1 = oracle.backward(q, k, v, dout, topn, 0.5, True)
     r2 = oracle.backward(q, k, v, 2.5 * dout, topn, 0.5, True, block=7)
