@@ -433,6 +433,8 @@ def main():
                     help="for HBM counter runs: 3 attention launches, then one plain "
                          "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
+    if args.traffic_probe or args.attention_only:
+        args.no_cpu_baseline = True  # profiling runs: no worker processes under the profiler
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only; --gpus must be 1 (the path would shard by "

@@ -236,6 +236,54 @@ had_status had_forward_noalloc(const float* q, const float* k, const void* v,
                                float* sigma_k, uint32_t* dev_status,
                                void* stream);
 
+/* Workspace bytes that had_backward needs for shape s (0 for an invalid
+ * shape or d > 128). */
+size_t had_backward_workspace_bytes(had_shape s);
+
+/*
+ * had_backward - the straight-through backward of had_attention, for the
+ * training stages that finish the binarization with a straight-through
+ * estimator.
+ *
+ * Defined by: Pith review, "What carries the argument" (a four-stage
+ * annealing schedule: a scaled tanh approaching sign, then a straight-through
+ * estimator finishing the binarization); the forward pass is had_attention's
+ * path.  Readings: sign's derivative is taken as 1 on the standardized input
+ * x / sigma (the plain straight-through estimator) with sigma a calibrated
+ * constant, and the top-N selection, a discrete choice, is held fixed.  For
+ * row i with kept set K_i (exactly had_attention's) and p_ij its softmax
+ * weights:
+ *   dP_ij = dout_i . V_j,  D_i = dout_i . out_i,
+ *   dS_ij = scale * p_ij * (dP_ij - D_i) for j in K_i (0 elsewhere),
+ *   dv_j  = sum_i p_ij dout_i,
+ *   dq_i  = (sum_j dS_ij Bk_j) / sigma_q,  dk_j = (sum_i dS_ij Bq_i) / sigma_k,
+ * with Bq, Bk the +-1 rows the sign words encode.
+ *
+ *  qbits, kbits, v, v_dtype, topn, scale, causal: as had_attention (the
+ *               same values as the forward call).  d <= 128.
+ *  out          [B,H,n,d] float32: had_attention's output for these inputs.
+ *  dout         [B,H,n,d] float32: the gradient of the loss at out.
+ *  sigma_q, sigma_k  device float* (had_pack's sigma), or NULL for 1
+ *               (gradients with respect to the standardized inputs).
+ *  dq, dk, dv   [B,H,n,d] float32 outputs, device; every element written.
+ *  workspace    had_backward_workspace_bytes(s) bytes, 256-byte aligned (per
+ *               row statistics; no initial contents needed).  Calls that may
+ *               overlap need distinct workspaces.
+ *  All pointers 4-byte aligned.  Precision: integer logits and selection;
+ *  float32 weights, products and sums (no floating-point atomics: results are
+ *  identical run to run).
+ *  Errors: HAD_ERR_INVALID_ARG for null or misaligned pointers, bad sizes,
+ *  topn < 1, bad scale, causal or v_dtype, a small workspace;
+ *  HAD_ERR_UNSUPPORTED for d > 128 or n above HAD_MAX_SEQ.
+ */
+had_status had_backward(const uint32_t* qbits, const uint32_t* kbits,
+                        const void* v, had_dtype v_dtype, had_shape s,
+                        int64_t topn, float scale, int causal,
+                        const float* out, const float* dout,
+                        const float* sigma_q, const float* sigma_k,
+                        float* dq, float* dk, float* dv, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /*
  * had_logits - inspection export of the integer logits s = d - 2*Hamming
  * computed by the same logit stage as had_attention (no mask, every key).

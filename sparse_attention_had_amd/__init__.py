@@ -111,6 +111,11 @@ def load_library():
         lib.had_forward_noalloc.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P,
                                             P, P]
         lib.had_forward_noalloc.restype = I
+        lib.had_backward_workspace_bytes.argtypes = [Shape]
+        lib.had_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.had_backward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P, P, P,
+                                     ctypes.c_size_t, P]
+        lib.had_backward.restype = I
         lib.had_pack_calibrate.argtypes = [P, Shape, P, P, P, ctypes.c_size_t, P, P]
         lib.had_pack_calibrate.restype = I
         lib.had_sigma_from_state.argtypes = [P, P, P]
@@ -378,6 +383,53 @@ def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int
     if not with_sigma:
         return out, qbits, kbits, None, None
     return out, qbits, kbits, sigma_q, sigma_k
+
+
+def backward(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+             dout: torch.Tensor, topn: int, scale: float, causal: bool = False, *,
+             sigma_q: torch.Tensor | None = None, sigma_k: torch.Tensor | None = None,
+             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+             dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Straight-through backward of attention() (had_backward): returns (dq, dk, dv)
+    float32 [B,H,n,d].  out is attention()'s output for the same inputs, dout
+    the gradient at out; sigma_q / sigma_k (1-element device tensors, e.g. from
+    pack()) divide dq / dk, None meaning 1."""
+    lib = load_library()
+    _need_cuda(qbits, "qbits", torch.int32)
+    _need_cuda(kbits, "kbits", torch.int32)
+    _need_cuda(v, "v")
+    _need_cuda(out, "out", torch.float32)
+    _need_cuda(dout, "dout", torch.float32)
+    B, H, n, d = _shape4(v, "v")
+    W = words_per_row(d)
+    if tuple(qbits.shape) != (B, H, n, W) or tuple(kbits.shape) != (B, H, n, W):
+        raise ValueError("qbits/kbits must have shape [B, H, n, ceil(d/32)]")
+    if tuple(out.shape) != (B, H, n, d) or tuple(dout.shape) != (B, H, n, d):
+        raise ValueError("out and dout must have the shape of v")
+    dev = v.device
+    grads = []
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        t = torch.empty((B, H, n, d), dtype=torch.float32, device=dev) if t is None else t
+        _need_cuda(t, name, torch.float32)
+        if tuple(t.shape) != (B, H, n, d):
+            raise ValueError(f"{name} must have the shape of v")
+        grads.append(t)
+    ptrs = []
+    for t, name in ((sigma_q, "sigma_q"), (sigma_k, "sigma_k")):
+        if t is not None:
+            _need_cuda(t, name, torch.float32)
+        ptrs.append(None if t is None else t.data_ptr())
+    shape = Shape(B, H, n, d)
+    need = int(lib.had_backward_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(dev, stream, need)
+    _need_cuda(workspace, "workspace")
+    _check("had_backward", lib.had_backward(
+        qbits.data_ptr(), kbits.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(topn),
+        float(scale), int(bool(causal)), out.data_ptr(), dout.data_ptr(), ptrs[0], ptrs[1],
+        grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(dev, stream)))
+    return tuple(grads)
 
 
 def decode_workspace_bytes(batch: int, heads: int, n_q: int, n_k: int, k_stride: int,

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libhad.so")
 LIB_POPCOUNT = os.path.join(PKG, "libhad_popcount.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip"]
+SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -564,6 +564,44 @@ void had_attn_kernel(AttnArgs a) {
   const uint32_t auT = lutc + 2u * static_cast<uint32_t>(uT);
   uint32_t sp = 0u - static_cast<uint32_t>(quota) - (auT << 15);
 
+  if (MODE == 4) {
+    // ===================================================== row statistics export
+    // For a backward pass that visits the keys in another order: Z in float64
+    // from the histogram with float32 weights exp(-2*scale*t), and the index
+    // of the last kept key at the threshold.  The kept keys at the threshold
+    // are the first r_tie of them in key order, so a key j with logit at the
+    // threshold is kept exactly when j <= that index; it is found by walking
+    // each half's keys in order as the selection export does (half 1's keys
+    // all follow half 0's).
+    double z = 0.0;
+    if (Ni > 0) {
+      for (int b = hmin; b <= T; ++b) {
+        const uint32_t x = hq[b * 32];
+        const int cnt = b < T ? static_cast<int>(x & 0xFFFFu) + static_cast<int>(x >> 16) : r_tie;
+        z += static_cast<double>(cnt) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
+      }
+    }
+    int last_tie = -1;
+    make_q(0x02u, 0xFCu);  // +-2
+    k_sweep(lutc, false, [&](const v16i& t, int gc, auto) {
+      const int kbase = half * Hh + 16 * gc;
+      const int L = lim - kbase;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t au = static_cast<uint32_t>(t[i]);
+        const bool keep = i < L && static_cast<int32_t>((au << 15) + sp) < 0;
+        if (keep && au == auT) last_tie = kbase + i;
+        sp += (au == auT) ? 1u : 0u;
+      }
+    });
+    last_tie = max(last_tie, __shfl_xor(last_tie, 32, 64));  // lanes L and L ^ 32 share a row
+    if (qvalid && half == 0) {
+      int32_t* dst = a.rowstats + (bh_local * n + i_row) * static_cast<int64_t>(4);
+      *reinterpret_cast<int4*>(dst) = make_int4(T, last_tie, hmin, __builtin_bit_cast(int32_t, static_cast<float>(z)));
+    }
+    return;
+  }
+
   if (MODE == 1) {
     // ======================================================= selection export
     int pos = half ? (below0 + quota0) : 0;
@@ -963,8 +1001,11 @@ had_status launch_one(const AttnArgs& args, hipStream_t st) {
   AttnArgs a = args;
   a.balance = blocks <= resident_capacity<W, VF32, MODE, VDIRECT>() ? 1 : 0;
   had_attn_kernel<W, VF32, MODE, VDIRECT><<<static_cast<unsigned>(blocks), C::kThreads, 0, st>>>(a);
-  return check_launch(MODE == 0 ? "had_attention"
-                      : (MODE == 1 ? "had_select" : (MODE == 2 ? "had_logits" : "had_topn_mass")));
+  return check_launch(MODE == 0   ? "had_attention"
+                      : MODE == 1 ? "had_select"
+                      : MODE == 2 ? "had_logits"
+                      : MODE == 3 ? "had_topn_mass"
+                                  : "had_backward (row statistics)");
 }
 
 template <int W>
@@ -981,6 +1022,8 @@ had_status launch_w(AttnMode mode, const AttnArgs& a, hipStream_t st) {
       return launch_one<W, false, 2>(a, st);
     case AttnMode::Mass:
       return launch_one<W, false, 3>(a, st);
+    case AttnMode::Stats:
+      return launch_one<W, false, 4>(a, st);
   }
   return fail(HAD_ERR_INVALID_ARG, "unknown mode");
 }

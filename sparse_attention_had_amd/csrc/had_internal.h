@@ -133,7 +133,7 @@ __device__ inline void sigma_from_partials(const double2* partials, int nparts, 
 }
 
 // ---- attention family (had_attention.hip) ----
-enum class AttnMode : int { Attend = 0, Select = 1, Logits = 2, Mass = 3 };
+enum class AttnMode : int { Attend = 0, Select = 1, Logits = 2, Mass = 3, Stats = 4 };
 
 struct AttnArgs {
   const uint32_t* qbits;
@@ -155,6 +155,10 @@ struct AttnArgs {
   int16_t* logits;   // Logits output [bh_count, row_count, n]
   double mass;       // Mass: softmax mass to reach
   int32_t* nmass;    // Mass output [bh_count, n]
+  // Stats output [bh_count, n, 4]: threshold bin T, index of the last kept key
+  // whose logit sits at the threshold (-1 if none), h_min, and Z (float bits)
+  // = the sum over the kept keys of exp(-2*scale*(h - h_min))
+  int32_t* rowstats;
   int balance;       // set by the launcher: the whole grid is resident at once
   // Optional sigma finalize (fused forward call): wave 0 of the last block
   // turns the partials of a preceding pack launch into sigma_out[t].

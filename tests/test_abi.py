@@ -253,3 +253,31 @@ def test_forward_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
     assert f(shape=Shape(1, 2, 128, 0)) == INVALID
     assert f(shape=Shape(1, 2, 70000, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
+
+
+def test_backward_rejects_bad_arguments(lib):
+    s = Shape(2, 3, 100, 64)
+    wsb = lib.had_backward_workspace_bytes(s)
+    assert wsb >= 2 * 3 * 100 * 20
+    assert lib.had_backward_workspace_bytes(Shape(2, 3, 100, 129)) == 0
+    assert lib.had_backward_workspace_bytes(Shape(0, 3, 100, 64)) == 0
+
+    def f(qb=A16, kb=A16B, v=A16C, vdt=1, shape=s, topn=8, scale=0.125, causal=0, out=0x40000,
+          dout=0x50000, sq=None, sk=None, dq=0x60000, dk=0x70000, dv=0x80000, ws=0x100000, n=wsb):
+        return lib.had_backward(qb, kb, v, vdt, shape, topn, scale, causal, out, dout, sq, sk, dq, dk,
+                                dv, ws, n, None)
+
+    assert f(qb=None) == INVALID
+    assert f(dout=None) == INVALID
+    assert f(dv=0x80002) == INVALID
+    assert f(sq=0x90002) == INVALID
+    assert f(vdt=3) == INVALID
+    assert f(topn=0) == INVALID
+    assert f(scale=float("inf")) == INVALID
+    assert f(causal=2) == INVALID
+    assert f(ws=None) == INVALID
+    assert f(ws=0x100010) == INVALID
+    assert f(n=wsb - 1) == INVALID
+    assert f(shape=Shape(2, 3, 100, 129)) == UNSUPPORTED
+    assert f(shape=Shape(2, 3, 70000, 64)) == UNSUPPORTED
+    assert lib.had_last_error() != b""
