@@ -166,9 +166,11 @@ def _oracle_slice(i):
     softmax, AV).  Returns the query rows done."""
     import oracle
 
-    kind, q, k, v, topn, scale, causal, q_pos0 = _TASKS[i]
+    kind, q, k, v, topn, scale, causal, extra = _TASKS[i]
     if kind == "decode":
-        oracle.decode(q, k, v, topn, scale, q_pos0=q_pos0, causal=causal)
+        oracle.decode(q, k, v, topn, scale, q_pos0=extra, causal=causal)
+    elif kind == "backward":
+        oracle.backward(q, k, v, extra, topn, scale, causal)
     else:
         oracle.sigma(q)
         oracle.forward(q, k, v, topn, scale, causal=causal)
@@ -286,6 +288,124 @@ def decode_model(w, fp32_rows=False):
     qbytes = w.dim * 4 if fp32_rows else W * 4
     per_slice = w.n_k * W * 4 + kept * w.dim * vbytes + w.n_q * (qbytes + w.dim * 4)
     return {"kept": bh * kept, "hbm_bytes": bh * per_slice}
+
+
+def backward_model(w):
+    """Work of one had_backward call on workload w.  Algorithmic: per kept pair
+    dP, dV, dQ and dK contributions, 2d flops each (8d), plus XOR + popcount
+    per word and the keep test per visible pair in each of the three launches.
+    Dense-masked: the fp32 matrix-core products the kernels issue, 32 x 32
+    tiles of (row, key) over every tile with a visible pair, 4d flops per pair
+    of a tile in the dQ launch (dP, dS Bk) and 6d in the dK/dV launch (dP,
+    P^T dout, dS^T Bq)."""
+    m = work_model(w)
+    W = (w.dim + 31) // 32
+    d = w.dim
+    n = w.seq
+    tiles = 0  # 32 x 32 (row, key) tiles with a visible pair, per slice
+    for t in range((n + 31) // 32):
+        tiles += (t + 1) if w.causal else (n + 31) // 32
+    bh = w.batch * w.heads
+    dense_pairs = bh * tiles * 1024
+    return {"kept": m["kept"], "visible_pairs": m["visible_pairs"],
+            "flops": 8.0 * d * m["kept"],
+            "int_ops": 3.0 * m["visible_pairs"] * (2 * W + 2),
+            "mfma_fp32_flops": 10.0 * d * dense_pairs,
+            "hbm_bytes": bh * n * (2 * W * 4 + d * (2 if w.v_dtype == "bf16" else 4) + 2 * d * 4 + 3 * d * 4)}
+
+
+def backward_cpu_baseline(w, inp, dout, budget_s, single_budget_s=None):
+    def tasks():
+        for bh in range(w.batch * w.heads):
+            b, h = divmod(bh, w.heads)
+            yield ("backward", inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale,
+                   w.causal, dout[b, h])
+
+    return _baseline(w.batch * w.heads, f"all {w.seq} rows each (sign, logits, stable-sort top-N, "
+                     "softmax, dP, dS, dQ, dK, dV in float64)", tasks, budget_s, single_budget_s)
+
+
+def bench_backward(args, w):
+    """One step = had_backward on workload w: the straight-through backward
+    (row statistics, dQ, dK and dV; 3 launches) with the sign words, V, the
+    forward output and a synthetic dout resident in HBM."""
+    import torch
+    import sparse_attention_had_amd as had
+    from had_workloads import workload_inputs
+
+    inp = workload_inputs(w)
+    dout_np = np.random.default_rng(w.seed + 1000).standard_normal(
+        (w.batch, w.heads, w.seq, w.dim)).astype(np.float32)
+    cpu = (None if args.no_cpu_baseline else
+           backward_cpu_baseline(w, inp, dout_np, args.cpu_budget))
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"])
+    v = (v.to(torch.bfloat16) if w.v_dtype == "bf16" else v).to(dev)
+    dout = torch.from_numpy(dout_np).to(dev)
+    qb, sq = had.pack(q)
+    kb, sk = had.pack(k)
+    out = had.attention(qb, kb, v, w.topn, w.scale, w.causal)
+    grads = [torch.empty_like(out) for _ in range(3)]
+    ws = torch.empty(had.load_library().had_backward_workspace_bytes(
+        had.Shape(w.batch, w.heads, w.seq, w.dim)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        had.backward(qb, kb, v, out, dout, w.topn, w.scale, w.causal, sigma_q=sq, sigma_k=sk,
+                     dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    settled = settle(step, args.settle_s)
+    steps = max(1, args.steps // 10) if w.causal else args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    durs = timed_launches(step, stream, 50 if not w.causal else 10, per_group=5 if not w.causal else 1)
+    call_s = float(np.median(durs))
+    m = backward_model(w)
+    achieved = m["flops"] / call_s
+    rec = {
+        "metric": f"query rows/sec of the HAD straight-through backward at n={w.seq},N={w.topn}; "
+                  "% of fp32 matrix-core roofline",
+        "value": w.rows / (ms_step / 1e3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "settle_steps": settled,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq": w.seq,
+                   "dim": w.dim, "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype,
+                   "scale": w.scale,
+                   "step": "had_backward: row statistics, dQ (query-major), dK and dV (key-major); "
+                           "3 launches, fp32 matrix-core products"},
+        "backward_us": call_s * 1e6,
+        "backward_timing": f"median over {len(durs)} groups of back-to-back calls",
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP32_MFMA_PEAK / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK, "traffic": None,
+                     "kernel": "had_backward (row statistics, bwd_dq_kernel, bwd_dkv_kernel)",
+                     "frac_kind": "algorithmic fp32 flops (8d per kept pair) at the dense fp32 "
+                                  "matrix-core peak",
+                     "dense_masked_frac": m["mfma_fp32_flops"] / call_s / FP32_MFMA_PEAK,
+                     "work_per_launch": {k2: float(v2) for k2, v2 in m.items()}},
+    }
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    print(json.dumps(rec), flush=True)
 
 
 def decode_cpu_baseline(w, inp, budget_s, single_budget_s=None):
@@ -429,6 +549,9 @@ def main():
                     help="step = had_pack(Q), had_pack(K), had_attention (5 launches) "
                          "instead of had_forward (2 launches); for a decode workload, "
                          "had_pack(new rows) + had_decode instead of had_decode_forward")
+    ap.add_argument("--backward", action="store_true",
+                    help="time had_backward (the straight-through backward) on the workload "
+                         "instead of the forward step")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for HBM counter runs: 3 attention launches, then one plain "
                          "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")
@@ -449,6 +572,8 @@ def main():
     if name in DECODE_WORKLOADS:
         return bench_decode(args, DECODE_WORKLOADS[name])
     w = WORKLOADS[name]
+    if args.backward:
+        return bench_backward(args, w)
     inp = workload_inputs(w)
     # the oracle baseline runs first, before this process touches the GPU
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget)

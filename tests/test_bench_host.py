@@ -146,3 +146,14 @@ def test_forked_workers_run_every_slice(monkeypatch):
     rec = bench.cpu_baseline(w, inp, 30.0, 30.0)
     assert rec["cores"] == 2 and rec["workers"] == 2
     assert rec["sample"].startswith("6 of 6 ") and rec["single_core"]["sample"].startswith("6 of 6 ")
+
+
+def test_backward_model_by_hand():
+    w = WORKLOADS["t5-base-n1024"]
+    m = bench.backward_model(w)
+    assert m["kept"] == 96 * 1024 * 256
+    assert m["flops"] == 8 * 64 * m["kept"]
+    assert m["mfma_fp32_flops"] == 10 * 64 * 96 * 1024 * 1024  # every 32 x 32 tile is visible
+    c = bench.backward_model(types.SimpleNamespace(batch=1, heads=1, seq=64, dim=32, topn=8,
+                                                    causal=True, v_dtype="bf16"))
+    assert c["mfma_fp32_flops"] == 10 * 32 * 3 * 1024  # tiles (0,0), (1,0), (1,1)
