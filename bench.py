@@ -408,6 +408,76 @@ def bench_backward(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def bench_vgather(args, w):
+    """The attention of workload w computed in the V-gather form: had_decode of
+    the whole sequence (n_q = n_k = n, q_pos0 = 0), which compacts each row's
+    kept keys and reads only their V rows (3 launches), timed beside
+    had_attention (dense-masked V products on the matrix cores) on the same
+    packed inputs.  The work model and roofline are the attention's."""
+    import torch
+    import sparse_attention_had_amd as had
+    from had_workloads import workload_inputs
+
+    inp = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"])
+    v = (v.to(torch.bfloat16) if w.v_dtype == "bf16" else v).to(dev)
+    qb, _ = had.pack(q, with_sigma=False)
+    kb, _ = had.pack(k, with_sigma=False)
+    del q, k
+    out = torch.empty((w.batch, w.heads, w.seq, w.dim), dtype=torch.float32, device=dev)
+    out2 = torch.empty_like(out)
+    ws = torch.empty(had.decode_workspace_bytes(w.batch, w.heads, w.seq, w.seq, w.seq, w.dim),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def gather():
+        had.decode(qb, kb, v, w.topn, w.scale, q_pos0=0, causal=w.causal, out=out, workspace=ws)
+
+    def dense():
+        had.attention(qb, kb, v, w.topn, w.scale, w.causal, out=out2)
+
+    for _ in range(args.warmup):
+        gather()
+        dense()
+    torch.cuda.synchronize()
+    settled = settle(gather, args.settle_s)
+    groups = 10 if w.causal else 50
+    per = 1 if w.causal else 5
+    g = float(np.median(timed_launches(gather, stream, groups, per)))
+    dd = float(np.median(timed_launches(dense, stream, groups, per)))
+    m = work_model(w)
+    rec = {
+        "metric": f"query rows/sec of HAD attention at n={w.seq},N={w.topn} in the V-gather form "
+                  "(had_decode of the whole sequence); % of VALU roofline",
+        "value": w.rows / g,
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": groups * per,
+        "warmup": args.warmup,
+        "settle_steps": settled,
+        "ms_per_step": g * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.v_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq": w.seq, "dim": w.dim,
+                   "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype, "scale": w.scale,
+                   "step": "had_decode with n_q = n_k = n, q_pos0 = 0 (dec_hist, dec_gather, dec_reduce)"},
+        "gather_us": g * 1e6,
+        "dense_masked_attention_us": dd * 1e6,
+        "gather_over_dense": g / dd,
+        "roofline": {"bound": "alu", "achieved": m["lane_ops"] / g / 1e12, "peak": VALU_PEAK / 1e12,
+                     "unit": "Tops/s", "frac": m["lane_ops"] / g / VALU_PEAK, "traffic": None,
+                     "kernel": "had_decode (dec_hist, dec_gather, dec_reduce)",
+                     "work_per_launch": {k2: float(v2) for k2, v2 in m.items()}},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def decode_cpu_baseline(w, inp, budget_s, single_budget_s=None):
     def tasks():
         for bh in range(w.batch * w.heads):
@@ -552,6 +622,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time had_backward (the straight-through backward) on the workload "
                          "instead of the forward step")
+    ap.add_argument("--v-gather", action="store_true",
+                    help="time the workload's attention in the V-gather form (had_decode of the "
+                         "whole sequence) beside had_attention")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for HBM counter runs: 3 attention launches, then one plain "
                          "64 MiB device copy that calibrates FETCH_SIZE / WRITE_SIZE")
@@ -574,6 +647,8 @@ def main():
     w = WORKLOADS[name]
     if args.backward:
         return bench_backward(args, w)
+    if args.v_gather:
+        return bench_vgather(args, w)
     inp = workload_inputs(w)
     # the oracle baseline runs first, before this process touches the GPU
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget)
@@ -591,7 +666,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ws_q = torch.zeros(had.pack_workspace_bytes(q.shape), dtype=torch.uint8, device=dev)
     ws_k = torch.zeros_like(ws_q)
-    ws_f = torch.zeros(2 * ws_q.numel(), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(had.load_library().had_forward_workspace_bytes(had.Shape(*q.shape)),
+                       dtype=torch.uint8, device=dev)
 
     if args.traffic_probe:
         from sparse_attention_had_amd.profiling import COPY_BYTES

@@ -58,7 +58,7 @@ typedef struct {
 } had_shape;
 
 /* Decoding against a key/value cache (had_decode). */
-#define HAD_MAX_DECODE_Q 64            /* new query rows per (batch, head) */
+#define HAD_MAX_DECODE_Q 65536         /* new query rows per (batch, head) */
 #define HAD_MAX_DECODE_KEYS (1 << 22)  /* rows of the cache (k_stride) */
 
 typedef struct {
@@ -354,7 +354,9 @@ size_t had_decode_workspace_bytes(had_decode_shape s);
  *  v      [B,H,k_stride,d] float32 (HAD_F32) or bfloat16 (HAD_BF16) values;
  *         rows >= n_k unused.  4-byte aligned.
  *  q_pos0 position of the first new row (>= 0).  causal = 1: row i sees the
- *         keys j <= q_pos0 + i (and j < n_k); causal = 0: every key.
+ *         keys j <= q_pos0 + i (and j < n_k); causal = 0: every key.  With
+ *         n_q = n_k and q_pos0 = 0 the call computes had_attention's outputs
+ *         for the whole sequence by gathering only the kept V rows.
  *  topn, scale: as had_attention; row i keeps N_i = min(N, visible_i) keys,
  *         lower key index first among equal logits.
  *  out    [B,H,n_q,d] float32.

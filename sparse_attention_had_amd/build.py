@@ -1,7 +1,9 @@
-"""Build libhad.so (gfx950) in-tree with hipcc, and libhad_popcount.so: the
-same library with the attention kernel's logit stage on the vector ALU (XOR +
-popcount) instead of the int8 matrix cores, kept to measure that choice
-(load it with HAD_LIBRARY=.../libhad_popcount.so).
+"""Build libhad.so (gfx950) in-tree with hipcc, plus two measurement builds
+of the same sources: libhad_popcount.so, whose attention kernel takes its
+logit tiles from XOR + popcount on the vector ALU instead of the int8 matrix
+cores, and libhad_fusedq.so, whose had_forward packs only K in a launch of its
+own and forms Q's sign words inside the attention launch.  Load either with
+HAD_LIBRARY=.../libhad_<name>.so.
 
 Usage: python -m sparse_attention_had_amd.build   (or __graft_entry__.build())
 """
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhad.so")
 LIB_POPCOUNT = os.path.join(PKG, "libhad_popcount.so")
+LIB_FUSEDQ = os.path.join(PKG, "libhad_fusedq.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip"]
@@ -66,14 +69,19 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = [(src, "", []) for src in SOURCES]
     jobs.append(("had_attention.hip", "_popcount", ["-DHAD_LOGITS_POPCOUNT=1"]))
+    jobs.append(("had_attention.hip", "_fusedq", ["-DHAD_FUSED_QPACK=1"]))
+    jobs.append(("had_api.hip", "_fusedq", ["-DHAD_FUSED_QPACK=1"]))
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         objs = list(ex.map(_compile, jobs))
     main_objs = objs[:len(SOURCES)]
     _link(main_objs, LIB)
-    pop_objs = [objs[-1] if src == "had_attention.hip" else o for src, o in zip(SOURCES, main_objs)]
+    variant = dict(zip([(j[0], j[1]) for j in jobs], objs))
+    pop_objs = [variant.get((src, "_popcount"), o) for src, o in zip(SOURCES, main_objs)]
     _link(pop_objs, LIB_POPCOUNT)
+    fq_objs = [variant.get((src, "_fusedq"), o) for src, o in zip(SOURCES, main_objs)]
+    _link(fq_objs, LIB_FUSEDQ)
     if verbose:
-        print(f"built {LIB} and {LIB_POPCOUNT}")
+        print(f"built {LIB}, {LIB_POPCOUNT} and {LIB_FUSEDQ}")
     return LIB
 
 

@@ -114,7 +114,12 @@ extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits
 
 extern "C" size_t had_forward_workspace_bytes(had_shape s) {
   if (check_shape(s) != HAD_OK) return 0;
+#if HAD_FUSED_QPACK
+  // the K partials (after an unused Q slot), then one pair per attend wave
+  return 2 * had_pack_workspace_bytes(s) + 2 * sizeof(double) * static_cast<size_t>(attend_wave_count(s));
+#else
   return 2 * had_pack_workspace_bytes(s);
+#endif
 }
 
 namespace had {
@@ -138,6 +143,27 @@ had_status forward_launch(const float* q, const float* k, const void* v, had_dty
   double* part[2] = {nullptr, nullptr};
   if (sigma_q != nullptr) part[0] = ws;
   if (sigma_k != nullptr) part[1] = ws + 2 * pack_partials(s);
+  const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
+#if HAD_FUSED_QPACK
+  // measurement build: K is packed by its own launch, Q inside the attend
+  // launch (one sigma partial pair per wave), then sigma_Q from those pairs
+  const PackJob kjob{k, kbits, part[1]};
+  if ((st = launch_pack(&kjob, 1, s, dev_status, hs)) != HAD_OK) return st;
+  if (!aligned(q, 4)) return failf(HAD_ERR_INVALID_ARG, "%s: q must be 4-byte aligned", who);
+  double* qpart = sigma_q != nullptr ? ws + 4 * pack_partials(s) : nullptr;
+  a.qf = q;
+  a.qf_vec = aligned(q, 16) && s.dim == 32 * words_per_row(s.dim) ? 1 : 0;
+  a.qbits_out = qbits;
+  a.qpartials = qpart;
+  a.dev_status = dev_status;
+  a.sigma_partials[1] = reinterpret_cast<const double2*>(part[1]);
+  a.sigma_out[1] = sigma_k;
+  a.sigma_nparts = pack_partials(s);
+  a.sigma_count = count;
+  if ((st = launch_attention_family(AttnMode::Attend, a, hs)) != HAD_OK) return st;
+  if (sigma_q == nullptr) return HAD_OK;
+  return launch_sigma_finalize_n(qpart, attend_wave_count(s), count, sigma_q, hs);
+#else
   const PackJob jobs[2] = {{q, qbits, part[0]}, {k, kbits, part[1]}};
   if ((st = launch_pack(jobs, 2, s, dev_status, hs)) != HAD_OK) return st;
   a.sigma_partials[0] = reinterpret_cast<const double2*>(part[0]);
@@ -145,8 +171,9 @@ had_status forward_launch(const float* q, const float* k, const void* v, had_dty
   a.sigma_out[0] = sigma_q;
   a.sigma_out[1] = sigma_k;
   a.sigma_nparts = pack_partials(s);
-  a.sigma_count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);
+  a.sigma_count = count;
   return launch_attention_family(AttnMode::Attend, a, hs);
+#endif
 }
 
 }  // namespace

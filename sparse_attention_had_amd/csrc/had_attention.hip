@@ -70,6 +70,16 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr bool kPopcountLogits = HAD_LOGITS_POPCOUNT != 0;
 
+// Build option: the attend launch takes the float32 Q rows and forms their
+// sign words itself (Q's pack fused into the attention launch), writing the
+// words and per-wave sigma partials on the side.  It builds
+// libhad_fusedq.so, the measurement of that fusion against had_forward's
+// separate pack launch.
+#ifndef HAD_FUSED_QPACK
+#define HAD_FUSED_QPACK 0
+#endif
+constexpr bool kFusedQ = HAD_FUSED_QPACK != 0;
+
 // weight table: d+1 weights, then a zero slot in the last bank of its
 // 64-dword row, away from the low entries every row uses
 constexpr int kLutEntries = 320;
@@ -292,7 +302,56 @@ void had_attn_kernel(AttnArgs a) {
   // ---- Q operand: -k*q as bytes, features 32w + 16*half + [0,16); pad = 0
   v4i qx[W];
   uint32_t qwords[W];
-  {
+  // (the fused form is taken only by a forward call, which passes the float32
+  // rows; had_attention in the same build passes sign words as usual)
+  if (kFusedQ && MODE == 0 && a.qf != nullptr) {
+    // float32 Q rows: this lane forms the 16 sign bits of each word that its
+    // half of the Q operand uses (features 32w + 16*half + [0, 16)); the two
+    // halves of a row swap theirs so that half 0 stores the row's words; the
+    // lane's float64 sums of the elements minus the tensor's first element
+    // (0 if not finite), as in had_pack, give one sigma partial pair per wave
+    const float* xr = a.qf + (bh * n + (qvalid ? i_row : 0)) * static_cast<int64_t>(d);
+    const float x0 = a.qf[0];
+    const float csh = __builtin_isfinite(x0) ? x0 : 0.0f;
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const int f0 = 32 * w + 16 * half;
+      float x[16];
+      if (a.qf_vec) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const float4 t = qvalid ? *reinterpret_cast<const float4*>(xr + f0 + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+          x[j] = t.x; x[j + 1] = t.y; x[j + 2] = t.z; x[j + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (qvalid && f0 + j < d) ? xr[f0 + j] : 0.0f;
+      }
+      uint32_t b16 = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool in = qvalid && f0 + j < d;
+        b16 |= static_cast<uint32_t>(in && x[j] < 0.0f) << j;
+        const double y = in ? static_cast<double>(x[j] - csh) : 0.0;
+        s1 += y;
+        s2 = fma(y, y, s2);
+      }
+      qwords[w] = ~(b16 << (16 * half));  // complement: the product is -s (only this half's bits are used)
+      const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b16), 32, 64));
+      if (qvalid && half == 0) a.qbits_out[(bh * n + i_row) * W + w] = b16 | (other << 16);
+    }
+    s1 = wave_sum_f64(s1);
+    s2 = wave_sum_f64(s2);
+    if (lane == 63) {
+      if (a.qpartials != nullptr) {
+        double* pp = a.qpartials + 2 * (static_cast<int64_t>(blockIdx.x) * C::kWaves + wid);
+        pp[0] = s1;
+        pp[1] = s2;
+      }
+      if (s2 != s2 && a.dev_status != nullptr) atomicOr(a.dev_status, HAD_DEV_NAN_INPUT);
+    }
+  } else {
     const uint32_t* qrow = a.qbits + (bh * n + (qvalid ? i_row : 0)) * W;
 #pragma unroll
     for (int w = 0; w < W; ++w) qwords[w] = qvalid ? ~qrow[w] : ~0u;  // complement: the product is -s
@@ -1029,6 +1088,12 @@ had_status launch_w(AttnMode mode, const AttnArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t attend_wave_count(const had_shape& s) {
+  const int W = static_cast<int>(words_per_row(s.dim));
+  const int waves = waves_for(W);
+  return (s.seq + 32 * waves - 1) / (32 * waves) * s.batch * s.heads * waves;
+}
 
 had_status launch_attention_family(AttnMode mode, const AttnArgs& a, hipStream_t st) {
   switch (words_per_row(a.d)) {

@@ -159,6 +159,14 @@ struct AttnArgs {
   // whose logit sits at the threshold (-1 if none), h_min, and Z (float bits)
   // = the sum over the kept keys of exp(-2*scale*(h - h_min))
   int32_t* rowstats;
+  // Build option HAD_FUSED_QPACK (a measurement build): the attend launch
+  // reads float32 Q rows itself, stores their sign words in qbits_out and
+  // one (sum, sum of squares) pair per wave in qpartials for sigma_Q.
+  const float* qf;
+  int qf_vec;          // rows 16-byte aligned and d a multiple of 32: vector loads
+  uint32_t* qbits_out;
+  double* qpartials;
+  uint32_t* dev_status;
   int balance;       // set by the launcher: the whole grid is resident at once
   // Optional sigma finalize (fused forward call): wave 0 of the last block
   // turns the partials of a preceding pack launch into sigma_out[t].
@@ -169,5 +177,11 @@ struct AttnArgs {
 };
 
 had_status launch_attention_family(AttnMode mode, const AttnArgs& a, hipStream_t st);
+// Waves one attend launch of shape s runs (the per-wave sigma partials of
+// the HAD_FUSED_QPACK build).
+int64_t attend_wave_count(const had_shape& s);
+// One wave: sigma from nparts partial pairs of count elements.
+had_status launch_sigma_finalize_n(const double* partials, int64_t nparts, double count, float* sigma,
+                                   hipStream_t st);
 
 }  // namespace had

@@ -406,6 +406,14 @@ had_status launch_pack(const PackJob* jobs, int njobs, const had_shape& s, uint3
   return HAD_OK;
 }
 
+had_status launch_sigma_finalize_n(const double* partials, int64_t nparts, double count, float* sigma,
+                                   hipStream_t st) {
+  if (nparts > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "too many sigma partials");
+  sigma_finalize_kernel<<<1, 64, 0, st>>>(reinterpret_cast<const double2*>(partials),
+                                          static_cast<int>(nparts), count, sigma);
+  return check_launch("sigma finalize");
+}
+
 had_status launch_sigma_finalize(const double* partials, const had_shape& s, float* sigma,
                                  hipStream_t st) {
   const double count = static_cast<double>(s.batch * s.heads * s.seq) * static_cast<double>(s.dim);

@@ -40,11 +40,12 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, fn), fn
 
 
-def test_popcount_logit_build_exports_every_declared_symbol():
-    """libhad_popcount.so (the build with the vector-ALU logit stage) is the
-    same C ABI."""
-    path = os.path.join(ROOT, "sparse_attention_had_amd", "libhad_popcount.so")
-    assert os.path.exists(path), "libhad_popcount.so not built"
+@pytest.mark.parametrize("name", ["libhad_popcount.so", "libhad_fusedq.so"])
+def test_measurement_builds_export_every_declared_symbol(name):
+    """The measurement builds (vector-ALU logit stage; Q's pack inside the
+    attention launch) are the same C ABI."""
+    path = os.path.join(ROOT, "sparse_attention_had_amd", name)
+    assert os.path.exists(path), f"{name} not built"
     alt = ctypes.CDLL(path)
     for fn in declared_functions():
         assert hasattr(alt, fn), fn
@@ -169,7 +170,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(ws=0x100010) == INVALID
     assert dec(wsb=ws_bytes - 1) == INVALID
     assert dec(s=D(1, 2, 0, 1000, 1024, 64)) == INVALID
-    assert dec(s=D(1, 2, 65, 1000, 1024, 64)) == UNSUPPORTED
+    assert dec(s=D(1, 2, 65537, 1000, 1024, 64)) == UNSUPPORTED
     assert dec(s=D(1, 2, 4, 1000, 1024, 300)) == UNSUPPORTED
     assert dec(s=D(1, 2, 4, 1000, (1 << 22) + 1, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
@@ -181,7 +182,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert fwd(q=A16 + 2) == INVALID
     assert fwd(k=None) == INVALID
     assert fwd(wsb=ws_bytes - 1) == INVALID
-    assert fwd(s=D(1, 2, 65, 1000, 1024, 64)) == UNSUPPORTED
+    assert fwd(s=D(1, 2, 65537, 1000, 1024, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
 
 

@@ -104,6 +104,33 @@ def test_decode_d256_key_opposite_to_every_query_sign(nq):
             check_out(out[0, h], r["out"], r["E"], inp["v"], "f32", where=f"head {h} scale {scale}")
 
 
+@pytest.mark.parametrize("case", [(2, 3, 300, 64, 37, True, "f32"), (1, 2, 257, 128, 40, False, "bf16"),
+                                  (1, 1, 97, 5, 10, True, "f32"), (4, 4, 1024, 64, 256, False, "f32")])
+def test_decode_of_the_whole_sequence_is_the_attention(case):
+    """n_q = n_k = n and q_pos0 = 0: had_decode gathers the kept V rows of every
+    row of the sequence, which is had_attention's computation in another form;
+    both match the oracle (fp32 V: 1e-5 * E, far below a tie swap)."""
+    B, H, n, d, topn, causal, vdt = case
+    log(f"decode whole sequence {case}")
+    inp = make_inputs(B, H, n, d, v_dtype=vdt, rank=8, noise="t3", seed=3 * n + d)
+    q_t = torch.from_numpy(inp["q"]).cuda()
+    k_t = torch.from_numpy(inp["k"]).cuda()
+    v_t = torch.from_numpy(inp["v"])
+    v_t = (v_t.to(torch.bfloat16) if vdt == "bf16" else v_t).cuda()
+    qb, _ = had.pack(q_t, with_sigma=False)
+    kb, _ = had.pack(k_t, with_sigma=False)
+    scale = 1.0 / np.sqrt(d)
+    out = had.decode(qb, kb, v_t, topn, scale, q_pos0=0, causal=causal).cpu().numpy()
+    att = had.attention(qb, kb, v_t, topn, scale, causal).cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            rows = np.arange(n) if n <= 300 else np.unique(np.r_[0, n - 1, np.arange(0, n, 37)])
+            r = oracle.forward(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], topn, scale,
+                               causal=causal, rows=rows)
+            check_out(out[b, h][rows], r["out"], r["E"], inp["v"], vdt, where=f"decode slice {(b, h)}")
+            check_out(att[b, h][rows], r["out"], r["E"], inp["v"], vdt, where=f"attention slice {(b, h)}")
+
+
 def test_decode_is_deterministic_and_reuses_its_workspace():
     B, H, nq, nk, d = 2, 4, 8, 3000, 64
     log(f"decode determinism {(B, H, nq, nk, d)}")
