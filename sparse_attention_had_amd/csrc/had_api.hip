@@ -58,7 +58,12 @@ using namespace had;
 extern "C" int64_t had_words_per_row(int64_t dim) { return dim > 0 ? words_per_row(dim) : 0; }
 
 extern "C" const char* had_status_string(had_status st) {
-  switch (st) {
+  // A C caller may pass any int: read the argument's bytes as one instead of
+  // loading a possibly out-of-range enum value.
+  int v;
+  static_assert(sizeof(v) == sizeof(st), "had_status is int-sized");
+  std::memcpy(&v, &st, sizeof(v));
+  switch (v) {
     case HAD_OK: return "HAD_OK";
     case HAD_ERR_INVALID_ARG: return "HAD_ERR_INVALID_ARG";
     case HAD_ERR_UNSUPPORTED: return "HAD_ERR_UNSUPPORTED";
@@ -71,14 +76,14 @@ extern "C" const char* had_last_error(void) { return g_last_error; }
 
 // Checks of had_attention's arguments; fills the launch arguments.
 static had_status attend_args(const uint32_t* qbits, const uint32_t* kbits, const void* v,
-                              had_dtype v_dtype, const had_shape& s, int64_t topn, float scale,
+                              int v_dtype, const had_shape& s, int64_t topn, float scale,
                               int causal, float* out, const char* fn, AttnArgs& a) {
   had_status st;
   if ((st = check_bits(qbits, kbits, fn)) != HAD_OK) return st;
   if (v == nullptr || out == nullptr) return failf(HAD_ERR_INVALID_ARG, "%s: null v or out", fn);
   if (!aligned(v, 16) || !aligned(out, 16))
     return failf(HAD_ERR_INVALID_ARG, "%s: v and out must be 16-byte aligned", fn);
-  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", fn);
+  if (!valid_dtype(v_dtype)) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", fn);
   if (topn < 1) return failf(HAD_ERR_INVALID_ARG, "%s: topn must be >= 1", fn);
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return failf(HAD_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
@@ -87,7 +92,7 @@ static had_status attend_args(const uint32_t* qbits, const uint32_t* kbits, cons
   a.qbits = qbits;
   a.kbits = kbits;
   a.v = v;
-  a.v_dtype = v_dtype;
+  a.v_dtype = static_cast<had_dtype>(v_dtype);
   a.bh_total = s.batch * s.heads;
   a.bh_begin = 0;
   a.bh_count = a.bh_total;
@@ -107,7 +112,8 @@ extern "C" had_status had_attention(const uint32_t* qbits, const uint32_t* kbits
   had_status st = check_shape(s);
   if (st != HAD_OK) return st;
   AttnArgs a;
-  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_attention", a)) != HAD_OK)
+  if ((st = attend_args(qbits, kbits, v, enum_bits(v_dtype), s, topn, scale, causal, out, "had_attention", a)) !=
+      HAD_OK)
     return st;
   return launch_attention_family(AttnMode::Attend, a, static_cast<hipStream_t>(stream));
 }
@@ -127,7 +133,7 @@ namespace {
 
 // The two launches of the forward call; ws holds 2 * pack_partials(s) partial
 // pairs per tensor that asks for sigma (checked by the caller).
-had_status forward_launch(const float* q, const float* k, const void* v, had_dtype v_dtype,
+had_status forward_launch(const float* q, const float* k, const void* v, int v_dtype,
                           const had_shape& s, int64_t topn, float scale, int causal,
                           uint32_t* qbits, uint32_t* kbits, float* out, float* sigma_q,
                           float* sigma_k, double* ws, uint32_t* dev_status, hipStream_t hs,
@@ -193,8 +199,8 @@ extern "C" had_status had_forward(const float* q, const float* k, const void* v,
     if (workspace_bytes < had_forward_workspace_bytes(s))
       return fail(HAD_ERR_INVALID_ARG, "had_forward: workspace smaller than had_forward_workspace_bytes()");
   }
-  return forward_launch(q, k, v, v_dtype, s, topn, scale, causal, qbits, kbits, out, sigma_q, sigma_k,
-                        static_cast<double*>(workspace), dev_status, static_cast<hipStream_t>(stream),
+  return forward_launch(q, k, v, enum_bits(v_dtype), s, topn, scale, causal, qbits, kbits, out, sigma_q,
+                        sigma_k, static_cast<double*>(workspace), dev_status, static_cast<hipStream_t>(stream),
                         "had_forward");
 }
 
@@ -261,15 +267,16 @@ extern "C" had_status had_forward_noalloc(const float* q, const float* k, const 
   if (dev_status != nullptr && !aligned(dev_status, 4))
     return fail(HAD_ERR_INVALID_ARG, "had_forward_noalloc: dev_status must be 4-byte aligned");
   AttnArgs unused;
-  if ((st = attend_args(qbits, kbits, v, v_dtype, s, topn, scale, causal, out, "had_forward_noalloc",
-                        unused)) != HAD_OK)
+  const int vdt = enum_bits(v_dtype);
+  if ((st = attend_args(qbits, kbits, v, vdt, s, topn, scale, causal, out, "had_forward_noalloc", unused)) !=
+      HAD_OK)
     return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
   if (sigma_q != nullptr || sigma_k != nullptr) {
     if ((st = scratch_address(hs, &ws)) != HAD_OK) return st;
   }
-  return forward_launch(q, k, v, v_dtype, s, topn, scale, causal, qbits, kbits, out, sigma_q, sigma_k,
+  return forward_launch(q, k, v, vdt, s, topn, scale, causal, qbits, kbits, out, sigma_q, sigma_k,
                         static_cast<double*>(ws), dev_status, hs, "had_forward_noalloc");
 }
 

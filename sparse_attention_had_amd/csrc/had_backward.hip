@@ -357,7 +357,8 @@ extern "C" had_status had_backward(const uint32_t* qbits, const uint32_t* kbits,
     return fail(HAD_ERR_INVALID_ARG, "had_backward: pointers must be 4-byte aligned");
   if ((sigma_q != nullptr && !aligned(sigma_q, 4)) || (sigma_k != nullptr && !aligned(sigma_k, 4)))
     return fail(HAD_ERR_INVALID_ARG, "had_backward: sigma pointers must be 4-byte aligned");
-  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, "had_backward: unknown v_dtype");
+  const int vdt = enum_bits(v_dtype);
+  if (!valid_dtype(vdt)) return fail(HAD_ERR_INVALID_ARG, "had_backward: unknown v_dtype");
   if (topn < 1) return fail(HAD_ERR_INVALID_ARG, "had_backward: topn must be >= 1");
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(HAD_ERR_INVALID_ARG, "had_backward: scale must be finite and > 0");
@@ -410,7 +411,7 @@ extern "C" had_status had_backward(const uint32_t* qbits, const uint32_t* kbits,
   const int64_t blocks = ((s.seq + kBwdRows - 1) / kBwdRows) * bh;
   if (blocks > 0x7FFFFFFF) return fail(HAD_ERR_UNSUPPORTED, "had_backward: grid too large");
   const unsigned nb = static_cast<unsigned>(blocks);
-  const bool vf32 = v_dtype == HAD_F32;
+  const bool vf32 = vdt == HAD_F32;
   switch (words_per_row(s.dim)) {
     case 1: return launch_bwd<1>(a, vf32, nb, hs);
     case 2: return launch_bwd<2>(a, vf32, nb, hs);

@@ -669,7 +669,7 @@ namespace {
 // had_decode (qbits given) and had_decode_forward (float32 rows qf, whose
 // sign words the histogram launch builds into the workspace).
 had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, const uint32_t* kbits,
-                       const void* v, had_dtype v_dtype, had_decode_shape s, int64_t q_pos0,
+                       const void* v, int v_dtype, had_decode_shape s, int64_t q_pos0,
                        int64_t topn, float scale, int causal, float* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
   had_status st = check_decode_shape(s);
@@ -679,7 +679,7 @@ had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, 
     return failf(HAD_ERR_INVALID_ARG, "%s: null queries, kbits, v or out", who);
   if (!aligned(q, 4) || !aligned(kbits, 4) || !aligned(v, 4) || !aligned(out, 4))
     return failf(HAD_ERR_INVALID_ARG, "%s: queries, kbits, v and out must be 4-byte aligned", who);
-  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", who);
+  if (!valid_dtype(v_dtype)) return failf(HAD_ERR_INVALID_ARG, "%s: unknown v_dtype", who);
   if (topn < 1) return failf(HAD_ERR_INVALID_ARG, "%s: topn must be >= 1", who);
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return failf(HAD_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
@@ -764,7 +764,7 @@ extern "C" had_status had_decode(const uint32_t* qbits, const uint32_t* kbits, c
                                  void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   if (qbits == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_decode: null qbits");
-  return decode_impl("had_decode", qbits, nullptr, kbits, v, v_dtype, s, q_pos0, topn, scale, causal, out,
+  return decode_impl("had_decode", qbits, nullptr, kbits, v, enum_bits(v_dtype), s, q_pos0, topn, scale, causal, out,
                      workspace, workspace_bytes, stream);
 }
 
@@ -774,6 +774,6 @@ extern "C" had_status had_decode_forward(const float* q, const uint32_t* kbits, 
                                          void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   if (q == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_decode_forward: null q");
-  return decode_impl("had_decode_forward", nullptr, q, kbits, v, v_dtype, s, q_pos0, topn, scale, causal,
+  return decode_impl("had_decode_forward", nullptr, q, kbits, v, enum_bits(v_dtype), s, q_pos0, topn, scale, causal,
                      out, workspace, workspace_bytes, stream);
 }

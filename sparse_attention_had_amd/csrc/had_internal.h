@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "had.h"
@@ -35,6 +36,17 @@ inline bool aligned(const void* p, uintptr_t a) {
 }
 
 inline int64_t words_per_row(int64_t d) { return (d + 31) / 32; }
+
+// The int a C caller passed for an enum parameter, read as bytes: a value
+// outside the enum's range must be rejected, not loaded as the enum type.
+template <typename E>
+inline int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  memcpy(&v, &e, sizeof(v));
+  return v;
+}
+inline bool valid_dtype(int v) { return v == HAD_F32 || v == HAD_BF16; }
 
 // Shape checks common to every entry point; seq may not exceed max_seq
 // (HAD_MAX_SEQ for the attention calls, the cache limit for had_pack).
