@@ -544,6 +544,269 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
   a.out[bhq * a.d + c] = sum * invZ;
 }
 
+// ---- single-launch path for few rows ---------------------------------------
+// When there are few (slice, row) pairs (one new token per sequence), one
+// 1024-thread work-group per pair does the row's whole decode and writes its
+// output: no split histograms in memory, no tie hand-off between splits and no
+// reduce launch.  Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys),
+// key order is (u, wave, lane) as in dec_gather.  Distances go to per-wave LDS
+// histograms; wave 0 sums them, finds T, h_min, the tie quota and Z; kept keys
+// get their list slot from per-(u, wave) ballot counts; the kept V rows are
+// gathered 16 bytes of a row per lane with several rows in flight per lane
+// group, the row groups' sums are added in a fixed order and divided by Z.
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / 64;
+constexpr int kOneKPT = 16;                              // keys per thread
+constexpr int kOneMaxKeys = kOneThreads * kOneKPT;       // 16384
+constexpr int kOneMaxList = 8192;                        // kept keys per row (LDS list)
+constexpr int kOneMaxPairs = 512;                        // (slice, row) pairs that take this path
+
+template <int W, bool VF32, bool kVec, bool kKVec, bool kQF>
+__global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
+  __shared__ uint32_t hist[kOneWaves * (HAD_MAX_DIM + 1)];
+  __shared__ uint32_t list[kOneMaxList];  // (key << 9) | h per kept key; then the row-group sums
+  __shared__ float wtab[HAD_MAX_DIM + 1];
+  __shared__ uint32_t cnt[kOneKPT][kOneWaves];  // strict | ties << 16, per (u, wave)
+  __shared__ uint32_t qws[W];
+  __shared__ int sh_T, sh_hmin, sh_quota;
+  __shared__ float sh_invz;
+  float* red = reinterpret_cast<float*>(list);
+  const int64_t bhq = blockIdx.x;
+  const int q = static_cast<int>(bhq % a.nq);
+  const int64_t bh = bhq / a.nq;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = a.d, nb = d + 1;
+  const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk) - 1;
+  const int kend = static_cast<int>(min(static_cast<int64_t>(a.nk), last + 1));  // visible keys [0, kend)
+  const int Ni = min(a.topn, kend);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // the row's sign words (built here from float32 rows for had_decode_forward)
+  if constexpr (kQF) {
+    if (wid == 0) {
+      const float* xr = a.qf + bhq * static_cast<int64_t>(d);
+#pragma unroll
+      for (int w2 = 0; w2 < W; w2 += 2) {
+        const int e = 32 * w2 + lane;
+        const uint64_t m = __ballot(e < d && xr[e < d ? e : 0] < 0.0f);
+        if (lane < 2 && w2 + lane < W) qws[w2 + lane] = static_cast<uint32_t>(m >> (32 * lane));
+      }
+    }
+  } else {
+    if (tid < W) qws[tid] = a.qbits[bhq * W + tid];
+  }
+  for (int t = tid; t < kOneWaves * nb; t += kOneThreads) hist[t] = 0u;
+  for (int t = tid; t <= d; t += kOneThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
+  __syncthreads();
+  uint32_t qw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) qw[w] = qws[w];
+
+  // distances of this thread's keys, a batch of kG keys in flight at a time
+  const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
+  constexpr int kG = W <= 2 ? 8 : (W <= 4 ? 4 : 2);
+  uint32_t hh[kOneKPT];
+  uint32_t* hw = hist + wid * nb;
+#pragma unroll
+  for (int u0 = 0; u0 < kOneKPT; u0 += kG) {
+    uint32_t kw[kG][W];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const int j = (u0 + g) * kOneThreads + tid;
+      if (j < kend) {
+        load_key_words<W, kKVec>(kb + static_cast<int64_t>(j) * W, kw[g]);
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) kw[g][w] = 0u;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      uint32_t h = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[g][w] ^ qw[w]);
+      hh[u0 + g] = h;
+      if ((u0 + g) * kOneThreads + tid < kend) atomicAdd(&hw[h], 1u);
+    }
+  }
+  __syncthreads();
+
+  // wave 0: total histogram, threshold bin T, h_min, tie quota r, Z
+  if (wid == 0) {
+    constexpr int kR = (32 * W + 1 + 63) / 64;
+    uint32_t c[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int b = 64 * r + lane;
+      uint32_t x = 0;
+      if (b < nb) {
+#pragma unroll
+        for (int w = 0; w < kOneWaves; ++w) x += hist[w * nb + b];
+      }
+      c[r] = x;
+    }
+    int T = -1, hmin = -1;
+    uint32_t below = 0, run = 0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const uint32_t incl = wave_scan_incl(c[r]) + run;
+      const uint32_t excl = incl - c[r];
+      const bool hit = 64 * r + lane < nb && excl < static_cast<uint32_t>(Ni) && incl >= static_cast<uint32_t>(Ni);
+      const uint64_t hm = __ballot(hit);
+      if (T < 0 && hm != 0) {
+        const int l = __builtin_ctzll(hm);
+        T = 64 * r + l;
+        below = __builtin_amdgcn_readlane(excl, l);
+      }
+      const uint64_t nz = __ballot(64 * r + lane < nb && c[r] > 0);
+      if (hmin < 0 && nz != 0) hmin = 64 * r + __builtin_ctzll(nz);
+      run = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (T < 0) T = d;  // unreachable: the visible count is >= N_i
+    if (hmin < 0) hmin = 0;
+    const uint32_t rtie = static_cast<uint32_t>(Ni) - below;
+    double z = 0.0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int b = 64 * r + lane;
+      const uint32_t cc = b < T ? c[r] : (b == T ? rtie : 0u);
+      if (cc != 0) z += static_cast<double>(cc) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
+    }
+    z = wave_sum_f64(z);
+    if (lane == 63) {
+      sh_T = T;
+      sh_hmin = hmin;
+      sh_quota = static_cast<int>(rtie);
+      const float zf = static_cast<float>(z);
+      sh_invz = zf > 0.0f ? 1.0f / zf : 0.0f;
+    }
+  }
+  __syncthreads();
+  const uint32_t T = static_cast<uint32_t>(sh_T);
+  const int hmin = sh_hmin;
+  const uint32_t quota = static_cast<uint32_t>(sh_quota);
+
+  // per-(u, wave) counts, then every kept key's slot in key order
+#pragma unroll
+  for (int u = 0; u < kOneKPT; ++u) {
+    const bool vis = u * kOneThreads + tid < kend;
+    const uint64_t sm = __ballot(vis && hh[u] < T);
+    const uint64_t tm = __ballot(vis && hh[u] == T);
+    if (lane == 0)
+      cnt[u][wid] = static_cast<uint32_t>(__builtin_popcountll(sm)) |
+                    (static_cast<uint32_t>(__builtin_popcountll(tm)) << 16);
+  }
+  __syncthreads();
+  uint32_t run = 0;
+#pragma unroll
+  for (int u = 0; u < kOneKPT; ++u) {
+    const int j = u * kOneThreads + tid;
+    const bool vis = j < kend;
+    const bool strict = vis && hh[u] < T;
+    const bool tie = vis && hh[u] == T;
+    const uint64_t sm = __ballot(strict);
+    const uint64_t tm = __ballot(tie);
+    uint32_t wb = 0, ut = 0;
+#pragma unroll
+    for (int w = 0; w < kOneWaves; ++w) {
+      const uint32_t cc = cnt[u][w];
+      wb += w < wid ? cc : 0u;
+      ut += cc;
+    }
+    const uint32_t b = run + wb;
+    const uint32_t sbefore = (b & 0xFFFFu) + static_cast<uint32_t>(__builtin_popcountll(sm & lt_mask));
+    const uint32_t tbefore = (b >> 16) + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
+    if (strict || (tie && tbefore < quota))
+      list[sbefore + min(tbefore, quota)] = (static_cast<uint32_t>(j) << 9) | hh[u];
+    run += ut;
+  }
+  const int nl = Ni;
+  __syncthreads();  // the list is complete
+
+  // gather the kept V rows: lpr lanes per row, 8 features each; R row groups
+  const int lpr = (d + 7) / 8;
+  const int R = kOneThreads / lpr;
+  const int g = tid / lpr, li = tid - (tid / lpr) * lpr;
+  float acc[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) acc[f] = 0.0f;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
+                               bh * static_cast<int64_t>(a.kstride) * d * (VF32 ? 4 : 2);
+  constexpr int kRows = VF32 ? 4 : 8;
+  if (g < R) {
+    const int c0 = 8 * li;
+    for (int e0 = g; e0 < nl; e0 += kRows * R) {
+      uint32_t raw[kRows][VF32 ? 8 : 4];
+      float wr[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int e = e0 + r * R;
+        const uint32_t ent = e < nl ? list[e] : list[e0];
+        const int hb = min(max(static_cast<int>(ent & 0x1FFu) - hmin, 0), d);
+        wr[r] = e < nl ? wtab[hb] : 0.0f;
+        const int64_t jj = min(static_cast<int>(ent >> 9), kend - 1);
+        if constexpr (VF32) {
+          const float* row = reinterpret_cast<const float*>(vbase) + jj * d;
+          if (kVec && c0 + 8 <= d) {
+            const uint4 u0 = *reinterpret_cast<const uint4*>(row + c0);
+            const uint4 u1 = *reinterpret_cast<const uint4*>(row + c0 + 4);
+            raw[r][0] = u0.x; raw[r][1] = u0.y; raw[r][2] = u0.z; raw[r][3] = u0.w;
+            raw[r][4] = u1.x; raw[r][5] = u1.y; raw[r][6] = u1.z; raw[r][7] = u1.w;
+          } else {
+#pragma unroll
+            for (int f = 0; f < 8; ++f) raw[r][f] = c0 + f < d ? __builtin_bit_cast(uint32_t, row[c0 + f]) : 0u;
+          }
+        } else {
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + jj * d;
+          if (kVec && c0 + 8 <= d) {
+            const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
+            raw[r][0] = u.x; raw[r][1] = u.y; raw[r][2] = u.z; raw[r][3] = u.w;
+          } else {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              const uint32_t lo = c0 + 2 * f < d ? row[c0 + 2 * f] : 0u;
+              const uint32_t hi = c0 + 2 * f + 1 < d ? row[c0 + 2 * f + 1] : 0u;
+              raw[r][f] = lo | (hi << 16);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        float x[8];
+        if constexpr (VF32) {
+#pragma unroll
+          for (int f = 0; f < 8; ++f) x[f] = __builtin_bit_cast(float, raw[r][f]);
+        } else {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            x[2 * f] = __builtin_bit_cast(float, raw[r][f] << 16);
+            x[2 * f + 1] = __builtin_bit_cast(float, raw[r][f] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int f = 0; f < 8; ++f) acc[f] = fmaf(wr[r], x[f], acc[f]);
+      }
+    }
+  }
+  __syncthreads();  // every group is done with the list: its space takes the group sums
+  if (g < R) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int c = 8 * li + f;
+      if (c < d) red[g * d + c] = acc[f];
+    }
+  }
+  __syncthreads();
+  const float invz = sh_invz;
+  float* orow = a.out + bhq * static_cast<int64_t>(d);
+  for (int c = tid; c < d; c += kOneThreads) {
+    float sum = 0.0f;
+    for (int gg = 0; gg < R; ++gg) sum += red[gg * d + c];
+    orow[c] = sum * invz;
+  }
+}
+
 // Work split and workspace layout, from the shape alone.  keys_per_split is
 // 256 times a power of two (at most 2048).  The per-(row, key) distance bins
 // are kept when n_q <= W (n_q bytes per key against the 4W bytes of key
@@ -653,6 +916,37 @@ void launch_gather(const DecArgs& a, bool vec, bool kvec, int64_t blocks, hipStr
   }
 }
 
+template <int W, bool VF32, bool kVec, bool kKVec>
+void launch_one_q(const DecArgs& a, int64_t rows, hipStream_t st) {
+  const unsigned nb = static_cast<unsigned>(rows);
+  if (a.qf != nullptr)
+    dec_one_kernel<W, VF32, kVec, kKVec, true><<<nb, kOneThreads, 0, st>>>(a);
+  else
+    dec_one_kernel<W, VF32, kVec, kKVec, false><<<nb, kOneThreads, 0, st>>>(a);
+}
+
+template <int W, bool VF32, bool kVec>
+void launch_one_k(const DecArgs& a, bool kvec, int64_t rows, hipStream_t st) {
+  if constexpr (W % 2 == 0) {
+    if (kvec) {
+      launch_one_q<W, VF32, kVec, true>(a, rows, st);
+      return;
+    }
+  }
+  launch_one_q<W, VF32, kVec, false>(a, rows, st);
+}
+
+template <int W>
+void launch_one(const DecArgs& a, bool vec, bool kvec, int64_t rows, hipStream_t st) {
+  if (a.vf32) {
+    if (vec) launch_one_k<W, true, true>(a, kvec, rows, st);
+    else launch_one_k<W, true, false>(a, kvec, rows, st);
+  } else {
+    if (vec) launch_one_k<W, false, true>(a, kvec, rows, st);
+    else launch_one_k<W, false, false>(a, kvec, rows, st);
+  }
+}
+
 }  // namespace
 }  // namespace had
 
@@ -727,6 +1021,22 @@ had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, 
   // key rows of W words load as 16-byte (W % 4 == 0) or 8-byte (W % 2 == 0)
   // vectors from an aligned base
   const bool kvec = aligned(kbits, a.W % 4 == 0 ? 16 : 8);
+  // 16-byte row slices need 16-byte aligned rows
+  const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
+  if (rows <= kOneMaxPairs && s.n_k <= kOneMaxKeys && a.topn <= kOneMaxList) {
+    // few rows: one work-group per (slice, row), one launch
+    switch (a.W) {
+      case 1: launch_one<1>(a, vec, kvec, rows, hs); break;
+      case 2: launch_one<2>(a, vec, kvec, rows, hs); break;
+      case 3: launch_one<3>(a, vec, kvec, rows, hs); break;
+      case 4: launch_one<4>(a, vec, kvec, rows, hs); break;
+      case 5: launch_one<5>(a, vec, kvec, rows, hs); break;
+      case 6: launch_one<6>(a, vec, kvec, rows, hs); break;
+      case 7: launch_one<7>(a, vec, kvec, rows, hs); break;
+      default: launch_one<8>(a, vec, kvec, rows, hs); break;
+    }
+    return check_launch(who);
+  }
   switch (a.W) {
     case 1: launch_hist<1>(a, kvec, hist_blocks, hs); break;
     case 2: launch_hist<2>(a, kvec, hist_blocks, hs); break;
@@ -738,8 +1048,6 @@ had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, 
     default: launch_hist<8>(a, kvec, hist_blocks, hs); break;
   }
   if ((st = check_launch(who)) != HAD_OK) return st;
-  // 16-byte row slices need 16-byte aligned rows
-  const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
   switch (a.W) {
     case 1: launch_gather<1>(a, vec, kvec, gather_blocks, hs); break;
     case 2: launch_gather<2>(a, vec, kvec, gather_blocks, hs); break;

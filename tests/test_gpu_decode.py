@@ -43,6 +43,10 @@ CASES = [
     (1, 8, 64, 1000, 1000, 64, 100, 936, True, "bf16", 0.125),    # 2 splits of 512 keys, recomputed
     (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 16 splits of 1024 keys, bins
     (1, 32, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 32 splits of 512 keys, bins
+    # more than 512 (slice, row) pairs: the split launches (up to 512 take one work-group each)
+    (1, 520, 1, 3000, 3000, 32, 300, 2999, True, "bf16", 0.25),      # split histograms, distance bins
+    (2, 300, 2, 2048, 2048, 64, 256, 2046, True, "f32", 0.125),      # bins for two rows
+    (1, 600, 1, 1000, 1024, 5, 40, 999, False, "bf16", 0.9),         # d = 5 ties, split path
 ]
 
 
