@@ -78,12 +78,17 @@ __device__ inline float load_v(const void* v, int64_t off, bool vf32) {
 }
 
 // ---- 2. dQ (query-major) -------------------------------------------------
+// Tiles of 32 keys are staged double-buffered: each thread requests its share
+// of tile t + 1 (key words, V values) into registers before computing tile
+// t, and writes it into the other LDS buffer afterwards, so the global loads
+// run under the matrix-core work and one barrier per tile suffices.
 template <int W, bool VF32>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DP = 32 * W;   // padded features
   constexpr int VS = DP + 1;   // LDS row stride of the V tile (no bank conflicts)
-  __shared__ float vt[32 * VS];
-  __shared__ uint32_t kw[32 * W];
+  constexpr int kVPT = DP / 8; // V values per thread per tile (32 * DP / 256)
+  __shared__ float vt[2][32 * VS];
+  __shared__ uint32_t kw[2][32 * W];
   __shared__ float wtab[DP + 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -137,50 +142,100 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
 
   const uint32_t* kbase = a.kbits + bh * static_cast<int64_t>(n) * W;
   const int64_t vbase = bh * static_cast<int64_t>(n) * d;
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // Every thread loads from a valid (clamped) address unconditionally and
+  // zeroes out-of-range values when it writes them, so all its loads are in
+  // flight together.
+  uint32_t pk = 0;
+  uint32_t pv[kVPT];  // raw V values (fp32 bits or a bf16 in the low half)
+  int staged_k0 = 0;  // first key of the tile in pk, pv
+  auto prefetch = [&](int tile) {
     const int k0 = 32 * tile;
-    __syncthreads();  // the previous tile is consumed
-    for (int e = tid; e < 32 * W; e += kBwdThreads) {
-      const int key = min(k0 + e / W, n - 1);
-      kw[e] = kbase[static_cast<int64_t>(key) * W + e % W];
-    }
-    for (int e = tid; e < 32 * DP; e += kBwdThreads) {
+    staged_k0 = k0;
+    pk = kbase[static_cast<int64_t>(min(k0 + min(tid, 32 * W - 1) / W, n - 1)) * W + tid % W];
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const int e = tid + j * kBwdThreads;
       const int r = e / DP, f = e - r * DP;
-      const int key = k0 + r;
-      vt[r * VS + f] = (key < n && f < d) ? load_v(a.v, vbase + static_cast<int64_t>(key) * d + f, VF32) : 0.0f;
+      const int64_t off = vbase + static_cast<int64_t>(min(k0 + r, n - 1)) * d + min(f, d - 1);
+      if constexpr (VF32)
+        pv[j] = __builtin_bit_cast(uint32_t, static_cast<const float*>(a.v)[off]);
+      else
+        pv[j] = static_cast<const uint16_t*>(a.v)[off];
     }
-    __syncthreads();
-    if (tile >= wtiles) continue;
-    // weights of this lane's 16 keys (zero where not kept)
-    float p[16];
+  };
+  auto commit = [&](int buf) {
+    if (tid < 32 * W) kw[buf][tid] = pk;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kl = tile_row(i, half);
-      const int key = k0 + kl;
-      int h = 0;
-#pragma unroll
-      for (int w = 0; w < W; ++w) h += __builtin_popcount(qw[w] ^ kw[kl * W + w]);
-      const bool keep = key < lim && (h < T || (h == T && key <= cut));
-      p[i] = keep ? wtab[min(max(h - hmin, 0), d)] * invZ : 0.0f;
+    for (int j = 0; j < kVPT; ++j) {
+      const int e = tid + j * kBwdThreads;
+      const int r = e / DP, f = e - r * DP;
+      const bool in = staged_k0 + r < n && f < d;
+      const float x = VF32 ? __builtin_bit_cast(float, pv[j]) : __builtin_bit_cast(float, pv[j] << 16);
+      vt[buf][r * VS + f] = in ? x : 0.0f;
     }
-    // dP tile: rows = keys, columns = query rows
-    v16f dp = v16f{};
-#pragma unroll
-    for (int s = 0; s < 16 * W; ++s)
-      dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[ql * VS + 2 * s + half], dr[s], dp, 0, 0, 0);
-    float ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ds[i] = a.scale * p[i] * (dp[i] - D);
-    // dQ^T += Bk^T dS: A = +-1 of feature 32t + ql of key tile_row(i, half)
-#pragma unroll
-    for (int t = 0; t < W; ++t) {
+  };
+  prefetch(0);
+  commit(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int k0 = 32 * tile;
+    if (tile + 1 < ntiles) prefetch(tile + 1);
+    if (tile < wtiles) {
+      const float* vtb = vt[buf];
+      const uint32_t* kwb = kw[buf];
+      // the 16 keys' words (also the +-1 operand of dS Bk below), their
+      // distances and weights, branch-free so that the LDS reads issue together
+      uint32_t kwv[16][W];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t word = kw[tile_row(i, half) * W + t];
-        const float b = ((word >> ql) & 1u) ? -1.0f : 1.0f;
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(b, ds[i], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int w = 0; w < W; ++w) kwv[i][w] = kwb[tile_row(i, half) * W + w];
+      }
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + tile_row(i, half);
+        int h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(qw[w] ^ kwv[i][w]);
+        const bool keep = (key < lim) & ((h < T) | ((h == T) & (key <= cut)));
+        const float wt = wtab[min(max(h - hmin, 0), d)];
+        p[i] = keep ? wt * invZ : 0.0f;
+      }
+      // dP tile: rows = keys, columns = query rows; the A operands of 8
+      // products are read while the previous 8 run
+      v16f dp = v16f{};
+      constexpr int kS = 16 * W;
+      float va[2][8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) va[0][k] = vtb[ql * VS + 2 * k + half];
+#pragma unroll
+      for (int c = 0; c < kS / 8; ++c) {
+        if (c + 1 < kS / 8) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) va[(c + 1) & 1][k] = vtb[ql * VS + 2 * (8 * (c + 1) + k) + half];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          dp = __builtin_amdgcn_mfma_f32_32x32x2f32(va[c & 1][k], dr[8 * c + k], dp, 0, 0, 0);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = a.scale * p[i] * (dp[i] - D);
+      // dQ^T += Bk^T dS: A = +-1 of feature 32t + ql of key tile_row(i, half);
+      // the W feature tiles' chains interleaved
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          const float b = ((kwv[i][t] >> ql) & 1u) ? -1.0f : 1.0f;
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(b, ds[i], acc[t], 0, 0, 0);
+        }
       }
     }
+    if (tile + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
   }
   if (!qvalid) return;
   const float g = a.sigma_q != nullptr ? 1.0f / *a.sigma_q : 1.0f;
@@ -196,19 +251,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---- 3. dK and dV (key-major) ----------------------------------------------
+// Tiles of 32 query rows (sign words, dout rows, row statistics, D) staged
+// double-buffered as in the dQ launch.  The key's V row, the B operand of
+// dP, is held as float32 (fp32 V) or as packed bf16 pairs (bf16 V).
 template <int W, bool VF32>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int DP = 32 * W;
   constexpr int OS = DP + 1;  // LDS row stride of the dout tile
-  __shared__ float ot[32 * OS];
-  __shared__ uint32_t qwt[32 * W];
-  __shared__ int4 qst[32];    // T, last kept tie, h_min, 1/Z bits
-  __shared__ float qd[32];    // D
+  constexpr int kOPT = DP / 8;  // dout values per thread per tile
+  constexpr int kVR = VF32 ? 16 * W : 8 * W;  // registers of the key's V row
+  __shared__ float ot[2][32 * OS];
+  __shared__ uint32_t qwt[2][32 * W];
+  __shared__ int4 qst[2][32];    // T, last kept tie, h_min, 1/Z bits
+  __shared__ float qd[2][32];    // D
   __shared__ float wtab[DP + 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, kl = lane & 31;
   const int n = a.n, d = a.d;
-  const int ntk = (n + kBwdRows - 1) / kBwdRows;
   const int64_t bh = blockIdx.x % a.bh_total;
   // causal: the first key tiles see the most query rows; dispatch them first
   const int kt = static_cast<int>(blockIdx.x / a.bh_total);
@@ -225,14 +284,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
 
   const int64_t krow = bh * n + (kvalid ? j : 0);
   uint32_t kw[W];
-  float vr[16 * W];  // V[j][2s + half] (the B operand of dP)
+  uint32_t vr[kVR];  // V[j][2s + half] for s < 16W: fp32 bits, or bf16 pairs (s even | s odd << 16)
 #pragma unroll
   for (int w = 0; w < W; ++w) kw[w] = a.kbits[krow * W + w];
 #pragma unroll
   for (int s = 0; s < 16 * W; ++s) {
     const int f = 2 * s + half;
-    vr[s] = (kvalid && f < d) ? load_v(a.v, krow * d + f, VF32) : 0.0f;
+    const float x = (kvalid && f < d) ? load_v(a.v, krow * d + f, VF32) : 0.0f;
+    if constexpr (VF32) {
+      vr[s] = __builtin_bit_cast(uint32_t, x);
+    } else {
+      const uint32_t b = __builtin_bit_cast(uint32_t, x) >> 16;  // exact: x is a bf16 value
+      vr[s >> 1] = (s & 1) ? (vr[s >> 1] | (b << 16)) : b;
+    }
   }
+  auto vval = [&](int s) {
+    if constexpr (VF32) return __builtin_bit_cast(float, vr[s]);
+    else return __builtin_bit_cast(float, (s & 1) ? (vr[s >> 1] & 0xFFFF0000u) : (vr[s >> 1] << 16));
+  };
   v16f accv[W], acck[W];
 #pragma unroll
   for (int t = 0; t < W; ++t) {
@@ -241,58 +310,115 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
   }
 
   const int64_t rbase = bh * static_cast<int64_t>(n);
-  for (int tile = qstart; tile < ntiles; ++tile) {
+  // unconditional loads from clamped addresses, out-of-range values zeroed
+  // when written (all of a thread's loads in flight together)
+  uint32_t pq = 0;
+  float po[kOPT];
+  int4 pst = make_int4(0, 0, 0, 0);
+  float pd = 0.0f;
+  int staged_r0 = 0;
+  auto prefetch = [&](int tile) {
     const int r0 = 32 * tile;
-    __syncthreads();
-    for (int e = tid; e < 32 * W; e += kBwdThreads) {
-      const int q = min(r0 + e / W, n - 1);
-      qwt[e] = a.qbits[(rbase + q) * W + e % W];
-    }
-    for (int e = tid; e < 32 * DP; e += kBwdThreads) {
+    staged_r0 = r0;
+    pq = a.qbits[(rbase + min(r0 + min(tid, 32 * W - 1) / W, n - 1)) * W + tid % W];
+#pragma unroll
+    for (int jj = 0; jj < kOPT; ++jj) {
+      const int e = tid + jj * kBwdThreads;
       const int r = e / DP, f = e - r * DP;
-      const int q = r0 + r;
-      ot[r * OS + f] = (q < n && f < d) ? a.dout[(rbase + q) * d + f] : 0.0f;
+      po[jj] = a.dout[(rbase + min(r0 + r, n - 1)) * d + min(f, d - 1)];
+    }
+    const int q = min(r0 + (tid & 31), n - 1);
+    pst = *reinterpret_cast<const int4*>(a.stats + (rbase + q) * 4);
+    pd = a.dsum[rbase + q];
+  };
+  auto commit = [&](int buf) {
+    if (tid < 32 * W) qwt[buf][tid] = pq;
+#pragma unroll
+    for (int jj = 0; jj < kOPT; ++jj) {
+      const int e = tid + jj * kBwdThreads;
+      const int r = e / DP, f = e - r * DP;
+      ot[buf][r * OS + f] = (staged_r0 + r < n && f < d) ? po[jj] : 0.0f;
     }
     if (tid < 32) {
-      const int q = min(r0 + tid, n - 1);
-      const int4 st = *reinterpret_cast<const int4*>(a.stats + (rbase + q) * 4);
-      const float Z = __builtin_bit_cast(float, st.w);
-      qst[tid] = make_int4(st.x, st.y, st.z, __builtin_bit_cast(int32_t, Z > 0.0f ? 1.0f / Z : 0.0f));
-      qd[tid] = a.dsum[rbase + q];
+      const float Z = __builtin_bit_cast(float, pst.w);
+      qst[buf][tid] = make_int4(pst.x, pst.y, pst.z, __builtin_bit_cast(int32_t, Z > 0.0f ? 1.0f / Z : 0.0f));
+      qd[buf][tid] = pd;
     }
-    __syncthreads();
-    if (!wactive || tile < wfirst) continue;
-    float p[16], dsv[16];
+  };
+  if (qstart < ntiles) {
+    prefetch(qstart);
+    commit(0);
+  }
+  __syncthreads();
+  for (int tile = qstart; tile < ntiles; ++tile) {
+    const int buf = (tile - qstart) & 1;
+    const int r0 = 32 * tile;
+    if (tile + 1 < ntiles) prefetch(tile + 1);
+    if (wactive && tile >= wfirst) {
+      const float* otb = ot[buf];
+      const uint32_t* qwb = qwt[buf];
+      // the 16 query rows' words (also the +-1 operand of dS^T Bq below),
+      // distances and weights, branch-free so that the LDS reads issue together
+      uint32_t qwv[16][W];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rl = tile_row(i, half);
-      const int q = r0 + rl;
-      int h = 0;
+      for (int i = 0; i < 16; ++i) {
 #pragma unroll
-      for (int w = 0; w < W; ++w) h += __builtin_popcount(qwt[rl * W + w] ^ kw[w]);
-      const int4 st = qst[rl];
-      const bool vis = kvalid && q < n && (!a.causal || j <= q);
-      const bool keep = vis && (h < st.x || (h == st.x && j <= st.y));
-      p[i] = keep ? wtab[min(max(h - st.z, 0), d)] * __builtin_bit_cast(float, st.w) : 0.0f;
-    }
-    // dP tile: rows = query rows, columns = keys
-    v16f dp = v16f{};
-#pragma unroll
-    for (int s = 0; s < 16 * W; ++s)
-      dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ot[kl * OS + 2 * s + half], vr[s], dp, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dsv[i] = a.scale * p[i] * (dp[i] - qd[tile_row(i, half)]);
-    // dV^T += dout^T P and dK^T += Bq^T dS: A = feature 32t + kl of query row tile_row(i, half)
-#pragma unroll
-    for (int t = 0; t < W; ++t) {
+        for (int w = 0; w < W; ++w) qwv[i][w] = qwb[tile_row(i, half) * W + w];
+      }
+      float p[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rl = tile_row(i, half);
-        accv[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ot[rl * OS + 32 * t + kl], p[i], accv[t], 0, 0, 0);
-        const float b = ((qwt[rl * W + t] >> kl) & 1u) ? -1.0f : 1.0f;
-        acck[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(b, dsv[i], acck[t], 0, 0, 0);
+        const int q = r0 + rl;
+        int h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(qwv[i][w] ^ kw[w]);
+        const int4 st = qst[buf][rl];
+        const bool vis = kvalid & (q < n) & (!a.causal | (j <= q));
+        const bool keep = vis & ((h < st.x) | ((h == st.x) & (j <= st.y)));
+        const float wt = wtab[min(max(h - st.z, 0), d)];
+        p[i] = keep ? wt * __builtin_bit_cast(float, st.w) : 0.0f;
+      }
+      // dP tile: rows = query rows, columns = keys; A operands read 8 ahead
+      v16f dp = v16f{};
+      constexpr int kS = 16 * W;
+      float va[2][8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) va[0][k] = otb[kl * OS + 2 * k + half];
+#pragma unroll
+      for (int c = 0; c < kS / 8; ++c) {
+        if (c + 1 < kS / 8) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) va[(c + 1) & 1][k] = otb[kl * OS + 2 * (8 * (c + 1) + k) + half];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          dp = __builtin_amdgcn_mfma_f32_32x32x2f32(va[c & 1][k], vval(8 * c + k), dp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dsv[i] = a.scale * p[i] * (dp[i] - qd[buf][tile_row(i, half)]);
+      // dV^T += dout^T P and dK^T += Bq^T dS: A = feature 32t + kl of query
+      // row tile_row(i, half); 2W independent chains, the dout operands of
+      // the next row read while the current row's products run
+      float ov[2][W];
+#pragma unroll
+      for (int t = 0; t < W; ++t) ov[0][t] = otb[tile_row(0, half) * OS + 32 * t + kl];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 1 < 16) {
+#pragma unroll
+          for (int t = 0; t < W; ++t) ov[(i + 1) & 1][t] = otb[tile_row(i + 1, half) * OS + 32 * t + kl];
+        }
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          accv[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ov[i & 1][t], p[i], accv[t], 0, 0, 0);
+          const float b = ((qwv[i][t] >> kl) & 1u) ? -1.0f : 1.0f;
+          acck[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(b, dsv[i], acck[t], 0, 0, 0);
+        }
       }
     }
+    if (tile + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
   }
   if (!kvalid) return;
   const float g = a.sigma_k != nullptr ? 1.0f / *a.sigma_k : 1.0f;
