@@ -568,6 +568,10 @@ def bench_decode(args, w):
     dec_s = float(np.median(durs))
     model = decode_model(w, fp32_rows=not args.separate_calls)
     achieved = model["hbm_bytes"] / dec_s
+    # the library's dispatch rule: few (slice, row) pairs, a short cache and a
+    # small N take the single launch
+    single = w.rows <= 512 and w.n_k <= 16384 and min(w.topn, w.n_k) <= 8192
+    kernels = "dec_one_kernel, one launch" if single else "dec_hist, dec_gather, dec_reduce"
     rec = {
         "metric": f"query rows/sec of HAD decode against a {w.n_k}-key cache; % of HBM roofline",
         "value": w.rows / (ms_step / 1e3),
@@ -585,16 +589,15 @@ def bench_decode(args, w):
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n_k": w.n_k,
                    "n_q": w.n_q, "dim": w.dim, "topn": w.topn, "causal": w.causal,
                    "v_dtype": w.v_dtype, "scale": w.scale,
-                   "step": ("had_pack(new rows' Q) + had_decode (4 launches)" if args.separate_calls
-                            else "had_decode_forward (3 launches; the new rows' sign words are built "
-                                 "inside the first)")},
+                   "step": ("had_pack(new rows' Q) + had_decode (%s)" % kernels if args.separate_calls
+                            else "had_decode_forward (%s; the new rows' sign words are built "
+                                 "inside the first launch)" % kernels)},
         "decode_us": dec_s * 1e6,
         "decode_us_mean": float(np.mean(durs)) * 1e6,
         "timed_calls": f"median over {len(durs)} groups of 5 back-to-back calls",
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "had_decode%s (dec_hist, dec_gather, dec_reduce)"
-                               % ("" if args.separate_calls else "_forward"),
+                     "kernel": "had_decode%s (%s)" % ("" if args.separate_calls else "_forward", kernels),
                      "work_per_launch": {k2: float(v2) for k2, v2 in model.items()}},
     }
     if cpu is not None:

@@ -33,6 +33,7 @@
 //  3. dec_reduce: out = (sum over splits, in split order) / Z.
 // HBM bytes per slice: the key words (d/8 bytes per key), and per row the
 // 2d bytes (bf16) of each kept key; everything else is small.
+#include <atomic>
 #include <cmath>
 
 #include "had_internal.h"
@@ -66,6 +67,7 @@ struct DecArgs {
   float* part;            // [BH, nq, splits, d]
   int splits;
   int keys_per_split;
+  int fparts;             // single-launch path: work-groups per (slice, row), each for 1/fparts of the columns
 };
 
 __device__ inline int visible_keys(const DecArgs& a, int q) {
@@ -545,15 +547,27 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
 }
 
 // ---- single-launch path for few rows ---------------------------------------
-// When there are few (slice, row) pairs (one new token per sequence), one
-// 1024-thread work-group per pair does the row's whole decode and writes its
-// output: no split histograms in memory, no tie hand-off between splits and no
-// reduce launch.  Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys),
-// key order is (u, wave, lane) as in dec_gather.  Distances go to per-wave LDS
-// histograms; wave 0 sums them, finds T, h_min, the tie quota and Z; kept keys
-// get their list slot from per-(u, wave) ballot counts; the kept V rows are
-// gathered 16 bytes of a row per lane with several rows in flight per lane
-// group, the row groups' sums are added in a fixed order and divided by Z.
+// When there are few (slice, row) pairs (one new token per sequence), each pair
+// gets fparts 1024-thread work-groups that share out the feature columns: every
+// one of them scans all of the row's keys (so each has the row's histogram,
+// threshold, tie quota and kept list without any exchange), then gathers only
+// its 1/fparts of each kept V row and writes those output columns.  No split
+// histograms or partial outputs go through memory and there is no reduce
+// launch.  fparts > 1 lets a few rows use every CU: gathering scattered V rows
+// is limited by the loads a CU keeps in flight, so one work-group per row on
+// half the CUs reaches little more than half the device rate.  The parts of a
+// pair are placed on one XCD (work-groups are dealt to the XCDs round robin by
+// index), so the repeated key scan is served by that XCD's L2.
+// Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys); key order is
+// (u, wave, lane) as in dec_gather.  Distances go to one LDS histogram; wave 0
+// finds T, h_min, the tie quota and Z from it; kept keys get their list slot
+// from per-(u, wave) ballot counts and one prefix over them; the kept V rows
+// are gathered 16 bytes of a row per lane with several rows in flight per lane
+// group, and the row groups' sums are added in a fixed order and divided by Z.
+// The per-key steps are written for few vector instructions (hidden keys carry
+// an out-of-range distance instead of a visibility test, in-wave ranks come
+// from mbcnt): every one of them costs 4 cycles of a SIMD per wave, and the
+// fparts copies of the scan and list repeat them.
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneKPT = 16;                              // keys per thread
@@ -562,16 +576,23 @@ constexpr int kOneMaxList = 8192;                        // kept keys per row (L
 constexpr int kOneMaxPairs = 512;                        // (slice, row) pairs that take this path
 
 template <int W, bool VF32, bool kVec, bool kKVec, bool kQF>
-__global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
-  __shared__ uint32_t hist[kOneWaves * (HAD_MAX_DIM + 1)];
-  __shared__ uint32_t list[kOneMaxList];  // (key << 9) | h per kept key; then the row-group sums
+__global__ __launch_bounds__(kOneThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void dec_one_kernel(DecArgs a) {
+  __shared__ uint32_t hist[1024];  // the row's histogram (d + 1 bins); then the final partial sums
+  __shared__ __attribute__((aligned(16))) uint32_t list[kOneMaxList];  // (key << 9) | (h - h_min) per kept key; then the row-group sums
   __shared__ float wtab[HAD_MAX_DIM + 1];
   __shared__ uint32_t cnt[kOneKPT][kOneWaves];  // strict | ties << 16, per (u, wave)
-  __shared__ uint32_t qws[W];
+  __shared__ __attribute__((aligned(16))) uint32_t pre[kOneWaves][kOneKPT];  // their prefix in key order
   __shared__ int sh_T, sh_hmin, sh_quota;
   __shared__ float sh_invz;
   float* red = reinterpret_cast<float*>(list);
-  const int64_t bhq = blockIdx.x;
+  float* red2 = reinterpret_cast<float*>(hist);
+  // work-group -> (pair, part): index = ((pair / 8) * fparts + part) * 8 + pair % 8
+  const int P = a.fparts;
+  const int rest = static_cast<int>(blockIdx.x >> 3);
+  const int part = rest % P;
+  const int64_t bhq = static_cast<int64_t>(rest / P) * 8 + (blockIdx.x & 7);
+  if (bhq >= a.bh_total * a.nq) return;  // padding of the last group of 8 pairs
   const int q = static_cast<int>(bhq % a.nq);
   const int64_t bh = bhq / a.nq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -579,45 +600,68 @@ __global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk) - 1;
   const int kend = static_cast<int>(min(static_cast<int64_t>(a.nk), last + 1));  // visible keys [0, kend)
   const int Ni = min(a.topn, kend);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // this part's feature columns: 8-column slots [s0, s0 + ns) of the row's (d + 7) / 8
+  const int slots = (d + 7) / 8;
+  const int sp = (slots + P - 1) / P;
+  const int s0 = part * sp;
+  const int ns = min(sp, slots - s0);  // >= 1: the host picks fparts so that every part has a slot
 
-  // the row's sign words (built here from float32 rows for had_decode_forward)
-  if constexpr (kQF) {
-    if (wid == 0) {
-      const float* xr = a.qf + bhq * static_cast<int64_t>(d);
+  // this thread's keys, a batch of kG in flight at a time; the first batch is
+  // requested before the row's sign words are ready.  The loads are
+  // unconditional (keys past the visible end read the last visible key,
+  // kend >= 1) and only the histogram update is predicated.
+  const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
+  constexpr int kG = W <= 2 ? 16 : (W <= 4 ? 8 : 4);
+  uint32_t kw[kG][W];
 #pragma unroll
-      for (int w2 = 0; w2 < W; w2 += 2) {
-        const int e = 32 * w2 + lane;
-        const uint64_t m = __ballot(e < d && xr[e < d ? e : 0] < 0.0f);
-        if (lane < 2 && w2 + lane < W) qws[w2 + lane] = static_cast<uint32_t>(m >> (32 * lane));
-      }
+  for (int g = 0; g < kG; ++g) {
+    const int j = min(g * kOneThreads + tid, kend - 1);
+    load_key_words<W, kKVec>(kb + static_cast<int64_t>(j) * W, kw[g]);
+  }
+
+  // the row's sign words, in every wave (wave-uniform): built from the
+  // float32 row for had_decode_forward (bit c of word w is [x_{32w+c} < 0],
+  // pad bits 0, as had_pack), else read; requested along with the keys
+  uint32_t qw[W];
+  constexpr int kQL = (W + 1) / 2;  // 64-element row chunks
+  float qx[kQF ? kQL : 1];
+  if constexpr (kQF) {
+    const float* xr = a.qf + bhq * static_cast<int64_t>(d);
+#pragma unroll
+    for (int i = 0; i < kQL; ++i) {
+      const int e = 64 * i + lane;
+      qx[i] = xr[e < d ? e : 0];
     }
   } else {
-    if (tid < W) qws[tid] = a.qbits[bhq * W + tid];
+#pragma unroll
+    for (int w = 0; w < W; ++w) qw[w] = a.qbits[bhq * W + w];
   }
-  for (int t = tid; t < kOneWaves * nb; t += kOneThreads) hist[t] = 0u;
+  for (int t = tid; t < nb; t += kOneThreads) hist[t] = 0u;
   for (int t = tid; t <= d; t += kOneThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
   __syncthreads();
-  uint32_t qw[W];
+  if constexpr (kQF) {
 #pragma unroll
-  for (int w = 0; w < W; ++w) qw[w] = qws[w];
+    for (int i = 0; i < kQL; ++i) {
+      const uint64_t m = __ballot(64 * i + lane < d && qx[i] < 0.0f);
+      qw[2 * i] = static_cast<uint32_t>(m);
+      if (2 * i + 1 < W) qw[2 * i + 1] = static_cast<uint32_t>(m >> 32);
+    }
+  }
 
-  // distances of this thread's keys, a batch of kG keys in flight at a time
-  const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
-  constexpr int kG = W <= 2 ? 8 : (W <= 4 ? 4 : 2);
+  // distances into the row's LDS histogram (one for the work-group: same-bin
+  // conflicts measured no slower than per-wave copies, and the threshold scan
+  // reads one row); a hidden key (past the visible end) keeps the distance
+  // kHidden, above every threshold bin (T <= d)
+  constexpr uint32_t kHidden = 0x1FFu;
   uint32_t hh[kOneKPT];
-  uint32_t* hw = hist + wid * nb;
+  uint32_t* hw = hist;
 #pragma unroll
   for (int u0 = 0; u0 < kOneKPT; u0 += kG) {
-    uint32_t kw[kG][W];
+    if (u0 > 0) {
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
-      const int j = (u0 + g) * kOneThreads + tid;
-      if (j < kend) {
+      for (int g = 0; g < kG; ++g) {
+        const int j = min((u0 + g) * kOneThreads + tid, kend - 1);
         load_key_words<W, kKVec>(kb + static_cast<int64_t>(j) * W, kw[g]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < W; ++w) kw[g][w] = 0u;
       }
     }
 #pragma unroll
@@ -625,25 +669,21 @@ __global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
       uint32_t h = 0;
 #pragma unroll
       for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[g][w] ^ qw[w]);
-      hh[u0 + g] = h;
-      if ((u0 + g) * kOneThreads + tid < kend) atomicAdd(&hw[h], 1u);
+      const bool vis = (u0 + g) * kOneThreads + tid < kend;
+      hh[u0 + g] = vis ? h : kHidden;
+      if (vis) atomicAdd(&hw[h], 1u);
     }
   }
   __syncthreads();
 
-  // wave 0: total histogram, threshold bin T, h_min, tie quota r, Z
+  // wave 0: threshold bin T, h_min, tie quota r, Z
   if (wid == 0) {
     constexpr int kR = (32 * W + 1 + 63) / 64;
     uint32_t c[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       const int b = 64 * r + lane;
-      uint32_t x = 0;
-      if (b < nb) {
-#pragma unroll
-        for (int w = 0; w < kOneWaves; ++w) x += hist[w * nb + b];
-      }
-      c[r] = x;
+      c[r] = b < nb ? hist[b] : 0u;
     }
     int T = -1, hmin = -1;
     uint32_t below = 0, run = 0;
@@ -670,7 +710,7 @@ __global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
     for (int r = 0; r < kR; ++r) {
       const int b = 64 * r + lane;
       const uint32_t cc = b < T ? c[r] : (b == T ? rtie : 0u);
-      if (cc != 0) z += static_cast<double>(cc) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
+      if (cc != 0) z += static_cast<double>(cc) * static_cast<double>(wtab[b - hmin]);  // b >= h_min here
     }
     z = wave_sum_f64(z);
     if (lane == 63) {
@@ -686,124 +726,177 @@ __global__ __launch_bounds__(kOneThreads) void dec_one_kernel(DecArgs a) {
   const int hmin = sh_hmin;
   const uint32_t quota = static_cast<uint32_t>(sh_quota);
 
-  // per-(u, wave) counts, then every kept key's slot in key order
+  // per-(u, wave) counts of kept-below-T and tied keys, packed strict |
+  // ties << 16 (each total <= 16384, so the halves never carry into each
+  // other; lane u of cv collects the wave's count for key step u), their
+  // exclusive prefix in key order (u, wave) by wave 0, then every kept key's
+  // slot in key order: the prefix plus the key's rank among the wave's lanes
+  uint32_t cv = 0;
 #pragma unroll
   for (int u = 0; u < kOneKPT; ++u) {
-    const bool vis = u * kOneThreads + tid < kend;
-    const uint64_t sm = __ballot(vis && hh[u] < T);
-    const uint64_t tm = __ballot(vis && hh[u] == T);
-    if (lane == 0)
-      cnt[u][wid] = static_cast<uint32_t>(__builtin_popcountll(sm)) |
-                    (static_cast<uint32_t>(__builtin_popcountll(tm)) << 16);
+    const uint64_t sm = __ballot(hh[u] < T);
+    const uint64_t tm = __ballot(hh[u] == T);
+    const uint32_t c = static_cast<uint32_t>(__builtin_popcountll(sm)) |
+                       (static_cast<uint32_t>(__builtin_popcountll(tm)) << 16);
+    cv = lane == u ? c : cv;
+  }
+  if (lane < kOneKPT) cnt[lane][wid] = cv;
+  __syncthreads();
+  if (wid == 0) {
+    static_assert(kOneKPT * kOneWaves == 4 * 64, "one wave, four counts per lane");
+    const uint32_t* cf = &cnt[0][0];
+    uint32_t c4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c4[i] = cf[4 * lane + i];
+    const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
+    uint32_t r = wave_scan_incl(tot) - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;  // = u * kOneWaves + wave
+      pre[e % kOneWaves][e / kOneWaves] = r;
+      r += c4[i];
+    }
   }
   __syncthreads();
-  uint32_t run = 0;
+  uint32_t pw[kOneKPT];
+#pragma unroll
+  for (int i = 0; i < kOneKPT / 4; ++i) {
+    const uint4 x = reinterpret_cast<const uint4*>(&pre[wid][0])[i];
+    pw[4 * i] = x.x; pw[4 * i + 1] = x.y; pw[4 * i + 2] = x.z; pw[4 * i + 3] = x.w;
+  }
 #pragma unroll
   for (int u = 0; u < kOneKPT; ++u) {
-    const int j = u * kOneThreads + tid;
-    const bool vis = j < kend;
-    const bool strict = vis && hh[u] < T;
-    const bool tie = vis && hh[u] == T;
+    const bool strict = hh[u] < T, tie = hh[u] == T;
     const uint64_t sm = __ballot(strict);
     const uint64_t tm = __ballot(tie);
-    uint32_t wb = 0, ut = 0;
-#pragma unroll
-    for (int w = 0; w < kOneWaves; ++w) {
-      const uint32_t cc = cnt[u][w];
-      wb += w < wid ? cc : 0u;
-      ut += cc;
-    }
-    const uint32_t b = run + wb;
-    const uint32_t sbefore = (b & 0xFFFFu) + static_cast<uint32_t>(__builtin_popcountll(sm & lt_mask));
-    const uint32_t tbefore = (b >> 16) + static_cast<uint32_t>(__builtin_popcountll(tm & lt_mask));
+    const uint32_t sr = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(sm >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(sm), 0u));
+    const uint32_t tr = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
+    const uint32_t sbefore = (pw[u] & 0xFFFFu) + sr, tbefore = (pw[u] >> 16) + tr;
     if (strict || (tie && tbefore < quota))
-      list[sbefore + min(tbefore, quota)] = (static_cast<uint32_t>(j) << 9) | hh[u];
-    run += ut;
+      list[sbefore + min(tbefore, quota)] = (static_cast<uint32_t>(u * kOneThreads + tid) << 9) | (hh[u] - hmin);
   }
   const int nl = Ni;
   __syncthreads();  // the list is complete
 
-  // gather the kept V rows: lpr lanes per row, 8 features each; R row groups
-  const int lpr = (d + 7) / 8;
-  const int R = kOneThreads / lpr;
-  const int g = tid / lpr, li = tid - (tid / lpr) * lpr;
+  // gather this part's columns of the kept V rows: ns lanes per row, 8
+  // features each; R row groups.  Each pass takes R * kRows list entries and
+  // row group g the kRows consecutive ones at g * kRows (read as 16-byte LDS
+  // vectors), so all kRows row loads of a lane are issued together.
+  const int R = kOneThreads / ns;
+  const int g = tid / ns, li = tid - (tid / ns) * ns;
+  const int fw = 8 * ns;  // columns per row group in the sums below
   float acc[8];
 #pragma unroll
   for (int f = 0; f < 8; ++f) acc[f] = 0.0f;
-  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
-                               bh * static_cast<int64_t>(a.kstride) * d * (VF32 ? 4 : 2);
-  constexpr int kRows = VF32 ? 4 : 8;
+  constexpr int kEs = VF32 ? 4 : 2;  // bytes per V element
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + bh * static_cast<int64_t>(a.kstride) * d * kEs;
+  constexpr int kRows = (VF32 || !kVec) ? 4 : 8;
+  const int c0 = 8 * (s0 + li);
   if (g < R) {
-    const int c0 = 8 * li;
-    for (int e0 = g; e0 < nl; e0 += kRows * R) {
-      uint32_t raw[kRows][VF32 ? 8 : 4];
-      float wr[kRows];
+    if constexpr (kVec) {
+      // 16-byte aligned rows (bf16: d % 8 == 0, so every slot is whole; fp32:
+      // d % 4 == 0, so the slot's second half is whole or wholly past the row)
+      // read through a buffer over the visible rows with 32-bit offsets
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(vbase), 0, kend * d * kEs, 0x00020000);
+      const int rowb = d * kEs, cb = c0 * kEs;
+      const bool hi_in = !VF32 || c0 + 4 < d;
+      for (int base = 0; base < nl; base += kRows * R) {
+        const int ef = base + g * kRows;
+        uint32_t ent[kRows];
+        const uint4* lp = reinterpret_cast<const uint4*>(list + min(ef, kOneMaxList - kRows));
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const int e = e0 + r * R;
-        const uint32_t ent = e < nl ? list[e] : list[e0];
-        const int hb = min(max(static_cast<int>(ent & 0x1FFu) - hmin, 0), d);
-        wr[r] = e < nl ? wtab[hb] : 0.0f;
-        const int64_t jj = min(static_cast<int>(ent >> 9), kend - 1);
-        if constexpr (VF32) {
-          const float* row = reinterpret_cast<const float*>(vbase) + jj * d;
-          if (kVec && c0 + 8 <= d) {
-            const uint4 u0 = *reinterpret_cast<const uint4*>(row + c0);
-            const uint4 u1 = *reinterpret_cast<const uint4*>(row + c0 + 4);
-            raw[r][0] = u0.x; raw[r][1] = u0.y; raw[r][2] = u0.z; raw[r][3] = u0.w;
-            raw[r][4] = u1.x; raw[r][5] = u1.y; raw[r][6] = u1.z; raw[r][7] = u1.w;
-          } else {
+        for (int i = 0; i < kRows / 4; ++i) {
+          const uint4 x = lp[i];
+          ent[4 * i] = x.x; ent[4 * i + 1] = x.y; ent[4 * i + 2] = x.z; ent[4 * i + 3] = x.w;
+        }
+        uint32_t raw[kRows][VF32 ? 8 : 4];
+        float wr[kRows];
 #pragma unroll
-            for (int f = 0; f < 8; ++f) raw[r][f] = c0 + f < d ? __builtin_bit_cast(uint32_t, row[c0 + f]) : 0u;
+        for (int r = 0; r < kRows; ++r) {
+          const bool ok = ef + r < nl;
+          const int jj = min(static_cast<int>(ent[r] >> 9), kend - 1);
+          wr[r] = ok ? wtab[min(static_cast<int>(ent[r] & 0x1FFu), d)] : 0.0f;
+          const int off = jj * rowb + cb;
+          const uint4 u0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
+          raw[r][0] = u0.x; raw[r][1] = u0.y; raw[r][2] = u0.z; raw[r][3] = u0.w;
+          if constexpr (VF32) {
+            const uint4 u1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, off + 16, 0, 0));
+            raw[r][4] = hi_in ? u1.x : 0u; raw[r][5] = hi_in ? u1.y : 0u;
+            raw[r][6] = hi_in ? u1.z : 0u; raw[r][7] = hi_in ? u1.w : 0u;
           }
-        } else {
-          const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + jj * d;
-          if (kVec && c0 + 8 <= d) {
-            const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
-            raw[r][0] = u.x; raw[r][1] = u.y; raw[r][2] = u.z; raw[r][3] = u.w;
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          float x[8];
+          if constexpr (VF32) {
+#pragma unroll
+            for (int f = 0; f < 8; ++f) x[f] = __builtin_bit_cast(float, raw[r][f]);
           } else {
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-              const uint32_t lo = c0 + 2 * f < d ? row[c0 + 2 * f] : 0u;
-              const uint32_t hi = c0 + 2 * f + 1 < d ? row[c0 + 2 * f + 1] : 0u;
-              raw[r][f] = lo | (hi << 16);
+              x[2 * f] = __builtin_bit_cast(float, raw[r][f] << 16);
+              x[2 * f + 1] = __builtin_bit_cast(float, raw[r][f] & 0xFFFF0000u);
             }
           }
+#pragma unroll
+          for (int f = 0; f < 8; ++f) acc[f] = fmaf(wr[r], x[f], acc[f]);
         }
       }
+    } else {
+      // unaligned rows: element loads, bounds-checked per column
+      for (int base = 0; base < nl; base += kRows * R) {
+        const int ef = base + g * kRows;
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        float x[8];
-        if constexpr (VF32) {
+        for (int r = 0; r < kRows; ++r) {
+          const bool ok = ef + r < nl;
+          const uint32_t ent = list[min(ef + r, kOneMaxList - 1)];
+          const int64_t jj = min(static_cast<int>(ent >> 9), kend - 1);
+          const float wgt = ok ? wtab[min(static_cast<int>(ent & 0x1FFu), d)] : 0.0f;
+          float x[8];
+          if constexpr (VF32) {
+            const float* row = reinterpret_cast<const float*>(vbase) + jj * d;
 #pragma unroll
-          for (int f = 0; f < 8; ++f) x[f] = __builtin_bit_cast(float, raw[r][f]);
-        } else {
+            for (int f = 0; f < 8; ++f) x[f] = c0 + f < d ? row[c0 + f] : 0.0f;
+          } else {
+            const uint16_t* row = reinterpret_cast<const uint16_t*>(vbase) + jj * d;
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            x[2 * f] = __builtin_bit_cast(float, raw[r][f] << 16);
-            x[2 * f + 1] = __builtin_bit_cast(float, raw[r][f] & 0xFFFF0000u);
+            for (int f = 0; f < 8; ++f)
+              x[f] = __builtin_bit_cast(float, c0 + f < d ? static_cast<uint32_t>(row[c0 + f]) << 16 : 0u);
           }
-        }
 #pragma unroll
-        for (int f = 0; f < 8; ++f) acc[f] = fmaf(wr[r], x[f], acc[f]);
+          for (int f = 0; f < 8; ++f) acc[f] = fmaf(wgt, x[f], acc[f]);
+        }
       }
     }
   }
   __syncthreads();  // every group is done with the list: its space takes the group sums
   if (g < R) {
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int c = 8 * li + f;
-      if (c < d) red[g * d + c] = acc[f];
+    for (int f = 0; f < 8; ++f) red[g * fw + 8 * li + f] = acc[f];
+  }
+  __syncthreads();
+  // sum the R group sums in a fixed order: chunk k adds groups k, k + K, ...,
+  // then one thread per column adds the K chunk sums in order
+  const int K = kOneThreads / fw;  // >= 4 (fw <= 256); R >= K
+  {
+    const int cl = tid % fw, k = tid / fw;
+    if (k < K) {
+      float sum = 0.0f;
+      for (int gg = k; gg < R; gg += K) sum += red[gg * fw + cl];
+      red2[k * fw + cl] = sum;
     }
   }
   __syncthreads();
   const float invz = sh_invz;
   float* orow = a.out + bhq * static_cast<int64_t>(d);
-  for (int c = tid; c < d; c += kOneThreads) {
+  const int cbase = 8 * s0;
+  if (tid < fw && cbase + tid < d) {
     float sum = 0.0f;
-    for (int gg = 0; gg < R; ++gg) sum += red[gg * d + c];
-    orow[c] = sum * invz;
+    for (int k = 0; k < K; ++k) sum += red2[k * fw + tid];
+    orow[cbase + tid] = sum * invz;
   }
 }
 
@@ -916,9 +1009,43 @@ void launch_gather(const DecArgs& a, bool vec, bool kvec, int64_t blocks, hipStr
   }
 }
 
+// Compute units of the current device (cached per device; 256 if the runtime
+// cannot say).
+int device_cus() {
+  static std::atomic<int> cache[64];  // 0: not known yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+// Work-groups per (slice, row) on the single-launch path: double them (up to
+// 4) while the pairs alone would leave CUs without a work-group and every part
+// still gets at least one 8-column slot.  (At 128 pairs, 2 parts measured
+// 23.5 us per decode and 4 parts 24.1 us: each part repeats the key scan.)
+int one_fparts(int64_t rows, int d) {
+  const int slots = (d + 7) / 8;
+  const int cus = device_cus();
+  int p = 1;
+  while (p < 4 && rows * p < cus) {
+    const int q = 2 * p;
+    if ((q - 1) * ((slots + q - 1) / q) >= slots) break;
+    p = q;
+  }
+  return p;
+}
+
 template <int W, bool VF32, bool kVec, bool kKVec>
 void launch_one_q(const DecArgs& a, int64_t rows, hipStream_t st) {
-  const unsigned nb = static_cast<unsigned>(rows);
+  // work-group index = ((pair / 8) * fparts + part) * 8 + pair % 8
+  const unsigned nb = static_cast<unsigned>((rows + 7) / 8 * 8 * a.fparts);
   if (a.qf != nullptr)
     dec_one_kernel<W, VF32, kVec, kKVec, true><<<nb, kOneThreads, 0, st>>>(a);
   else
@@ -1024,7 +1151,8 @@ had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, 
   // 16-byte row slices need 16-byte aligned rows
   const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
   if (rows <= kOneMaxPairs && s.n_k <= kOneMaxKeys && a.topn <= kOneMaxList) {
-    // few rows: one work-group per (slice, row), one launch
+    // few rows: fparts work-groups per (slice, row), one launch
+    a.fparts = one_fparts(rows, a.d);
     switch (a.W) {
       case 1: launch_one<1>(a, vec, kvec, rows, hs); break;
       case 2: launch_one<2>(a, vec, kvec, rows, hs); break;
