@@ -560,14 +560,17 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
 // index), so the repeated key scan is served by that XCD's L2.
 // Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys); key order is
 // (u, wave, lane) as in dec_gather.  Distances go to one LDS histogram; wave 0
-// finds T, h_min, the tie quota and Z from it; kept keys get their list slot
-// from per-(u, wave) ballot counts and one prefix over them; the kept V rows
+// finds T, h_min, the tie quota and Z from it; the distances, stored by key,
+// are read back 16 consecutive keys per thread, and a thread's kept keys get
+// their list slots from its counts, a scan over the threads and a walk in key
+// order; the kept V rows
 // are gathered 16 bytes of a row per lane with several rows in flight per lane
 // group, and the row groups' sums are added in a fixed order and divided by Z.
 // The per-key steps are written for few vector instructions (hidden keys carry
-// an out-of-range distance instead of a visibility test, in-wave ranks come
-// from mbcnt): every one of them costs 4 cycles of a SIMD per wave, and the
-// fparts copies of the scan and list repeat them.
+// an out-of-range distance instead of a visibility test; slots come from
+// per-thread counts rather than per-key ballots): every one of them costs 4
+// cycles of a SIMD per wave, and the fparts copies of the scan and list
+// repeat them.
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneKPT = 16;                              // keys per thread
@@ -581,8 +584,7 @@ void dec_one_kernel(DecArgs a) {
   __shared__ uint32_t hist[1024];  // the row's histogram (d + 1 bins); then the final partial sums
   __shared__ __attribute__((aligned(16))) uint32_t list[kOneMaxList];  // (key << 9) | (h - h_min) per kept key; then the row-group sums
   __shared__ float wtab[HAD_MAX_DIM + 1];
-  __shared__ uint32_t cnt[kOneKPT][kOneWaves];  // strict | ties << 16, per (u, wave)
-  __shared__ __attribute__((aligned(16))) uint32_t pre[kOneWaves][kOneKPT];  // their prefix in key order
+  __shared__ __attribute__((aligned(16))) uint32_t wtot[kOneWaves];  // per-wave strict | ties << 16
   __shared__ int sh_T, sh_hmin, sh_quota;
   __shared__ float sh_invz;
   float* red = reinterpret_cast<float*>(list);
@@ -650,10 +652,12 @@ void dec_one_kernel(DecArgs a) {
 
   // distances into the row's LDS histogram (one for the work-group: same-bin
   // conflicts measured no slower than per-wave copies, and the threshold scan
-  // reads one row); a hidden key (past the visible end) keeps the distance
-  // kHidden, above every threshold bin (T <= d)
+  // reads one row), and every key's distance into the list's space as a
+  // 16-bit value at the key's index (the list stage reads them back 16
+  // consecutive keys per thread); a hidden key (past the visible end) keeps
+  // the distance kHidden, above every threshold bin (T <= d)
   constexpr uint32_t kHidden = 0x1FFu;
-  uint32_t hh[kOneKPT];
+  uint16_t* hkey = reinterpret_cast<uint16_t*>(list);
   uint32_t* hw = hist;
 #pragma unroll
   for (int u0 = 0; u0 < kOneKPT; u0 += kG) {
@@ -670,7 +674,7 @@ void dec_one_kernel(DecArgs a) {
 #pragma unroll
       for (int w = 0; w < W; ++w) h += __builtin_popcount(kw[g][w] ^ qw[w]);
       const bool vis = (u0 + g) * kOneThreads + tid < kend;
-      hh[u0 + g] = vis ? h : kHidden;
+      hkey[(u0 + g) * kOneThreads + tid] = static_cast<uint16_t>(vis ? h : kHidden);
       if (vis) atomicAdd(&hw[h], 1u);
     }
   }
@@ -726,56 +730,49 @@ void dec_one_kernel(DecArgs a) {
   const int hmin = sh_hmin;
   const uint32_t quota = static_cast<uint32_t>(sh_quota);
 
-  // per-(u, wave) counts of kept-below-T and tied keys, packed strict |
-  // ties << 16 (each total <= 16384, so the halves never carry into each
-  // other; lane u of cv collects the wave's count for key step u), their
-  // exclusive prefix in key order (u, wave) by wave 0, then every kept key's
-  // slot in key order: the prefix plus the key's rank among the wave's lanes
-  uint32_t cv = 0;
+  // the kept list in key order: thread t takes keys 16 t .. 16 t + 15 (their
+  // distances read back from the list's space), counts its keys below T and
+  // tied with T, packed strict | ties << 16 (each total <= 16384, so the
+  // halves never carry into each other), and gets the counts of the keys
+  // before its own from a wave scan and the wave totals; walking its keys in
+  // order, a key below T, or one of the first `quota` ties, goes to slot
+  // (strict keys before) + min(ties before, quota)
+  uint32_t hv[kOneKPT];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(hkey + tid * kOneKPT);
 #pragma unroll
-  for (int u = 0; u < kOneKPT; ++u) {
-    const uint64_t sm = __ballot(hh[u] < T);
-    const uint64_t tm = __ballot(hh[u] == T);
-    const uint32_t c = static_cast<uint32_t>(__builtin_popcountll(sm)) |
-                       (static_cast<uint32_t>(__builtin_popcountll(tm)) << 16);
-    cv = lane == u ? c : cv;
-  }
-  if (lane < kOneKPT) cnt[lane][wid] = cv;
-  __syncthreads();
-  if (wid == 0) {
-    static_assert(kOneKPT * kOneWaves == 4 * 64, "one wave, four counts per lane");
-    const uint32_t* cf = &cnt[0][0];
-    uint32_t c4[4];
+    for (int i = 0; i < kOneKPT / 8; ++i) {
+      const uint4 x = hp[i];
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c4[i] = cf[4 * lane + i];
-    const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
-    uint32_t r = wave_scan_incl(tot) - tot;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i;  // = u * kOneWaves + wave
-      pre[e % kOneWaves][e / kOneWaves] = r;
-      r += c4[i];
+      for (int k = 0; k < 4; ++k) {
+        hv[8 * i + 2 * k] = xs[k] & 0xFFFFu;
+        hv[8 * i + 2 * k + 1] = xs[k] >> 16;
+      }
     }
   }
-  __syncthreads();
-  uint32_t pw[kOneKPT];
+  uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < kOneKPT / 4; ++i) {
-    const uint4 x = reinterpret_cast<const uint4*>(&pre[wid][0])[i];
-    pw[4 * i] = x.x; pw[4 * i + 1] = x.y; pw[4 * i + 2] = x.z; pw[4 * i + 3] = x.w;
+  for (int u = 0; u < kOneKPT; ++u) c += (hv[u] < T ? 1u : 0u) + (hv[u] == T ? 0x10000u : 0u);
+  const uint32_t incl = wave_scan_incl(c);
+  if (lane == 63) wtot[wid] = incl;
+  __syncthreads();  // also: every thread has its distances out of the list's space
+  uint32_t b = incl - c;
+#pragma unroll
+  for (int i = 0; i < kOneWaves / 4; ++i) {
+    const uint4 x = reinterpret_cast<const uint4*>(wtot)[i];
+    b += (4 * i < wid ? x.x : 0u) + (4 * i + 1 < wid ? x.y : 0u) + (4 * i + 2 < wid ? x.z : 0u) +
+         (4 * i + 3 < wid ? x.w : 0u);
   }
+  uint32_t sb = b & 0xFFFFu, tb = b >> 16;
 #pragma unroll
   for (int u = 0; u < kOneKPT; ++u) {
-    const bool strict = hh[u] < T, tie = hh[u] == T;
-    const uint64_t sm = __ballot(strict);
-    const uint64_t tm = __ballot(tie);
-    const uint32_t sr = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(sm >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(sm), 0u));
-    const uint32_t tr = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
-    const uint32_t sbefore = (pw[u] & 0xFFFFu) + sr, tbefore = (pw[u] >> 16) + tr;
-    if (strict || (tie && tbefore < quota))
-      list[sbefore + min(tbefore, quota)] = (static_cast<uint32_t>(u * kOneThreads + tid) << 9) | (hh[u] - hmin);
+    const uint32_t h = hv[u];
+    const bool strict = h < T, tie = h == T;
+    if (strict || (tie && tb < quota))
+      list[sb + min(tb, quota)] = (static_cast<uint32_t>(tid * kOneKPT + u) << 9) | (h - hmin);
+    sb += strict ? 1u : 0u;
+    tb += tie ? 1u : 0u;
   }
   const int nl = Ni;
   __syncthreads();  // the list is complete
