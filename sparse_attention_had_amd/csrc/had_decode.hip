@@ -579,7 +579,7 @@ constexpr int kOneMaxList = 8192;                        // kept keys per row (L
 constexpr int kOneMaxPairs = 512;                        // (slice, row) pairs that take this path
 
 template <int W, bool VF32, bool kVec, bool kKVec, bool kQF>
-__global__ __launch_bounds__(kOneThreads) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(kOneThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void dec_one_kernel(DecArgs a) {
   __shared__ uint32_t hist[1024];  // the row's histogram (d + 1 bins); then the final partial sums
   __shared__ __attribute__((aligned(16))) uint32_t list[kOneMaxList];  // (key << 9) | (h - h_min) per kept key; then the row-group sums
@@ -613,7 +613,12 @@ void dec_one_kernel(DecArgs a) {
   // unconditional (keys past the visible end read the last visible key,
   // kend >= 1) and only the histogram update is predicated.
   const uint32_t* kb = a.kbits + bh * static_cast<int64_t>(a.kstride) * W;
-  constexpr int kG = W <= 2 ? 16 : (W <= 4 ? 8 : 4);
+  // 32 bytes of key words per lane per batch: at d = 128 (W = 4), 2 keys per
+  // batch measured 21.1 us per decode, 1 key 22.6, 4 keys 21.6, 8 keys 22.0
+  // and 16 keys 24.4 (fewer requests in flight per lane, staggered over the
+  // batches, are served faster)
+  constexpr int kG = W >= 5 ? 1 : (W >= 3 ? 2 : 8 / W);
+  static_assert(kOneKPT % kG == 0, "whole batches");
   uint32_t kw[kG][W];
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
@@ -789,7 +794,9 @@ void dec_one_kernel(DecArgs a) {
   for (int f = 0; f < 8; ++f) acc[f] = 0.0f;
   constexpr int kEs = VF32 ? 4 : 2;  // bytes per V element
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + bh * static_cast<int64_t>(a.kstride) * d * kEs;
-  constexpr int kRows = (VF32 || !kVec) ? 4 : 8;
+  // bf16 rows: 16 in flight per lane group (at two parts per row, one pass
+  // over N = 2048: 20.9 us per decode against 21.1 with 8)
+  constexpr int kRows = (VF32 || !kVec) ? 4 : 16;
   const int c0 = 8 * (s0 + li);
   if (g < R) {
     if constexpr (kVec) {
