@@ -32,9 +32,11 @@
 //     query rows (their sign words, dout rows, statistics and D staged in
 //     LDS) each wave forms h, the weights and dP (A = the dout tile, B = the
 //     key's V row in registers), dS, and accumulates P^T dout and dS^T Bq.
-// Everything is float32 on the matrix cores (their fp32 products round like
-// the vector ALU's); no floating-point atomics, so results are identical run
-// to run.  Masked elements take weight 0.
+// With fp32 V, or d > 64, everything is float32 on the matrix cores (their
+// fp32 products round like the vector ALU's).  With bf16 V and d <= 64 the
+// products run on the bf16 matrix cores with the float32 operands split into
+// three bf16 terms (see the bf16 kernels below).  No floating-point atomics,
+// so results are identical run to run.  Masked elements take weight 0.
 #include <cmath>
 
 #include "had_internal.h"
@@ -250,6 +252,232 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---- bf16 V, d <= 64: the products on the bf16 matrix cores ----------------
+// Every float32 x is exactly hi + mid + lo with three bf16 values (hi = the
+// top 16 bits of x, mid the top 16 bits of the remainder, lo the rest, which
+// has at most 8 significant bits).  A product with an operand that is exact
+// in bf16 (the +-1 sign bits, bf16 V) is then three bf16 products with
+// exact partial products and float32 accumulation; a product of two split
+// float32 operands keeps the six partial products above 2^-24 relative.
+// v_mfma_f32_32x32x16_bf16 sums over 16 k-slots, slot s of lane half h in A
+// and in B; the kernels give the slot (h, s) the same index on both sides:
+// a feature 16 c + 8 h + s for the products over features, and for the
+// products over the 32 keys (dQ) or query rows (dK, dV) of a tile the
+// element 8 cc + s of the lane's own 32 x 32 tile registers (row
+// tile_row(8 cc + s, h)), so dS and P feed the next products as they are.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct Split3 {
+  uint32_t h, m, l;  // bf16 bit patterns in the low 16 bits
+};
+__device__ inline Split3 split3(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const float r = x - __builtin_bit_cast(float, u & 0xFFFF0000u);  // exact
+  const uint32_t ur = __builtin_bit_cast(uint32_t, r);
+  const float l = r - __builtin_bit_cast(float, ur & 0xFFFF0000u);  // exact, <= 8 significant bits
+  return {u >> 16, ur >> 16, __builtin_bit_cast(uint32_t, l) >> 16};
+}
+
+// Eight float32 values as three bf16 operand vectors (element s = x[s]).
+__device__ inline void split8(const float* x, v8bf* o) {
+  u32x4 ph, pm, pl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const Split3 a = split3(x[2 * k]), b = split3(x[2 * k + 1]);
+    ph[k] = a.h | (b.h << 16);
+    pm[k] = a.m | (b.m << 16);
+    pl[k] = a.l | (b.l << 16);
+  }
+  o[0] = __builtin_bit_cast(v8bf, ph);
+  o[1] = __builtin_bit_cast(v8bf, pm);
+  o[2] = __builtin_bit_cast(v8bf, pl);
+}
+
+// The +-1 operand: element s = -1 if bit `bit` of w[s] is set, else +1.
+__device__ inline v8bf sign_operand(const uint32_t* w, int bit) {
+  const int sh = 31 - bit;
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t s0 = (w[2 * k] << sh) >> 16;  // bit 15 = the sign of element 2k
+    const uint32_t s1 = w[2 * k + 1] << sh;      // bit 31 = the sign of element 2k + 1
+    o[k] = (s0 & 0x8000u) | (s1 & 0x80000000u) | 0x3F803F80u;
+  }
+  return __builtin_bit_cast(v8bf, o);
+}
+
+#define MFMA_BF16(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+
+// dQ, query-major, bf16 V, W <= 2.  As bwd_dq_kernel; the V tile is staged
+// as bf16 rows, dout of the wave's rows is split once into bf16 operands,
+// dP takes 3 products per 16 features and dQ^T += Bk^T dS 3 per 16 keys.
+template <int W>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_bf_kernel(BwdArgs a) {
+  static_assert(W <= 2, "bf16 path for d <= 64");
+  constexpr int DP = 32 * W;
+  constexpr int NC = DP / 16;   // 16-feature steps of dP
+  constexpr int VSB = DP + 8;   // LDS row stride of the V tile, bf16 elements (16-byte rows, odd multiple)
+  constexpr int kVPT = DP / 8;  // V values per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][32 * VSB];
+  __shared__ uint32_t kw[2][32 * W];
+  __shared__ float wtab[DP + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int half = lane >> 5, ql = lane & 31;
+  const int n = a.n, d = a.d;
+  const int ntq = (n + kBwdRows - 1) / kBwdRows;
+  const int64_t bh = blockIdx.x % a.bh_total;
+  const int qt = ntq - 1 - static_cast<int>(blockIdx.x / a.bh_total);  // heaviest causal tiles first
+  const int q0 = qt * kBwdRows;
+  const int i_row = q0 + 32 * wid + ql;
+  const bool qvalid = i_row < n;
+  const int lim = !qvalid ? 0 : (a.causal ? i_row + 1 : n);
+  const int kend = a.causal ? min(n, q0 + kBwdRows) : n;
+  const int ntiles = (kend + 31) / 32;
+  const int wq0 = q0 + 32 * wid;
+  const int wlim = wq0 >= n ? 0 : (a.causal ? min(n, wq0 + 32) : n);
+  const int wtiles = (wlim + 31) / 32;
+
+  for (int t = tid; t <= d; t += kBwdThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
+
+  const int64_t row = bh * n + (qvalid ? i_row : 0);
+  int T = 0, cut = -1, hmin = 0;
+  float invZ = 0.0f;
+  uint32_t qw[W];
+  v8bf db[NC][3];  // dout[i_row][16c + 8 half + s] as hi, mid, lo (the B operand of dP)
+  float D = 0.0f;
+  {
+    const int4 st = *reinterpret_cast<const int4*>(a.stats + row * 4);
+    T = st.x;
+    cut = st.y;
+    hmin = st.z;
+    const float Z = __builtin_bit_cast(float, st.w);
+    invZ = (qvalid && Z > 0.0f) ? 1.0f / Z : 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) qw[w] = a.qbits[row * W + w];
+    const float* drow = a.dout + row * d;
+    const float* orow = a.out + row * d;
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float x[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int f = 16 * c + 8 * half + s;
+        const bool in = qvalid && f < d;
+        x[s] = in ? drow[in ? f : 0] : 0.0f;
+        part = fmaf(x[s], in ? orow[in ? f : 0] : 0.0f, part);
+      }
+      split8(x, db[c]);
+    }
+    D = part + __shfl_xor(part, 32, 64);  // both halves of the row
+  }
+  if (qvalid && half == 0) a.dsum[row] = D;
+
+  v16f acc[W];
+#pragma unroll
+  for (int t = 0; t < W; ++t) acc[t] = v16f{};
+
+  const uint32_t* kbase = a.kbits + bh * static_cast<int64_t>(n) * W;
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a.v) + bh * static_cast<int64_t>(n) * d;
+  uint32_t pk = 0;
+  uint16_t pv[kVPT];
+  int staged_k0 = 0;
+  auto prefetch = [&](int tile) {
+    const int k0 = 32 * tile;
+    staged_k0 = k0;
+    pk = kbase[static_cast<int64_t>(min(k0 + min(tid, 32 * W - 1) / W, n - 1)) * W + tid % W];
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const int e = tid + j * kBwdThreads;
+      const int r = e / DP, f = e - r * DP;
+      pv[j] = vsrc[static_cast<int64_t>(min(k0 + r, n - 1)) * d + min(f, d - 1)];
+    }
+  };
+  auto commit = [&](int buf) {
+    if (tid < 32 * W) kw[buf][tid] = pk;
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const int e = tid + j * kBwdThreads;
+      const int r = e / DP, f = e - r * DP;
+      vt[buf][r * VSB + f] = (staged_k0 + r < n && f < d) ? pv[j] : static_cast<uint16_t>(0);
+    }
+  };
+  prefetch(0);
+  commit(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int k0 = 32 * tile;
+    if (tile + 1 < ntiles) prefetch(tile + 1);
+    if (tile < wtiles) {
+      const uint32_t* kwb = kw[buf];
+      uint32_t kwv[16][W];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) kwv[i][w] = kwb[tile_row(i, half) * W + w];
+      }
+      // dP tile (rows = keys, columns = query rows): A = the V tile row of
+      // key ql, features 16c + 8 half .. + 7
+      v8bf va[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        va[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&vt[buf][ql * VSB + 16 * c + 8 * half]));
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + tile_row(i, half);
+        int h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(qw[w] ^ kwv[i][w]);
+        const bool keep = (key < lim) & ((h < T) | ((h == T) & (key <= cut)));
+        const float wt = wtab[min(max(h - hmin, 0), d)];
+        p[i] = keep ? wt * invZ : 0.0f;
+      }
+      v16f dp = v16f{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        dp = MFMA_BF16(va[c], db[c][0], dp);
+        dp = MFMA_BF16(va[c], db[c][1], dp);
+        dp = MFMA_BF16(va[c], db[c][2], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = a.scale * p[i] * (dp[i] - D);
+      // dQ^T += Bk^T dS: slot (half, s) of step cc is the key tile_row(8cc + s, half)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        v8bf b[3];
+        split8(ds + 8 * cc, b);
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          uint32_t wsel[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) wsel[s] = kwv[8 * cc + s][t];
+          const v8bf sa = sign_operand(wsel, ql);
+          acc[t] = MFMA_BF16(sa, b[0], acc[t]);
+          acc[t] = MFMA_BF16(sa, b[1], acc[t]);
+          acc[t] = MFMA_BF16(sa, b[2], acc[t]);
+        }
+      }
+    }
+    if (tile + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
+  }
+  if (!qvalid) return;
+  const float g = a.sigma_q != nullptr ? 1.0f / *a.sigma_q : 1.0f;
+  float* drow = a.dq + row * d;
+#pragma unroll
+  for (int t = 0; t < W; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int f = 32 * t + tile_row(i, half);
+      if (f < d) drow[f] = acc[t][i] * g;
+    }
+  }
+}
+
 // ---- 3. dK and dV (key-major) ----------------------------------------------
 // Tiles of 32 query rows (sign words, dout rows, row statistics, D) staged
 // double-buffered as in the dQ launch.  The key's V row, the B operand of
@@ -437,9 +665,234 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
+// dK and dV, key-major, bf16 V, W <= 2.  As bwd_dkv_kernel; each dout tile
+// is staged split (hi, mid, lo) twice: row-major for the A operand of dP
+// (16 features of one query row per lane) and feature-major for the A
+// operand of dV^T += dout^T P (for one feature, the 8 query rows whose
+// weights the lane holds).  The key's V row stays in registers as bf16
+// operands.  Products per tile: dP 3 per 16 features, dV 6 and dK 3 per 16
+// query rows and 32 features.
+template <int W>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
+  static_assert(W <= 2, "bf16 path for d <= 64");
+  constexpr int DP = 32 * W;
+  constexpr int NC = DP / 16;
+  constexpr int OSB = DP + 8;       // row-major tile stride (bf16): 16-byte rows, odd multiple
+  constexpr int TSB = 32 + 8;       // feature-major tile stride (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t ob[2][3][32 * OSB];
+  __shared__ __attribute__((aligned(16))) uint16_t obt[2][3][DP * TSB];
+  __shared__ uint32_t qwt[2][32 * W];
+  __shared__ int4 qst[2][32];    // T, last kept tie, h_min, 1/Z bits
+  __shared__ float qd[2][32];    // D
+  __shared__ float wtab[DP + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int half = lane >> 5, kl = lane & 31;
+  const int n = a.n, d = a.d;
+  const int64_t bh = blockIdx.x % a.bh_total;
+  const int kt = static_cast<int>(blockIdx.x / a.bh_total);
+  const int k0 = kt * kBwdRows;
+  const int j = k0 + 32 * wid + kl;
+  const bool kvalid = j < n;
+  const int qstart = a.causal ? (k0 / 32) : 0;
+  const int ntiles = (n + 31) / 32;
+  const int wk0 = k0 + 32 * wid;
+  const int wfirst = a.causal ? (wk0 / 32) : 0;
+  const bool wactive = wk0 < n;
+
+  for (int t = tid; t <= d; t += kBwdThreads) wtab[t] = expf(-2.0f * a.scale * static_cast<float>(t));
+
+  const int64_t krow = bh * n + (kvalid ? j : 0);
+  uint32_t kw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) kw[w] = a.kbits[krow * W + w];
+  // the key's V row, features 16c + 8 half + s (the B operand of dP; exact in bf16)
+  v8bf vb[NC];
+  {
+    const uint16_t* vr = static_cast<const uint16_t*>(a.v) + krow * d;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int f = 16 * c + 8 * half + 2 * k;
+        const uint32_t lo = (kvalid && f < d) ? vr[f] : 0u;
+        const uint32_t hi = (kvalid && f + 1 < d) ? vr[f + 1] : 0u;
+        u[k] = lo | (hi << 16);
+      }
+      vb[c] = __builtin_bit_cast(v8bf, u);
+    }
+  }
+  v16f accv[W], acck[W];
+#pragma unroll
+  for (int t = 0; t < W; ++t) {
+    accv[t] = v16f{};
+    acck[t] = v16f{};
+  }
+
+  const int64_t rbase = bh * static_cast<int64_t>(n);
+  // staging share: thread t takes feature f = t % DP of query rows
+  // 8 (t / DP) .. + 7 (coalesced loads across the lanes)
+  const int sf = tid % DP, sr0 = 8 * (tid / DP);
+  uint32_t pq = 0;
+  float po[8];
+  int4 pst = make_int4(0, 0, 0, 0);
+  float pd = 0.0f;
+  int staged_r0 = 0;
+  auto prefetch = [&](int tile) {
+    const int r0 = 32 * tile;
+    staged_r0 = r0;
+    pq = a.qbits[(rbase + min(r0 + min(tid, 32 * W - 1) / W, n - 1)) * W + tid % W];
+    if (sr0 < 32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) po[u] = a.dout[(rbase + min(r0 + sr0 + u, n - 1)) * d + min(sf, d - 1)];
+    }
+    const int q = min(r0 + (tid & 31), n - 1);
+    pst = *reinterpret_cast<const int4*>(a.stats + (rbase + q) * 4);
+    pd = a.dsum[rbase + q];
+  };
+  auto commit = [&](int buf) {
+    if (tid < 32 * W) qwt[buf][tid] = pq;
+    if (sr0 < 32) {
+      uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = staged_r0 + sr0 + u < n && sf < d;
+        const Split3 x = split3(in ? po[u] : 0.0f);
+        ob[buf][0][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.h);
+        ob[buf][1][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.m);
+        ob[buf][2][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.l);
+        if (u & 1) {
+          ph[u >> 1] |= x.h << 16; pm[u >> 1] |= x.m << 16; pl[u >> 1] |= x.l << 16;
+        } else {
+          ph[u >> 1] = x.h; pm[u >> 1] = x.m; pl[u >> 1] = x.l;
+        }
+      }
+      *reinterpret_cast<u32x4*>(&obt[buf][0][sf * TSB + sr0]) = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      *reinterpret_cast<u32x4*>(&obt[buf][1][sf * TSB + sr0]) = u32x4{pm[0], pm[1], pm[2], pm[3]};
+      *reinterpret_cast<u32x4*>(&obt[buf][2][sf * TSB + sr0]) = u32x4{pl[0], pl[1], pl[2], pl[3]};
+    }
+    if (tid < 32) {
+      const float Z = __builtin_bit_cast(float, pst.w);
+      qst[buf][tid] = make_int4(pst.x, pst.y, pst.z, __builtin_bit_cast(int32_t, Z > 0.0f ? 1.0f / Z : 0.0f));
+      qd[buf][tid] = pd;
+    }
+  };
+  if (qstart < ntiles) {
+    prefetch(qstart);
+    commit(0);
+  }
+  __syncthreads();
+  for (int tile = qstart; tile < ntiles; ++tile) {
+    const int buf = (tile - qstart) & 1;
+    const int r0 = 32 * tile;
+    if (tile + 1 < ntiles) prefetch(tile + 1);
+    if (wactive && tile >= wfirst) {
+      const uint32_t* qwb = qwt[buf];
+      uint32_t qwv[16][W];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) qwv[i][w] = qwb[tile_row(i, half) * W + w];
+      }
+      // dP tile (rows = query rows, columns = keys): A = row kl of the split
+      // dout tile, features 16c + 8 half .. + 7
+      v8bf oa[NC][3];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp)
+          oa[c][pp] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&ob[buf][pp][kl * OSB + 16 * c + 8 * half]));
+      }
+      float p[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = tile_row(i, half);
+        const int q = r0 + rl;
+        int h = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) h += __builtin_popcount(qwv[i][w] ^ kw[w]);
+        const int4 st = qst[buf][rl];
+        const bool vis = kvalid & (q < n) & (!a.causal | (j <= q));
+        const bool keep = vis & ((h < st.x) | ((h == st.x) & (j <= st.y)));
+        const float wt = wtab[min(max(h - st.z, 0), d)];
+        p[i] = keep ? wt * __builtin_bit_cast(float, st.w) : 0.0f;
+      }
+      v16f dp = v16f{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        dp = MFMA_BF16(oa[c][0], vb[c], dp);
+        dp = MFMA_BF16(oa[c][1], vb[c], dp);
+        dp = MFMA_BF16(oa[c][2], vb[c], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dsv[i] = a.scale * p[i] * (dp[i] - qd[buf][tile_row(i, half)]);
+      // slot (half, s) of step cc is the query row tile_row(8cc + s, half):
+      // rows 16cc + 4 half + s (s < 4) and 16cc + 8 + 4 half + s - 4
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        v8bf pb[3], sb[3];
+        split8(p + 8 * cc, pb);
+        split8(dsv + 8 * cc, sb);
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+          v8bf da[3];
+#pragma unroll
+          for (int pp = 0; pp < 3; ++pp) {
+            const uint16_t* col = &obt[buf][pp][(32 * t + kl) * TSB + 16 * cc + 4 * half];
+            const uint2 lo = *reinterpret_cast<const uint2*>(col);
+            const uint2 hi = *reinterpret_cast<const uint2*>(col + 8);
+            da[pp] = __builtin_bit_cast(v8bf, u32x4{lo.x, lo.y, hi.x, hi.y});
+          }
+          // dV^T += dout^T P: the six partial products above 2^-24
+          accv[t] = MFMA_BF16(da[0], pb[0], accv[t]);
+          accv[t] = MFMA_BF16(da[0], pb[1], accv[t]);
+          accv[t] = MFMA_BF16(da[1], pb[0], accv[t]);
+          accv[t] = MFMA_BF16(da[0], pb[2], accv[t]);
+          accv[t] = MFMA_BF16(da[1], pb[1], accv[t]);
+          accv[t] = MFMA_BF16(da[2], pb[0], accv[t]);
+          // dK^T += Bq^T dS
+          uint32_t wsel[8];
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) wsel[s2] = qwv[8 * cc + s2][t];
+          const v8bf sa = sign_operand(wsel, kl);
+          acck[t] = MFMA_BF16(sa, sb[0], acck[t]);
+          acck[t] = MFMA_BF16(sa, sb[1], acck[t]);
+          acck[t] = MFMA_BF16(sa, sb[2], acck[t]);
+        }
+      }
+    }
+    if (tile + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
+  }
+  if (!kvalid) return;
+  const float g = a.sigma_k != nullptr ? 1.0f / *a.sigma_k : 1.0f;
+  float* vrow = a.dv + krow * d;
+  float* krow_out = a.dk + krow * d;
+#pragma unroll
+  for (int t = 0; t < W; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int f = 32 * t + tile_row(i, half);
+      if (f < d) {
+        vrow[f] = accv[t][i];
+        krow_out[f] = acck[t][i] * g;
+      }
+    }
+  }
+}
+
 // Launches 2 and 3 for W words per row.
 template <int W>
 had_status launch_bwd(const BwdArgs& a, bool vf32, unsigned blocks, hipStream_t hs) {
+  if constexpr (W <= 2) {
+    if (!vf32) {
+      bwd_dq_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
+      had_status st = check_launch("had_backward");
+      if (st != HAD_OK) return st;
+      bwd_dkv_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
+      return check_launch("had_backward");
+    }
+  }
   if (vf32)
     bwd_dq_kernel<W, true><<<blocks, kBwdThreads, 0, hs>>>(a);
   else
