@@ -32,10 +32,10 @@
 //     query rows (their sign words, dout rows, statistics and D staged in
 //     LDS) each wave forms h, the weights and dP (A = the dout tile, B = the
 //     key's V row in registers), dS, and accumulates P^T dout and dS^T Bq.
-// With fp32 V, or d > 64, everything is float32 on the matrix cores (their
-// fp32 products round like the vector ALU's).  With bf16 V and d <= 64 the
-// products run on the bf16 matrix cores with the float32 operands split into
-// three bf16 terms (see the bf16 kernels below).  No floating-point atomics,
+// With fp32 V everything is float32 on the matrix cores (their fp32
+// products round like the vector ALU's).  With bf16 V the products run on
+// the bf16 matrix cores with the float32 operands split into three bf16
+// terms (see the bf16 kernels below).  No floating-point atomics,
 // so results are identical run to run.  Masked elements take weight 0.
 #include <cmath>
 
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// ---- bf16 V, d <= 64: the products on the bf16 matrix cores ----------------
+// ---- bf16 V: the products on the bf16 matrix cores ------------------------
 // Every float32 x is exactly hi + mid + lo with three bf16 values (hi = the
 // top 16 bits of x, mid the top 16 bits of the remainder, lo the rest, which
 // has at most 8 significant bits).  A product with an operand that is exact
@@ -309,12 +309,12 @@ __device__ inline v8bf sign_operand(const uint32_t* w, int bit) {
 
 #define MFMA_BF16(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
-// dQ, query-major, bf16 V, W <= 2.  As bwd_dq_kernel; the V tile is staged
+// dQ, query-major, bf16 V.  As bwd_dq_kernel; the V tile is staged
 // as bf16 rows, dout of the wave's rows is split once into bf16 operands,
 // dP takes 3 products per 16 features and dQ^T += Bk^T dS 3 per 16 keys.
 template <int W>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_bf_kernel(BwdArgs a) {
-  static_assert(W <= 2, "bf16 path for d <= 64");
+  static_assert(W <= 4, "d <= 128");
   constexpr int DP = 32 * W;
   constexpr int NC = DP / 16;   // 16-feature steps of dP
   constexpr int VSB = DP + 8;   // LDS row stride of the V tile, bf16 elements (16-byte rows, odd multiple)
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// dK and dV, key-major, bf16 V, W <= 2.  As bwd_dkv_kernel; each dout tile
+// dK and dV, key-major, bf16 V.  As bwd_dkv_kernel; each dout tile
 // is staged split (hi, mid, lo) twice: row-major for the A operand of dP
 // (16 features of one query row per lane) and feature-major for the A
 // operand of dV^T += dout^T P (for one feature, the 8 query rows whose
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
 // query rows and 32 features.
 template <int W>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
-  static_assert(W <= 2, "bf16 path for d <= 64");
+  static_assert(W <= 4, "d <= 128");
   constexpr int DP = 32 * W;
   constexpr int NC = DP / 16;
   constexpr int OSB = DP + 8;       // row-major tile stride (bf16): 16-byte rows, odd multiple
@@ -730,11 +730,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
   }
 
   const int64_t rbase = bh * static_cast<int64_t>(n);
-  // staging share: thread t takes feature f = t % DP of query rows
-  // 8 (t / DP) .. + 7 (coalesced loads across the lanes)
-  const int sf = tid % DP, sr0 = 8 * (tid / DP);
+  // staging share: item e (4 DP of them: a feature and a group of 8 query
+  // rows) is feature e % DP of rows 8 (e / DP) .. + 7 (coalesced loads
+  // across the lanes); thread t takes items t, t + 256, ...
+  constexpr int kItems = (4 * DP + kBwdThreads - 1) / kBwdThreads;
   uint32_t pq = 0;
-  float po[8];
+  float po[kItems][8];
   int4 pst = make_int4(0, 0, 0, 0);
   float pd = 0.0f;
   int staged_r0 = 0;
@@ -742,9 +743,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
     const int r0 = 32 * tile;
     staged_r0 = r0;
     pq = a.qbits[(rbase + min(r0 + min(tid, 32 * W - 1) / W, n - 1)) * W + tid % W];
-    if (sr0 < 32) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) po[u] = a.dout[(rbase + min(r0 + sr0 + u, n - 1)) * d + min(sf, d - 1)];
+    for (int it = 0; it < kItems; ++it) {
+      const int e = min(tid + it * kBwdThreads, 4 * DP - 1);
+      const int sf = e % DP, sr0 = 8 * (e / DP);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) po[it][u] = a.dout[(rbase + min(r0 + sr0 + u, n - 1)) * d + min(sf, d - 1)];
     }
     const int q = min(r0 + (tid & 31), n - 1);
     pst = *reinterpret_cast<const int4*>(a.stats + (rbase + q) * 4);
@@ -752,12 +756,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
   };
   auto commit = [&](int buf) {
     if (tid < 32 * W) qwt[buf][tid] = pq;
-    if (sr0 < 32) {
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int e = tid + it * kBwdThreads;
+      if (e >= 4 * DP) break;
+      const int sf = e % DP, sr0 = 8 * (e / DP);
       uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const bool in = staged_r0 + sr0 + u < n && sf < d;
-        const Split3 x = split3(in ? po[u] : 0.0f);
+        const Split3 x = split3(in ? po[it][u] : 0.0f);
         ob[buf][0][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.h);
         ob[buf][1][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.m);
         ob[buf][2][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.l);
@@ -884,25 +892,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
 // Launches 2 and 3 for W words per row.
 template <int W>
 had_status launch_bwd(const BwdArgs& a, bool vf32, unsigned blocks, hipStream_t hs) {
-  if constexpr (W <= 2) {
-    if (!vf32) {
-      bwd_dq_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
-      had_status st = check_launch("had_backward");
-      if (st != HAD_OK) return st;
-      bwd_dkv_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
-      return check_launch("had_backward");
-    }
+  if (!vf32) {
+    bwd_dq_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
+    had_status st = check_launch("had_backward");
+    if (st != HAD_OK) return st;
+    bwd_dkv_bf_kernel<W><<<blocks, kBwdThreads, 0, hs>>>(a);
+    return check_launch("had_backward");
   }
-  if (vf32)
-    bwd_dq_kernel<W, true><<<blocks, kBwdThreads, 0, hs>>>(a);
-  else
-    bwd_dq_kernel<W, false><<<blocks, kBwdThreads, 0, hs>>>(a);
+  bwd_dq_kernel<W, true><<<blocks, kBwdThreads, 0, hs>>>(a);
   had_status st = check_launch("had_backward");
   if (st != HAD_OK) return st;
-  if (vf32)
-    bwd_dkv_kernel<W, true><<<blocks, kBwdThreads, 0, hs>>>(a);
-  else
-    bwd_dkv_kernel<W, false><<<blocks, kBwdThreads, 0, hs>>>(a);
+  bwd_dkv_kernel<W, true><<<blocks, kBwdThreads, 0, hs>>>(a);
   return check_launch("had_backward");
 }
 
