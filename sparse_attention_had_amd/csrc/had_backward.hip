@@ -279,15 +279,22 @@ __device__ inline Split3 split3(float x) {
   return {u >> 16, ur >> 16, __builtin_bit_cast(uint32_t, l) >> 16};
 }
 
-// Eight float32 values as three bf16 operand vectors (element s = x[s]).
+// Eight float32 values as three bf16 operand vectors (element s = x[s]);
+// the top halves of two words are joined by one byte permute.
 __device__ inline void split8(const float* x, v8bf* o) {
   u32x4 ph, pm, pl;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const Split3 a = split3(x[2 * k]), b = split3(x[2 * k + 1]);
-    ph[k] = a.h | (b.h << 16);
-    pm[k] = a.m | (b.m << 16);
-    pl[k] = a.l | (b.l << 16);
+    const float xa = x[2 * k], xb = x[2 * k + 1];
+    const uint32_t ua = __builtin_bit_cast(uint32_t, xa), ub = __builtin_bit_cast(uint32_t, xb);
+    const float ra = xa - __builtin_bit_cast(float, ua & 0xFFFF0000u);
+    const float rb = xb - __builtin_bit_cast(float, ub & 0xFFFF0000u);
+    const uint32_t ura = __builtin_bit_cast(uint32_t, ra), urb = __builtin_bit_cast(uint32_t, rb);
+    const float la = ra - __builtin_bit_cast(float, ura & 0xFFFF0000u);
+    const float lb = rb - __builtin_bit_cast(float, urb & 0xFFFF0000u);
+    ph[k] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+    pm[k] = __builtin_amdgcn_perm(urb, ura, 0x07060302u);
+    pl[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lb), __builtin_bit_cast(uint32_t, la), 0x07060302u);
   }
   o[0] = __builtin_bit_cast(v8bf, ph);
   o[1] = __builtin_bit_cast(v8bf, pm);
@@ -373,6 +380,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_bf_kernel(BwdArgs a) {
     D = part + __shfl_xor(part, 32, 64);  // both halves of the row
   }
   if (qvalid && half == 0) a.dsum[row] = D;
+  const int tcut = cut >= 0 ? ((T << 16) | cut) : ((T << 16) - 1);
+  const float pscale = a.scale * invZ;
 
   v16f acc[W];
 #pragma unroll
@@ -424,16 +433,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_bf_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         va[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&vt[buf][ql * VSB + 16 * c + 8 * half]));
-      float p[16];
+      // scale * p: kept iff visible and (h, key) <= (T, cut) in the order of
+      // h << 16 | key (keys < 2^16); the table index h - h_min is clamped as
+      // unsigned (a hidden key may lie below h_min)
+      float sp[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + tile_row(i, half);
         int h = 0;
 #pragma unroll
         for (int w = 0; w < W; ++w) h += __builtin_popcount(qw[w] ^ kwv[i][w]);
-        const bool keep = (key < lim) & ((h < T) | ((h == T) & (key <= cut)));
-        const float wt = wtab[min(max(h - hmin, 0), d)];
-        p[i] = keep ? wt * invZ : 0.0f;
+        const bool keep = (((h << 16) | key) <= tcut) & (key < lim);
+        const float wt = wtab[min(static_cast<uint32_t>(h - hmin), static_cast<uint32_t>(d))];
+        sp[i] = keep ? wt * pscale : 0.0f;
       }
       v16f dp = v16f{};
 #pragma unroll
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_bf_kernel(BwdArgs a) {
       }
       float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = a.scale * p[i] * (dp[i] - D);
+      for (int i = 0; i < 16; ++i) ds[i] = sp[i] * (dp[i] - D);
       // dQ^T += Bk^T dS: slot (half, s) of step cc is the key tile_row(8cc + s, half)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -673,17 +685,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
 // operands.  Products per tile: dP 3 per 16 features, dV 6 and dK 3 per 16
 // query rows and 32 features.
 template <int W>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf_kernel(BwdArgs a) {
   static_assert(W <= 4, "d <= 128");
   constexpr int DP = 32 * W;
   constexpr int NC = DP / 16;
   constexpr int OSB = DP + 8;       // row-major tile stride (bf16): 16-byte rows, odd multiple
-  constexpr int TSB = 32 + 8;       // feature-major tile stride (bf16)
+  constexpr int TSB = 32 + 4;       // feature-major tile stride (bf16): 72-byte rows, so the 32
+                                    // lanes' 8-byte reads of a column spread over the banks
   __shared__ __attribute__((aligned(16))) uint16_t ob[2][3][32 * OSB];
   __shared__ __attribute__((aligned(16))) uint16_t obt[2][3][DP * TSB];
-  __shared__ uint32_t qwt[2][32 * W];
-  __shared__ int4 qst[2][32];    // T, last kept tie, h_min, 1/Z bits
-  __shared__ float qd[2][32];    // D
+  __shared__ __attribute__((aligned(8))) uint32_t qwt[2][32 * W];
+  __shared__ int4 qst[2][32];    // (h << 16 | key) bound, h_min, 1/Z bits, D bits
   __shared__ float wtab[DP + 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, kl = lane & 31;
@@ -730,12 +742,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
   }
 
   const int64_t rbase = bh * static_cast<int64_t>(n);
-  // staging share: item e (4 DP of them: a feature and a group of 8 query
-  // rows) is feature e % DP of rows 8 (e / DP) .. + 7 (coalesced loads
-  // across the lanes); thread t takes items t, t + 256, ...
+  // staging share: item e (4 DP of them) is features 2 (e % (DP/2)) and
+  // + 1 of query rows 4 (e / (DP/2)) .. + 3; thread t takes items t, t + 256,
+  // ...  The split terms of two features of a row (row-major planes) or of
+  // two rows of a feature (feature-major planes) go into one dword.
   constexpr int kItems = (4 * DP + kBwdThreads - 1) / kBwdThreads;
   uint32_t pq = 0;
-  float po[kItems][8];
+  float po[kItems][4][2];
   int4 pst = make_int4(0, 0, 0, 0);
   float pd = 0.0f;
   int staged_r0 = 0;
@@ -746,9 +759,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
       const int e = min(tid + it * kBwdThreads, 4 * DP - 1);
-      const int sf = e % DP, sr0 = 8 * (e / DP);
+      const int f0 = 2 * (e % (DP / 2)), sr0 = 4 * (e / (DP / 2));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) po[it][u] = a.dout[(rbase + min(r0 + sr0 + u, n - 1)) * d + min(sf, d - 1)];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t ro = (rbase + min(r0 + sr0 + u, n - 1)) * d;
+        po[it][u][0] = a.dout[ro + min(f0, d - 1)];
+        po[it][u][1] = a.dout[ro + min(f0 + 1, d - 1)];
+      }
     }
     const int q = min(r0 + (tid & 31), n - 1);
     pst = *reinterpret_cast<const int4*>(a.stats + (rbase + q) * 4);
@@ -760,29 +777,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
     for (int it = 0; it < kItems; ++it) {
       const int e = tid + it * kBwdThreads;
       if (e >= 4 * DP) break;
-      const int sf = e % DP, sr0 = 8 * (e / DP);
-      uint32_t ph[4], pm[4], pl[4];
+      const int f0 = 2 * (e % (DP / 2)), sr0 = 4 * (e / (DP / 2));
+      // the three split terms of each value, as float32 words whose top
+      // halves are the bf16 terms
+      uint32_t t3[3][4][2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = staged_r0 + sr0 + u < n && sf < d;
-        const Split3 x = split3(in ? po[it][u] : 0.0f);
-        ob[buf][0][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.h);
-        ob[buf][1][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.m);
-        ob[buf][2][(sr0 + u) * OSB + sf] = static_cast<uint16_t>(x.l);
-        if (u & 1) {
-          ph[u >> 1] |= x.h << 16; pm[u >> 1] |= x.m << 16; pl[u >> 1] |= x.l << 16;
-        } else {
-          ph[u >> 1] = x.h; pm[u >> 1] = x.m; pl[u >> 1] = x.l;
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bool in = staged_r0 + sr0 + u < n && f0 + c < d;
+          const float x = in ? po[it][u][c] : 0.0f;
+          const uint32_t ux = __builtin_bit_cast(uint32_t, x);
+          const float r = x - __builtin_bit_cast(float, ux & 0xFFFF0000u);
+          const uint32_t ur = __builtin_bit_cast(uint32_t, r);
+          const float l = r - __builtin_bit_cast(float, ur & 0xFFFF0000u);
+          t3[0][u][c] = ux;
+          t3[1][u][c] = ur;
+          t3[2][u][c] = __builtin_bit_cast(uint32_t, l);
         }
       }
-      *reinterpret_cast<u32x4*>(&obt[buf][0][sf * TSB + sr0]) = u32x4{ph[0], ph[1], ph[2], ph[3]};
-      *reinterpret_cast<u32x4*>(&obt[buf][1][sf * TSB + sr0]) = u32x4{pm[0], pm[1], pm[2], pm[3]};
-      *reinterpret_cast<u32x4*>(&obt[buf][2][sf * TSB + sr0]) = u32x4{pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<uint32_t*>(&ob[buf][pp][(sr0 + u) * OSB + f0]) =
+              __builtin_amdgcn_perm(t3[pp][u][1], t3[pp][u][0], 0x07060302u);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          *reinterpret_cast<uint2*>(&obt[buf][pp][(f0 + c) * TSB + sr0]) =
+              make_uint2(__builtin_amdgcn_perm(t3[pp][1][c], t3[pp][0][c], 0x07060302u),
+                         __builtin_amdgcn_perm(t3[pp][3][c], t3[pp][2][c], 0x07060302u));
+      }
     }
     if (tid < 32) {
+      // (h << 16 | key) bound of the row's kept keys (none for rows past the
+      // end), h_min, 1/Z, D
       const float Z = __builtin_bit_cast(float, pst.w);
-      qst[buf][tid] = make_int4(pst.x, pst.y, pst.z, __builtin_bit_cast(int32_t, Z > 0.0f ? 1.0f / Z : 0.0f));
-      qd[buf][tid] = pd;
+      const int tc = staged_r0 + tid >= n ? -1 : (pst.y >= 0 ? ((pst.x << 16) | pst.y) : ((pst.x << 16) - 1));
+      qst[buf][tid] = make_int4(tc, pst.z, __builtin_bit_cast(int32_t, Z > 0.0f ? 1.0f / Z : 0.0f),
+                                __builtin_bit_cast(int32_t, pd));
     }
   };
   if (qstart < ntiles) {
@@ -799,18 +832,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
       uint32_t qwv[16][W];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        if constexpr (W % 2 == 0) {
 #pragma unroll
-        for (int w = 0; w < W; ++w) qwv[i][w] = qwb[tile_row(i, half) * W + w];
+          for (int w = 0; w < W; w += 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(&qwb[tile_row(i, half) * W + w]);
+            qwv[i][w] = x.x;
+            qwv[i][w + 1] = x.y;
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < W; ++w) qwv[i][w] = qwb[tile_row(i, half) * W + w];
+        }
       }
-      // dP tile (rows = query rows, columns = keys): A = row kl of the split
-      // dout tile, features 16c + 8 half .. + 7
-      v8bf oa[NC][3];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int pp = 0; pp < 3; ++pp)
-          oa[c][pp] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&ob[buf][pp][kl * OSB + 16 * c + 8 * half]));
-      }
+      // kept iff visible and (h, j) <= (T, cut) in the order of h << 16 | j;
+      // a lane past the end writes nothing, so its weights need no mask
       float p[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -820,20 +855,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_bf_kernel(BwdArgs a) {
 #pragma unroll
         for (int w = 0; w < W; ++w) h += __builtin_popcount(qwv[i][w] ^ kw[w]);
         const int4 st = qst[buf][rl];
-        const bool vis = kvalid & (q < n) & (!a.causal | (j <= q));
-        const bool keep = vis & ((h < st.x) | ((h == st.x) & (j <= st.y)));
-        const float wt = wtab[min(max(h - st.z, 0), d)];
-        p[i] = keep ? wt * __builtin_bit_cast(float, st.w) : 0.0f;
+        const bool keep = (((h << 16) | j) <= st.x) & (!a.causal | (j <= q));
+        const float wt = wtab[min(static_cast<uint32_t>(h - st.y), static_cast<uint32_t>(d))];
+        p[i] = keep ? wt * __builtin_bit_cast(float, st.z) : 0.0f;
       }
+      // dP tile (rows = query rows, columns = keys): A = row kl of the split
+      // dout tile, features 16c + 8 half .. + 7, read step by step
       v16f dp = v16f{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        dp = MFMA_BF16(oa[c][0], vb[c], dp);
-        dp = MFMA_BF16(oa[c][1], vb[c], dp);
-        dp = MFMA_BF16(oa[c][2], vb[c], dp);
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+          const v8bf oa = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&ob[buf][pp][kl * OSB + 16 * c + 8 * half]));
+          dp = MFMA_BF16(oa, vb[c], dp);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsv[i] = a.scale * p[i] * (dp[i] - qd[buf][tile_row(i, half)]);
+      for (int i = 0; i < 16; ++i)
+        dsv[i] = a.scale * p[i] * (dp[i] - __builtin_bit_cast(float, qst[buf][tile_row(i, half)].w));
       // slot (half, s) of step cc is the query row tile_row(8cc + s, half):
       // rows 16cc + 4 half + s (s < 4) and 16cc + 8 + 4 half + s - 4
 #pragma unroll
