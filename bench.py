@@ -570,7 +570,7 @@ def bench_decode(args, w):
     achieved = model["hbm_bytes"] / dec_s
     # the library's dispatch rule: few (slice, row) pairs, a short cache and a
     # small N take the single launch
-    single = w.rows <= 512 and w.n_k <= 16384 and min(w.topn, w.n_k) <= 8192
+    single = w.rows <= 4096 and w.n_q <= 16 and w.n_k <= 16384 and min(w.topn, w.n_k) <= 8192
     kernels = "dec_one_kernel, one launch" if single else "dec_hist, dec_gather, dec_reduce"
     rec = {
         "metric": f"query rows/sec of HAD decode against a {w.n_k}-key cache; % of HBM roofline",

@@ -547,8 +547,8 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
 }
 
 // ---- single-launch path for few rows ---------------------------------------
-// When there are few (slice, row) pairs (one new token per sequence), each pair
-// gets fparts 1024-thread work-groups that share out the feature columns: every
+// When there are few (slice, row) pairs (at most 4096, and at most 16 new rows
+// per slice), each pair gets fparts 1024-thread work-groups that share out the feature columns: every
 // one of them scans all of the row's keys (so each has the row's histogram,
 // threshold, tie quota and kept list without any exchange), then gathers only
 // its 1/fparts of each kept V row and writes those output columns.  No split
@@ -576,7 +576,8 @@ constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneKPT = 16;                              // keys per thread
 constexpr int kOneMaxKeys = kOneThreads * kOneKPT;       // 16384
 constexpr int kOneMaxList = 8192;                        // kept keys per row (LDS list)
-constexpr int kOneMaxPairs = 512;                        // (slice, row) pairs that take this path
+constexpr int kOneMaxPairs = 4096;                       // (slice, row) pairs that take this path
+constexpr int kOneMaxRows = 16;                          // new rows per slice that take this path
 
 template <int W, bool VF32, bool kVec, bool kKVec, bool kQF>
 __global__ __launch_bounds__(kOneThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -589,14 +590,18 @@ void dec_one_kernel(DecArgs a) {
   __shared__ float sh_invz;
   float* red = reinterpret_cast<float*>(list);
   float* red2 = reinterpret_cast<float*>(hist);
-  // work-group -> (pair, part): index = ((pair / 8) * fparts + part) * 8 + pair % 8
+  // index = ((slice / 8) * nq * fparts + row * fparts + part) * 8 + slice % 8:
+  // every row and part of a slice on one XCD (work-groups are dealt to the
+  // XCDs round robin by index), so its key words and kept V rows are shared
+  // in that XCD's L2
   const int P = a.fparts;
   const int rest = static_cast<int>(blockIdx.x >> 3);
   const int part = rest % P;
-  const int64_t bhq = static_cast<int64_t>(rest / P) * 8 + (blockIdx.x & 7);
-  if (bhq >= a.bh_total * a.nq) return;  // padding of the last group of 8 pairs
-  const int q = static_cast<int>(bhq % a.nq);
-  const int64_t bh = bhq / a.nq;
+  const int r2 = rest / P;
+  const int q = r2 % a.nq;
+  const int64_t bh = static_cast<int64_t>(r2 / a.nq) * 8 + (blockIdx.x & 7);
+  if (bh >= a.bh_total) return;  // padding of the last group of 8 slices
+  const int64_t bhq = bh * a.nq + q;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int d = a.d, nb = d + 1;
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk) - 1;
@@ -1048,8 +1053,8 @@ int one_fparts(int64_t rows, int d) {
 
 template <int W, bool VF32, bool kVec, bool kKVec>
 void launch_one_q(const DecArgs& a, int64_t rows, hipStream_t st) {
-  // work-group index = ((pair / 8) * fparts + part) * 8 + pair % 8
-  const unsigned nb = static_cast<unsigned>((rows + 7) / 8 * 8 * a.fparts);
+  // work-group index = ((slice / 8) * nq * fparts + row * fparts + part) * 8 + slice % 8
+  const unsigned nb = static_cast<unsigned>((a.bh_total + 7) / 8 * 8 * a.nq * a.fparts);
   if (a.qf != nullptr)
     dec_one_kernel<W, VF32, kVec, kKVec, true><<<nb, kOneThreads, 0, st>>>(a);
   else
@@ -1154,8 +1159,12 @@ had_status decode_impl(const char* who, const uint32_t* qbits, const float* qf, 
   const bool kvec = aligned(kbits, a.W % 4 == 0 ? 16 : 8);
   // 16-byte row slices need 16-byte aligned rows
   const bool vec = aligned(v, 16) && (a.vf32 ? (a.d % 4 == 0) : (a.d % 8 == 0));
-  if (rows <= kOneMaxPairs && s.n_k <= kOneMaxKeys && a.topn <= kOneMaxList) {
-    // few rows: fparts work-groups per (slice, row), one launch
+  // Few rows: fparts work-groups per (slice, row), one launch.  Each of its
+  // work-groups scans the keys for one row, where the split histogram launch
+  // reads a key once for up to 16 rows; at 16 new rows per slice (4 x 32
+  // slices, 16384 keys) the single launch measured 174 us and the split
+  // launches 186 us.
+  if (rows <= kOneMaxPairs && s.n_q <= kOneMaxRows && s.n_k <= kOneMaxKeys && a.topn <= kOneMaxList) {
     a.fparts = one_fparts(rows, a.d);
     switch (a.W) {
       case 1: launch_one<1>(a, vec, kvec, rows, hs); break;

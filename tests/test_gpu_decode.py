@@ -41,12 +41,13 @@ CASES = [
     (1, 1, 2, 100, 100, 64, 10, 500, True, "f32", 0.3),       # every key visible
     (3, 1, 17, 777, 800, 33, 20, 760, False, "bf16", 0.25),   # two row batches
     (1, 8, 64, 1000, 1000, 64, 100, 936, True, "bf16", 0.125),    # 2 splits of 512 keys, recomputed
-    (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 16 splits of 1024 keys, bins
-    (1, 32, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # 32 splits of 512 keys, bins
-    # more than 512 (slice, row) pairs: the split launches (up to 512 take one work-group each)
-    (1, 520, 1, 3000, 3000, 32, 300, 2999, True, "bf16", 0.25),      # split histograms, distance bins
-    (2, 300, 2, 2048, 2048, 64, 256, 2046, True, "f32", 0.125),      # bins for two rows
-    (1, 600, 1, 1000, 1024, 5, 40, 999, False, "bf16", 0.9),         # d = 5 ties, split path
+    (1, 64, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # full cache, single launch, 4 parts
+    (1, 32, 1, 16384, 16384, 32, 1024, 16383, True, "bf16", 0.18),  # full cache, single launch, 4 parts
+    # hundreds of (slice, row) pairs: the single launch with one work-group per pair
+    # (more than 16 new rows per slice, or caches above 16384 keys, take the split launches)
+    (1, 520, 1, 3000, 3000, 32, 300, 2999, True, "bf16", 0.25),
+    (2, 300, 2, 2048, 2048, 64, 256, 2046, True, "f32", 0.125),
+    (1, 600, 1, 1000, 1024, 5, 40, 999, False, "bf16", 0.9),         # d = 5 ties
 ]
 
 
@@ -154,9 +155,8 @@ def test_decode_is_deterministic_and_reuses_its_workspace():
 @pytest.mark.parametrize("name", sorted(DECODE_WORKLOADS))
 def test_decode_workload_sampled(name):
     """The decode workloads at full size, in the launch configuration bench.py
-    times (the work split for 128 rows x 16384 keys is 8 splits of 2048 keys
-    with stored distance bins; for 2048 rows, 8 splits of 2048 keys with the
-    distances recomputed from the key words), checked against the oracle on
+    times (both take the single launch: 128 rows x 16384 keys with two
+    work-groups per row, 2048 rows with one), checked against the oracle on
     sampled (batch, head) slices, all new rows of each."""
     w = DECODE_WORKLOADS[name]
     log(f"decode workload {name}: B={w.batch} H={w.heads} n_k={w.n_k} n_q={w.n_q} d={w.dim} "
