@@ -590,18 +590,29 @@ void dec_one_kernel(DecArgs a) {
   __shared__ float sh_invz;
   float* red = reinterpret_cast<float*>(list);
   float* red2 = reinterpret_cast<float*>(hist);
-  // index = ((slice / 8) * nq * fparts + row * fparts + part) * 8 + slice % 8:
-  // every row and part of a slice on one XCD (work-groups are dealt to the
-  // XCDs round robin by index), so its key words and kept V rows are shared
-  // in that XCD's L2
+  // With at least 8 slices, index = ((slice / 8) * nq * fparts + row * fparts
+  // + part) * 8 + slice % 8: every row and part of a slice on one XCD
+  // (work-groups are dealt to the XCDs round robin by index), so its key
+  // words and kept V rows are shared in that XCD's L2.  With fewer slices,
+  // index = ((pair / 8) * fparts + part) * 8 + pair % 8, so that the pairs
+  // still spread over the XCDs (the parts of a pair stay together).
   const int P = a.fparts;
   const int rest = static_cast<int>(blockIdx.x >> 3);
   const int part = rest % P;
   const int r2 = rest / P;
-  const int q = r2 % a.nq;
-  const int64_t bh = static_cast<int64_t>(r2 / a.nq) * 8 + (blockIdx.x & 7);
-  if (bh >= a.bh_total) return;  // padding of the last group of 8 slices
-  const int64_t bhq = bh * a.nq + q;
+  int q;
+  int64_t bh, bhq;
+  if (a.bh_total >= 8) {
+    q = r2 % a.nq;
+    bh = static_cast<int64_t>(r2 / a.nq) * 8 + (blockIdx.x & 7);
+    if (bh >= a.bh_total) return;  // padding of the last group of 8 slices
+    bhq = bh * a.nq + q;
+  } else {
+    bhq = static_cast<int64_t>(r2) * 8 + (blockIdx.x & 7);
+    if (bhq >= a.bh_total * a.nq) return;  // padding of the last group of 8 pairs
+    q = static_cast<int>(bhq % a.nq);
+    bh = bhq / a.nq;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int d = a.d, nb = d + 1;
   const int64_t last = a.causal ? a.qpos0 + q : static_cast<int64_t>(a.nk) - 1;
@@ -1053,8 +1064,9 @@ int one_fparts(int64_t rows, int d) {
 
 template <int W, bool VF32, bool kVec, bool kKVec>
 void launch_one_q(const DecArgs& a, int64_t rows, hipStream_t st) {
-  // work-group index = ((slice / 8) * nq * fparts + row * fparts + part) * 8 + slice % 8
-  const unsigned nb = static_cast<unsigned>((a.bh_total + 7) / 8 * 8 * a.nq * a.fparts);
+  // work-group index: by slice (8 slices or more) or by pair, as in the kernel
+  const unsigned nb = static_cast<unsigned>(a.bh_total >= 8 ? (a.bh_total + 7) / 8 * 8 * a.nq * a.fparts
+                                                            : (rows + 7) / 8 * 8 * a.fparts);
   if (a.qf != nullptr)
     dec_one_kernel<W, VF32, kVec, kKVec, true><<<nb, kOneThreads, 0, st>>>(a);
   else
