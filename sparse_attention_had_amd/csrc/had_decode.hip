@@ -547,30 +547,30 @@ __global__ __launch_bounds__(HAD_MAX_DIM) void dec_reduce_kernel(DecArgs a) {
 }
 
 // ---- single-launch path for few rows ---------------------------------------
-// When there are few (slice, row) pairs (at most 4096, and at most 16 new rows
-// per slice), each pair gets fparts 1024-thread work-groups that share out the feature columns: every
-// one of them scans all of the row's keys (so each has the row's histogram,
-// threshold, tie quota and kept list without any exchange), then gathers only
-// its 1/fparts of each kept V row and writes those output columns.  No split
-// histograms or partial outputs go through memory and there is no reduce
-// launch.  fparts > 1 lets a few rows use every CU: gathering scattered V rows
-// is limited by the loads a CU keeps in flight, so one work-group per row on
-// half the CUs reaches little more than half the device rate.  The parts of a
-// pair are placed on one XCD (work-groups are dealt to the XCDs round robin by
-// index), so the repeated key scan is served by that XCD's L2.
-// Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys); key order is
-// (u, wave, lane) as in dec_gather.  Distances go to one LDS histogram; wave 0
-// finds T, h_min, the tie quota and Z from it; the distances, stored by key,
-// are read back 16 consecutive keys per thread, and a thread's kept keys get
-// their list slots from its counts, a scan over the threads and a walk in key
-// order; the kept V rows
-// are gathered 16 bytes of a row per lane with several rows in flight per lane
-// group, and the row groups' sums are added in a fixed order and divided by Z.
-// The per-key steps are written for few vector instructions (hidden keys carry
-// an out-of-range distance instead of a visibility test; slots come from
-// per-thread counts rather than per-key ballots): every one of them costs 4
-// cycles of a SIMD per wave, and the fparts copies of the scan and list
-// repeat them.
+// When there are few (slice, row) pairs (at most 4096, and at most 16 new
+// rows per slice), each pair gets fparts 1024-thread work-groups that share
+// out the feature columns: every one of them scans all of the row's keys (so
+// each has the row's histogram, threshold, tie quota and kept list without
+// any exchange), then gathers only its 1/fparts of each kept V row and writes
+// those output columns.  No split histograms or partial outputs go through
+// memory and there is no reduce launch.  fparts > 1 lets a few rows use every
+// CU: gathering scattered V rows is limited by the loads a CU keeps in
+// flight, so one work-group per row on half the CUs reaches little more than
+// half the device rate.  The work-groups of a slice (or, with fewer than 8
+// slices, of a pair) are placed on one XCD, so the repeated key scan and the
+// shared V rows are served by that XCD's L2.
+// Thread t owns keys t + 1024 u (u < 16, so at most 16384 keys); key order
+// is (u, wave, lane) as in dec_gather.  Distances go to one LDS histogram;
+// wave 0 finds T, h_min, the tie quota and Z from it; the distances, stored
+// by key, are read back 16 consecutive keys per thread, and a thread's kept
+// keys get their list slots from its counts, a scan over the threads and a
+// walk in key order; the kept V rows are gathered 16 bytes of a row per lane
+// with several rows in flight per lane group, and the row groups' sums are
+// added in a fixed order and divided by Z.  The per-key steps are written
+// for few vector instructions (hidden keys carry an out-of-range distance
+// instead of a visibility test; slots come from per-thread counts rather than
+// per-key ballots): each costs 4 cycles of a SIMD per wave, and the fparts
+// copies of the scan and list repeat them.
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneKPT = 16;                              // keys per thread
