@@ -258,7 +258,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
 // has at most 8 significant bits).  A product with an operand that is exact
 // in bf16 (the +-1 sign bits, bf16 V) is then three bf16 products with
 // exact partial products and float32 accumulation; a product of two split
-// float32 operands keeps the six partial products above 2^-24 relative.
+// float32 operands keeps six of the nine partial products (each dropped one
+// is below 2^-21 of the product: |mid| < 2^-7 |x| and |lo| < 2^-14 |x|).
 // v_mfma_f32_32x32x16_bf16 sums over 16 k-slots, slot s of lane half h in A
 // and in B; the kernels give the slot (h, s) the same index on both sides:
 // a feature 16 c + 8 h + s for the products over features, and for the
@@ -267,17 +268,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
 // tile_row(8 cc + s, h)), so dS and P feed the next products as they are.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-struct Split3 {
-  uint32_t h, m, l;  // bf16 bit patterns in the low 16 bits
-};
-__device__ inline Split3 split3(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const float r = x - __builtin_bit_cast(float, u & 0xFFFF0000u);  // exact
-  const uint32_t ur = __builtin_bit_cast(uint32_t, r);
-  const float l = r - __builtin_bit_cast(float, ur & 0xFFFF0000u);  // exact, <= 8 significant bits
-  return {u >> 16, ur >> 16, __builtin_bit_cast(uint32_t, l) >> 16};
-}
 
 // Eight float32 values as three bf16 operand vectors (element s = x[s]);
 // the top halves of two words are joined by one byte permute.
