@@ -640,17 +640,19 @@ void had_attn_kernel(AttnArgs a) {
         z += static_cast<double>(cnt) * static_cast<double>(expf(-2.0f * a.scale * static_cast<float>(b - hmin)));
       }
     }
+    // Only the visible keys at the threshold matter here: such a key is kept
+    // while fewer than this half's quota of them precede it.
     int last_tie = -1;
+    int ties = 0;
     make_q(0x02u, 0xFCu);  // +-2
-    k_sweep(lutc, false, [&](const v16i& t, int gc, auto) {
+    k_sweep(lutc, false, [&](const v16i& t, int gc, auto full) {
       const int kbase = half * Hh + 16 * gc;
       const int L = lim - kbase;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t au = static_cast<uint32_t>(t[i]);
-        const bool keep = i < L && static_cast<int32_t>((au << 15) + sp) < 0;
-        if (keep && au == auT) last_tie = kbase + i;
-        sp += (au == auT) ? 1u : 0u;
+        const bool tie = (decltype(full)::value || i < L) && static_cast<uint32_t>(t[i]) == auT;
+        last_tie = (tie && ties < quota) ? kbase + i : last_tie;
+        ties += tie ? 1 : 0;
       }
     });
     last_tie = max(last_tie, __shfl_xor(last_tie, 32, 64));  // lanes L and L ^ 32 share a row
