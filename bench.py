@@ -391,14 +391,18 @@ def bench_backward(args, w):
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq": w.seq,
                    "dim": w.dim, "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype,
                    "scale": w.scale,
-                   "step": "had_backward: row statistics, dQ (query-major), dK and dV (key-major); "
-                           "3 launches, fp32 matrix-core products"},
+                   "step": "had_backward: row statistics, dQ (query-major), dK and dV (key-major); 3 launches",
+                   "arithmetic": ("bf16 matrix-core products of exact three-way bf16 splits of the float32 "
+                                  "operands (the +-1 signs and bf16 V unsplit), float32 accumulation"
+                                  if w.v_dtype == "bf16" else "fp32 matrix-core products")},
         "backward_us": call_s * 1e6,
         "backward_timing": f"median over {len(durs)} groups of back-to-back calls",
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP32_MFMA_PEAK / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK, "traffic": None,
-                     "kernel": "had_backward (row statistics, bwd_dq_kernel, bwd_dkv_kernel)",
-                     "frac_kind": "algorithmic fp32 flops (8d per kept pair) at the dense fp32 "
+                     "kernel": ("had_backward (row statistics, bwd_dq_bf_kernel, bwd_dkv_bf_kernel)"
+                                if w.v_dtype == "bf16" else
+                                "had_backward (row statistics, bwd_dq_kernel, bwd_dkv_kernel)"),
+                     "frac_kind": "algorithmic flops (8d per kept pair, counted as fp32) at the dense fp32 "
                                   "matrix-core peak",
                      "dense_masked_frac": m["mfma_fp32_flops"] / call_s / FP32_MFMA_PEAK,
                      "work_per_launch": {k2: float(v2) for k2, v2 in m.items()}},
