@@ -48,6 +48,9 @@ CASES = [
     (1, 520, 1, 3000, 3000, 32, 300, 2999, True, "bf16", 0.25),
     (2, 300, 2, 2048, 2048, 64, 256, 2046, True, "f32", 0.125),
     (1, 600, 1, 1000, 1024, 5, 40, 999, False, "bf16", 0.9),         # d = 5 ties
+    # the single launch's placement by slice (8 slices or more) with several parts and rows:
+    (2, 4, 3, 900, 900, 64, 90, 897, True, "bf16", 0.125),           # 8 slices x 3 rows, 4 parts
+    (3, 3, 2, 700, 704, 64, 70, 698, True, "f32", 0.2),              # 9 slices: a padded group of 8
 ]
 
 
