@@ -79,6 +79,10 @@ CASES = [
     (2, 1, 257, 32, 20, True, "bf16", 0.5),     # one word per row, ragged tail
     (1, 1, 33, 1, 5, False, "f32", 1.0),        # d = 1
     (1, 2, 160, 100, 30, False, "bf16", 2.0),   # sharp softmax, d not a multiple of 32
+    # the bf16-product kernels at the other feature widths
+    (1, 2, 150, 128, 20, False, "bf16", 0.09),  # d = 128
+    (1, 1, 90, 33, 12, True, "bf16", 0.3),      # d = 33: padded features
+    (1, 1, 40, 1, 7, True, "bf16", 1.0),        # d = 1
 ]
 
 
