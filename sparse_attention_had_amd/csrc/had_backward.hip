@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
 // operands.  Products per tile: dP 3 per 16 features, dV 6 and dK 3 per 16
 // query rows and 32 features.
 template <int W>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(W == 2 ? 2 : 1))) void bwd_dkv_bf_kernel(BwdArgs a) {
   static_assert(W <= 4, "d <= 128");
   constexpr int DP = 32 * W;
   constexpr int NC = DP / 16;
