@@ -42,6 +42,8 @@ __all__ = [
     "topn_mass",
     "sparse_softmax_av_backward",
     "backward",
+    "soft_binarize",
+    "soft_forward",
 ]
 
 
@@ -410,3 +412,58 @@ def backward(q, k, v, dout, topn: int, scale: float, causal: bool = False,
         e_dv += e_dvb
     return {"dq": dq / sigma_q, "dk": dk / sigma_k, "dv": dv,
             "e_dq": e_dq / sigma_q, "e_dk": e_dk / sigma_k, "e_dv": e_dv, "idx": idx_all}
+
+
+# ---------------------------------------------------------------------------
+# training-side variant: the scaled-tanh (soft-binarized) forward
+# ---------------------------------------------------------------------------
+def soft_binarize(x, sigma_x: float, c: float) -> np.ndarray:
+    """Scaled-tanh soft sign of the standardized tensor, in float64.
+
+    [review] "What carries the argument": the first training stages replace
+    the sign by a scaled tanh whose scale c decays, so that it approaches the
+    sign function smoothly.  The form itself (Eqs. 13/15, which the referee's
+    minor comment 1 finds duplicated) is not printed.  Reading taken: the
+    plain form tanh(u / c) on the standardized input u = x / sigma_x, c > 0;
+    as c -> 0 it tends to sign(u) for every u != 0.  Parity unpinned with
+    respect to the paper's exact form; pinned to its two limits (c -> 0: the
+    sign path, c -> inf: the standardized dot product) in the tests.
+    """
+    if not (c > 0.0) or not np.isfinite(c):
+        raise ValueError("c must be finite and positive")
+    if not (sigma_x > 0.0) or not np.isfinite(sigma_x):
+        raise ValueError("sigma must be finite and positive")
+    a = np.asarray(x, dtype=np.float64)
+    if np.isnan(a).any():
+        raise ValueError("NaN in input")
+    return np.tanh(a / (float(sigma_x) * float(c)))
+
+
+def soft_forward(q, k, v, topn: int, scale: float, c: float, causal: bool = False,
+                 sigma_q=None, sigma_k=None, rows=None):
+    """The path with the scaled-tanh soft sign in place of sign, on one head.
+
+    Readings taken (the pages name the stage but print neither its forward
+    nor whether the top-N mask is on during it): the logits are the real dot
+    products S = Bq Bk^T of the soft rows Bq = soft_binarize(q), Bk =
+    soft_binarize(k); the same top-N rule as select_topn() (exactly N_i kept,
+    the lower key index first among equal logits, causal mask first) and the
+    same softmax over the kept set and AV as sparse_softmax_av().  sigma_q and
+    sigma_k default to sigma() of q and k.  Everything float64.  Returns a
+    dict with S (float64), idx, out, E and the rows used.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    n = q.shape[0]
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows, dtype=np.int64)
+    sq = sigma(q) if sigma_q is None else float(sigma_q)
+    sk = sigma(k) if sigma_k is None else float(sigma_k)
+    bq = soft_binarize(q[rows], sq, c)
+    bk = soft_binarize(k, sk, c)
+    S = bq @ bk.T
+    idx = select_topn(S, topn, causal, row_index=rows)
+    out, mag = sparse_softmax_av(S, idx, v, scale)
+    return {"S": S, "idx": idx, "out": out, "E": mag, "rows": rows,
+            "sigma_q": sq, "sigma_k": sk}

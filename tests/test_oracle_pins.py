@@ -489,3 +489,84 @@ def test_backward_invariants():
     for x in ("dq", "dk", "dv"):
         np.testing.assert_allclose(r2[x], 2.5 * r1[x], rtol=1e-12, atol=1e-13)
     assert np.all(r1["e_dq"] >= np.abs(r1["dq"])) and np.all(r1["e_dv"] >= np.abs(r1["dv"]))
+
+
+# ------------------------------------------ scaled-tanh (soft) forward ----
+def _away_from_zero(x, floor):
+    """Move every element at least `floor` away from 0, keeping its sign."""
+    return np.where(x >= 0, x + floor, x - floor)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_soft_forward_small_c_is_the_sign_path(causal):
+    # tanh(u / c) is exactly +-1 in float64 once |u / c| > 19.1; with every
+    # |x| >= 0.05 sigma and c = 1e-3 that holds for all elements, so the soft
+    # path must give the sign path's logits, kept sets and outputs exactly.
+    # Catches tanh(u * c) in place of tanh(u / c) and a missing standardization
+    # factor that pushes |u / c| back into tanh's curved range.
+    w = make_inputs(1, 1, 60, 24, v_dtype="f32", rank=3, noise="t3", seed=31)
+    q, k, v = w["q"][0, 0], w["k"][0, 0], w["v"][0, 0]
+    q = _away_from_zero(q, 0.05 * oracle.sigma(q) + 0.05 * 3 * np.abs(q).max())
+    k = _away_from_zero(k, 0.05 * oracle.sigma(k) + 0.05 * 3 * np.abs(k).max())
+    assert np.abs(q).min() >= 0.05 * oracle.sigma(q) and np.abs(k).min() >= 0.05 * oracle.sigma(k)
+    for topn in (1, 7, 60):
+        soft = oracle.soft_forward(q, k, v, topn, 0.3, 1e-3, causal=causal)
+        hard = oracle.forward(q, k, v, topn, 0.3, causal=causal)
+        assert np.array_equal(soft["S"], hard["S"].astype(np.float64))
+        assert np.array_equal(soft["idx"], hard["idx"])
+        np.testing.assert_array_equal(soft["out"], hard["out"])
+
+
+def test_soft_forward_large_c_is_topn_attention_on_the_standardized_inputs():
+    # c^2 tanh(a / c) tanh(b / c) = a b (1 - (a^2 + b^2) / (3 c^2) + ...), so
+    # with scale * c^2 and c = 1e4 the soft path is top-N softmax attention
+    # over the dot products of x / sigma, up to ~1e-7 relative.  The reference
+    # here is built directly: standardized products, argsort, scipy softmax.
+    # Catches a dropped or squared sigma (the inputs have sigma far from 1).
+    rng = np.random.default_rng(5)
+    n, d, topn, scale, c = 48, 16, 9, 0.2, 1.0e4
+    q = 3.0 * rng.standard_normal((n, d)) + 0.4
+    k = 0.5 * rng.standard_normal((n, d)) - 0.1
+    v = rng.standard_normal((n, 6))
+    soft = oracle.soft_forward(q, k, v, topn, scale * c * c, c)
+    u = (q / q.std()) @ (k / k.std()).T
+    for i in range(n):
+        kept = np.sort(np.argsort(-u[i], kind="stable")[:topn])
+        assert soft["idx"][i].tolist() == kept.tolist()
+        p = scipy.special.softmax(scale * u[i, kept])
+        np.testing.assert_allclose(soft["out"][i], p @ v[kept], rtol=1e-5, atol=1e-7)
+
+
+def test_soft_forward_two_keys_closed_form():
+    # atanh inverts the soft sign at c = 1, sigma = 1: q = atanh(0.8) and keys
+    # atanh(+-0.5) give logits +-0.4, and the two kept keys mix by the logistic
+    # function of the gap 0.8 * scale.
+    q = np.array([[math.atanh(0.8)]])
+    k = np.array([[math.atanh(0.5)], [math.atanh(-0.5)], [math.atanh(0.1)]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 5.0]])
+    r = oracle.soft_forward(q, k, v, 2, 1.5, 1.0, sigma_q=1.0, sigma_k=1.0)
+    np.testing.assert_allclose(r["S"], [[0.4, -0.4, 0.08]], rtol=1e-14)
+    assert r["idx"].tolist() == [[0, 2]]
+    p0 = 1.0 / (1.0 + math.exp(-1.5 * (0.4 - 0.08)))
+    np.testing.assert_allclose(r["out"][0], p0 * v[0] + (1 - p0) * v[2], rtol=1e-14)
+
+
+def test_soft_forward_symmetries_and_bounds():
+    # tanh is odd: negating both q and k leaves the logits and the output
+    # unchanged, negating q alone negates every logit; |S| <= d always.
+    rng = np.random.default_rng(17)
+    n, d = 30, 12
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, 4))
+    a = oracle.soft_forward(q, k, v, 5, 0.7, 0.6)
+    b = oracle.soft_forward(-q, -k, v, 5, 0.7, 0.6)
+    np.testing.assert_array_equal(a["S"], b["S"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    neg = oracle.soft_forward(-q, k, v, 5, 0.7, 0.6)
+    np.testing.assert_array_equal(neg["S"], -a["S"])
+    assert np.abs(a["S"]).max() <= d
+    tiny = oracle.soft_forward(q, k, v, 5, 0.7, 1e-9)
+    assert np.abs(tiny["S"]).max() <= d and np.all(np.abs(np.rint(tiny["S"]) - tiny["S"]) == 0)
+    with pytest.raises(ValueError):
+        oracle.soft_forward(q, k, v, 5, 0.7, 0.0)
