@@ -284,6 +284,70 @@ had_status had_backward(const uint32_t* qbits, const uint32_t* kbits,
                         float* dq, float* dk, float* dv, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Limit of the soft (scaled-tanh) forward: the logit block of 32 query rows
+   and every key stays in registers. */
+#define HAD_SOFT_MAX_SEQ 1024
+
+/* Workspace bytes that had_soft_forward / had_soft_select need for shape s
+ * (0 for an invalid shape, d > 128 or n > HAD_SOFT_MAX_SEQ). */
+size_t had_soft_workspace_bytes(had_shape s);
+
+/*
+ * had_soft_forward - the attention path with the sign replaced by a scaled
+ * tanh, for the training stages that approach the binarization smoothly.
+ *
+ * Defined by: Pith review, "What carries the argument" (a four-stage
+ * annealing schedule whose first stages use a scaled tanh with a decaying
+ * scale c that approaches the sign function); referee minor comment 1 (the
+ * stage's Eqs. 13/15 are printed twice and never settled).  Reading: the soft
+ * sign is B_c(x) = tanh(x / (sigma * c)), c > 0 (c -> 0 gives the sign path);
+ * the logits are the real dot products s_ij = B_c(q_i) . B_c(k_j); row i keeps
+ * its N_i = min(N, visible_i) largest logits (lower key index first among
+ * equal float32 logits, causal mask first); out_i = softmax over the kept set
+ * of scale * s_ij, times V.
+ *
+ *  q, k       [B,H,n,d] float32, device, 4-byte aligned.  n <= 1024, d <= 128.
+ *  v, v_dtype as had_attention (float32 or bf16, 4-byte aligned).
+ *  topn, scale, causal  as had_attention.
+ *  c          the tanh scale, finite and > 0.
+ *  sigma_q, sigma_k  device float* (had_pack's or had_sigma_from_state's
+ *             sigma), or NULL for 1.
+ *  out        [B,H,n,d] float32, device; every element written.
+ *  workspace  had_soft_workspace_bytes(s) bytes, 256-byte aligned (the soft
+ *             rows; no initial contents needed).  Calls that may overlap need
+ *             distinct workspaces.
+ *  Precision: float32 tanh, logits on the fp32 matrix cores, the kept set the
+ *  exact top-N of those float32 logits, float32 weights, products and sums
+ *  (no floating-point atomics: results are identical run to run).
+ *  Errors: HAD_ERR_INVALID_ARG for null or misaligned pointers, bad sizes,
+ *  topn < 1, bad scale, c, causal or v_dtype, a small workspace;
+ *  HAD_ERR_UNSUPPORTED for d > 128 or n > HAD_SOFT_MAX_SEQ.
+ */
+had_status had_soft_forward(const float* q, const float* k, const void* v,
+                            had_dtype v_dtype, had_shape s, int64_t topn,
+                            float scale, float c, int causal,
+                            const float* sigma_q, const float* sigma_k,
+                            float* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * had_soft_select - inspection export of the kept sets of had_soft_forward
+ * (same kernel code, same selection).
+ *
+ * Defined by: as had_soft_forward; the top-N rule of "What carries the
+ * argument".
+ *
+ *  Arguments as had_soft_forward; slices bh in [bh_begin, bh_begin +
+ *  bh_count) of the B*H slices, all n query rows.
+ *  keep  [bh_count, n, n] uint8, device: 1 where row i keeps key j, else 0
+ *        (cleared by the call).
+ */
+had_status had_soft_select(const float* q, const float* k, had_shape s,
+                           int64_t topn, float c, int causal,
+                           const float* sigma_q, const float* sigma_k,
+                           int64_t bh_begin, int64_t bh_count, uint8_t* keep,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * had_logits - inspection export of the integer logits s = d - 2*Hamming
  * computed by the same logit stage as had_attention (no mask, every key).

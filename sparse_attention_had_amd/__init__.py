@@ -116,6 +116,14 @@ def load_library():
         lib.had_backward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, I, P, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, P]
         lib.had_backward.restype = I
+        lib.had_soft_workspace_bytes.argtypes = [Shape]
+        lib.had_soft_workspace_bytes.restype = ctypes.c_size_t
+        lib.had_soft_forward.argtypes = [P, P, P, I, Shape, I64, ctypes.c_float, ctypes.c_float, I, P, P,
+                                         P, P, ctypes.c_size_t, P]
+        lib.had_soft_forward.restype = I
+        lib.had_soft_select.argtypes = [P, P, Shape, I64, ctypes.c_float, I, P, P, I64, I64, P, P,
+                                        ctypes.c_size_t, P]
+        lib.had_soft_select.restype = I
         lib.had_pack_calibrate.argtypes = [P, Shape, P, P, P, ctypes.c_size_t, P, P]
         lib.had_pack_calibrate.restype = I
         lib.had_sigma_from_state.argtypes = [P, P, P]
@@ -430,6 +438,69 @@ def backward(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, out: tor
         grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(dev, stream)))
     return tuple(grads)
+
+
+def _soft_common(q, k, sigma_q, sigma_k):
+    _need_cuda(q, "q", torch.float32)
+    _need_cuda(k, "k", torch.float32)
+    B, H, n, d = _shape4(q, "q")
+    if tuple(k.shape) != (B, H, n, d):
+        raise ValueError("k must have the shape of q")
+    ptrs = []
+    for t, name in ((sigma_q, "sigma_q"), (sigma_k, "sigma_k")):
+        if t is not None:
+            _need_cuda(t, name, torch.float32)
+        ptrs.append(None if t is None else t.data_ptr())
+    return Shape(B, H, n, d), ptrs
+
+
+def soft_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topn: int, scale: float, c: float,
+                 causal: bool = False, *, sigma_q: torch.Tensor | None = None,
+                 sigma_k: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """had_soft_forward: the path with tanh(x / (sigma c)) in place of sign;
+    returns out float32 [B,H,n,d].  sigma_q / sigma_k are 1-element device
+    tensors (e.g. from pack()), None meaning 1."""
+    lib = load_library()
+    shape, ptrs = _soft_common(q, k, sigma_q, sigma_k)
+    _need_cuda(v, "v")
+    if tuple(v.shape) != tuple(q.shape):
+        raise ValueError("v must have the shape of q")
+    dev = q.device
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+    _need_cuda(out, "out", torch.float32)
+    need = int(lib.had_soft_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(dev, stream, max(need, 256))
+    _need_cuda(workspace, "workspace")
+    _check("had_soft_forward", lib.had_soft_forward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _v_dtype(v), shape, int(topn), float(scale), float(c),
+        int(bool(causal)), ptrs[0], ptrs[1], out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(dev, stream)))
+    return out
+
+
+def soft_select(q: torch.Tensor, k: torch.Tensor, topn: int, c: float, causal: bool = False, *,
+                sigma_q: torch.Tensor | None = None, sigma_k: torch.Tensor | None = None,
+                bh_begin: int = 0, bh_count: int | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """had_soft_select: keep mask [bh_count, n, n] uint8 of soft_forward()'s kept sets."""
+    lib = load_library()
+    shape, ptrs = _soft_common(q, k, sigma_q, sigma_k)
+    dev = q.device
+    n = shape.seq
+    bh_count = shape.batch * shape.heads - bh_begin if bh_count is None else bh_count
+    keep = torch.empty((bh_count, n, n), dtype=torch.uint8, device=dev)
+    need = int(lib.had_soft_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(dev, stream, max(need, 256))
+    _need_cuda(workspace, "workspace")
+    _check("had_soft_select", lib.had_soft_select(
+        q.data_ptr(), k.data_ptr(), shape, int(topn), float(c), int(bool(causal)), ptrs[0], ptrs[1],
+        int(bh_begin), int(bh_count), keep.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(dev, stream)))
+    return keep
 
 
 def decode_workspace_bytes(batch: int, heads: int, n_q: int, n_k: int, k_stride: int,

@@ -24,7 +24,8 @@ LIB_POPCOUNT = os.path.join(PKG, "libhad_popcount.so")
 LIB_FUSEDQ = os.path.join(PKG, "libhad_fusedq.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip"]
+SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip",
+           "had_soft.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

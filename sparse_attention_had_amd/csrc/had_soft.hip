@@ -1,0 +1,510 @@
+// had_soft: the scaled-tanh (soft-binarized) forward of the HAD path.
+//
+// Method (Pith review of "Hamming Attention Distillation", section "What
+// carries the argument"): the first training stages replace the sign of the
+// standardized Q and K by a scaled tanh whose scale c decays, so that it
+// approaches the sign smoothly; the referee's minor comment 1 notes that the
+// form (Eqs. 13/15) is printed twice and never settled.  Read here as
+// B_c(x) = tanh(x / (sigma * c)), c > 0, with the rest of the path unchanged:
+// the logits are the real dot products s_ij = B_c(q_i) . B_c(k_j), every query
+// row keeps its N_i = min(N, visible_i) largest logits (the lower key index
+// first among equal ones, causal mask first), and the softmax of scale * s over
+// the kept set weights the full-precision V rows.
+//
+// GPU design (gfx950), two launches:
+//  1. transform: Q and K -> B_c(Q), B_c(K) in float32, rows padded with zeros
+//     to DP = 32, 64 or 128 features (one HBM pass each way).
+//  2. attention: a work-group is 4 waves and 32 query rows of one (batch,
+//     head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
+//     tiles w, w + 4, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
+//     A = the key rows, B = the query rows; lane L then holds query row
+//     L % 32 and 16 keys of each tile) and keeps them in registers: at most
+//     8 tiles of 16 values per lane.  The kept set is an exact radix select
+//     over the composite (order-preserving bits of the float32 logit, then
+//     the key index inverted), so exactly N_i keys are kept with no separate
+//     tie rule: four levels of 8-bit digits of the logit's key and two of
+//     5-bit digits of the index, each a per-row LDS histogram of the
+//     elements still matching the prefix (ds_add_u32) and a scan that finds
+//     the digit holding the N_i-th largest.  Then the row maximum, the
+//     weights exp(scale * (s - max)) of the kept keys, their sum Z, and the
+//     weighted V rows on the fp32 matrix cores (A = the weights straight from
+//     the logit registers, B = V rows), reduced over the four waves in a
+//     fixed order and divided by Z.
+// No floating-point atomics: results are identical run to run.
+#include <algorithm>
+#include <cmath>
+
+#include "had_internal.h"
+
+namespace had {
+namespace {
+
+constexpr int kSoftWaves = 4;
+constexpr int kSoftThreads = 64 * kSoftWaves;
+constexpr int kSoftMaxSeq = 1024;                            // keys a work-group keeps in registers
+constexpr int kSoftTiles = kSoftMaxSeq / 32 / kSoftWaves;    // key tiles per wave
+constexpr int kBins = 256;                                   // histogram bins per row and level
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// MFMA output register i of lane half `half`: the 32 x 32 tile's lane L holds
+// column L % 32 and rows 8*(i/4) + 4*half + i%4.
+__device__ inline int tile_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+// Unsigned key whose order is the float order (-0 is folded onto +0 first).
+__device__ inline uint32_t order_key(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+inline int soft_dp(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// ---- 1. transform ----------------------------------------------------------
+struct SoftTransformArgs {
+  const float* x[2];
+  float* xs[2];
+  const float* sigma[2];  // device scalars or null (1)
+  int64_t rows;           // B*H*n
+  int d, dp;
+  float c;
+};
+
+constexpr int kTfThreads = 256;
+constexpr int kTfRows = 16;  // rows per block
+
+__global__ __launch_bounds__(kTfThreads) void soft_transform_kernel(SoftTransformArgs a) {
+  const int t = blockIdx.y;
+  const float* x = a.x[t];
+  float* xs = a.xs[t];
+  const float sg = a.sigma[t] != nullptr ? *a.sigma[t] : 1.0f;
+  const float mul = static_cast<float>(1.0 / (static_cast<double>(sg) * static_cast<double>(a.c)));
+  const int d = a.d, dp = a.dp;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTfRows; r0 < a.rows;
+       r0 += static_cast<int64_t>(gridDim.x) * kTfRows) {
+    const int nr = static_cast<int>(min<int64_t>(kTfRows, a.rows - r0));
+    for (int e = threadIdx.x; e < nr * dp; e += kTfThreads) {
+      const int r = e / dp, f = e - r * dp;
+      const int64_t row = r0 + r;
+      xs[row * dp + f] = f < d ? tanhf(x[row * d + f] * mul) : 0.0f;
+    }
+  }
+}
+
+// ---- 2. attention ----------------------------------------------------------
+struct SoftArgs {
+  const float* qs;  // [BH, n, DP]
+  const float* ks;  // [BH, n, DP]
+  const void* v;    // [BH, n, d] float32 or bf16
+  float* out;       // [BH, n, d]
+  uint8_t* keep;    // mask mode: [bh_count, n, n], pre-cleared; 1 where kept
+  int64_t bh_begin, bh_count;
+  int n, d, topn;
+  float scale;
+  int causal;
+};
+
+template <bool VF32>
+__device__ inline float load_v(const void* v, int64_t off) {
+  if (VF32) return static_cast<const float*>(v)[off];
+  const uint32_t b = static_cast<const uint16_t*>(v)[off];
+  return __builtin_bit_cast(float, b << 16);
+}
+
+// One level of the radix select: a per-row histogram of the digit of the
+// elements that still match the prefix found so far, then the scan that finds
+// the digit holding the row's remaining quota.  Levels 0-3 take the four bytes
+// of the logit's order key (highest first), levels 4 and 5 the two 5-bit
+// digits of the key index, inverted so that lower indices come first among
+// equal logits.  All threads of the work-group call it.
+template <int L>
+__device__ __forceinline__ void select_level(const v16f (&s)[kSoftTiles], uint32_t* hist, uint32_t* st_key,
+                                             int* st_idx, int* st_need, int wid, int lane, int ntk, int lim) {
+  const int half = lane >> 5, ql = lane & 31;
+  const uint32_t kpre = st_key[ql];
+  const int ipre = st_idx[ql];
+  uint32_t* hrow = hist + ql * kBins;
+#pragma unroll
+  for (int u = 0; u < kSoftTiles; ++u) {
+    const int kt = wid + kSoftWaves * u;
+    if (kt < ntk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = 32 * kt + tile_row(r, half);
+        const uint32_t k = order_key(s[u][r]);
+        bool m = j < lim;
+        uint32_t dig;
+        if constexpr (L == 0) {
+          dig = k >> 24;
+        } else if constexpr (L < 4) {
+          m = m && (k >> (32 - 8 * L)) == kpre;
+          dig = (k >> (24 - 8 * L)) & 255u;
+        } else if constexpr (L == 4) {
+          m = m && k == kpre;
+          dig = 31u - static_cast<uint32_t>(j >> 5);
+        } else {
+          m = m && k == kpre && (j >> 5) == ipre;
+          dig = 31u - static_cast<uint32_t>(j & 31);
+        }
+        if (m) atomicAdd(hrow + dig, 1u);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // wave w scans rows 8w .. 8w + 7, eight lanes per row
+    constexpr int kPer = (L < 4 ? kBins : 32) / 8;
+    const int srow = 8 * wid + (lane >> 3), g = lane & 7;
+    uint32_t* hb = hist + srow * kBins + kPer * g;
+    uint32_t c[kPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+      c[b] = hb[b];
+      sum += c[b];
+    }
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) hb[b] = 0u;
+    uint32_t S = sum;  // bins of lanes g .. 7 of the row, i.e. digits >= kPer * g
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      const uint32_t t = __shfl_down(S, off, 8);
+      if (g + off < 8) S += t;
+    }
+    const int nd = st_need[srow];
+    const uint32_t above = S - sum;
+    if (nd > 0 && above < static_cast<uint32_t>(nd) && static_cast<uint32_t>(nd) <= S) {
+      uint32_t acc = above;
+      int tb = 0;
+      bool found = false;
+#pragma unroll
+      for (int b = kPer - 1; b >= 0; --b) {
+        const bool hit = !found && acc + c[b] >= static_cast<uint32_t>(nd);
+        if (hit) {
+          tb = b;
+          found = true;
+        }
+        if (!found) acc += c[b];
+      }
+      const uint32_t digit = static_cast<uint32_t>(kPer * g + tb);
+      if constexpr (L < 4)
+        st_key[srow] = (L == 0 ? 0u : (st_key[srow] << 8)) | digit;
+      else if constexpr (L == 4)
+        st_idx[srow] = 31 - static_cast<int>(digit);
+      else
+        st_idx[srow] = 32 * st_idx[srow] + (31 - static_cast<int>(digit));
+      st_need[srow] = nd - static_cast<int>(acc);
+    }
+  }
+  __syncthreads();
+}
+
+template <int DP, bool VF32, bool MASK>
+__global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
+  constexpr int HD = DP / 2;  // features of lane half h: h * HD .. h * HD + HD - 1
+  constexpr int NFT = DP / 32;
+  __shared__ uint32_t hist[32 * kBins];  // per row, one level at a time; then the output partials
+  __shared__ uint32_t st_key[32];        // logit key prefix, then the threshold key K*
+  __shared__ int st_idx[32];             // index prefix, then the last kept index at K*
+  __shared__ int st_need[32];            // kept keys still to place at the current level
+  __shared__ float red[kSoftWaves][32];
+  __shared__ float rinvz[32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int half = lane >> 5, ql = lane & 31;
+  const int n = a.n, d = a.d;
+  const int nqt = (n + 31) / 32;
+  const int64_t bh = a.bh_begin + blockIdx.x % a.bh_count;
+  const int qt = nqt - 1 - static_cast<int>(blockIdx.x / a.bh_count);  // heaviest causal tiles first
+  const int q0 = 32 * qt;
+  const int i_row = q0 + ql;
+  const bool rvalid = i_row < n;
+  const int lim = !rvalid ? 0 : (a.causal ? i_row + 1 : n);  // row i sees keys j < lim
+  const int kend = a.causal ? min(n, q0 + 32) : n;
+  const int ntk = (kend + 31) / 32;  // key tiles some row of the block sees
+
+  for (int e = tid; e < 32 * kBins; e += kSoftThreads) hist[e] = 0u;
+  if (tid < 32) {
+    const int r = q0 + tid;
+    const int vis = r >= n ? 0 : (a.causal ? r + 1 : n);
+    st_need[tid] = min(a.topn, vis);
+    st_key[tid] = 0u;
+    st_idx[tid] = 0;
+  }
+
+  // ---- logits: s[u] = tile (key tile wid + 4u) x (the block's 32 rows)
+  float qv[HD];
+  {
+    const float* qr = a.qs + (bh * n + (rvalid ? i_row : n - 1)) * DP + HD * half;
+#pragma unroll
+    for (int t = 0; t < HD; t += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(qr + t);
+      qv[t] = x.x;
+      qv[t + 1] = x.y;
+      qv[t + 2] = x.z;
+      qv[t + 3] = x.w;
+    }
+  }
+  v16f s[kSoftTiles];
+#pragma unroll
+  for (int u = 0; u < kSoftTiles; ++u) {
+    const int kt = wid + kSoftWaves * u;
+    v16f acc = {};
+    if (kt < ntk) {
+      const int key = min(32 * kt + ql, n - 1);
+      const float* kr = a.ks + (bh * n + key) * DP + HD * half;
+#pragma unroll
+      for (int t = 0; t < HD; t += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(kr + t);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, qv[t], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, qv[t + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, qv[t + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, qv[t + 3], acc, 0, 0, 0);
+      }
+    }
+    s[u] = acc;
+  }
+  __syncthreads();
+
+  // ---- exact top-N: radix select over (logit key, inverted index)
+  select_level<0>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  select_level<1>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  select_level<2>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  select_level<3>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  select_level<4>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  select_level<5>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+
+  // key j of this row is kept iff visible and (key > K*, or key == K* and j <= j*)
+  const uint32_t kst = st_key[ql];
+  const int jst = st_idx[ql];
+
+  if (MASK) {
+    uint8_t* mrow = a.keep + ((bh - a.bh_begin) * n + (rvalid ? i_row : 0)) * static_cast<int64_t>(n);
+#pragma unroll
+    for (int u = 0; u < kSoftTiles; ++u) {
+      const int kt = wid + kSoftWaves * u;
+      if (kt < ntk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * kt + tile_row(r, half);
+          const uint32_t k = order_key(s[u][r]);
+          if (j < lim && (k > kst || (k == kst && j <= jst))) mrow[j] = 1;
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- row maximum (always kept), weights, Z
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kSoftTiles; ++u) {
+    const int kt = wid + kSoftWaves * u;
+    if (kt < ntk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = 32 * kt + tile_row(r, half);
+        if (j < lim) mx = fmaxf(mx, s[u][r]);
+      }
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (half == 0) red[wid][ql] = mx;
+  __syncthreads();
+  const float rmax = fmaxf(fmaxf(red[0][ql], red[1][ql]), fmaxf(red[2][ql], red[3][ql]));
+  const float c2 = a.scale * 1.4426950408889634f;
+  const float off2 = rvalid ? rmax * c2 : 0.0f;
+  float z = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kSoftTiles; ++u) {
+    const int kt = wid + kSoftWaves * u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * kt + tile_row(r, half);
+      const float x = s[u][r];
+      const uint32_t k = order_key(x);
+      const bool keep = kt < ntk && j < lim && (k > kst || (k == kst && j <= jst));
+      const float p = keep ? exp2f(fmaf(x, c2, -off2)) : 0.0f;
+      s[u][r] = p;
+      z += p;
+    }
+  }
+  z += __shfl_xor(z, 32);
+  __syncthreads();  // every wave has read red[][] (the maxima)
+  if (half == 0) red[wid][ql] = z;
+  __syncthreads();
+  if (tid < 32) {
+    const float Z = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    rinvz[tid] = Z > 0.0f ? 1.0f / Z : 0.0f;
+  }
+
+  // ---- out = P V / Z, one 32-feature tile at a time, the waves' partials summed in LDS
+  float* part = reinterpret_cast<float*>(hist);  // [4 waves][32 rows][32 features]
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft) {
+    const int feat = 32 * ft + ql;
+    const bool fvalid = feat < d;
+    v16f o = {};
+#pragma unroll
+    for (int u = 0; u < kSoftTiles; ++u) {
+      const int kt = wid + kSoftWaves * u;
+      if (kt < ntk) {
+        float vv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * kt + tile_row(r, half);
+          vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the previous tile's partials are consumed (and rinvz is written)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[r];
+    __syncthreads();
+    for (int e = tid; e < 1024; e += kSoftThreads) {
+      const int row = e >> 5, f = e & 31;
+      const int i = q0 + row, fe = 32 * ft + f;
+      if (i < n && fe < d) {
+        const float val = (part[e] + part[1024 + e]) + (part[2048 + e] + part[3072 + e]);
+        a.out[(bh * n + i) * d + fe] = val * rinvz[row];
+      }
+    }
+  }
+}
+
+template <int DP, bool MASK>
+had_status launch_soft_attn(const SoftArgs& a, had_dtype vdt, hipStream_t st) {
+  const int nqt = (a.n + 31) / 32;
+  const dim3 grid(static_cast<unsigned>(a.bh_count * nqt));
+  if (MASK || vdt == HAD_F32)
+    hipLaunchKernelGGL((soft_attn_kernel<DP, true, MASK>), grid, dim3(kSoftThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((soft_attn_kernel<DP, false, MASK>), grid, dim3(kSoftThreads), 0, st, a);
+  return check_launch("soft_attn_kernel");
+}
+
+template <bool MASK>
+had_status launch_soft_attn_dp(const SoftArgs& a, int dp, had_dtype vdt, hipStream_t st) {
+  if (dp == 32) return launch_soft_attn<32, MASK>(a, vdt, st);
+  if (dp == 64) return launch_soft_attn<64, MASK>(a, vdt, st);
+  return launch_soft_attn<128, MASK>(a, vdt, st);
+}
+
+had_status check_soft(const float* q, const float* k, const had_shape& s, int64_t topn, float c,
+                      int causal, const float* sigma_q, const float* sigma_k, void* workspace,
+                      size_t workspace_bytes, const char* fn) {
+  had_status st = check_shape(s);
+  if (st != HAD_OK) return st;
+  if (s.dim > 128) return failf(HAD_ERR_UNSUPPORTED, "%s: dim above 128", fn);
+  if (s.seq > HAD_SOFT_MAX_SEQ) return failf(HAD_ERR_UNSUPPORTED, "%s: seq above HAD_SOFT_MAX_SEQ (1024)", fn);
+  if (q == nullptr || k == nullptr) return failf(HAD_ERR_INVALID_ARG, "%s: null q or k", fn);
+  if (!aligned(q, 4) || !aligned(k, 4)) return failf(HAD_ERR_INVALID_ARG, "%s: q and k must be 4-byte aligned", fn);
+  if ((sigma_q != nullptr && !aligned(sigma_q, 4)) || (sigma_k != nullptr && !aligned(sigma_k, 4)))
+    return failf(HAD_ERR_INVALID_ARG, "%s: sigma pointers must be 4-byte aligned", fn);
+  if (topn < 1) return failf(HAD_ERR_INVALID_ARG, "%s: topn must be >= 1", fn);
+  if (!std::isfinite(c) || !(c > 0.0f)) return failf(HAD_ERR_INVALID_ARG, "%s: c must be finite and > 0", fn);
+  if (causal != 0 && causal != 1) return failf(HAD_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  if (workspace == nullptr || !aligned(workspace, 256))
+    return failf(HAD_ERR_INVALID_ARG, "%s: workspace must be non-null and 256-byte aligned", fn);
+  if (workspace_bytes < had_soft_workspace_bytes(s))
+    return failf(HAD_ERR_INVALID_ARG, "%s: workspace smaller than had_soft_workspace_bytes()", fn);
+  return HAD_OK;
+}
+
+// Launch 1 into the workspace; fills the soft-row pointers of a.
+had_status soft_transform(const float* q, const float* k, const had_shape& s, float c, const float* sigma_q,
+                          const float* sigma_k, void* workspace, SoftArgs& a, hipStream_t st) {
+  const int dp = soft_dp(s.dim);
+  const int64_t rows = s.batch * s.heads * s.seq;
+  float* qs = static_cast<float*>(workspace);
+  float* ks = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                       align256(static_cast<size_t>(rows) * dp * sizeof(float)));
+  SoftTransformArgs t{};
+  t.x[0] = q;
+  t.x[1] = k;
+  t.xs[0] = qs;
+  t.xs[1] = ks;
+  t.sigma[0] = sigma_q;
+  t.sigma[1] = sigma_k;
+  t.rows = rows;
+  t.d = static_cast<int>(s.dim);
+  t.dp = dp;
+  t.c = c;
+  const int64_t blocks = (rows + kTfRows - 1) / kTfRows;
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(blocks, 4096)), 2);
+  hipLaunchKernelGGL(soft_transform_kernel, grid, dim3(kTfThreads), 0, st, t);
+  had_status r = check_launch("soft_transform_kernel");
+  if (r != HAD_OK) return r;
+  a.qs = qs;
+  a.ks = ks;
+  a.n = static_cast<int>(s.seq);
+  a.d = static_cast<int>(s.dim);
+  return HAD_OK;
+}
+
+}  // namespace
+}  // namespace had
+
+using namespace had;
+
+extern "C" size_t had_soft_workspace_bytes(had_shape s) {
+  if (check_shape(s) != HAD_OK || s.dim > 128 || s.seq > HAD_SOFT_MAX_SEQ) return 0;
+  const size_t rows = static_cast<size_t>(s.batch * s.heads * s.seq);
+  return 2 * align256(rows * soft_dp(s.dim) * sizeof(float));
+}
+
+extern "C" had_status had_soft_forward(const float* q, const float* k, const void* v, had_dtype v_dtype,
+                                       had_shape s, int64_t topn, float scale, float c, int causal,
+                                       const float* sigma_q, const float* sigma_k, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  had_status st = check_soft(q, k, s, topn, c, causal, sigma_q, sigma_k, workspace, workspace_bytes,
+                             "had_soft_forward");
+  if (st != HAD_OK) return st;
+  if (v == nullptr || out == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_soft_forward: null v or out");
+  if (!aligned(v, 4) || !aligned(out, 4))
+    return fail(HAD_ERR_INVALID_ARG, "had_soft_forward: v and out must be 4-byte aligned");
+  const int vdt = enum_bits(v_dtype);
+  if (!valid_dtype(vdt)) return fail(HAD_ERR_INVALID_ARG, "had_soft_forward: unknown v_dtype");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(HAD_ERR_INVALID_ARG, "had_soft_forward: scale must be finite and > 0");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  SoftArgs a{};
+  if ((st = soft_transform(q, k, s, c, sigma_q, sigma_k, workspace, a, hs)) != HAD_OK) return st;
+  a.v = v;
+  a.out = out;
+  a.bh_begin = 0;
+  a.bh_count = s.batch * s.heads;
+  a.topn = static_cast<int>(topn > s.seq ? s.seq : topn);
+  a.scale = scale;
+  a.causal = causal;
+  return launch_soft_attn_dp<false>(a, soft_dp(s.dim), static_cast<had_dtype>(vdt), hs);
+}
+
+extern "C" had_status had_soft_select(const float* q, const float* k, had_shape s, int64_t topn, float c,
+                                      int causal, const float* sigma_q, const float* sigma_k,
+                                      int64_t bh_begin, int64_t bh_count, uint8_t* keep, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  clear_error();
+  had_status st = check_soft(q, k, s, topn, c, causal, sigma_q, sigma_k, workspace, workspace_bytes,
+                             "had_soft_select");
+  if (st != HAD_OK) return st;
+  if (keep == nullptr) return fail(HAD_ERR_INVALID_ARG, "had_soft_select: null keep");
+  const int64_t bht = s.batch * s.heads;
+  if (bh_begin < 0 || bh_count < 1 || bh_begin + bh_count > bht)
+    return fail(HAD_ERR_INVALID_ARG, "had_soft_select: slice range outside [0, B*H)");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(keep, 0, static_cast<size_t>(bh_count) * s.seq * s.seq, hs) != hipSuccess)
+    return fail(HAD_ERR_HIP, "had_soft_select: clearing keep failed");
+  SoftArgs a{};
+  if ((st = soft_transform(q, k, s, c, sigma_q, sigma_k, workspace, a, hs)) != HAD_OK) return st;
+  a.keep = keep;
+  a.bh_begin = bh_begin;
+  a.bh_count = bh_count;
+  a.topn = static_cast<int>(topn > s.seq ? s.seq : topn);
+  a.scale = 1.0f;
+  a.causal = causal;
+  return launch_soft_attn_dp<true>(a, soft_dp(s.dim), HAD_F32, hs);
+}

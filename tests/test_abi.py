@@ -282,3 +282,46 @@ def test_backward_rejects_bad_arguments(lib):
     assert f(shape=Shape(2, 3, 100, 129)) == UNSUPPORTED
     assert f(shape=Shape(2, 3, 70000, 64)) == UNSUPPORTED
     assert lib.had_last_error() != b""
+
+
+def test_soft_forward_and_select_reject_bad_arguments(lib):
+    s = Shape(2, 3, 100, 64)
+    wsb = lib.had_soft_workspace_bytes(s)
+    assert wsb >= 2 * 2 * 3 * 100 * 64 * 4
+    assert lib.had_soft_workspace_bytes(Shape(2, 3, 100, 129)) == 0
+    assert lib.had_soft_workspace_bytes(Shape(2, 3, 1025, 64)) == 0
+    assert lib.had_soft_workspace_bytes(Shape(0, 3, 100, 64)) == 0
+
+    def f(q=A16, k=A16B, v=A16C, vdt=1, shape=s, topn=8, scale=0.125, c=0.5, causal=0, sq=None, sk=None,
+          out=0x40000, ws=0x100000, n=wsb):
+        return lib.had_soft_forward(q, k, v, vdt, shape, topn, scale, c, causal, sq, sk, out, ws, n, None)
+
+    assert f(q=None) == INVALID
+    assert f(out=None) == INVALID
+    assert f(k=0x20002) == INVALID
+    assert f(sq=0x90002) == INVALID
+    assert f(vdt=3) == INVALID
+    assert f(topn=0) == INVALID
+    assert f(scale=0.0) == INVALID
+    assert f(c=0.0) == INVALID
+    assert f(c=float("nan")) == INVALID
+    assert f(c=float("inf")) == INVALID
+    assert f(causal=2) == INVALID
+    assert f(ws=None) == INVALID
+    assert f(ws=0x100010) == INVALID
+    assert f(n=wsb - 1) == INVALID
+    assert f(shape=Shape(2, 3, 100, 129)) == UNSUPPORTED
+    assert f(shape=Shape(2, 3, 1025, 64)) == UNSUPPORTED
+    assert f(shape=Shape(2, 0, 100, 64)) == INVALID
+    assert lib.had_last_error() != b""
+
+    def g(q=A16, k=A16B, shape=s, topn=8, c=0.5, causal=0, b0=0, bc=6, keep=0x40000, ws=0x100000, n=wsb):
+        return lib.had_soft_select(q, k, shape, topn, c, causal, None, None, b0, bc, keep, ws, n, None)
+
+    assert g(keep=None) == INVALID
+    assert g(b0=-1) == INVALID
+    assert g(bc=0) == INVALID
+    assert g(b0=3, bc=4) == INVALID
+    assert g(c=-1.0) == INVALID
+    assert g(n=0) == INVALID
+    assert g(shape=Shape(2, 3, 2000, 64)) == UNSUPPORTED
