@@ -171,6 +171,8 @@ def _oracle_slice(i):
         oracle.decode(q, k, v, topn, scale, q_pos0=extra, causal=causal)
     elif kind == "backward":
         oracle.backward(q, k, v, extra, topn, scale, causal)
+    elif kind == "soft":
+        oracle.soft_forward(q, k, v, topn, scale, extra, causal)
     else:
         oracle.sigma(q)
         oracle.forward(q, k, v, topn, scale, causal=causal)
@@ -412,6 +414,122 @@ def bench_backward(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def soft_model(w):
+    """Work of one had_soft_forward call on workload w.  Algorithmic: a real
+    dot product of d features per visible pair (2d flops) and the weighted V
+    row per kept pair (2d flops).  Dense-masked: the fp32 matrix-core products
+    the attention launch issues, every 32 x 32 (row, key) tile with a visible
+    pair in both the logit and the V product (4d flops per pair of a tile).
+    HBM: Q and K read and their soft rows written and read back, V read, out
+    written."""
+    m = work_model(w)
+    d, n = w.dim, w.seq
+    dp = 32 if d <= 32 else (64 if d <= 64 else 128)
+    tiles = 0
+    for t in range((n + 31) // 32):
+        tiles += (t + 1) if w.causal else (n + 31) // 32
+    bh = w.batch * w.heads
+    return {"kept": m["kept"], "visible_pairs": m["visible_pairs"],
+            "flops": 2.0 * d * (m["visible_pairs"] + m["kept"]),
+            "mfma_fp32_flops": 2.0 * 2 * dp * bh * tiles * 1024,
+            "hbm_bytes": bh * n * (2 * d * 4 + 2 * 2 * dp * 4 + d * (2 if w.v_dtype == "bf16" else 4) + d * 4)}
+
+
+def soft_cpu_baseline(w, inp, c, budget_s, single_budget_s=None):
+    def tasks():
+        for bh in range(w.batch * w.heads):
+            b, h = divmod(bh, w.heads)
+            yield ("soft", inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.topn, w.scale, w.causal, c)
+
+    return _baseline(w.batch * w.heads, f"all {w.seq} rows each (sigma of the slice, tanh, float64 "
+                     "logits, stable-sort top-N, softmax, AV)", tasks, budget_s, single_budget_s)
+
+
+def bench_soft(args, w):
+    """One step = had_soft_forward on workload w: the scaled-tanh soft forward
+    (transform launch, attention launch) with Q, K, V and sigma resident in
+    HBM."""
+    import torch
+    import sparse_attention_had_amd as had
+    from had_workloads import workload_inputs
+
+    if w.seq > 1024:
+        print(f"bench.py --soft: {w.name} has n = {w.seq}; the soft forward holds at most 1024 keys "
+              "per work-group", file=sys.stderr)
+        sys.exit(2)
+    c = args.soft_c
+    inp = workload_inputs(w)
+    cpu = None if args.no_cpu_baseline else soft_cpu_baseline(w, inp, c, args.cpu_budget)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"]).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"])
+    v = (v.to(torch.bfloat16) if w.v_dtype == "bf16" else v).to(dev)
+    _, sq = had.pack(q)
+    _, sk = had.pack(k)
+    out = torch.empty((w.batch, w.heads, w.seq, w.dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(had.load_library().had_soft_workspace_bytes(had.Shape(*q.shape)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        had.soft_forward(q, k, v, w.topn, w.scale, c, w.causal, sigma_q=sq, sigma_k=sk, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    settled = settle(step, args.settle_s)
+    steps = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    durs = timed_launches(step, stream, 50)
+    call_s = float(np.median(durs))
+    m = soft_model(w)
+    achieved = m["flops"] / call_s
+    rec = {
+        "metric": f"query rows/sec of the HAD scaled-tanh soft forward at n={w.seq},N={w.topn},c={c}; "
+                  "% of fp32 matrix-core roofline",
+        "value": w.rows / (ms_step / 1e3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "settle_steps": settled,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq": w.seq,
+                   "dim": w.dim, "topn": w.topn, "causal": w.causal, "v_dtype": w.v_dtype,
+                   "scale": w.scale, "c": c,
+                   "step": "had_soft_forward: tanh transform of Q and K, attention (logits, exact top-N, "
+                           "softmax, AV); 2 launches",
+                   "arithmetic": "float32 tanh, fp32 matrix-core logits and V products, exact radix top-N "
+                                 "of the float32 logits, float32 weights and sums"},
+        "soft_us": call_s * 1e6,
+        "soft_timing": f"median over {len(durs)} groups of 5 back-to-back calls",
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": FP32_MFMA_PEAK / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK, "traffic": None,
+                     "kernel": "had_soft_forward (soft_transform_kernel, soft_attn_kernel)",
+                     "frac_kind": "algorithmic flops (2d per visible pair, 2d per kept pair) at the dense "
+                                  "fp32 matrix-core peak, over the whole call",
+                     "dense_masked_frac": m["mfma_fp32_flops"] / call_s / FP32_MFMA_PEAK,
+                     "hbm_frac": m["hbm_bytes"] / call_s / HBM_PEAK,
+                     "work_per_launch": {k2: float(v2) for k2, v2 in m.items()}},
+    }
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    print(json.dumps(rec), flush=True)
+
+
 def bench_vgather(args, w):
     """The attention of workload w computed in the V-gather form: had_decode of
     the whole sequence (n_q = n_k = n, q_pos0 = 0), which compacts each row's
@@ -629,6 +747,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time had_backward (the straight-through backward) on the workload "
                          "instead of the forward step")
+    ap.add_argument("--soft", action="store_true",
+                    help="time had_soft_forward (the scaled-tanh soft forward) on the workload")
+    ap.add_argument("--soft-c", type=float, default=0.5, help="the tanh scale c of --soft")
     ap.add_argument("--v-gather", action="store_true",
                     help="time the workload's attention in the V-gather form (had_decode of the "
                          "whole sequence) beside had_attention")
@@ -654,6 +775,8 @@ def main():
     w = WORKLOADS[name]
     if args.backward:
         return bench_backward(args, w)
+    if args.soft:
+        return bench_soft(args, w)
     if args.v_gather:
         return bench_vgather(args, w)
     inp = workload_inputs(w)

@@ -14,12 +14,12 @@
 // GPU design (gfx950), two launches:
 //  1. transform: Q and K -> B_c(Q), B_c(K) in float32, rows padded with zeros
 //     to DP = 32, 64 or 128 features (one HBM pass each way).
-//  2. attention: a work-group is 4 waves and 32 query rows of one (batch,
+//  2. attention: a work-group is 8 waves and 32 query rows of one (batch,
 //     head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
-//     tiles w, w + 4, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
+//     tiles w, w + 8, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
 //     A = the key rows, B = the query rows; lane L then holds query row
 //     L % 32 and 16 keys of each tile) and keeps them in registers: at most
-//     8 tiles of 16 values per lane.  The kept set is an exact radix select
+//     4 tiles of 16 values per lane.  The kept set is an exact radix select
 //     over the composite (order-preserving bits of the float32 logit, then
 //     the key index inverted), so exactly N_i keys are kept with no separate
 //     tie rule: four levels of 8-bit digits of the logit's key and two of
@@ -28,7 +28,7 @@
 //     the digit holding the N_i-th largest.  Then the row maximum, the
 //     weights exp(scale * (s - max)) of the kept keys, their sum Z, and the
 //     weighted V rows on the fp32 matrix cores (A = the weights straight from
-//     the logit registers, B = V rows), reduced over the four waves in a
+//     the logit registers, B = V rows), reduced over the eight waves in a
 //     fixed order and divided by Z.
 // No floating-point atomics: results are identical run to run.
 #include <algorithm>
@@ -39,11 +39,14 @@
 namespace had {
 namespace {
 
-constexpr int kSoftWaves = 4;
+constexpr int kSoftWaves = 8;
 constexpr int kSoftThreads = 64 * kSoftWaves;
 constexpr int kSoftMaxSeq = 1024;                            // keys a work-group keeps in registers
 constexpr int kSoftTiles = kSoftMaxSeq / 32 / kSoftWaves;    // key tiles per wave
 constexpr int kBins = 256;                                   // histogram bins per row and level
+// LDS histogram row stride (words): odd, so the 32 rows' copies of one bin sit on 32 banks.
+constexpr int kHistStride = 257;
+constexpr int kScanLanes = 64 * kSoftWaves / 32;             // lanes per row in the scans
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -55,6 +58,11 @@ __device__ inline int tile_row(int i, int half) { return 8 * (i >> 2) + 4 * half
 __device__ inline uint32_t order_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The float whose order key is k (k != 0).
+__device__ inline float key_value(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 inline int soft_dp(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
@@ -111,51 +119,51 @@ __device__ inline float load_v(const void* v, int64_t off) {
   return __builtin_bit_cast(float, b << 16);
 }
 
-// One level of the radix select: a per-row histogram of the digit of the
-// elements that still match the prefix found so far, then the scan that finds
-// the digit holding the row's remaining quota.  Levels 0-3 take the four bytes
-// of the logit's order key (highest first), levels 4 and 5 the two 5-bit
-// digits of the key index, inverted so that lower indices come first among
-// equal logits.  All threads of the work-group call it.
+// One level of the radix select over the composite (order key of the logit,
+// inverted key index): a per-row histogram of the digit of the elements that
+// still match the prefix found so far, then the scan that finds the digit
+// holding the row's remaining quota.  Levels 0-3 take the four bytes of the
+// order key (highest first), levels 4 and 5 the two 5-bit digits of the key
+// index, inverted so that lower indices come first among equal logits.  The
+// key registers hold order keys, 0 for keys the row does not see: a visible key's
+// top byte is never 0 (|s| <= d), so those sit below every visible one.  A row
+// is resolved once its remaining quota takes the whole chosen bin: its
+// threshold becomes the lowest composite of that bin.  All threads of the
+// work-group call it; it returns (uniformly) whether every row is resolved.
 template <int L>
-__device__ __forceinline__ void select_level(const v16f (&s)[kSoftTiles], uint32_t* hist, uint32_t* st_key,
-                                             int* st_idx, int* st_need, int wid, int lane, int ntk, int lim) {
+__device__ __forceinline__ bool select_level(const uint32_t (&key)[kSoftTiles][16], uint32_t* hist, uint32_t* st_key,
+                                             int* st_idx, int* st_need, int* st_done, int wid, int lane,
+                                             int ntk) {
   const int half = lane >> 5, ql = lane & 31;
   const uint32_t kpre = st_key[ql];
   const int ipre = st_idx[ql];
-  uint32_t* hrow = hist + ql * kBins;
+  uint32_t* hrow = hist + ql * kHistStride;
 #pragma unroll
   for (int u = 0; u < kSoftTiles; ++u) {
     const int kt = wid + kSoftWaves * u;
     if (kt < ntk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = 32 * kt + tile_row(r, half);
-        const uint32_t k = order_key(s[u][r]);
-        bool m = j < lim;
-        uint32_t dig;
+        const uint32_t k = key[u][r];
         if constexpr (L == 0) {
-          dig = k >> 24;
+          atomicAdd(hrow + (k >> 24), 1u);
         } else if constexpr (L < 4) {
-          m = m && (k >> (32 - 8 * L)) == kpre;
-          dig = (k >> (24 - 8 * L)) & 255u;
+          if ((k >> (32 - 8 * L)) == kpre) atomicAdd(hrow + ((k >> (24 - 8 * L)) & 255u), 1u);
         } else if constexpr (L == 4) {
-          m = m && k == kpre;
-          dig = 31u - static_cast<uint32_t>(j >> 5);
+          if (k == kpre) atomicAdd(hrow + (31 - kt), 1u);  // key j = 32 kt + ...: j >> 5 == kt
         } else {
-          m = m && k == kpre && (j >> 5) == ipre;
-          dig = 31u - static_cast<uint32_t>(j & 31);
+          if (k == kpre && kt == ipre) atomicAdd(hrow + (31 - tile_row(r, half)), 1u);
         }
-        if (m) atomicAdd(hrow + dig, 1u);
       }
     }
   }
   __syncthreads();
   {
-    // wave w scans rows 8w .. 8w + 7, eight lanes per row
-    constexpr int kPer = (L < 4 ? kBins : 32) / 8;
-    const int srow = 8 * wid + (lane >> 3), g = lane & 7;
-    uint32_t* hb = hist + srow * kBins + kPer * g;
+    // wave w scans rows 4w .. 4w + 3, sixteen lanes per row; lane g holds bins
+    // kPer * g .. kPer * g + kPer - 1
+    constexpr int kPer = (L < 4 ? kBins : 32) / kScanLanes;
+    const int srow = (32 / kSoftWaves) * wid + lane / kScanLanes, g = lane % kScanLanes;
+    uint32_t* hb = hist + srow * kHistStride + kPer * g;
     uint32_t c[kPer];
     uint32_t sum = 0;
 #pragma unroll
@@ -165,16 +173,16 @@ __device__ __forceinline__ void select_level(const v16f (&s)[kSoftTiles], uint32
     }
 #pragma unroll
     for (int b = 0; b < kPer; ++b) hb[b] = 0u;
-    uint32_t S = sum;  // bins of lanes g .. 7 of the row, i.e. digits >= kPer * g
+    uint32_t S = sum;  // bins of lanes g .. kScanLanes - 1 of the row, i.e. digits >= kPer * g
 #pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      const uint32_t t = __shfl_down(S, off, 8);
-      if (g + off < 8) S += t;
+    for (int off = 1; off < kScanLanes; off <<= 1) {
+      const uint32_t t = __shfl_down(S, off, kScanLanes);
+      if (g + off < kScanLanes) S += t;
     }
     const int nd = st_need[srow];
     const uint32_t above = S - sum;
     if (nd > 0 && above < static_cast<uint32_t>(nd) && static_cast<uint32_t>(nd) <= S) {
-      uint32_t acc = above;
+      uint32_t acc = above, ct = 0;
       int tb = 0;
       bool found = false;
 #pragma unroll
@@ -182,33 +190,44 @@ __device__ __forceinline__ void select_level(const v16f (&s)[kSoftTiles], uint32
         const bool hit = !found && acc + c[b] >= static_cast<uint32_t>(nd);
         if (hit) {
           tb = b;
+          ct = c[b];
           found = true;
         }
         if (!found) acc += c[b];
       }
       const uint32_t digit = static_cast<uint32_t>(kPer * g + tb);
-      if constexpr (L < 4)
-        st_key[srow] = (L == 0 ? 0u : (st_key[srow] << 8)) | digit;
-      else if constexpr (L == 4)
-        st_idx[srow] = 31 - static_cast<int>(digit);
-      else
+      const int rem = nd - static_cast<int>(acc);
+      const bool whole = static_cast<uint32_t>(rem) == ct || L == 5;
+      if constexpr (L < 4) {
+        const uint32_t key = (L == 0 ? 0u : (st_key[srow] << 8)) | digit;
+        st_key[srow] = whole ? key << (24 - 8 * L) : key;
+        if (whole) st_idx[srow] = 0x7FFFFFFF;
+      } else if constexpr (L == 4) {
+        st_idx[srow] = whole ? 32 * (31 - static_cast<int>(digit)) + 31 : 31 - static_cast<int>(digit);
+      } else {
         st_idx[srow] = 32 * st_idx[srow] + (31 - static_cast<int>(digit));
-      st_need[srow] = nd - static_cast<int>(acc);
+      }
+      st_need[srow] = whole ? 0 : rem;
+      if (whole) atomicAdd(st_done, 1);
     }
   }
   __syncthreads();
+  return *st_done == 32;
 }
 
 template <int DP, bool VF32, bool MASK>
-__global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
+__global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4))) void soft_attn_kernel(SoftArgs a) {
   constexpr int HD = DP / 2;  // features of lane half h: h * HD .. h * HD + HD - 1
   constexpr int NFT = DP / 32;
-  __shared__ uint32_t hist[32 * kBins];  // per row, one level at a time; then the output partials
+  __shared__ uint32_t hist[32 * kHistStride];  // per row, one level at a time; then the output partials
   __shared__ uint32_t st_key[32];        // logit key prefix, then the threshold key K*
   __shared__ int st_idx[32];             // index prefix, then the last kept index at K*
   __shared__ int st_need[32];            // kept keys still to place at the current level
+  __shared__ int st_done;                // rows whose threshold is found
   __shared__ float red[kSoftWaves][32];
+  __shared__ uint32_t redk[kSoftWaves][32];
   __shared__ float rinvz[32];
+  __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -223,28 +242,31 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
   const int kend = a.causal ? min(n, q0 + 32) : n;
   const int ntk = (kend + 31) / 32;  // key tiles some row of the block sees
 
-  for (int e = tid; e < 32 * kBins; e += kSoftThreads) hist[e] = 0u;
+  for (int e = tid; e < 32 * kHistStride; e += kSoftThreads) hist[e] = 0u;
+  if (tid == 0) st_done = 0;
+  // the block's 32 soft query rows (the B operand of every logit tile)
+  for (int e = tid; e < 8 * DP; e += kSoftThreads) {
+    const int row = e / (DP / 4), c4 = e % (DP / 4);
+    const int i = min(q0 + row, n - 1);
+    *reinterpret_cast<float4*>(qlds + row * (DP + 4) + 4 * c4) =
+        *reinterpret_cast<const float4*>(a.qs + (bh * n + i) * DP + 4 * c4);
+  }
+  __syncthreads();
   if (tid < 32) {
+    // a row that keeps every key it sees (or a row past n) is resolved from
+    // the start: threshold key 1 is below every visible key and above 0
     const int r = q0 + tid;
     const int vis = r >= n ? 0 : (a.causal ? r + 1 : n);
-    st_need[tid] = min(a.topn, vis);
-    st_key[tid] = 0u;
-    st_idx[tid] = 0;
+    const int need = min(a.topn, vis);
+    const bool all = need == vis;
+    st_need[tid] = all ? 0 : need;
+    st_key[tid] = all ? 1u : 0u;
+    st_idx[tid] = all ? 0x7FFFFFFF : 0;
+    if (all) atomicAdd(&st_done, 1);
   }
 
-  // ---- logits: s[u] = tile (key tile wid + 4u) x (the block's 32 rows)
-  float qv[HD];
-  {
-    const float* qr = a.qs + (bh * n + (rvalid ? i_row : n - 1)) * DP + HD * half;
-#pragma unroll
-    for (int t = 0; t < HD; t += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(qr + t);
-      qv[t] = x.x;
-      qv[t + 1] = x.y;
-      qv[t + 2] = x.z;
-      qv[t + 3] = x.w;
-    }
-  }
+  // ---- logits: s[u] = tile (key tile wid + 8u) x (the block's 32 rows)
+  const float* qrow = qlds + ql * (DP + 4) + HD * half;  // B operand: the row's features t + HD * half
   v16f s[kSoftTiles];
 #pragma unroll
   for (int u = 0; u < kSoftTiles; ++u) {
@@ -256,23 +278,36 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
 #pragma unroll
       for (int t = 0; t < HD; t += 4) {
         const float4 x = *reinterpret_cast<const float4*>(kr + t);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, qv[t], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, qv[t + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, qv[t + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, qv[t + 3], acc, 0, 0, 0);
+        const float4 y = *reinterpret_cast<const float4*>(qrow + t);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
       }
     }
     s[u] = acc;
+    __builtin_amdgcn_sched_barrier(0);  // one tile's key rows in registers at a time
   }
   __syncthreads();
 
   // ---- exact top-N: radix select over (logit key, inverted index)
-  select_level<0>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
-  select_level<1>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
-  select_level<2>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
-  select_level<3>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
-  select_level<4>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
-  select_level<5>(s, hist, st_key, st_idx, st_need, wid, lane, ntk, lim);
+  // order keys of the logits, 0 for the keys this row does not see
+  uint32_t key[kSoftTiles][16];
+#pragma unroll
+  for (int u = 0; u < kSoftTiles; ++u) {
+    const int kt = wid + kSoftWaves * u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * kt + tile_row(r, half);
+      key[u][r] = (kt < ntk && j < lim) ? order_key(s[u][r]) : 0u;
+    }
+  }
+  if (!select_level<0>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<1>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<2>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<3>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<4>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk))
+    select_level<5>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk);
 
   // key j of this row is kept iff visible and (key > K*, or key == K* and j <= j*)
   const uint32_t kst = st_key[ql];
@@ -287,31 +322,27 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = 32 * kt + tile_row(r, half);
-          const uint32_t k = order_key(s[u][r]);
-          if (j < lim && (k > kst || (k == kst && j <= jst))) mrow[j] = 1;
+          const uint32_t k = key[u][r];
+          if (k > kst || (k == kst && j <= jst)) mrow[j] = 1;
         }
       }
     }
     return;
   }
 
-  // ---- row maximum (always kept), weights, Z
-  float mx = -INFINITY;
+  // ---- row maximum (the largest key, always kept), weights, Z
+  uint32_t mk = 0;
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u) {
-    const int kt = wid + kSoftWaves * u;
-    if (kt < ntk) {
+  for (int u = 0; u < kSoftTiles; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = 32 * kt + tile_row(r, half);
-        if (j < lim) mx = fmaxf(mx, s[u][r]);
-      }
-    }
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (half == 0) red[wid][ql] = mx;
+    for (int r = 0; r < 16; ++r) mk = max(mk, key[u][r]);
+  mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), 32)));
+  if (half == 0) redk[wid][ql] = mk;
   __syncthreads();
-  const float rmax = fmaxf(fmaxf(red[0][ql], red[1][ql]), fmaxf(red[2][ql], red[3][ql]));
+  uint32_t rk = redk[0][ql];
+#pragma unroll
+  for (int w = 1; w < kSoftWaves; ++w) rk = max(rk, redk[w][ql]);
+  const float rmax = key_value(rk);
   const float c2 = a.scale * 1.4426950408889634f;
   const float off2 = rvalid ? rmax * c2 : 0.0f;
   float z = 0.0f;
@@ -321,25 +352,26 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 32 * kt + tile_row(r, half);
-      const float x = s[u][r];
-      const uint32_t k = order_key(x);
-      const bool keep = kt < ntk && j < lim && (k > kst || (k == kst && j <= jst));
-      const float p = keep ? exp2f(fmaf(x, c2, -off2)) : 0.0f;
+      const uint32_t k = key[u][r];
+      const bool keep = k > kst || (k == kst && j <= jst);
+      const float p = keep ? exp2f(fmaf(key_value(k), c2, -off2)) : 0.0f;
       s[u][r] = p;
       z += p;
     }
   }
   z += __shfl_xor(z, 32);
-  __syncthreads();  // every wave has read red[][] (the maxima)
   if (half == 0) red[wid][ql] = z;
   __syncthreads();
   if (tid < 32) {
-    const float Z = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    float Z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSoftWaves; ++w) Z += red[w][tid];
     rinvz[tid] = Z > 0.0f ? 1.0f / Z : 0.0f;
   }
 
   // ---- out = P V / Z, one 32-feature tile at a time, the waves' partials summed in LDS
-  float* part = reinterpret_cast<float*>(hist);  // [4 waves][32 rows][32 features]
+  float* part = reinterpret_cast<float*>(hist);  // [waves][32 rows][32 features]
+  static_assert(kSoftWaves * 1024 <= 32 * kHistStride, "partials fit the histogram area");
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft) {
     const int feat = 32 * ft + ql;
@@ -358,6 +390,8 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
       }
+      // keep the next tile's V loads after this tile's products (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // the previous tile's partials are consumed (and rinvz is written)
 #pragma unroll
@@ -367,7 +401,9 @@ __global__ __launch_bounds__(kSoftThreads) void soft_attn_kernel(SoftArgs a) {
       const int row = e >> 5, f = e & 31;
       const int i = q0 + row, fe = 32 * ft + f;
       if (i < n && fe < d) {
-        const float val = (part[e] + part[1024 + e]) + (part[2048 + e] + part[3072 + e]);
+        float val = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSoftWaves; ++w) val += part[1024 * w + e];
         a.out[(bh * n + i) * d + fe] = val * rinvz[row];
       }
     }

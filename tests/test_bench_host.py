@@ -157,3 +157,16 @@ def test_backward_model_by_hand():
     c = bench.backward_model(types.SimpleNamespace(batch=1, heads=1, seq=64, dim=32, topn=8,
                                                     causal=True, v_dtype="bf16"))
     assert c["mfma_fp32_flops"] == 10 * 32 * 3 * 1024  # tiles (0,0), (1,0), (1,1)
+
+
+def test_soft_model_by_hand():
+    w = WORKLOADS["t5-base-n1024"]
+    m = bench.soft_model(w)
+    pairs, kept = 96 * 1024 * 1024, 96 * 1024 * 256
+    assert m["flops"] == 2 * 64 * (pairs + kept)
+    assert m["mfma_fp32_flops"] == 4 * 64 * pairs  # logits and V product over every tile
+    # Q and K read (4 B), their 64-feature soft rows written and read (2 x 4 B each), V bf16, out fp32
+    assert m["hbm_bytes"] == 96 * 1024 * (2 * 64 * 4 + 4 * 64 * 4 + 64 * 2 + 64 * 4)
+    c = bench.soft_model(types.SimpleNamespace(batch=1, heads=1, seq=64, dim=40, topn=8,
+                                                causal=True, v_dtype="f32"))
+    assert c["mfma_fp32_flops"] == 4 * 64 * 3 * 1024  # 40 features padded to 64; 3 visible tiles
