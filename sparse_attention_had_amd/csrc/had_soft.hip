@@ -99,6 +99,12 @@ __global__ __launch_bounds__(kTfThreads) void soft_transform_kernel(SoftTransfor
   }
 }
 
+// Zero fill of the keep mask (a kernel, so that a captured graph holds no memset node).
+__global__ __launch_bounds__(256) void soft_clear_kernel(uint8_t* p, int64_t bytes) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < bytes; i += stride) p[i] = 0;
+}
+
 // ---- 2. attention ----------------------------------------------------------
 struct SoftArgs {
   const float* qs;  // [BH, n, DP]
@@ -532,8 +538,10 @@ extern "C" had_status had_soft_select(const float* q, const float* k, had_shape 
   if (bh_begin < 0 || bh_count < 1 || bh_begin + bh_count > bht)
     return fail(HAD_ERR_INVALID_ARG, "had_soft_select: slice range outside [0, B*H)");
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (hipMemsetAsync(keep, 0, static_cast<size_t>(bh_count) * s.seq * s.seq, hs) != hipSuccess)
-    return fail(HAD_ERR_HIP, "had_soft_select: clearing keep failed");
+  const int64_t keep_bytes = bh_count * s.seq * s.seq;
+  hipLaunchKernelGGL(soft_clear_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((keep_bytes + 255) / 256, 4096))),
+                     dim3(256), 0, hs, keep, keep_bytes);
+  if ((st = check_launch("soft_clear_kernel")) != HAD_OK) return st;
   SoftArgs a{};
   if ((st = soft_transform(q, k, s, c, sigma_q, sigma_k, workspace, a, hs)) != HAD_OK) return st;
   a.keep = keep;
