@@ -116,7 +116,11 @@ struct SoftArgs {
   int n, d, topn;
   float scale;
   int causal;
+  int vlds;         // bf16 V, d % 16 == 0, 16-byte aligned: V operands through LDS
 };
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 template <bool VF32>
 __device__ inline float load_v(const void* v, int64_t off) {
@@ -234,6 +238,7 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   __shared__ uint32_t redk[kSoftWaves][32];
   __shared__ float rinvz[32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
+  __shared__ __attribute__((aligned(16))) uint16_t vst[(MASK || VF32) ? 8 : kSoftWaves * 1024];  // per wave: a bf16 V tile
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -387,14 +392,55 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
     for (int u = 0; u < kSoftTiles; ++u) {
       const int kt = wid + kSoftWaves * u;
       if (kt < ntk) {
-        float vv[16];
+        if (!VF32 && a.vlds) {
+          // stage the wave's 32 keys x 32 features of V (bf16) in LDS with 16-byte
+          // loads: lane L takes key 32 kt + L / 2, features 32 ft + 16 (L % 2) ..
+          const int key = min(32 * kt + (lane >> 1), n - 1);
+          const int f = 32 * ft + 16 * (lane & 1);
+          uint4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+          if (f < d) {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + f);
+            v0 = src[0];
+            v1 = src[1];
+          }
+          uint16_t* dst = vst + wid * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
+          *reinterpret_cast<uint4*>(dst) = v0;
+          *reinterpret_cast<uint4*>(dst + 8) = v1;
+          // one wave writes and reads its own tile: LDS keeps a wave's operations in
+          // order, so only the compiler must not move the reads above the writes
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
+          // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
+          // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
+          // S = 8 g + 4 (G / 2): register 4g + k of this lane is key 8 g + 4 half + k
+          // and feature 32 ft + L % 32, as the weight registers and the product need.
+          const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * kt + tile_row(r, half);
-          vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+          for (int g = 0; g < 4; ++g) {
+            const int row = 8 * g + 4 * (G >> 1) + kk;
+            const v4s r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s*)(vst + wid * 1024 + row * 32 + 16 * (G & 1) + 4 * qq));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float bv = __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(r4[k])) << 16);
+              o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][4 * g + k], bv, o, 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else {
+          float vv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * kt + tile_row(r, half);
+            vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
       }
       // keep the next tile's V loads after this tile's products (register pressure)
       __builtin_amdgcn_sched_barrier(0);
@@ -517,6 +563,7 @@ extern "C" had_status had_soft_forward(const float* q, const float* k, const voi
   if ((st = soft_transform(q, k, s, c, sigma_q, sigma_k, workspace, a, hs)) != HAD_OK) return st;
   a.v = v;
   a.out = out;
+  a.vlds = vdt == HAD_BF16 && s.dim % 16 == 0 && aligned(v, 16);
   a.bh_begin = 0;
   a.bh_count = s.batch * s.heads;
   a.topn = static_cast<int>(topn > s.seq ? s.seq : topn);

@@ -153,6 +153,9 @@ CASES = [
     ((1, 2, 1024, 64), 256, 0.5, False, "f32", 12),
     ((1, 1, 1024, 128), 200, 0.8, True, "bf16", 13),
     ((1, 2, 333, 64), 40, 30.0, False, "f32", 14),
+    ((1, 2, 77, 64), 9, 0.7, True, "bf16", 15),
+    ((1, 1, 100, 32), 12, 0.6, False, "bf16", 16),
+    ((2, 1, 150, 48), 30, 0.9, True, "bf16", 17),
 ]
 
 
