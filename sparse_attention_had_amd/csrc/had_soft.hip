@@ -121,6 +121,8 @@ struct SoftArgs {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool VF32>
 __device__ inline float load_v(const void* v, int64_t off) {
@@ -414,19 +416,42 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
           // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
           // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
           // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
-          // S = 8 g + 4 (G / 2): register 4g + k of this lane is key 8 g + 4 half + k
-          // and feature 32 ft + L % 32, as the weight registers and the product need.
+          // S = 8 g + 4 (G / 2): keys 8 g + 4 half + k at feature 32 ft + L % 32,
+          // the keys of this lane's weight registers 4g .. 4g + 3.
+          // v_mfma_f32_32x32x16_bf16 sums 16 k-slots, slots 8 half .. 8 half + 7
+          // from each lane: here the lane's registers 4 g0 .. 4 g0 + 7 (keys
+          // 8 (g0 + i / 4) + 4 half + i % 4) in both operands.  Each float32 weight
+          // is exactly hi + mid + lo, three bf16 values (the top 16 bits, those of
+          // the remainder, the rest), so three bf16 products give P V with exact
+          // partial products and float32 accumulation.
           const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int row = 8 * g + 4 * (G >> 1) + kk;
-            const v4s r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4s*)(vst + wid * 1024 + row * 32 + 16 * (G & 1) + 4 * qq));
+          for (int g0 = 0; g0 < 4; g0 += 2) {
+            const uint16_t* tb = vst + wid * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
+            const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
+            const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
+            const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+            uint32_t ph[8], pm[8], pl[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float bv = __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(r4[k])) << 16);
-              o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][4 * g + k], bv, o, 0, 0, 0);
+            for (int i = 0; i < 8; ++i) {
+              const float x = s[u][4 * g0 + i];
+              const uint32_t h = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
+              const float r1 = x - __builtin_bit_cast(float, h);
+              const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+              ph[i] = h;
+              pm[i] = m;
+              pl[i] = __builtin_bit_cast(uint32_t, r1 - __builtin_bit_cast(float, m));
             }
+            u32x4 ah, am, al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ah[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
+              am[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
+              al[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
+            }
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o, 0, 0, 0);
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
