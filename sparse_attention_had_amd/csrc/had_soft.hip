@@ -27,9 +27,13 @@
 //     elements still matching the prefix (ds_add_u32) and a scan that finds
 //     the digit holding the N_i-th largest.  Then the row maximum, the
 //     weights exp(scale * (s - max)) of the kept keys, their sum Z, and the
-//     weighted V rows on the fp32 matrix cores (A = the weights straight from
-//     the logit registers, B = V rows), reduced over the eight waves in a
-//     fixed order and divided by Z.
+//     weighted V rows on the matrix cores, reduced over the eight waves in a
+//     fixed order and divided by Z.  bf16 V (d a multiple of 16): each wave
+//     stages its V tile in LDS with 16-byte loads and reads the operand back
+//     transposed (ds_read_b64_tr_b16); each float32 weight is split exactly into
+//     three bf16 values for v_mfma_f32_32x32x16_bf16.  fp32 V: the weights
+//     straight from the logit registers and V rows from L2 on the fp32 matrix
+//     cores.
 // No floating-point atomics: results are identical run to run.
 #include <algorithm>
 #include <cmath>
