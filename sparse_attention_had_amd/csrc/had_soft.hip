@@ -14,8 +14,8 @@
 // GPU design (gfx950), two launches:
 //  1. transform: Q and K -> B_c(Q), B_c(K) in float32, rows padded with zeros
 //     to DP = 32, 64 or 128 features (one HBM pass each way).
-//  2. attention: a work-group is 8 waves and 32 query rows of one (batch,
-//     head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
+//  2. attention: a work-group is 8 waves (4 for n <= 256) and 32 query rows
+//     of one (batch, head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
 //     tiles w, w + 8, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
 //     A = the key rows, B = the query rows; lane L then holds query row
 //     L % 32 and 16 keys of each tile) and keeps them in registers: at most
@@ -43,14 +43,19 @@
 namespace had {
 namespace {
 
-constexpr int kSoftWaves = 8;
-constexpr int kSoftThreads = 64 * kSoftWaves;
+// A work-group holds 32 query rows and every key: 8 waves of 4 key tiles for
+// n <= 1024, or 4 waves of 2 key tiles for n <= 256 (no idle waves at short n).
+template <int NW>
+struct SoftCfg {
+  static constexpr int kWaves = NW;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kTiles = NW == 8 ? 4 : 2;        // key tiles per wave
+  static constexpr int kScanLanes = 64 * NW / 32;       // lanes per row in the scans
+};
 constexpr int kSoftMaxSeq = 1024;                            // keys a work-group keeps in registers
-constexpr int kSoftTiles = kSoftMaxSeq / 32 / kSoftWaves;    // key tiles per wave
 constexpr int kBins = 256;                                   // histogram bins per row and level
 // LDS histogram row stride (words): odd, so the 32 rows' copies of one bin sit on 32 banks.
 constexpr int kHistStride = 257;
-constexpr int kScanLanes = 64 * kSoftWaves / 32;             // lanes per row in the scans
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -146,17 +151,18 @@ __device__ inline float load_v(const void* v, int64_t off) {
 // is resolved once its remaining quota takes the whole chosen bin: its
 // threshold becomes the lowest composite of that bin.  All threads of the
 // work-group call it; it returns (uniformly) whether every row is resolved.
-template <int L>
-__device__ __forceinline__ bool select_level(const uint32_t (&key)[kSoftTiles][16], uint32_t* hist, uint32_t* st_key,
+template <int L, int NW>
+__device__ __forceinline__ bool select_level(const uint32_t (&key)[SoftCfg<NW>::kTiles][16], uint32_t* hist, uint32_t* st_key,
                                              int* st_idx, int* st_need, int* st_done, int wid, int lane,
                                              int ntk) {
+  using C = SoftCfg<NW>;
   const int half = lane >> 5, ql = lane & 31;
   const uint32_t kpre = st_key[ql];
   const int ipre = st_idx[ql];
   uint32_t* hrow = hist + ql * kHistStride;
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u) {
-    const int kt = wid + kSoftWaves * u;
+  for (int u = 0; u < C::kTiles; ++u) {
+    const int kt = wid + C::kWaves * u;
     if (kt < ntk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -177,8 +183,8 @@ __device__ __forceinline__ bool select_level(const uint32_t (&key)[kSoftTiles][1
   {
     // wave w scans rows 4w .. 4w + 3, sixteen lanes per row; lane g holds bins
     // kPer * g .. kPer * g + kPer - 1
-    constexpr int kPer = (L < 4 ? kBins : 32) / kScanLanes;
-    const int srow = (32 / kSoftWaves) * wid + lane / kScanLanes, g = lane % kScanLanes;
+    constexpr int kPer = (L < 4 ? kBins : 32) / C::kScanLanes;
+    const int srow = (32 / C::kWaves) * wid + lane / C::kScanLanes, g = lane % C::kScanLanes;
     uint32_t* hb = hist + srow * kHistStride + kPer * g;
     uint32_t c[kPer];
     uint32_t sum = 0;
@@ -189,11 +195,11 @@ __device__ __forceinline__ bool select_level(const uint32_t (&key)[kSoftTiles][1
     }
 #pragma unroll
     for (int b = 0; b < kPer; ++b) hb[b] = 0u;
-    uint32_t S = sum;  // bins of lanes g .. kScanLanes - 1 of the row, i.e. digits >= kPer * g
+    uint32_t S = sum;  // bins of lanes g .. C::kScanLanes - 1 of the row, i.e. digits >= kPer * g
 #pragma unroll
-    for (int off = 1; off < kScanLanes; off <<= 1) {
-      const uint32_t t = __shfl_down(S, off, kScanLanes);
-      if (g + off < kScanLanes) S += t;
+    for (int off = 1; off < C::kScanLanes; off <<= 1) {
+      const uint32_t t = __shfl_down(S, off, C::kScanLanes);
+      if (g + off < C::kScanLanes) S += t;
     }
     const int nd = st_need[srow];
     const uint32_t above = S - sum;
@@ -231,8 +237,9 @@ __device__ __forceinline__ bool select_level(const uint32_t (&key)[kSoftTiles][1
   return *st_done == 32;
 }
 
-template <int DP, bool VF32, bool MASK>
-__global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4))) void soft_attn_kernel(SoftArgs a) {
+template <int DP, bool VF32, bool MASK, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void soft_attn_kernel(SoftArgs a) {
+  using C = SoftCfg<NW>;
   constexpr int HD = DP / 2;  // features of lane half h: h * HD .. h * HD + HD - 1
   constexpr int NFT = DP / 32;
   __shared__ uint32_t hist[32 * kHistStride];  // per row, one level at a time; then the output partials
@@ -240,11 +247,11 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   __shared__ int st_idx[32];             // index prefix, then the last kept index at K*
   __shared__ int st_need[32];            // kept keys still to place at the current level
   __shared__ int st_done;                // rows whose threshold is found
-  __shared__ float red[kSoftWaves][32];
-  __shared__ uint32_t redk[kSoftWaves][32];
+  __shared__ float red[C::kWaves][32];
+  __shared__ uint32_t redk[C::kWaves][32];
   __shared__ float rinvz[32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
-  __shared__ __attribute__((aligned(16))) uint16_t vst[(MASK || VF32) ? 8 : kSoftWaves * 1024];  // per wave: a bf16 V tile
+  __shared__ __attribute__((aligned(16))) uint16_t vst[(MASK || VF32) ? 8 : C::kWaves * 1024];  // per wave: a bf16 V tile
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -259,10 +266,10 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   const int kend = a.causal ? min(n, q0 + 32) : n;
   const int ntk = (kend + 31) / 32;  // key tiles some row of the block sees
 
-  for (int e = tid; e < 32 * kHistStride; e += kSoftThreads) hist[e] = 0u;
+  for (int e = tid; e < 32 * kHistStride; e += C::kThreads) hist[e] = 0u;
   if (tid == 0) st_done = 0;
   // the block's 32 soft query rows (the B operand of every logit tile)
-  for (int e = tid; e < 8 * DP; e += kSoftThreads) {
+  for (int e = tid; e < 8 * DP; e += C::kThreads) {
     const int row = e / (DP / 4), c4 = e % (DP / 4);
     const int i = min(q0 + row, n - 1);
     *reinterpret_cast<float4*>(qlds + row * (DP + 4) + 4 * c4) =
@@ -284,10 +291,10 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
 
   // ---- logits: s[u] = tile (key tile wid + 8u) x (the block's 32 rows)
   const float* qrow = qlds + ql * (DP + 4) + HD * half;  // B operand: the row's features t + HD * half
-  v16f s[kSoftTiles];
+  v16f s[C::kTiles];
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u) {
-    const int kt = wid + kSoftWaves * u;
+  for (int u = 0; u < C::kTiles; ++u) {
+    const int kt = wid + C::kWaves * u;
     v16f acc = {};
     if (kt < ntk) {
       const int key = min(32 * kt + ql, n - 1);
@@ -309,22 +316,22 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
 
   // ---- exact top-N: radix select over (logit key, inverted index)
   // order keys of the logits, 0 for the keys this row does not see
-  uint32_t key[kSoftTiles][16];
+  uint32_t key[C::kTiles][16];
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u) {
-    const int kt = wid + kSoftWaves * u;
+  for (int u = 0; u < C::kTiles; ++u) {
+    const int kt = wid + C::kWaves * u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 32 * kt + tile_row(r, half);
       key[u][r] = (kt < ntk && j < lim) ? order_key(s[u][r]) : 0u;
     }
   }
-  if (!select_level<0>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
-      !select_level<1>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
-      !select_level<2>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
-      !select_level<3>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
-      !select_level<4>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk))
-    select_level<5>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk);
+  if (!select_level<0, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<1, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<2, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<3, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
+      !select_level<4, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk))
+    select_level<5, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk);
 
   // key j of this row is kept iff visible and (key > K*, or key == K* and j <= j*)
   const uint32_t kst = st_key[ql];
@@ -333,8 +340,8 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   if (MASK) {
     uint8_t* mrow = a.keep + ((bh - a.bh_begin) * n + (rvalid ? i_row : 0)) * static_cast<int64_t>(n);
 #pragma unroll
-    for (int u = 0; u < kSoftTiles; ++u) {
-      const int kt = wid + kSoftWaves * u;
+    for (int u = 0; u < C::kTiles; ++u) {
+      const int kt = wid + C::kWaves * u;
       if (kt < ntk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   // ---- row maximum (the largest key, always kept), weights, Z
   uint32_t mk = 0;
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u)
+  for (int u = 0; u < C::kTiles; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mk = max(mk, key[u][r]);
   mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), 32)));
@@ -358,14 +365,14 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   __syncthreads();
   uint32_t rk = redk[0][ql];
 #pragma unroll
-  for (int w = 1; w < kSoftWaves; ++w) rk = max(rk, redk[w][ql]);
+  for (int w = 1; w < C::kWaves; ++w) rk = max(rk, redk[w][ql]);
   const float rmax = key_value(rk);
   const float c2 = a.scale * 1.4426950408889634f;
   const float off2 = rvalid ? rmax * c2 : 0.0f;
   float z = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kSoftTiles; ++u) {
-    const int kt = wid + kSoftWaves * u;
+  for (int u = 0; u < C::kTiles; ++u) {
+    const int kt = wid + C::kWaves * u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 32 * kt + tile_row(r, half);
@@ -382,21 +389,21 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
   if (tid < 32) {
     float Z = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kSoftWaves; ++w) Z += red[w][tid];
+    for (int w = 0; w < C::kWaves; ++w) Z += red[w][tid];
     rinvz[tid] = Z > 0.0f ? 1.0f / Z : 0.0f;
   }
 
   // ---- out = P V / Z, one 32-feature tile at a time, the waves' partials summed in LDS
   float* part = reinterpret_cast<float*>(hist);  // [waves][32 rows][32 features]
-  static_assert(kSoftWaves * 1024 <= 32 * kHistStride, "partials fit the histogram area");
+  static_assert(C::kWaves * 1024 <= 32 * kHistStride, "partials fit the histogram area");
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft) {
     const int feat = 32 * ft + ql;
     const bool fvalid = feat < d;
     v16f o = {};
 #pragma unroll
-    for (int u = 0; u < kSoftTiles; ++u) {
-      const int kt = wid + kSoftWaves * u;
+    for (int u = 0; u < C::kTiles; ++u) {
+      const int kt = wid + C::kWaves * u;
       if (kt < ntk) {
         if (!VF32 && a.vlds) {
           // stage the wave's 32 keys x 32 features of V (bf16) in LDS with 16-byte
@@ -478,28 +485,33 @@ __global__ __launch_bounds__(kSoftThreads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[r];
     __syncthreads();
-    for (int e = tid; e < 1024; e += kSoftThreads) {
+    for (int e = tid; e < 1024; e += C::kThreads) {
       const int row = e >> 5, f = e & 31;
       const int i = q0 + row, fe = 32 * ft + f;
       if (i < n && fe < d) {
         float val = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kSoftWaves; ++w) val += part[1024 * w + e];
+        for (int w = 0; w < C::kWaves; ++w) val += part[1024 * w + e];
         a.out[(bh * n + i) * d + fe] = val * rinvz[row];
       }
     }
   }
 }
 
-template <int DP, bool MASK>
+template <int DP, bool MASK, int NW>
 had_status launch_soft_attn(const SoftArgs& a, had_dtype vdt, hipStream_t st) {
   const int nqt = (a.n + 31) / 32;
   const dim3 grid(static_cast<unsigned>(a.bh_count * nqt));
   if (MASK || vdt == HAD_F32)
-    hipLaunchKernelGGL((soft_attn_kernel<DP, true, MASK>), grid, dim3(kSoftThreads), 0, st, a);
+    hipLaunchKernelGGL((soft_attn_kernel<DP, true, MASK, NW>), grid, dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((soft_attn_kernel<DP, false, MASK>), grid, dim3(kSoftThreads), 0, st, a);
+    hipLaunchKernelGGL((soft_attn_kernel<DP, false, MASK, NW>), grid, dim3(64 * NW), 0, st, a);
   return check_launch("soft_attn_kernel");
+}
+
+template <int DP, bool MASK>
+had_status launch_soft_attn(const SoftArgs& a, had_dtype vdt, hipStream_t st) {
+  return a.n <= 256 ? launch_soft_attn<DP, MASK, 4>(a, vdt, st) : launch_soft_attn<DP, MASK, 8>(a, vdt, st);
 }
 
 template <bool MASK>
