@@ -140,6 +140,29 @@ int main() {
                       A(0x10000), bws, nullptr),
          HAD_ERR_INVALID_ARG);
 
+  // had_soft_forward / had_soft_select
+  const had_shape soft_long = {1, 2, 1025, 64};
+  if (had_soft_workspace_bytes(soft_long) != 0 || had_soft_workspace_bytes(bigd) != 0) ++g_fail;
+  const size_t sws = had_soft_workspace_bytes(ok);
+  EXPECT(had_soft_forward(P<float>(0x1000), P<float>(0x2000), A(0x3000), HAD_BF16, ok, 8, 0.1f, 0.5f, 0, nullptr,
+                          nullptr, P<float>(0x4000), A(0x10000), sws - 1, nullptr),
+         HAD_ERR_INVALID_ARG);
+  EXPECT(had_soft_forward(P<float>(0x1000), P<float>(0x2000), A(0x3000), HAD_BF16, ok, 8, 0.1f, 0.0f, 0, nullptr,
+                          nullptr, P<float>(0x4000), A(0x10000), sws, nullptr),
+         HAD_ERR_INVALID_ARG);
+  EXPECT(had_soft_forward(P<float>(0x1000), P<float>(0x2000), A(0x3000), static_cast<had_dtype>(7), ok, 8, 0.1f,
+                          0.5f, 0, nullptr, nullptr, P<float>(0x4000), A(0x10000), sws, nullptr),
+         HAD_ERR_INVALID_ARG);
+  EXPECT(had_soft_forward(P<float>(0x1000), P<float>(0x2000), A(0x3000), HAD_BF16, soft_long, 8, 0.1f, 0.5f, 0,
+                          nullptr, nullptr, P<float>(0x4000), A(0x10000), sws, nullptr),
+         HAD_ERR_UNSUPPORTED);
+  EXPECT(had_soft_select(P<float>(0x1000), P<float>(0x2000), ok, 8, 0.5f, 0, nullptr, nullptr, 0, 0,
+                         P<uint8_t>(0x4000), A(0x10000), sws, nullptr),
+         HAD_ERR_INVALID_ARG);
+  EXPECT(had_soft_select(P<float>(0x1000), P<float>(0x2000), ok, 8, 0.5f, 0, nullptr, nullptr, 0, 1, nullptr,
+                         A(0x10000), sws, nullptr),
+         HAD_ERR_INVALID_ARG);
+
   if (g_fail == 0) std::printf("abi validation: all checks held\n");
   return g_fail == 0 ? 0 : 1;
 }

@@ -21,7 +21,8 @@ CSRC = os.path.join(ROOT, "sparse_attention_had_amd", "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANGXX = "/opt/rocm/llvm/bin/clang++"
-SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip"]
+SOURCES = ["had_api.hip", "had_pack.hip", "had_attention.hip", "had_decode.hip", "had_backward.hip",
+           "had_soft.hip"]
 
 
 def _run(cmd):
