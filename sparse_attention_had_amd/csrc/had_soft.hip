@@ -396,6 +396,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // ---- out = P V / Z, one 32-feature tile at a time, the waves' partials summed in LDS
   float* part = reinterpret_cast<float*>(hist);  // [waves][32 rows][32 features]
   static_assert(C::kWaves * 1024 <= 32 * kHistStride, "partials fit the histogram area");
+  const bool vlds = !VF32 && a.vlds;
+  // bf16 V through LDS: lane L loads key 32 kt + L / 2, features 32 ft + 16 (L % 2)
+  // .. + 15 of the wave's tile (two 16-byte loads, rows clamped to n - 1, features
+  // past d read as zeros); the loads of the next (feature block, tile) are issued
+  // before the current tile's products, one step ahead.
+  auto vload = [&](int ft, int u, uint4& v0, uint4& v1) {
+    const int kt = wid + C::kWaves * u;
+    const int key = min(32 * kt + (lane >> 1), n - 1);
+    const int f = 32 * ft + 16 * (lane & 1);
+    v0 = uint4{0u, 0u, 0u, 0u};
+    v1 = uint4{0u, 0u, 0u, 0u};
+    if (f < d && kt < ntk) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + f);
+      v0 = src[0];
+      v1 = src[1];
+    }
+  };
+  uint4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};
+  if (vlds) vload(0, 0, pv0, pv1);
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft) {
     const int feat = 32 * ft + ql;
@@ -404,79 +423,75 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int u = 0; u < C::kTiles; ++u) {
       const int kt = wid + C::kWaves * u;
-      if (kt < ntk) {
-        if (!VF32 && a.vlds) {
-          // stage the wave's 32 keys x 32 features of V (bf16) in LDS with 16-byte
-          // loads: lane L takes key 32 kt + L / 2, features 32 ft + 16 (L % 2) ..
-          const int key = min(32 * kt + (lane >> 1), n - 1);
-          const int f = 32 * ft + 16 * (lane & 1);
-          uint4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-          if (f < d) {
-            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + f);
-            v0 = src[0];
-            v1 = src[1];
-          }
+      if (vlds) {
+        if (kt < ntk) {
           uint16_t* dst = vst + wid * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
-          *reinterpret_cast<uint4*>(dst) = v0;
-          *reinterpret_cast<uint4*>(dst + 8) = v1;
-          // one wave writes and reads its own tile: LDS keeps a wave's operations in
-          // order, so only the compiler must not move the reads above the writes
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
-          // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
-          // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
-          // S = 8 g + 4 (G / 2): keys 8 g + 4 half + k at feature 32 ft + L % 32,
-          // the keys of this lane's weight registers 4g .. 4g + 3.
-          // v_mfma_f32_32x32x16_bf16 sums 16 k-slots, slots 8 half .. 8 half + 7
-          // from each lane: here the lane's registers 4 g0 .. 4 g0 + 7 (keys
-          // 8 (g0 + i / 4) + 4 half + i % 4) in both operands.  Each float32 weight
-          // is exactly hi + mid + lo, three bf16 values (the top 16 bits, those of
-          // the remainder, the rest), so three bf16 products give P V with exact
-          // partial products and float32 accumulation.
-          const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
-#pragma unroll
-          for (int g0 = 0; g0 < 4; g0 += 2) {
-            const uint16_t* tb = vst + wid * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
-            const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
-            const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
-            const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
-            uint32_t ph[8], pm[8], pl[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float x = s[u][4 * g0 + i];
-              const uint32_t h = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
-              const float r1 = x - __builtin_bit_cast(float, h);
-              const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
-              ph[i] = h;
-              pm[i] = m;
-              pl[i] = __builtin_bit_cast(uint32_t, r1 - __builtin_bit_cast(float, m));
-            }
-            u32x4 ah, am, al;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ah[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
-              am[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
-              al[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
-            }
-            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o, 0, 0, 0);
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        } else {
-          float vv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = 32 * kt + tile_row(r, half);
-            vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
+          *reinterpret_cast<uint4*>(dst) = pv0;
+          *reinterpret_cast<uint4*>(dst + 8) = pv1;
         }
+        // one wave writes and reads its own tile: LDS keeps a wave's operations in
+        // order, so only the compiler must not move the reads above the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (u + 1 < C::kTiles)
+          vload(ft, u + 1, pv0, pv1);
+        else if (ft + 1 < NFT)
+          vload(ft + 1, 0, pv0, pv1);
+        if (kt < ntk) {
+            // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
+            // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
+            // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
+            // S = 8 g + 4 (G / 2): keys 8 g + 4 half + k at feature 32 ft + L % 32,
+            // the keys of this lane's weight registers 4g .. 4g + 3.
+            // v_mfma_f32_32x32x16_bf16 sums 16 k-slots, slots 8 half .. 8 half + 7
+            // from each lane: here the lane's registers 4 g0 .. 4 g0 + 7 (keys
+            // 8 (g0 + i / 4) + 4 half + i % 4) in both operands.  Each float32 weight
+            // is exactly hi + mid + lo, three bf16 values (the top 16 bits, those of
+            // the remainder, the rest), so three bf16 products give P V with exact
+            // partial products and float32 accumulation.
+            const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
+#pragma unroll
+            for (int g0 = 0; g0 < 4; g0 += 2) {
+              const uint16_t* tb = vst + wid * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
+              const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
+              const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
+              const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+              uint32_t ph[8], pm[8], pl[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const float x = s[u][4 * g0 + i];
+                const uint32_t h = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
+                const float r1 = x - __builtin_bit_cast(float, h);
+                const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+                ph[i] = h;
+                pm[i] = m;
+                pl[i] = __builtin_bit_cast(uint32_t, r1 - __builtin_bit_cast(float, m));
+              }
+              u32x4 ah, am, al;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ah[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
+                am[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
+                al[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
+              }
+              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o, 0, 0, 0);
+              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o, 0, 0, 0);
+              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o, 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      } else if (kt < ntk) {
+        float vv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * kt + tile_row(r, half);
+          vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
       }
       // keep the next tile's V loads after this tile's products (register pressure)
       __builtin_amdgcn_sched_barrier(0);
