@@ -314,7 +314,7 @@ size_t had_soft_workspace_bytes(had_shape s);
  *             sigma), or NULL for 1.
  *  out        [B,H,n,d] float32, device; every element written.
  *  workspace  had_soft_workspace_bytes(s) bytes, 256-byte aligned (the soft
- *             rows; no initial contents needed).  Calls that may overlap need
+ *             key rows; no initial contents needed).  Calls that may overlap need
  *             distinct workspaces.
  *  Precision: float32 tanh, logits on the fp32 matrix cores, the kept set the
  *  exact top-N of those float32 logits, float32 weights, products and sums

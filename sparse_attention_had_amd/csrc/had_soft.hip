@@ -12,8 +12,9 @@
 // the kept set weights the full-precision V rows.
 //
 // GPU design (gfx950), two launches:
-//  1. transform: Q and K -> B_c(Q), B_c(K) in float32, rows padded with zeros
-//     to DP = 32, 64 or 128 features (one HBM pass each way).
+//  1. transform: K -> B_c(K) in float32, rows padded with zeros to DP = 32,
+//     64 or 128 features (one HBM pass each way).  The attention launch forms
+//     B_c(Q) of its own 32 query rows while it stages them.
 //  2. attention: a work-group is 8 waves (4 for n <= 256) and 32 query rows
 //     of one (batch, head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
 //     tiles w, w + 8, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
@@ -78,33 +79,48 @@ inline int soft_dp(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // ---- 1. transform ----------------------------------------------------------
+// K -> B_c(K) in float32, rows padded with zeros to DP features.  (The query
+// rows are transformed by the attention launch itself, as it stages them.)
 struct SoftTransformArgs {
-  const float* x[2];
-  float* xs[2];
-  const float* sigma[2];  // device scalars or null (1)
-  int64_t rows;           // B*H*n
-  int d, dp;
+  const float* x;
+  float* xs;
+  const float* sigma;  // device scalar or null (1)
+  int64_t rows;        // B*H*n
+  int d, dp, dp4_log2; // dp / 4 == 1 << dp4_log2
+  int vec;             // d % 4 == 0 and x 16-byte aligned: float4 loads
   float c;
 };
 
 constexpr int kTfThreads = 256;
-constexpr int kTfRows = 16;  // rows per block
+
+__device__ inline float soft_mul(const float* sigma, float c) {
+  const float sg = sigma != nullptr ? *sigma : 1.0f;
+  return static_cast<float>(1.0 / (static_cast<double>(sg) * static_cast<double>(c)));
+}
+
+// Four soft features f .. f + 3 of row x (zeros past d).
+__device__ inline float4 soft_four(const float* x, int f, int d, bool vec, float mul) {
+  float4 y;
+  if (vec && f + 4 <= d) {
+    const float4 v = *reinterpret_cast<const float4*>(x + f);
+    y = make_float4(tanhf(v.x * mul), tanhf(v.y * mul), tanhf(v.z * mul), tanhf(v.w * mul));
+  } else {
+    y.x = f < d ? tanhf(x[f] * mul) : 0.0f;
+    y.y = f + 1 < d ? tanhf(x[f + 1] * mul) : 0.0f;
+    y.z = f + 2 < d ? tanhf(x[f + 2] * mul) : 0.0f;
+    y.w = f + 3 < d ? tanhf(x[f + 3] * mul) : 0.0f;
+  }
+  return y;
+}
 
 __global__ __launch_bounds__(kTfThreads) void soft_transform_kernel(SoftTransformArgs a) {
-  const int t = blockIdx.y;
-  const float* x = a.x[t];
-  float* xs = a.xs[t];
-  const float sg = a.sigma[t] != nullptr ? *a.sigma[t] : 1.0f;
-  const float mul = static_cast<float>(1.0 / (static_cast<double>(sg) * static_cast<double>(a.c)));
-  const int d = a.d, dp = a.dp;
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTfRows; r0 < a.rows;
-       r0 += static_cast<int64_t>(gridDim.x) * kTfRows) {
-    const int nr = static_cast<int>(min<int64_t>(kTfRows, a.rows - r0));
-    for (int e = threadIdx.x; e < nr * dp; e += kTfThreads) {
-      const int r = e / dp, f = e - r * dp;
-      const int64_t row = r0 + r;
-      xs[row * dp + f] = f < d ? tanhf(x[row * d + f] * mul) : 0.0f;
-    }
+  const float mul = soft_mul(a.sigma, a.c);
+  const int64_t groups = a.rows << a.dp4_log2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kTfThreads;
+  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kTfThreads + threadIdx.x; gi < groups; gi += stride) {
+    const int64_t row = gi >> a.dp4_log2;
+    const int f = 4 * static_cast<int>(gi & ((1 << a.dp4_log2) - 1));
+    *reinterpret_cast<float4*>(a.xs + row * a.dp + f) = soft_four(a.x + row * a.d, f, a.d, a.vec != 0, mul);
   }
 }
 
@@ -116,8 +132,11 @@ __global__ __launch_bounds__(256) void soft_clear_kernel(uint8_t* p, int64_t byt
 
 // ---- 2. attention ----------------------------------------------------------
 struct SoftArgs {
-  const float* qs;  // [BH, n, DP]
-  const float* ks;  // [BH, n, DP]
+  const float* q;        // [BH, n, d] float32: the query rows, transformed while staged
+  const float* sigma_q;  // device scalar or null (1)
+  float c;
+  int qvec;              // d % 4 == 0 and q 16-byte aligned
+  const float* ks;       // [BH, n, DP] the soft key rows
   const void* v;    // [BH, n, d] float32 or bf16
   float* out;       // [BH, n, d]
   uint8_t* keep;    // mask mode: [bh_count, n, n], pre-cleared; 1 where kept
@@ -268,12 +287,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 
   for (int e = tid; e < 32 * kHistStride; e += C::kThreads) hist[e] = 0u;
   if (tid == 0) st_done = 0;
-  // the block's 32 soft query rows (the B operand of every logit tile)
-  for (int e = tid; e < 8 * DP; e += C::kThreads) {
-    const int row = e / (DP / 4), c4 = e % (DP / 4);
-    const int i = min(q0 + row, n - 1);
-    *reinterpret_cast<float4*>(qlds + row * (DP + 4) + 4 * c4) =
-        *reinterpret_cast<const float4*>(a.qs + (bh * n + i) * DP + 4 * c4);
+  // the block's 32 soft query rows B_c(q) (the B operand of every logit tile)
+  {
+    const float mulq = soft_mul(a.sigma_q, a.c);
+    for (int e = tid; e < 8 * DP; e += C::kThreads) {
+      const int row = e / (DP / 4), c4 = e % (DP / 4);
+      const int i = min(q0 + row, n - 1);
+      *reinterpret_cast<float4*>(qlds + row * (DP + 4) + 4 * c4) =
+          soft_four(a.q + (bh * n + i) * d, 4 * c4, d, a.qvec != 0, mulq);
+    }
   }
   __syncthreads();
   if (tid < 32) {
@@ -557,31 +579,31 @@ had_status check_soft(const float* q, const float* k, const had_shape& s, int64_
   return HAD_OK;
 }
 
-// Launch 1 into the workspace; fills the soft-row pointers of a.
+// Launch 1 (the soft key rows) into the workspace; fills the input fields of a.
 had_status soft_transform(const float* q, const float* k, const had_shape& s, float c, const float* sigma_q,
                           const float* sigma_k, void* workspace, SoftArgs& a, hipStream_t st) {
   const int dp = soft_dp(s.dim);
   const int64_t rows = s.batch * s.heads * s.seq;
-  float* qs = static_cast<float*>(workspace);
-  float* ks = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                       align256(static_cast<size_t>(rows) * dp * sizeof(float)));
+  float* ks = static_cast<float*>(workspace);
   SoftTransformArgs t{};
-  t.x[0] = q;
-  t.x[1] = k;
-  t.xs[0] = qs;
-  t.xs[1] = ks;
-  t.sigma[0] = sigma_q;
-  t.sigma[1] = sigma_k;
+  t.x = k;
+  t.xs = ks;
+  t.sigma = sigma_k;
   t.rows = rows;
   t.d = static_cast<int>(s.dim);
   t.dp = dp;
+  t.dp4_log2 = dp == 32 ? 3 : (dp == 64 ? 4 : 5);
+  t.vec = s.dim % 4 == 0 && aligned(k, 16);
   t.c = c;
-  const int64_t blocks = (rows + kTfRows - 1) / kTfRows;
-  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(blocks, 4096)), 2);
+  const int64_t groups = rows * (dp / 4);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((groups + kTfThreads - 1) / kTfThreads, 8192)));
   hipLaunchKernelGGL(soft_transform_kernel, grid, dim3(kTfThreads), 0, st, t);
   had_status r = check_launch("soft_transform_kernel");
   if (r != HAD_OK) return r;
-  a.qs = qs;
+  a.q = q;
+  a.sigma_q = sigma_q;
+  a.c = c;
+  a.qvec = s.dim % 4 == 0 && aligned(q, 16);
   a.ks = ks;
   a.n = static_cast<int>(s.seq);
   a.d = static_cast<int>(s.dim);
@@ -596,7 +618,7 @@ using namespace had;
 extern "C" size_t had_soft_workspace_bytes(had_shape s) {
   if (check_shape(s) != HAD_OK || s.dim > 128 || s.seq > HAD_SOFT_MAX_SEQ) return 0;
   const size_t rows = static_cast<size_t>(s.batch * s.heads * s.seq);
-  return 2 * align256(rows * soft_dp(s.dim) * sizeof(float));
+  return align256(rows * soft_dp(s.dim) * sizeof(float));
 }
 
 extern "C" had_status had_soft_forward(const float* q, const float* k, const void* v, had_dtype v_dtype,
