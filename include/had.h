@@ -307,6 +307,8 @@ size_t had_soft_workspace_bytes(had_shape s);
  * of scale * s_ij, times V.
  *
  *  q, k       [B,H,n,d] float32, device, 4-byte aligned.  n <= 1024, d <= 128.
+ *             NaN inputs are outside the contract: the kept sets and outputs
+ *             are then unspecified (every access stays in bounds).
  *  v, v_dtype as had_attention (float32 or bf16, 4-byte aligned).
  *  topn, scale, causal  as had_attention.
  *  c          the tanh scale, finite and > 0.
