@@ -16,11 +16,11 @@
 //     64 or 128 features (one HBM pass each way).  The attention launch forms
 //     B_c(Q) of its own 32 query rows while it stages them.
 //  2. attention: a work-group is 8 waves (4 for n <= 256) and 32 query rows
-//     of one (batch, head) slice, n <= 1024.  Wave w forms the 32 x 32 logit tiles of key
-//     tiles w, w + 8, ... on the fp32 matrix cores (v_mfma_f32_32x32x2f32,
-//     A = the key rows, B = the query rows; lane L then holds query row
-//     L % 32 and 16 keys of each tile) and keeps them in registers: at most
-//     4 tiles of 16 values per lane.  The kept set is an exact radix select
+//     of one (batch, head) slice, n <= 1024.  Wave w of W forms the 32 x 32
+//     logit tiles of key tiles w, w + W, ... on the fp32 matrix cores
+//     (v_mfma_f32_32x32x2f32, A = the key rows, B = the query rows staged in
+//     LDS; lane L then holds query row L % 32 and 16 keys of each tile) and
+//     keeps them in registers: at most 4 tiles of 16 values per lane.  The kept set is an exact radix select
 //     over the composite (order-preserving bits of the float32 logit, then
 //     the key index inverted), so exactly N_i keys are kept with no separate
 //     tie rule: four levels of 8-bit digits of the logit's key and two of
@@ -28,9 +28,11 @@
 //     elements still matching the prefix (ds_add_u32) and a scan that finds
 //     the digit holding the N_i-th largest.  Then the row maximum, the
 //     weights exp(scale * (s - max)) of the kept keys, their sum Z, and the
-//     weighted V rows on the matrix cores, reduced over the eight waves in a
-//     fixed order and divided by Z.  bf16 V (d a multiple of 16): each wave
-//     stages its V tile in LDS with 16-byte loads and reads the operand back
+//     weighted V rows on the matrix cores, reduced over the waves in a fixed
+//     order and divided by Z.  A row is resolved as soon as its quota takes a
+//     whole bin, and the levels stop once every row is.  bf16 V (d a multiple
+//     of 16): each wave stages its V tile in LDS with 16-byte loads, the next
+//     tile's loads issued one step ahead, and reads the operand back
 //     transposed (ds_read_b64_tr_b16); each float32 weight is split exactly into
 //     three bf16 values for v_mfma_f32_32x32x16_bf16.  fp32 V: the weights
 //     straight from the logit registers and V rows from L2 on the fp32 matrix
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
         for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
       }
-      // keep the next tile's V loads after this tile's products (register pressure)
+      // no instruction moves across tiles (the register budget holds one tile's operands)
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // the previous tile's partials are consumed (and rinvz is written)
