@@ -106,10 +106,12 @@ def stats(stats_csv, out_md, cmd, title):
     print("\n".join(lines))
 
 
-def counters(csvs, cmds, kernel, workload, out_md):
+def counters(csvs, cmds, kernel, workload, out_md, sources=ATTENTION_SOURCES):
     """SQ counters of one kernel, one rocprofv3 --pmc pass per CSV: the mean
     over its dispatches of each counter (summed over the counter's instances
-    within a dispatch), and that mean divided by SQ_WAVES (waves per dispatch)."""
+    within a dispatch), and that mean divided by SQ_WAVES (waves per dispatch).
+    `sources` are the files the kernel is compiled from (their hash heads the
+    summary)."""
     means, ndisp = {}, {}
     for path in csvs:
         per = {}
@@ -124,8 +126,8 @@ def counters(csvs, cmds, kernel, workload, out_md):
             ndisp[name] = len(vals)
     waves = means.get("SQ_WAVES")
     lines = [f"# SQ counters, `{kernel}`, {workload}", "",
-             f"Kernel sources: sha256 prefix `{source_hash()}` of "
-             f"{', '.join('`' + f + '`' for f in ATTENTION_SOURCES)}.", "",
+             f"Kernel sources: sha256 prefix `{source_hash(sources)}` of "
+             f"{', '.join('`' + f + '`' for f in sources)}.", "",
              "Commands (one counter pass each):", "", "```"] + list(cmds) + ["```", "",
              "| counter | mean per dispatch | per wave | dispatches |", "|---|---|---|---|"]
     for name, v in means.items():
@@ -152,6 +154,8 @@ def main(argv=None):
     t.add_argument("--cmd", required=True)
     c = sub.add_parser("counters")
     c.add_argument("--csv", action="append", required=True)
+    c.add_argument("--sources", action="append", default=None,
+                   help="source files of the kernel (default: the attention kernel's)")
     c.add_argument("--cmd", action="append", required=True)
     c.add_argument("--kernel", default="had_attn_kernel")
     c.add_argument("--workload", required=True)
@@ -160,7 +164,8 @@ def main(argv=None):
     if a.cmd_name == "stats":
         stats(a.csv, a.out, a.cmd, a.title)
     elif a.cmd_name == "counters":
-        counters(a.csv, a.cmd, a.kernel, a.workload, a.out)
+        counters(a.csv, a.cmd, a.kernel, a.workload, a.out,
+                 tuple(a.sources) if a.sources else ATTENTION_SOURCES)
     else:
         traffic(a.fetch, a.write, a.workload, a.out, a.cmd)
 
