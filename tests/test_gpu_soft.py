@@ -156,6 +156,7 @@ CASES = [
     ((1, 2, 77, 64), 9, 0.7, True, "bf16", 15),
     ((1, 1, 100, 32), 12, 0.6, False, "bf16", 16),
     ((2, 1, 150, 48), 30, 0.9, True, "bf16", 17),
+    ((1, 1, 600, 128), 70, 0.5, True, "f32", 18),
 ]
 
 
@@ -220,3 +221,15 @@ def test_soft_forward_sigma_is_applied():
     two = torch.full((1,), 2.0, device="cuda")
     c2 = had.soft_forward(q, k, v, 11, 0.2, 0.25, False, sigma_q=two, sigma_k=two)
     assert torch.equal(a, c2)
+
+
+def test_soft_select_slice_range_equals_the_full_export():
+    """had_soft_select on slices [1, 3) of 4 gives those slices of the full export."""
+    log("soft select slice range")
+    inp = make_inputs(2, 2, 300, 64, v_dtype="f32", rank=4, noise="t3", seed=9)
+    q, k, _ = _dev(inp)
+    _, _, tsq, tsk = _sigmas(inp)
+    full = had.soft_select(q, k, 40, 0.5, True, sigma_q=tsq, sigma_k=tsk)
+    part = had.soft_select(q, k, 40, 0.5, True, sigma_q=tsq, sigma_k=tsk, bh_begin=1, bh_count=2)
+    assert torch.equal(part, full[1:3])
+    assert int(full.sum()) == sum(min(40, i + 1) for i in range(300)) * 4
