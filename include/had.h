@@ -313,7 +313,8 @@ size_t had_soft_workspace_bytes(had_shape s);
  *  topn, scale, causal  as had_attention.
  *  c          the tanh scale, finite and > 0.
  *  sigma_q, sigma_k  device float* (had_pack's or had_sigma_from_state's
- *             sigma), or NULL for 1.
+ *             sigma), or NULL for 1.  1 / (sigma * c) is taken as at most
+ *             FLT_MAX (a sigma of 0 gives the sign, and 0 for x = 0).
  *  out        [B,H,n,d] float32, device; every element written.
  *  workspace  had_soft_workspace_bytes(s) bytes, 256-byte aligned (the soft
  *             key rows; no initial contents needed).  Calls that may overlap need

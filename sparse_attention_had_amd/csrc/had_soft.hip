@@ -95,9 +95,11 @@ struct SoftTransformArgs {
 
 constexpr int kTfThreads = 256;
 
+// 1 / (sigma c) in float32, at most FLT_MAX: a sigma of 0 (a constant tensor)
+// or a subnormal c then still gives tanh(0) = 0 for x = 0 instead of 0 * inf.
 __device__ inline float soft_mul(const float* sigma, float c) {
   const float sg = sigma != nullptr ? *sigma : 1.0f;
-  return static_cast<float>(1.0 / (static_cast<double>(sg) * static_cast<double>(c)));
+  return static_cast<float>(fmin(1.0 / (static_cast<double>(sg) * static_cast<double>(c)), 3.4028234663852886e38));
 }
 
 // Four soft features f .. f + 3 of row x (zeros past d).

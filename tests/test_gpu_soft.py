@@ -233,3 +233,21 @@ def test_soft_select_slice_range_equals_the_full_export():
     part = had.soft_select(q, k, 40, 0.5, True, sigma_q=tsq, sigma_k=tsk, bh_begin=1, bh_count=2)
     assert torch.equal(part, full[1:3])
     assert int(full.sum()) == sum(min(40, i + 1) for i in range(300)) * 4
+
+
+def test_soft_forward_with_sigma_zero_is_finite():
+    """A sigma of 0 (the sigma had_pack reports for a constant tensor) takes
+    1 / (sigma c) as FLT_MAX: the soft signs are the signs, 0 for an element
+    equal to 0, so with every query element 0 all logits are 0 and each row is
+    the mean of its N_i lowest-index visible V rows."""
+    log("soft forward sigma 0")
+    n, d, topn = 70, 64, 9
+    q = torch.zeros((1, 1, n, d), device="cuda")
+    k = torch.randn((1, 1, n, d), device="cuda")
+    v = torch.randn((1, 1, n, d), device="cuda")
+    zero = torch.zeros(1, device="cuda")
+    out = had.soft_forward(q, k, v, topn, 0.3, 0.5, True, sigma_q=zero, sigma_k=zero).cpu().numpy()[0, 0]
+    vv = v.cpu().numpy()[0, 0].astype(np.float64)
+    for i in range(n):
+        want = vv[: min(topn, i + 1)].mean(0)
+        assert np.all(np.abs(out[i] - want) <= 1e-5 * np.abs(vv[: min(topn, i + 1)]).mean(0) + 1e-6)
