@@ -57,8 +57,9 @@ struct SoftCfg {
 };
 constexpr int kSoftMaxSeq = 1024;                            // keys a work-group keeps in registers
 constexpr int kBins = 256;                                   // histogram bins per row and level
-// LDS histogram row stride (words): odd, so the 32 rows' copies of one bin sit on 32 banks.
-constexpr int kHistStride = 257;
+// LDS histogram row stride (words): 16-byte rows for the scan's vector reads;
+// 260 = 4 (mod 64) puts the 32 rows' copies of one bin on 16 banks.
+constexpr int kHistStride = 260;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -204,42 +205,100 @@ __device__ __forceinline__ bool select_level(const uint32_t (&key)[SoftCfg<NW>::
   }
   __syncthreads();
   {
-    // wave w scans rows 4w .. 4w + 3, sixteen lanes per row; lane g holds bins
-    // kPer * g .. kPer * g + kPer - 1
+    // each wave scans 32 / W rows, 64 W / 32 lanes per row; lane g holds bins
+    // kPer * g .. kPer * g + kPer - 1 of its row
     constexpr int kPer = (L < 4 ? kBins : 32) / C::kScanLanes;
     const int srow = (32 / C::kWaves) * wid + lane / C::kScanLanes, g = lane % C::kScanLanes;
     uint32_t* hb = hist + srow * kHistStride + kPer * g;
-    uint32_t c[kPer];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) {
-      c[b] = hb[b];
-      sum += c[b];
-    }
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) hb[b] = 0u;
-    uint32_t S = sum;  // bins of lanes g .. C::kScanLanes - 1 of the row, i.e. digits >= kPer * g
-#pragma unroll
-    for (int off = 1; off < C::kScanLanes; off <<= 1) {
-      const uint32_t t = __shfl_down(S, off, C::kScanLanes);
-      if (g + off < C::kScanLanes) S += t;
-    }
     const int nd = st_need[srow];
-    const uint32_t above = S - sum;
-    if (nd > 0 && above < static_cast<uint32_t>(nd) && static_cast<uint32_t>(nd) <= S) {
-      uint32_t acc = above, ct = 0;
-      int tb = 0;
-      bool found = false;
+    uint32_t acc = 0, ct = 0;
+    int tb = 0;
+    bool mine = false;
+    if constexpr (kPer % 4 == 0) {
+      // 16-byte reads of groups of four bins; the lane holding the quota finds
+      // its group from the group sums, re-reads that group (before the zeroing,
+      // which LDS performs after it: one wave, in order) and finds the bin in it
+      constexpr int kQ = kPer / 4;
+      uint32_t gs[kQ];
+      uint32_t sum = 0;
 #pragma unroll
-      for (int b = kPer - 1; b >= 0; --b) {
-        const bool hit = !found && acc + c[b] >= static_cast<uint32_t>(nd);
-        if (hit) {
-          tb = b;
-          ct = c[b];
-          found = true;
-        }
-        if (!found) acc += c[b];
+      for (int q = 0; q < kQ; ++q) {
+        const uint4 x = *reinterpret_cast<const uint4*>(hb + 4 * q);
+        gs[q] = (x.x + x.y) + (x.z + x.w);
+        sum += gs[q];
       }
+      uint32_t S = sum;  // bins of lanes g .. of the row, i.e. digits >= kPer * g
+#pragma unroll
+      for (int off = 1; off < C::kScanLanes; off <<= 1) {
+        const uint32_t t = __shfl_down(S, off, C::kScanLanes);
+        if (g + off < C::kScanLanes) S += t;
+      }
+      acc = S - sum;
+      mine = nd > 0 && acc < static_cast<uint32_t>(nd) && static_cast<uint32_t>(nd) <= S;
+      uint4 cg = {0u, 0u, 0u, 0u};
+      int tq = 0;
+      if (mine) {
+        bool found = false;
+#pragma unroll
+        for (int q = kQ - 1; q >= 0; --q) {
+          const bool hit = !found && acc + gs[q] >= static_cast<uint32_t>(nd);
+          if (hit) {
+            tq = q;
+            found = true;
+          }
+          if (!found) acc += gs[q];
+        }
+        cg = *reinterpret_cast<const uint4*>(hb + 4 * tq);
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) *reinterpret_cast<uint4*>(hb + 4 * q) = uint4{0u, 0u, 0u, 0u};
+      if (mine) {
+        const uint32_t cc[4] = {cg.x, cg.y, cg.z, cg.w};
+        bool found = false;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const bool hit = !found && acc + cc[i] >= static_cast<uint32_t>(nd);
+          if (hit) {
+            tb = 4 * tq + i;
+            ct = cc[i];
+            found = true;
+          }
+          if (!found) acc += cc[i];
+        }
+      }
+    } else {
+      uint32_t c[kPer];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int b = 0; b < kPer; ++b) {
+        c[b] = hb[b];
+        sum += c[b];
+      }
+#pragma unroll
+      for (int b = 0; b < kPer; ++b) hb[b] = 0u;
+      uint32_t S = sum;
+#pragma unroll
+      for (int off = 1; off < C::kScanLanes; off <<= 1) {
+        const uint32_t t = __shfl_down(S, off, C::kScanLanes);
+        if (g + off < C::kScanLanes) S += t;
+      }
+      acc = S - sum;
+      mine = nd > 0 && acc < static_cast<uint32_t>(nd) && static_cast<uint32_t>(nd) <= S;
+      if (mine) {
+        bool found = false;
+#pragma unroll
+        for (int b = kPer - 1; b >= 0; --b) {
+          const bool hit = !found && acc + c[b] >= static_cast<uint32_t>(nd);
+          if (hit) {
+            tb = b;
+            ct = c[b];
+            found = true;
+          }
+          if (!found) acc += c[b];
+        }
+      }
+    }
+    if (mine) {
       const uint32_t digit = static_cast<uint32_t>(kPer * g + tb);
       const int rem = nd - static_cast<int>(acc);
       const bool whole = static_cast<uint32_t>(rem) == ct || L == 5;
@@ -265,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   using C = SoftCfg<NW>;
   constexpr int HD = DP / 2;  // features of lane half h: h * HD .. h * HD + HD - 1
   constexpr int NFT = DP / 32;
-  __shared__ uint32_t hist[32 * kHistStride];  // per row, one level at a time; then the output partials
+  __shared__ __attribute__((aligned(16))) uint32_t hist[32 * kHistStride];  // per row, one level at a time; then the output partials
   __shared__ uint32_t st_key[32];        // logit key prefix, then the threshold key K*
   __shared__ int st_idx[32];             // index prefix, then the last kept index at K*
   __shared__ int st_need[32];            // kept keys still to place at the current level
