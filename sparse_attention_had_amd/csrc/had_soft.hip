@@ -18,8 +18,9 @@
 //  2. attention: a work-group is 8 waves (4 for n <= 256) and 32 query rows
 //     of one (batch, head) slice, n <= 1024.  Wave w of W forms the 32 x 32
 //     logit tiles of key tiles w, w + W, ... on the fp32 matrix cores
-//     (v_mfma_f32_32x32x2f32, A = the key rows, B = the query rows staged in
-//     LDS; lane L then holds query row L % 32 and 16 keys of each tile) and
+//     (v_mfma_f32_32x32x2f32, A = the key rows, the next tile's requested
+//     before the current tile's products at d <= 64, B = the query rows staged
+//     in LDS; lane L then holds query row L % 32 and 16 keys of each tile) and
 //     keeps them in registers: at most 4 tiles of 16 values per lane.  The kept set is an exact radix select
 //     over the composite (order-preserving bits of the float32 logit, then
 //     the key index inverted), so exactly N_i keys are kept with no separate
@@ -377,25 +378,60 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // ---- logits: s[u] = tile (key tile wid + 8u) x (the block's 32 rows)
   const float* qrow = qlds + ql * (DP + 4) + HD * half;  // B operand: the row's features t + HD * half
   v16f s[C::kTiles];
-#pragma unroll
-  for (int u = 0; u < C::kTiles; ++u) {
-    const int kt = wid + C::kWaves * u;
-    v16f acc = {};
-    if (kt < ntk) {
+  if constexpr (DP <= 64) {
+    // the next tile's key rows are requested before this tile's products
+    // (at DP = 128 the second set of operands would not fit the register budget)
+    float4 kx[HD / 4];
+    auto kload = [&](int u) {
+      const int kt = wid + C::kWaves * u;
       const int key = min(32 * kt + ql, n - 1);
       const float* kr = a.ks + (bh * n + key) * DP + HD * half;
 #pragma unroll
-      for (int t = 0; t < HD; t += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(kr + t);
-        const float4 y = *reinterpret_cast<const float4*>(qrow + t);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
+      for (int t = 0; t < HD / 4; ++t) kx[t] = kt < ntk ? *reinterpret_cast<const float4*>(kr + 4 * t) : float4{};
+    };
+    kload(0);
+#pragma unroll
+    for (int u = 0; u < C::kTiles; ++u) {
+      const int kt = wid + C::kWaves * u;
+      float4 kc[HD / 4];
+#pragma unroll
+      for (int t = 0; t < HD / 4; ++t) kc[t] = kx[t];
+      if (u + 1 < C::kTiles) kload(u + 1);
+      v16f acc = {};
+      if (kt < ntk) {
+#pragma unroll
+        for (int t = 0; t < HD; t += 4) {
+          const float4 x = kc[t / 4];
+          const float4 y = *reinterpret_cast<const float4*>(qrow + t);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
+        }
       }
+      s[u] = acc;
     }
-    s[u] = acc;
-    __builtin_amdgcn_sched_barrier(0);  // one tile's key rows in registers at a time
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::kTiles; ++u) {
+      const int kt = wid + C::kWaves * u;
+      v16f acc = {};
+      if (kt < ntk) {
+        const int key = min(32 * kt + ql, n - 1);
+        const float* kr = a.ks + (bh * n + key) * DP + HD * half;
+#pragma unroll
+        for (int t = 0; t < HD; t += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(kr + t);
+          const float4 y = *reinterpret_cast<const float4*>(qrow + t);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
+        }
+      }
+      s[u] = acc;
+      __builtin_amdgcn_sched_barrier(0);  // one tile's key rows in registers at a time
+    }
   }
   __syncthreads();
 
