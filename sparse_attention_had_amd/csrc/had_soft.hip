@@ -32,12 +32,13 @@
 //     weighted V rows on the matrix cores, reduced over the waves in a fixed
 //     order and divided by Z.  A row is resolved as soon as its quota takes a
 //     whole bin, and the levels stop once every row is.  bf16 V (d a multiple
-//     of 16): each wave stages its V tile in LDS with 16-byte loads, the next
-//     tile's loads issued one step ahead, and reads the operand back
+//     of 16): each wave stages its tile of 32 keys and up to 64 features (two
+//     32-feature blocks per pass over the tiles) in LDS with 16-byte loads, in
+//     the histogram area the select no longer needs, and reads the operand back
 //     transposed (ds_read_b64_tr_b16); each float32 weight is split exactly into
-//     three bf16 values for v_mfma_f32_32x32x16_bf16.  fp32 V: the weights
-//     straight from the logit registers and V rows from L2 on the fp32 matrix
-//     cores.
+//     three bf16 values, once per tile and pass, for v_mfma_f32_32x32x16_bf16.
+//     fp32 V: the weights straight from the logit registers and V rows from L2
+//     on the fp32 matrix cores.
 // No floating-point atomics: results are identical run to run.
 #include <algorithm>
 #include <cmath>
@@ -334,7 +335,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ uint32_t redk[C::kWaves][32];
   __shared__ float rinvz[32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
-  __shared__ __attribute__((aligned(16))) uint16_t vst[(MASK || VF32) ? 8 : C::kWaves * 1024];  // per wave: a bf16 V tile
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -514,123 +514,146 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     rinvz[tid] = Z > 0.0f ? 1.0f / Z : 0.0f;
   }
 
-  // ---- out = P V / Z, one 32-feature tile at a time, the waves' partials summed in LDS
+  // ---- out = P V / Z: passes over the key tiles, FC 32-feature blocks per pass (each
+  // weight split once per pass), the waves' partials summed in LDS after each pass
+  constexpr int FC = NFT < 2 ? NFT : 2;
   float* part = reinterpret_cast<float*>(hist);  // [waves][32 rows][32 features]
-  static_assert(C::kWaves * 1024 <= 32 * kHistStride, "partials fit the histogram area");
+  static_assert(C::kWaves * 1024 <= 32 * kHistStride, "partials and V tiles fit the histogram area");
+  // bf16 V tiles are staged in the histogram area as well (free once the select is
+  // done): wave w's 32 keys x 32 FC features in the 4 KB its partials take later
+  uint16_t* vst = reinterpret_cast<uint16_t*>(hist) + wid * 2048;
   const bool vlds = !VF32 && a.vlds;
-  // bf16 V through LDS: lane L loads key 32 kt + L / 2, features 32 ft + 16 (L % 2)
-  // .. + 15 of the wave's tile (two 16-byte loads, rows clamped to n - 1, features
-  // past d read as zeros); the loads of the next (feature block, tile) are issued
-  // before the current tile's products, one step ahead.
-  auto vload = [&](int ft, int u, uint4& v0, uint4& v1) {
+  // bf16 V through LDS: lane L loads key 32 kt + L / 2, features 32 (fc + f) + 16 (L % 2)
+  // .. + 15 of the wave's tile for each block f of the pass (two 16-byte loads per block,
+  // rows clamped to n - 1, features past d read as zeros).  The loads are not issued a
+  // tile ahead: holding them across the products spills registers (the other waves of
+  // the SIMD cover their latency).
+  auto vload = [&](int fc, int u, uint4 (&pv)[2 * FC]) {
     const int kt = wid + C::kWaves * u;
     const int key = min(32 * kt + (lane >> 1), n - 1);
-    const int f = 32 * ft + 16 * (lane & 1);
-    v0 = uint4{0u, 0u, 0u, 0u};
-    v1 = uint4{0u, 0u, 0u, 0u};
-    if (f < d && kt < ntk) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + f);
-      v0 = src[0];
-      v1 = src[1];
+#pragma unroll
+    for (int f = 0; f < FC; ++f) {
+      const int fe = 32 * (fc + f) + 16 * (lane & 1);
+      pv[2 * f] = uint4{0u, 0u, 0u, 0u};
+      pv[2 * f + 1] = uint4{0u, 0u, 0u, 0u};
+      if (fe < d && kt < ntk) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + fe);
+        pv[2 * f] = src[0];
+        pv[2 * f + 1] = src[1];
+      }
     }
   };
-  uint4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};
-  if (vlds) vload(0, 0, pv0, pv1);
+  uint4 pv[2 * FC];
 #pragma unroll
-  for (int ft = 0; ft < NFT; ++ft) {
-    const int feat = 32 * ft + ql;
-    const bool fvalid = feat < d;
-    v16f o = {};
+  for (int fc = 0; fc < NFT; fc += FC) {
+    v16f o[FC];
+#pragma unroll
+    for (int f = 0; f < FC; ++f) o[f] = v16f{};
 #pragma unroll
     for (int u = 0; u < C::kTiles; ++u) {
       const int kt = wid + C::kWaves * u;
       if (vlds) {
+        vload(fc, u, pv);
         if (kt < ntk) {
-          uint16_t* dst = vst + wid * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
-          *reinterpret_cast<uint4*>(dst) = pv0;
-          *reinterpret_cast<uint4*>(dst + 8) = pv1;
+#pragma unroll
+          for (int f = 0; f < FC; ++f) {
+            uint16_t* dst = vst + f * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
+            *reinterpret_cast<uint4*>(dst) = pv[2 * f];
+            *reinterpret_cast<uint4*>(dst + 8) = pv[2 * f + 1];
+          }
         }
         // one wave writes and reads its own tile: LDS keeps a wave's operations in
         // order, so only the compiler must not move the reads above the writes
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (u + 1 < C::kTiles)
-          vload(ft, u + 1, pv0, pv1);
-        else if (ft + 1 < NFT)
-          vload(ft + 1, 0, pv0, pv1);
         if (kt < ntk) {
-            // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
-            // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
-            // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
-            // S = 8 g + 4 (G / 2): keys 8 g + 4 half + k at feature 32 ft + L % 32,
-            // the keys of this lane's weight registers 4g .. 4g + 3.
-            // v_mfma_f32_32x32x16_bf16 sums 16 k-slots, slots 8 half .. 8 half + 7
-            // from each lane: here the lane's registers 4 g0 .. 4 g0 + 7 (keys
-            // 8 (g0 + i / 4) + 4 half + i % 4) in both operands.  Each float32 weight
-            // is exactly hi + mid + lo, three bf16 values (the top 16 bits, those of
-            // the remainder, the rest), so three bf16 products give P V with exact
-            // partial products and float32 accumulation.
-            const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
+          // ds_read_b64_tr_b16: in each 16-lane group G, lane 4k + q gives the
+          // address of (key S + k, features f0 + 4q .. f0 + 4q + 3) and lane j gets
+          // (key S + k, feature f0 + j) for k = 0..3, with f0 = 16 (G % 2) and
+          // S = 8 g + 4 (G / 2): keys 8 g + 4 half + k at feature 32 ft + L % 32,
+          // the keys of this lane's weight registers 4g .. 4g + 3.
+          // v_mfma_f32_32x32x16_bf16 sums 16 k-slots, slots 8 half .. 8 half + 7
+          // from each lane: here the lane's registers 4 g0 .. 4 g0 + 7 (keys
+          // 8 (g0 + i / 4) + 4 half + i % 4) in both operands.  Each float32 weight
+          // is exactly hi + mid + lo, three bf16 values (the top 16 bits, those of
+          // the remainder, the rest), so three bf16 products give P V with exact
+          // partial products and float32 accumulation.
+          const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll
-            for (int g0 = 0; g0 < 4; g0 += 2) {
-              const uint16_t* tb = vst + wid * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
+          for (int g0 = 0; g0 < 4; g0 += 2) {
+            uint32_t ph[8], pm[8], pl[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float x = s[u][4 * g0 + i];
+              const uint32_t h = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
+              const float r1 = x - __builtin_bit_cast(float, h);
+              const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+              ph[i] = h;
+              pm[i] = m;
+              pl[i] = __builtin_bit_cast(uint32_t, r1 - __builtin_bit_cast(float, m));
+            }
+            u32x4 ah, am, al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ah[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
+              am[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
+              al[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
+            }
+#pragma unroll
+            for (int f = 0; f < FC; ++f) {
+              const uint16_t* tb = vst + f * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
               const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
               const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
               const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
-              uint32_t ph[8], pm[8], pl[8];
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const float x = s[u][4 * g0 + i];
-                const uint32_t h = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
-                const float r1 = x - __builtin_bit_cast(float, h);
-                const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
-                ph[i] = h;
-                pm[i] = m;
-                pl[i] = __builtin_bit_cast(uint32_t, r1 - __builtin_bit_cast(float, m));
-              }
-              u32x4 ah, am, al;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                ah[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
-                am[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
-                al[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
-              }
-              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o, 0, 0, 0);
-              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o, 0, 0, 0);
-              o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o, 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o[f], 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o[f], 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o[f], 0, 0, 0);
             }
+          }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       } else if (kt < ntk) {
-        float vv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * kt + tile_row(r, half);
-          vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+        for (int f = 0; f < FC; ++f) {
+          const int feat = 32 * (fc + f) + ql;
+          const bool fvalid = feat < d;
+          float vv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * kt + tile_row(r, half);
+            vv[r] = (j < n && fvalid) ? load_v<VF32>(a.v, (bh * n + j) * d + feat) : 0.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[f] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o[f], 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o = __builtin_amdgcn_mfma_f32_32x32x2f32(s[u][r], vv[r], o, 0, 0, 0);
       }
       // no instruction moves across tiles (the register budget holds one tile's operands)
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();  // the previous tile's partials are consumed (and rinvz is written)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[r];
-    __syncthreads();
-    for (int e = tid; e < 1024; e += C::kThreads) {
-      const int row = e >> 5, f = e & 31;
-      const int i = q0 + row, fe = 32 * ft + f;
-      if (i < n && fe < d) {
-        float val = 0.0f;
+    for (int f = 0; f < FC; ++f) {
+      const int ft = fc + f;
+      // every wave is past its V reads and the previous block's partials are consumed
+      // (and rinvz is written)
+      __syncthreads();
 #pragma unroll
-        for (int w = 0; w < C::kWaves; ++w) val += part[1024 * w + e];
-        a.out[(bh * n + i) * d + fe] = val * rinvz[row];
+      for (int r = 0; r < 16; ++r) part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[f][r];
+      __syncthreads();
+      for (int e = tid; e < 1024; e += C::kThreads) {
+        const int row = e >> 5, fo = e & 31;
+        const int i = q0 + row, fe = 32 * ft + fo;
+        if (i < n && fe < d) {
+          float val = 0.0f;
+#pragma unroll
+          for (int w = 0; w < C::kWaves; ++w) val += part[1024 * w + e];
+          a.out[(bh * n + i) * d + fe] = val * rinvz[row];
+        }
       }
     }
+    if (fc + FC < NFT) __syncthreads();  // the partials are read before the next pass stages V over them
   }
 }
 
