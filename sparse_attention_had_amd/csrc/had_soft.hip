@@ -349,7 +349,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int kend = a.causal ? min(n, q0 + 32) : n;
   const int ntk = (kend + 31) / 32;  // key tiles some row of the block sees
 
-  for (int e = tid; e < 32 * kHistStride; e += C::kThreads) hist[e] = 0u;
+  static_assert((32 * kHistStride) % 4 == 0, "histogram rows clear in 16-byte pieces");
+  for (int e = tid; e < 8 * kHistStride; e += C::kThreads) reinterpret_cast<uint4*>(hist)[e] = uint4{0u, 0u, 0u, 0u};
   if (tid == 0) st_done = 0;
   // the block's 32 soft query rows B_c(q) (the B operand of every logit tile)
   {
