@@ -448,6 +448,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       key[u][r] = (kt < ntk && j < lim) ? order_key(s[u][r]) : 0u;
     }
   }
+  // the row maximum (the largest key, always kept): each wave's partial goes to LDS
+  // here, and the first level's barrier publishes it
+  {
+    uint32_t mk = 0;
+#pragma unroll
+    for (int u = 0; u < C::kTiles; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mk = max(mk, key[u][r]);
+    mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), 32)));
+    if (!MASK && half == 0) redk[wid][ql] = mk;
+  }
   if (!select_level<0, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
       !select_level<1, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
       !select_level<2, NW>(key, hist, st_key, st_idx, st_need, &st_done, wid, lane, ntk) &&
@@ -476,15 +487,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     return;
   }
 
-  // ---- row maximum (the largest key, always kept), weights, Z
-  uint32_t mk = 0;
-#pragma unroll
-  for (int u = 0; u < C::kTiles; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mk = max(mk, key[u][r]);
-  mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), 32)));
-  if (half == 0) redk[wid][ql] = mk;
-  __syncthreads();
+  // ---- weights and Z (the row maximum's partials are in redk since the first level)
   uint32_t rk = redk[0][ql];
 #pragma unroll
   for (int w = 1; w < C::kWaves; ++w) rk = max(rk, redk[w][ql]);
