@@ -333,7 +333,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ int st_done;                // rows whose threshold is found
   __shared__ float red[C::kWaves][32];
   __shared__ uint32_t redk[C::kWaves][32];
-  __shared__ float rinvz[32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -434,7 +433,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       __builtin_amdgcn_sched_barrier(0);  // one tile's key rows in registers at a time
     }
   }
-  __syncthreads();
+  // (no barrier here: the first level's barriers order the row state written above)
 
   // ---- exact top-N: radix select over (logit key, inverted index)
   // order keys of the logits, 0 for the keys this row does not see
@@ -509,14 +508,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
   }
   z += __shfl_xor(z, 32);
-  if (half == 0) red[wid][ql] = z;
-  __syncthreads();
-  if (tid < 32) {
-    float Z = 0.0f;
-#pragma unroll
-    for (int w = 0; w < C::kWaves; ++w) Z += red[w][tid];
-    rinvz[tid] = Z > 0.0f ? 1.0f / Z : 0.0f;
-  }
+  if (half == 0) red[wid][ql] = z;  // summed after the first barrier of the P V reduction
 
   // ---- out = P V / Z: passes over the key tiles, FC 32-feature blocks per pass (each
   // weight split once per pass), the waves' partials summed in LDS after each pass
@@ -548,6 +540,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
   };
   uint4 pv[2 * FC];
+  float rz[1024 / C::kThreads];  // 1 / Z of the rows this thread writes
 #pragma unroll
   for (int fc = 0; fc < NFT; fc += FC) {
     v16f o[FC];
@@ -640,20 +633,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int f = 0; f < FC; ++f) {
       const int ft = fc + f;
-      // every wave is past its V reads and the previous block's partials are consumed
-      // (and rinvz is written)
-      __syncthreads();
+      // a wave's partials take the LDS its own V tiles took, so only a later block
+      // waits for the previous block's partials to be consumed
+      if (f > 0) __syncthreads();
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[f][r];
-      __syncthreads();
-      for (int e = tid; e < 1024; e += C::kThreads) {
+      __syncthreads();  // (before the first block it also publishes the waves' Z partials)
+#pragma unroll
+      for (int it = 0; it < 1024 / C::kThreads; ++it) {
+        const int e = tid + it * C::kThreads;
         const int row = e >> 5, fo = e & 31;
         const int i = q0 + row, fe = 32 * ft + fo;
+        if (ft == 0) {  // this thread's rows are the same in every block
+          float Z = 0.0f;
+#pragma unroll
+          for (int w = 0; w < C::kWaves; ++w) Z += red[w][row];
+          rz[it] = Z > 0.0f ? 1.0f / Z : 0.0f;
+        }
         if (i < n && fe < d) {
           float val = 0.0f;
 #pragma unroll
           for (int w = 0; w < C::kWaves; ++w) val += part[1024 * w + e];
-          a.out[(bh * n + i) * d + fe] = val * rinvz[row];
+          a.out[(bh * n + i) * d + fe] = val * rz[it];
         }
       }
     }
