@@ -334,6 +334,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ float red[C::kWaves][32];
   __shared__ uint32_t redk[C::kWaves][32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
+  // d <= 64 with 8 waves: the second feature block's partials (both blocks reduced after one
+  // barrier; the work-groups of this size are held to two per CU by registers, not LDS)
+  constexpr bool kPart1 = !MASK && !VF32 && NW == 8 && DP == 64;
+  __shared__ __attribute__((aligned(16))) float part1[kPart1 ? NW * 1024 : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -511,8 +515,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (half == 0) red[wid][ql] = z;  // summed after the first barrier of the P V reduction
 
   // ---- out = P V / Z: passes over the key tiles, FC 32-feature blocks per pass (each
-  // weight split once per pass), the waves' partials summed in LDS after each pass
-  constexpr int FC = NFT < 2 ? NFT : 2;
+  // weight split once per pass), the waves' partials summed in LDS after each pass.  fp32
+  // V takes one block per pass: it has no splits to share, and a second block's
+  // accumulators and V rows would not fit the register budget.
+  constexpr int FC = VF32 ? 1 : (NFT < 2 ? NFT : 2);
+  static_assert(!kPart1 || FC == 2, "the one-barrier reduction takes two blocks");
   float* part = reinterpret_cast<float*>(hist);  // [waves][32 rows][32 features]
   static_assert(C::kWaves * 1024 <= 32 * kHistStride, "partials and V tiles fit the histogram area");
   // bf16 V tiles are staged in the histogram area as well (free once the select is
@@ -630,6 +637,35 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       // no instruction moves across tiles (the register budget holds one tile's operands)
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kPart1) {
+      // one pass, blocks 0 (in the histogram area) and 1 (in part1) at once
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        part[wid * 1024 + tile_row(r, half) * 32 + ql] = o[0][r];
+        part1[wid * 1024 + tile_row(r, half) * 32 + ql] = o[1][r];
+      }
+      __syncthreads();  // (it also publishes the waves' Z partials)
+#pragma unroll
+      for (int it = 0; it < 1024 / C::kThreads; ++it) {
+        const int e = tid + it * C::kThreads;
+        const int row = e >> 5, fo = e & 31;
+        const int i = q0 + row;
+        float Z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < C::kWaves; ++w) Z += red[w][row];
+        const float rzi = Z > 0.0f ? 1.0f / Z : 0.0f;
+        if (i < n) {
+          float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+          for (int w = 0; w < C::kWaves; ++w) {
+            v0 += part[1024 * w + e];
+            v1 += part1[1024 * w + e];
+          }
+          if (fo < d) a.out[(bh * n + i) * d + fo] = v0 * rzi;
+          if (32 + fo < d) a.out[(bh * n + i) * d + 32 + fo] = v1 * rzi;
+        }
+      }
+    } else {
 #pragma unroll
     for (int f = 0; f < FC; ++f) {
       const int ft = fc + f;
@@ -657,6 +693,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
           a.out[(bh * n + i) * d + fe] = val * rz[it];
         }
       }
+    }
     }
     if (fc + FC < NFT) __syncthreads();  // the partials are read before the next pass stages V over them
   }
