@@ -34,7 +34,9 @@
 //     whole bin, and the levels stop once every row is.  bf16 V (d a multiple
 //     of 16): each wave stages its tile of 32 keys and up to 64 features (two
 //     32-feature blocks per pass over the tiles) in LDS with 16-byte loads, in
-//     the histogram area the select no longer needs, and reads the operand back
+//     the histogram area the select no longer needs (at d = 64 by asynchronous
+//     global -> LDS copies into two buffers, the next tile's copies running
+//     during the current tile's products), and reads the operand back
 //     transposed (ds_read_b64_tr_b16); each float32 weight is split exactly into
 //     three bf16 values, once per tile and pass, for v_mfma_f32_32x32x16_bf16.
 //     fp32 V: the weights straight from the logit registers and V rows from L2
@@ -156,6 +158,7 @@ struct SoftArgs {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -334,8 +337,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   __shared__ float red[C::kWaves][32];
   __shared__ uint32_t redk[C::kWaves][32];
   __shared__ __attribute__((aligned(16))) float qlds[32 * (DP + 4)];
-  // d <= 64 with 8 waves: the second feature block's partials (both blocks reduced after one
-  // barrier; the work-groups of this size are held to two per CU by registers, not LDS)
+  // d = 64 with 8 waves and bf16 V: the second buffer of the V tiles, then the second feature
+  // block's partials (both blocks reduced after one barrier; the work-groups of this size are
+  // held to two per CU by registers, not LDS)
   constexpr bool kPart1 = !MASK && !VF32 && NW == 8 && DP == 64;
   __shared__ __attribute__((aligned(16))) float part1[kPart1 ? NW * 1024 : 4];
 
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // .. + 15 of the wave's tile for each block f of the pass (two 16-byte loads per block,
   // rows clamped to n - 1, features past d read as zeros).  The loads are not issued a
   // tile ahead: holding them across the products spills registers (the other waves of
-  // the SIMD cover their latency).
+  // the SIMD cover their latency; at d = 64 the copies below need no registers).
   auto vload = [&](int fc, int u, uint4 (&pv)[2 * FC]) {
     const int kt = wid + C::kWaves * u;
     const int key = min(32 * kt + (lane >> 1), n - 1);
@@ -548,6 +552,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   };
   uint4 pv[2 * FC];
   float rz[1024 / C::kThreads];  // 1 / Z of the rows this thread writes
+  // bf16 V with d = 64 and 8 waves: asynchronous global -> LDS copies (16 bytes per lane,
+  // lane-ordered, no registers held), tile u in buffer u % 2 (the wave's 4 KB of the
+  // histogram area, or of part1).  Copy i of block f holds keys 16 i .. 16 i + 15: lane L
+  // brings key 16 i + L / 4, features 32 f + 8 (L % 4) .. + 7 (past d: feature 0, read
+  // only by output columns that are dropped).  Tile u + 1 is requested right after tile
+  // u's operands are read, so its copies run during tile u's products.
+  auto vdma = [&](int uu) {
+    const int kt2 = wid + C::kWaves * uu;
+    if (kt2 < ntk) {
+      uint16_t* db = (uu & 1) ? reinterpret_cast<uint16_t*>(part1) + wid * 2048 : vst;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int key = min(32 * kt2 + 16 * i + (lane >> 2), n - 1);
+          const int fe0 = 32 * f + 8 * (lane & 3);
+          const int fe = fe0 < d ? fe0 : 0;
+          __builtin_amdgcn_global_load_lds(static_cast<const uint16_t*>(a.v) + (bh * n + key) * d + fe,
+                                           (lds_void*)(db + f * 1024 + i * 512), 16, 0, 0);
+        }
+    }
+  };
 #pragma unroll
   for (int fc = 0; fc < NFT; fc += FC) {
     v16f o[FC];
@@ -556,14 +582,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int u = 0; u < C::kTiles; ++u) {
       const int kt = wid + C::kWaves * u;
+      uint16_t* vb = vst;  // this tile's staged V
       if (vlds) {
-        vload(fc, u, pv);
-        if (kt < ntk) {
+        if constexpr (kPart1) {
+          if (u == 0) vdma(0);
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: tile u has landed
+          if (u & 1) vb = reinterpret_cast<uint16_t*>(part1) + wid * 2048;
+        } else {
+          vload(fc, u, pv);
+          if (kt < ntk) {
 #pragma unroll
-          for (int f = 0; f < FC; ++f) {
-            uint16_t* dst = vst + f * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
-            *reinterpret_cast<uint4*>(dst) = pv[2 * f];
-            *reinterpret_cast<uint4*>(dst + 8) = pv[2 * f + 1];
+            for (int f = 0; f < FC; ++f) {
+              uint16_t* dst = vst + f * 1024 + (lane >> 1) * 32 + 16 * (lane & 1);
+              *reinterpret_cast<uint4*>(dst) = pv[2 * f];
+              *reinterpret_cast<uint4*>(dst + 8) = pv[2 * f + 1];
+            }
           }
         }
         // one wave writes and reads its own tile: LDS keeps a wave's operations in
@@ -584,6 +617,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
           // the remainder, the rest), so three bf16 products give P V with exact
           // partial products and float32 accumulation.
           const int G = lane >> 4, kk = (lane >> 2) & 3, qq = lane & 3;
+          v8bf bv[2][FC];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int f = 0; f < FC; ++f) {
+              const uint16_t* tb = vb + f * 1024 + (16 * g + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
+              const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
+              const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
+              bv[g][f] = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+          if constexpr (kPart1) {
+            if (u + 1 < C::kTiles) vdma(u + 1);  // into the other buffer, during this tile's products
+          }
 #pragma unroll
           for (int g0 = 0; g0 < 4; g0 += 2) {
             uint32_t ph[8], pm[8], pl[8];
@@ -606,13 +652,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
             }
 #pragma unroll
             for (int f = 0; f < FC; ++f) {
-              const uint16_t* tb = vst + f * 1024 + (8 * g0 + 4 * (G >> 1) + kk) * 32 + 16 * (G & 1) + 4 * qq;
-              const v4s ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tb);
-              const v4s rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tb + 8 * 32));
-              const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
-              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv, o[f], 0, 0, 0);
-              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv, o[f], 0, 0, 0);
-              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv, o[f], 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bv[g0 / 2][f], o[f], 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, am), bv[g0 / 2][f], o[f], 0, 0, 0);
+              o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bv[g0 / 2][f], o[f], 0, 0, 0);
             }
           }
         }
