@@ -157,6 +157,12 @@ CASES = [
     ((1, 1, 100, 32), 12, 0.6, False, "bf16", 16),
     ((2, 1, 150, 48), 30, 0.9, True, "bf16", 17),
     ((1, 1, 600, 128), 70, 0.5, True, "f32", 18),
+    # 8-wave work-groups with bf16 V: d = 64 takes the asynchronous V copies (causal and
+    # ragged: tiles past the diagonal are skipped), d = 48 clamps the copies' features past d,
+    # d = 32 stages V through registers
+    ((1, 2, 700, 64), 90, 0.6, True, "bf16", 19),
+    ((1, 1, 520, 48), 64, 0.5, False, "bf16", 20),
+    ((1, 1, 400, 32), 50, 0.7, True, "bf16", 21),
 ]
 
 
